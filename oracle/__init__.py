@@ -1,0 +1,33 @@
+"""CPU oracle for one EAGLE-2 draft-and-verify cycle.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously correct
+statement of what the hot path computes, written from the pages' description
+of EAGLE-2 in numpy (fp64 for floating point, except where the method's own
+definition fixes a narrower type: cumulative tree values are single fp32
+additions, and sampling decisions are taken in fp64).  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  It shares no code with the HIP path in
+``speculative_decoding_parent_amd`` and imports nothing from it; the product
+path never calls it.
+
+Sources (the pages):
+  * "EAGLE-2: Feature-Level Speculative Decoding Guide" (aifetchly blog),
+    Key Architectural Mechanics sections 1-3 and the Reference Implementation
+    listing;
+  * "Support Eagle-3 Speculative Decoding in llama.cpp" (llama.cpp discussion
+    #15902), the opening post and the yuhuili/EAGLE3-LLaMA3.1-Instruct-8B
+    module printout;
+  * "EAGLE-2 Speculative Decoding Support for llama.cpp - Phase 1" (llama.cpp
+    PR #13908), Implementation Characteristics (single-sequence inference).
+
+Parity status: every function here is pinned by tests under ``tests/`` marked
+``not gpu`` (closed forms, library routines on special cases, brute force on
+tiny inputs, invariants the pages state).  No function is parity unpinned.
+"""
+from .mask import build_tree_mask, mask_bits, mask_popcount  # noqa: F401
+from .attention import tree_attention  # noqa: F401
+from .lmhead import lm_head_logits, softmax_stats, topk_ids, lm_head_topk, confidence_ratio  # noqa: F401
+from .tree import Pool, expand, rerank  # noqa: F401
+from .accept import accept_greedy, accept_sample  # noqa: F401
+from .layer import rms_norm, rope, silu, decoder_layer, LayerWeights  # noqa: F401
+from .cycle import CycleWeights, draft_and_verify_cycle  # noqa: F401

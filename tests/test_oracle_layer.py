@@ -1,0 +1,162 @@
+"""Pins of the oracle's decoder layer pieces and of the full cycle."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle.cycle import CycleWeights, draft_and_verify_cycle
+from oracle.layer import LayerWeights, decoder_layer, rms_norm, rope, silu
+from oracle.mask import build_tree_mask
+from speculative_decoding_parent_amd import inputs
+
+
+def test_rms_norm_matches_library():
+    g = inputs.rng(1, 0)
+    x = inputs.normal(g, (6, 48), dtype=torch.float32)
+    w = inputs.normal(g, (48,), dtype=torch.float32)
+    ref = F.rms_norm(x.double(), (48,), w.double(), eps=1e-5)
+    np.testing.assert_allclose(rms_norm(x, w, 1e-5), ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_silu_matches_library():
+    x = torch.linspace(-30, 30, 1001, dtype=torch.float64)
+    np.testing.assert_allclose(silu(x), F.silu(x).numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_rope_is_complex_rotation():
+    g = inputs.rng(2, 0)
+    hd = 16
+    x = g.standard_normal((5, 3, hd))
+    pos = np.array([0, 1, 7, 4096, 32768])
+    got = rope(x, pos, 500000.0)
+    z = x[..., :hd // 2] + 1j * x[..., hd // 2:]
+    w = np.exp(1j * pos[:, None, None] * 500000.0 ** (-np.arange(hd // 2) * 2 / hd))
+    r = z * w
+    np.testing.assert_allclose(got, np.concatenate([r.real, r.imag], -1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[0], x[0], rtol=0, atol=0)              # position 0: identity
+    np.testing.assert_allclose(np.linalg.norm(got, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    # dot products depend only on the position difference
+    q, k = g.standard_normal(hd), g.standard_normal(hd)
+    d1 = rope(q[None, None], [10])[0, 0] @ rope(k[None, None], [3])[0, 0]
+    d2 = rope(q[None, None], [107])[0, 0] @ rope(k[None, None], [100])[0, 0]
+    assert abs(d1 - d2) < 1e-12
+
+
+def rand_layer(g, d, hq, hkv, hd, ff):
+    n = lambda *s: inputs.normal(g, s, std=float(1 / np.sqrt(s[-1])), dtype=torch.float32)
+    return LayerWeights(norm1=1 + 0.1 * inputs.normal(g, (d,), dtype=torch.float32),
+                        wq=n(hq * hd, d), wk=n(hkv * hd, d), wv=n(hkv * hd, d), wo=n(d, hq * hd),
+                        norm2=1 + 0.1 * inputs.normal(g, (d,), dtype=torch.float32),
+                        wgate=n(ff, d), wup=n(ff, d), wdown=n(d, ff))
+
+
+def torch_rope(x, pos, theta=500000.0):
+    """Rotate [n][H][hd] with torch complex numbers (library formulation)."""
+    hd = x.shape[-1]
+    inv = theta ** (-torch.arange(hd // 2, dtype=torch.float64) * 2 / hd)
+    ang = torch.as_tensor(pos, dtype=torch.float64)[:, None] * inv
+    z = torch.complex(x[..., :hd // 2], x[..., hd // 2:]) * torch.polar(torch.ones_like(ang), ang)[:, None]
+    return torch.cat([z.real, z.imag], -1)
+
+
+def torch_layer_causal(x, w, pos, hq, hkv, hd, kc, vc, eps=1e-5):
+    """A Llama layer over a chain of rows after a prefix, from torch library
+    ops (causal SDPA), to pin the oracle's tree layer on the chain case."""
+    dd = lambda t: torch.as_tensor(t).double()
+    n = x.shape[0]
+    L = kc.shape[1]
+    h = F.rms_norm(x, (x.shape[1],), dd(w.norm1), eps=eps)
+    q = torch_rope(F.linear(h, dd(w.wq)).view(n, hq, hd), pos)
+    k = torch_rope(F.linear(h, dd(w.wk)).view(n, hkv, hd), pos)
+    v = F.linear(h, dd(w.wv)).view(n, hkv, hd)
+    G = hq // hkv
+    keys = torch.cat([dd(kc), k.permute(1, 0, 2)], 1).repeat_interleave(G, 0)
+    vals = torch.cat([dd(vc), v.permute(1, 0, 2)], 1).repeat_interleave(G, 0)
+    allowed = torch.ones(n, L + n, dtype=torch.bool)
+    allowed[:, L:] = torch.tril(torch.ones(n, n, dtype=torch.bool))
+    a = F.scaled_dot_product_attention(q.permute(1, 0, 2)[:, None], keys[:, None], vals[:, None],
+                                       attn_mask=allowed)[:, 0].permute(1, 0, 2)
+    x2 = x + F.linear(a.reshape(n, hq * hd), dd(w.wo))
+    h2 = F.rms_norm(x2, (x.shape[1],), dd(w.norm2), eps=eps)
+    return x2 + F.linear(F.silu(F.linear(h2, dd(w.wgate))) * F.linear(h2, dd(w.wup)), dd(w.wdown))
+
+
+def test_layer_chain_matches_library_layer():
+    g = inputs.rng(3, 0)
+    d, hq, hkv, hd, ff, L, n = 32, 4, 2, 8, 48, 6, 5
+    w = rand_layer(g, d, hq, hkv, hd, ff)
+    x = inputs.normal(g, (n, d), dtype=torch.float32).double()
+    kc = inputs.normal(g, (hkv, L, hd), dtype=torch.float32)
+    vc = inputs.normal(g, (hkv, L, hd), dtype=torch.float32)
+    pos = np.arange(L, L + n)
+    mask, _ = build_tree_mask(inputs.chain_tree(n))
+    zeros = np.zeros((hkv, n, hd))
+    out, kt, vt = decoder_layer(x, w, pos, hq, hkv, hd, kc, vc, L, zeros, zeros, list(range(n)),
+                                mask, list(range(n)))
+    ref = torch_layer_causal(x, w, pos, hq, hkv, hd, kc, vc)
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-11)
+
+
+# ----------------------------------------------------------------- cycle
+
+def small_cycle_weights(seed, d, hq, hkv, hd, ff, V, L):
+    g = inputs.rng(seed, 0)
+    n = lambda *s: inputs.normal(g, s, std=float(1 / np.sqrt(s[-1])), dtype=torch.float32)
+    return CycleWeights(
+        w_fuse=n(d, 2 * d), draft=rand_layer(g, d, hq, hkv, hd, ff),
+        draft_norm=torch.ones(d), embed=inputs.normal(g, (V, d), dtype=torch.float32),
+        w_lm=inputs.normal(g, (V, d), std=float(4 / np.sqrt(d)), dtype=torch.float32),
+        target=rand_layer(g, d, hq, hkv, hd, ff), target_norm=torch.ones(d),
+        draft_k_cache=inputs.normal(g, (hkv, L, hd), dtype=torch.float32),
+        draft_v_cache=inputs.normal(g, (hkv, L, hd), dtype=torch.float32),
+        target_k_cache=inputs.normal(g, (hkv, L, hd), dtype=torch.float32),
+        target_v_cache=inputs.normal(g, (hkv, L, hd), dtype=torch.float32))
+
+
+def test_chain_cycle_follows_listing_loop():
+    """k = k_select = 1: the draft is the Reference Implementation's loop —
+    pair the feature with the token it predicted, step the layer (causal over
+    prefix + chain), take the argmax — computed here with torch library ops."""
+    d, hq, hkv, hd, ff, V, L, R = 32, 4, 2, 8, 48, 50, 5, 5
+    cw = small_cycle_weights(4, d, hq, hkv, hd, ff, V, L)
+    g = inputs.rng(4, 1)
+    f0 = inputs.normal(g, (d,), dtype=torch.float32)
+    y0 = 7
+    res = draft_and_verify_cycle(cw, y0, f0, hq=hq, hkv=hkv, hd=hd, L=L, rounds=R, k=1,
+                                 k_select=1, T=R + 1, temperature=1.0,
+                                 uniforms=inputs.uniforms(g, 2 * (R + 1)))
+    dd = lambda t: torch.as_tensor(t).double()
+    f, y = dd(f0), y0
+    xs, toks = [], [y0]
+    for step in range(R):
+        xs.append(F.linear(torch.cat([f, dd(cw.embed)[y]]), dd(cw.w_fuse)))
+        out = torch_layer_causal(torch.stack(xs), cw.draft, np.arange(L, L + len(xs)), hq, hkv, hd,
+                                 cw.draft_k_cache, cw.draft_v_cache)[-1]
+        z = F.rms_norm(out, (d,), dd(cw.draft_norm), eps=1e-5)
+        y = int(torch.argmax(F.linear(z, dd(cw.w_lm))))
+        f = out
+        toks.append(y)
+    assert res["node_token"].tolist() == toks
+    assert res["node_parent"].tolist() == list(range(-1, R))
+
+
+def test_tree_cycle_structure():
+    d, hq, hkv, hd, ff, V, L = 32, 4, 2, 8, 48, 60, 6
+    R, k, ks, T = 4, 4, 3, 16
+    cw = small_cycle_weights(5, d, hq, hkv, hd, ff, V, L)
+    g = inputs.rng(5, 1)
+    res = draft_and_verify_cycle(cw, 3, inputs.normal(g, (d,), dtype=torch.float32), hq=hq, hkv=hkv,
+                                 hd=hd, L=L, rounds=R, k=k, k_select=ks, T=T, temperature=0.7,
+                                 uniforms=inputs.uniforms(g, 2 * T))
+    assert len(res["pool"]) == 1 + k + (R - 1) * ks * k
+    par, dep = res["node_parent"], res["node_depth"]
+    assert par[0] == -1 and all(0 <= par[i] < i for i in range(1, T))
+    assert all(dep[i] == dep[par[i]] + 1 for i in range(1, T)) and dep.max() <= R
+    for r in res["rounds"]:
+        # each round's frontier are children of that round's rows, in ascending pool order
+        assert r["frontier"] == sorted(r["frontier"])
+    path = res["path"]
+    assert path[0] == 0 and all(par[b] == a for a, b in zip(path, path[1:]))
+    assert 0 <= res["bonus"] < V
