@@ -1,0 +1,247 @@
+/*
+ * eagle.h - C ABI of the EAGLE-2 draft-and-verify hot path for AMD MI355X
+ * (gfx950).
+ *
+ * One cycle of EAGLE-2 speculative decoding over a dynamic draft tree:
+ * build the tree's ancestor mask, run tree-masked attention of the tree nodes
+ * against a KV prefix, project features through the LM head with softmax
+ * statistics and top-k, grow and prune the tree by cumulative log-probability,
+ * and accept the longest verified path (greedy, or speculative sampling).
+ *
+ * The method is described on the pages
+ *   [G] "EAGLE-2: Feature-Level Speculative Decoding Guide" (aifetchly blog),
+ *   [D] "Support Eagle-3 Speculative Decoding in llama.cpp" (discussion #15902),
+ *   [P] "EAGLE-2 Speculative Decoding Support for llama.cpp - Phase 1"
+ *       (PR #13908).
+ * Each entry point below names the passage that defines its operation.
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a DEVICE pointer unless marked (host).  The caller owns
+ *     all memory; the library never allocates, frees or keeps a pointer after
+ *     the call returns.  Workspaces are caller-provided scratch whose size the
+ *     matching *_workspace() query returns; their contents need no
+ *     initialisation and are garbage afterwards.
+ *   - Single sequence (batch 1), as [P] "Implementation Characteristics"
+ *     states.
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns EAGLE_EINVAL (or EAGLE_EUNSUPPORTED for a valid shape
+ *     this build does not implement) and enqueues nothing.
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without synchronising.  A launch failure returns EAGLE_EHIP.
+ *   - Errors in device data (a parent that is not an earlier node, a token
+ *     outside [0, V), ...) cannot be seen on the host; kernels OR an
+ *     EAGLE_DEV_* bit into *dev_status when dev_status is non-null and then
+ *     finish with a defined (but meaningless) output.  dev_status is never
+ *     cleared by the library.
+ *   - Calls keep no global state and are reentrant; calls on different streams
+ *     may overlap if their buffers do not.
+ *   - Element types: EAGLE_BF16 = bfloat16 (round-to-nearest-even), EAGLE_F32.
+ *     Accumulation is always fp32.
+ */
+#ifndef EAGLE_H_
+#define EAGLE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EAGLE_ABI_VERSION 1
+
+typedef enum {
+  EAGLE_OK = 0,
+  EAGLE_EINVAL = -1,        /* bad argument (null pointer, size, alignment)  */
+  EAGLE_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. hd = 96)      */
+  EAGLE_EWORKSPACE = -3,    /* workspace smaller than the query's answer     */
+  EAGLE_EHIP = -4           /* a HIP launch or runtime call failed           */
+} eagle_status;
+
+typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
+
+enum { EAGLE_EXPAND = 0, EAGLE_RERANK = 1 };
+enum { EAGLE_GREEDY = 0, EAGLE_SAMPLE = 1 };
+
+/* Bits OR-ed into *dev_status by kernels. */
+enum {
+  EAGLE_DEV_BAD_PARENT = 1,     /* parents[i] not -1 and not in [0, i)        */
+  EAGLE_DEV_BAD_ROOT = 2,       /* node 0 not the single root (acceptance)    */
+  EAGLE_DEV_BAD_TOKEN = 4,      /* token outside [0, V)                       */
+  EAGLE_DEV_BAD_INDEX = 8,      /* frontier / mask-row index out of range     */
+  EAGLE_DEV_ORPHAN = 16,        /* rerank kept an entry without its parent    */
+  EAGLE_DEV_PATH_TRUNC = 32     /* accepted path longer than max_path         */
+};
+
+/* Limits of this build. */
+#define EAGLE_MAX_TREE 256      /* T, Tk: tree nodes per call (words <= 4)    */
+#define EAGLE_MAX_TOPK 64       /* k of eagle_lmhead_topk                     */
+#define EAGLE_MAX_POOL 8192     /* candidate-pool entries of expand/rerank    */
+#define EAGLE_MAX_APPEND 4096   /* kf * k entries appended by one EXPAND      */
+
+int eagle_abi_version(void);
+const char* eagle_status_string(int status);   /* static string, never NULL */
+
+/*
+ * eagle_build_tree_mask - ancestor-only visibility of a draft tree.
+ *
+ * [G] Key Architectural Mechanics 3 (Single-Pass Tree Verification): a tree
+ * token attends to the tokens on its own branch and never to another branch;
+ * a node also sees itself, so a chain gives the causal mask ([G] section 1).
+ *
+ *   parents  int32[T]       parent of node i, -1 for a root; a valid parent
+ *                           precedes its child (parents[i] < i).  Several
+ *                           roots (a forest) are allowed here.
+ *   T        1..256         nodes.
+ *   words    >= ceil(T/64), <= 4: uint64 words per mask row.
+ *   mask     uint64[T][words] out: bit (j % 64) of word (j / 64) of row i is
+ *                           set iff node j is i or an ancestor of i; bits >= T
+ *                           are zero.
+ *   depth    int32[T]       out: edges from i to its root.
+ *   dev_status int32[1] or NULL: EAGLE_DEV_BAD_PARENT on a bad parent (the
+ *                           walk stops there).
+ */
+int eagle_build_tree_mask(const int32_t* parents, int32_t T, int32_t words,
+                          uint64_t* mask, int32_t* depth, int32_t* dev_status,
+                          hipStream_t stream);
+
+/*
+ * eagle_tree_attn - tree-masked attention of tree nodes against a KV prefix.
+ *
+ * [G] Key Architectural Mechanics 3: the target scores every tree node in one
+ * batched pass under the tree mask.  [D] LlamaAttention printout: grouped-
+ * query attention (q 4096 -> 32 heads, k/v 4096 -> 8 heads of 128).
+ *
+ * For query row i and head h (KV head g = h / (Hq / Hkv)):
+ *   visible = prefix positions 0..L-1, plus tree nodes j < Tk whose bit is set
+ *             in mask row m(i) (m(i) = q_mask_row[i], or i when NULL);
+ *   out[i][h] = sum_j softmax_j(scale * q[i][h] . k_j) v_j over visible j.
+ *
+ *   q        [Tq][Hq][hd] in_dt (RoPE already applied).
+ *   k_cache, v_cache [Hkv][ld_cache][hd] in_dt, rows 0..L-1 used; L >= 0.
+ *   k_tree, v_tree   [Hkv][ld_tree][hd] in_dt, rows 0..Tk-1 used.
+ *   mask     uint64[mask_rows][words] (eagle_build_tree_mask layout).
+ *   q_mask_row int32[Tq] or NULL; entries outside [0, mask_rows) set
+ *            EAGLE_DEV_BAD_INDEX and the row sees the prefix only.
+ *   Tq 1..256, Tk 1..256, Hq % Hkv == 0, hd in {64, 128}; every row must see
+ *   at least one position (L > 0, or its own node in the tree).
+ *   scale    score scale (1/sqrt(hd) for standard attention).
+ *   in_dt    EAGLE_BF16 or EAGLE_F32; out_dt EAGLE_BF16 or EAGLE_F32.
+ *   out      [Tq][Hq][hd] out_dt.
+ *   workspace >= eagle_tree_attn_workspace(...) bytes, 256-byte aligned.
+ *   Rows of K/V, q and out must be 16-byte aligned (hd contiguous).
+ */
+size_t eagle_tree_attn_workspace(int32_t Tq, int32_t Hq, int32_t Hkv, int32_t hd,
+                                 int64_t L, int32_t Tk, eagle_dtype in_dt);
+int eagle_tree_attn(const void* q,
+                    const void* k_cache, const void* v_cache, int64_t L, int64_t ld_cache,
+                    const void* k_tree, const void* v_tree, int32_t Tk, int32_t ld_tree,
+                    const uint64_t* mask, int32_t words, int32_t mask_rows,
+                    const int32_t* q_mask_row, int32_t Tq,
+                    int32_t Hq, int32_t Hkv, int32_t hd, float scale,
+                    eagle_dtype in_dt, eagle_dtype out_dt, void* out,
+                    void* workspace, size_t ws_bytes, int32_t* dev_status,
+                    hipStream_t stream);
+
+/*
+ * eagle_lmhead_topk - LM head, softmax statistics and top-k.
+ *
+ * [G] Key Architectural Mechanics 1: P = softmax(W_LM f) with the target's own
+ * LM head; section 2: the confidence C = P(y_(1))/P(y_(2)) of the two most
+ * likely tokens, which equals exp(topk_logp[t][0] - topk_logp[t][1]).
+ * [D] printout: no bias.
+ *
+ *   f        [T][d] dt, row t is one feature (final norm already applied).
+ *   W        [V][d] dt, one row per vocabulary entry.
+ *   T 1..256, d % 128 == 0 (bf16) or any d >= 1 (f32), 1 <= k <= min(V, 64).
+ *   topk_id  int32[T][k] out: the k largest logits of row t, larger first,
+ *            the lower vocabulary index first among equal logits.
+ *   topk_logp f32[T][k] out: logit - lse (temperature 1).
+ *   lse      f32[T] out: log sum_v exp(logit[t][v]).
+ *   logits   f32[T][V] out, or NULL: the fp32 logits.
+ *   workspace >= eagle_lmhead_topk_workspace(...) bytes, 256-byte aligned.
+ */
+size_t eagle_lmhead_topk_workspace(int32_t T, int32_t d, int32_t V, int32_t k, eagle_dtype dt);
+int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
+                      int32_t k, eagle_dtype dt, int32_t* topk_id, float* topk_logp,
+                      float* lse, float* logits, void* workspace, size_t ws_bytes,
+                      hipStream_t stream);
+
+/*
+ * eagle_expand_rerank - grow the dynamic draft tree and prune it.
+ *
+ * [D] (reply on static vs dynamic trees): the draft's confidence approximates
+ * acceptance; the tree is grown from it and pruned at the end of drafting.
+ * [G] section 2: the token budget goes where confidence is high.  Reading:
+ * confidence = cumulative log-probability, value[child] =
+ * fp32(value[parent] + logp), root value 0; ties go to the lower pool index.
+ *
+ * The candidate pool is four parallel device arrays (token, parent, depth,
+ * value) of capacity pool_cap; entry 0 is the root.  pool_n (host) is the
+ * number of valid entries before this call.
+ *
+ * EXPAND: for frontier slot s < kf and child rank j < k (s-major) append
+ *   entry pool_n + s*k + j = {child_id[s][j], frontier[s],
+ *   depth[frontier[s]] + 1, fp32(value[frontier[s]] + child_logp[s][j])};
+ *   new_frontier[0..k_select) = the k_select best appended entries by
+ *   (value desc, index asc), in ascending pool index.
+ *   Needs pool_n + kf*k <= pool_cap, kf*k <= 4096, 1 <= k_select <= kf*k.
+ * RERANK: keep the root and the T-1 best non-root entries by (value desc,
+ *   index asc); write them in ascending pool index as node_token,
+ *   node_parent (index into this list, -1 for the root), node_depth and
+ *   node_pool_idx.  Needs 1 <= T <= min(pool_n, 256), pool_n <= 8192.
+ * Unused pointers of the other mode may be NULL.
+ */
+int eagle_expand_rerank(int32_t mode,
+                        int32_t* pool_token, int32_t* pool_parent, int32_t* pool_depth,
+                        float* pool_value, int32_t pool_n, int32_t pool_cap,
+                        const int32_t* frontier, int32_t kf,
+                        const int32_t* child_id, const float* child_logp, int32_t k,
+                        int32_t k_select, int32_t* new_frontier,
+                        int32_t T, int32_t* node_token, int32_t* node_parent,
+                        int32_t* node_depth, int32_t* node_pool_idx,
+                        int32_t* dev_status, hipStream_t stream);
+
+/*
+ * eagle_accept - accept the longest verified path through the tree.
+ *
+ * [G] Key Architectural Mechanics 3: a greedy or sampling verifier walks the
+ * tree from the root and accepts matching tokens until the first discrepancy;
+ * the output equals plain decoding.  [G] The Problem 1 and [D] opening post:
+ * speculative sampling's accept/reject rule (Leviathan et al., Chen et al.).
+ *
+ * Tree: node_token/node_parent int32[T], node 0 the single root, parents
+ * before children.
+ * GREEDY (target_top1 int32[T], the target's argmax at each node): node c
+ *   matches when node_token[c] == target_top1[parent(c)]; the path ends at
+ *   the deepest node whose whole root path matches (lowest index among equally
+ *   deep ones); bonus = target_top1[end].
+ * SAMPLE (target_logits f32[T][V], temperature > 0, uniforms f32[2T] in
+ *   [0,1)): at node u, p = exp((l_u - max l_u) / temperature) in fp64 and
+ *   Z_res = sum p minus the mass of tokens already rejected at u; children
+ *   in ascending index: a child whose token was rejected is rejected,
+ *   otherwise child c with token x is accepted iff uniforms[c] * Z_res < p[x]
+ *   (the walk moves to c), else x is rejected.  When all children are
+ *   rejected or u is a leaf, bonus = the smallest token i whose running sum of
+ *   non-rejected p exceeds uniforms[T + u] * Z_res.
+ *   workspace >= eagle_accept_workspace(T, V) bytes (SAMPLE only).
+ * Outputs: path int32[max_path] = node ids from the root (path[0] = 0), the
+ *   rest -1; n_accepted int32[1] = accepted draft nodes (path length - 1);
+ *   bonus_token int32[1].  A path longer than max_path is cut and sets
+ *   EAGLE_DEV_PATH_TRUNC.
+ */
+size_t eagle_accept_workspace(int32_t T, int32_t V);
+int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
+                 const int32_t* node_parent, const int32_t* target_top1,
+                 const float* target_logits, int32_t V, float temperature,
+                 const float* uniforms, int32_t max_path, int32_t* path,
+                 int32_t* n_accepted, int32_t* bonus_token,
+                 void* workspace, size_t ws_bytes, int32_t* dev_status,
+                 hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EAGLE_H_ */

@@ -19,7 +19,7 @@ sampling, the tree's tokens were chosen by top-k, so the draft distribution at
 a node is a point mass on each child's token: accepting child token x with
 probability min(1, p(x)/q(x)) becomes p_res(x), and the residual max(p - q, 0)
 becomes p with the rejected tokens removed (renormalised).  Sampling decisions
-are taken in fp64 from fp32 logits.
+are taken in fp64 from fp32 logits, fp32 uniforms and an fp32 temperature.
 
 Uniform layout: ``U[c]`` (c >= 1) is the accept test of node c, ``U[T + u]``
 the residual draw at node u; U[0] is unused.
@@ -113,6 +113,7 @@ def accept_sample(token, parent, logits, temperature: float, U, return_margin: b
     if not (temperature > 0 and np.isfinite(temperature)):
         raise ValueError("temperature must be positive and finite")
     U = np.asarray(U, dtype=np.float32).astype(np.float64)
+    temperature = np.float64(np.float32(temperature))   # an fp32 argument of the method
     kids = _children(parent)
     u = 0
     path = [0]

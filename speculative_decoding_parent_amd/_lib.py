@@ -1,0 +1,222 @@
+"""Python binding of the eagle.h C ABI (argument marshalling only).
+
+Every function here has the name of the C entry point it calls, takes torch
+tensors where the C call takes device pointers, and enqueues on torch's
+current HIP stream.  Output and workspace tensors may be passed in; when they
+are not, they are allocated with torch (device memory is the only thing torch
+provides).  Every step of the path runs in libeagle.so; if the library is
+missing this module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libeagle.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "eagle.h")
+
+EAGLE_OK, EAGLE_EINVAL, EAGLE_EUNSUPPORTED, EAGLE_EWORKSPACE, EAGLE_EHIP = 0, -1, -2, -3, -4
+EAGLE_F32, EAGLE_BF16 = 0, 1
+EAGLE_EXPAND, EAGLE_RERANK = 0, 1
+EAGLE_GREEDY, EAGLE_SAMPLE = 0, 1
+DEV_BAD_PARENT, DEV_BAD_ROOT, DEV_BAD_TOKEN, DEV_BAD_INDEX, DEV_ORPHAN, DEV_PATH_TRUNC = (
+    1, 2, 4, 8, 16, 32)
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_PROTOS = {
+    "eagle_abi_version": (_I32, []),
+    "eagle_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "eagle_build_tree_mask": (_I32, [_P, _I32, _I32, _P, _P, _P, _P]),
+    "eagle_tree_attn_workspace": (_SZ, [_I32, _I32, _I32, _I32, _I64, _I32, ctypes.c_int]),
+    "eagle_tree_attn": (_I32, [_P, _P, _P, _I64, _I64, _P, _P, _I32, _I32, _P, _I32, _I32, _P,
+                               _I32, _I32, _I32, _I32, _F32, ctypes.c_int, ctypes.c_int, _P, _P,
+                               _SZ, _P, _P]),
+    "eagle_lmhead_topk_workspace": (_SZ, [_I32, _I32, _I32, _I32, ctypes.c_int]),
+    "eagle_lmhead_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _P,
+                                 _SZ, _P]),
+    "eagle_expand_rerank": (_I32, [_I32, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32,
+                                   _P, _I32, _P, _P, _P, _P, _P, _P]),
+    "eagle_accept_workspace": (_SZ, [_I32, _I32]),
+    "eagle_accept": (_I32, [_I32, _I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ,
+                            _P, _P]),
+}
+
+_lib = None
+
+
+class EagleError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        msg = lib().eagle_status_string(code).decode() if _lib else str(code)
+        super().__init__(f"{fn} returned {code} ({msg})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libeagle.so once and declare every prototype."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m speculative_decoding_parent_amd.build`")
+        so = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            if hasattr(so, name):
+                fn = getattr(so, name)
+                fn.restype = res
+                fn.argtypes = args
+        _lib = so
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Names of the entry points declared in include/eagle.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*\s]+?)\b(eagle_\w+)\s*\(", text, re.M)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, rc: int):
+    if rc != EAGLE_OK:
+        raise EagleError(fn, rc)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return EAGLE_BF16
+    if t.dtype == torch.float32:
+        return EAGLE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- entry points
+
+def eagle_abi_version() -> int:
+    return lib().eagle_abi_version()
+
+
+def eagle_build_tree_mask(parents: torch.Tensor, words: Optional[int] = None,
+                          mask: Optional[torch.Tensor] = None, depth: Optional[torch.Tensor] = None,
+                          dev_status: Optional[torch.Tensor] = None):
+    """Returns (mask int64[T][words] holding the uint64 bit patterns, depth int32[T])."""
+    T = parents.shape[0]
+    words = (T + 63) // 64 if words is None else words
+    dev = parents.device
+    mask = torch.empty((T, words), dtype=torch.int64, device=dev) if mask is None else mask
+    depth = torch.empty(T, dtype=torch.int32, device=dev) if depth is None else depth
+    _check("eagle_build_tree_mask",
+           lib().eagle_build_tree_mask(_ptr(parents), T, words, _ptr(mask), _ptr(depth),
+                                       _ptr(dev_status), _stream()))
+    return mask, depth
+
+
+def eagle_tree_attn(q, k_cache, v_cache, L, k_tree, v_tree, Tk, mask, q_mask_row=None,
+                    scale=None, out_dtype=None, out=None, workspace=None, dev_status=None):
+    """q [Tq][Hq][hd]; caches [Hkv][ld][hd]; mask int64 [rows][words]."""
+    Tq, Hq, hd = q.shape
+    Hkv = k_tree.shape[0]
+    in_dt = _dt(q)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((Tq, Hq, hd), dtype=out_dtype, device=q.device)
+    scale = 1.0 / (hd ** 0.5) if scale is None else scale
+    ld_cache = k_cache.shape[1] if k_cache is not None else 0
+    nb = lib().eagle_tree_attn_workspace(Tq, Hq, Hkv, hd, L, Tk, in_dt)
+    ws = _workspace(nb, q.device, workspace)
+    _check("eagle_tree_attn", lib().eagle_tree_attn(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), L, ld_cache, _ptr(k_tree), _ptr(v_tree), Tk,
+        k_tree.shape[1], _ptr(mask), mask.shape[1], mask.shape[0], _ptr(q_mask_row), Tq, Hq, Hkv,
+        hd, scale, in_dt, _dt(out), _ptr(out), _ptr(ws), nb, _ptr(dev_status), _stream()))
+    return out
+
+
+def eagle_lmhead_topk(f, W, k, want_logits=False, topk_id=None, topk_logp=None, lse=None,
+                      logits=None, workspace=None):
+    """Returns (topk_id int32[T][k], topk_logp f32[T][k], lse f32[T], logits or None)."""
+    T, d = f.shape
+    V = W.shape[0]
+    dt = _dt(f)
+    dev = f.device
+    topk_id = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_id is None else topk_id
+    topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_logp is None else topk_logp
+    lse = torch.empty(T, dtype=torch.float32, device=dev) if lse is None else lse
+    if want_logits and logits is None:
+        logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    nb = lib().eagle_lmhead_topk_workspace(T, d, V, k, dt)
+    ws = _workspace(nb, dev, workspace)
+    _check("eagle_lmhead_topk", lib().eagle_lmhead_topk(
+        _ptr(f), _ptr(W), T, d, V, k, dt, _ptr(topk_id), _ptr(topk_logp), _ptr(lse),
+        _ptr(logits), _ptr(ws), nb, _stream()))
+    return topk_id, topk_logp, lse, logits
+
+
+def eagle_expand_rerank(mode, pool_token, pool_parent, pool_depth, pool_value, pool_n,
+                        frontier=None, child_id=None, child_logp=None, k_select=0,
+                        new_frontier=None, T=0, node_token=None, node_parent=None,
+                        node_depth=None, node_pool_idx=None, dev_status=None):
+    """EXPAND returns new_frontier; RERANK returns (token, parent, depth, pool_idx)."""
+    cap = pool_token.shape[0]
+    dev = pool_token.device
+    if mode == EAGLE_EXPAND:
+        kf, k = child_id.shape
+        if new_frontier is None:
+            new_frontier = torch.empty(k_select, dtype=torch.int32, device=dev)
+        _check("eagle_expand_rerank", lib().eagle_expand_rerank(
+            mode, _ptr(pool_token), _ptr(pool_parent), _ptr(pool_depth), _ptr(pool_value), pool_n,
+            cap, _ptr(frontier), kf, _ptr(child_id), _ptr(child_logp), k, k_select,
+            _ptr(new_frontier), 0, None, None, None, None, _ptr(dev_status), _stream()))
+        return new_frontier
+    mk = lambda t: torch.empty(T, dtype=torch.int32, device=dev) if t is None else t
+    node_token, node_parent, node_depth, node_pool_idx = (mk(node_token), mk(node_parent),
+                                                          mk(node_depth), mk(node_pool_idx))
+    _check("eagle_expand_rerank", lib().eagle_expand_rerank(
+        mode, _ptr(pool_token), _ptr(pool_parent), _ptr(pool_depth), _ptr(pool_value), pool_n, cap,
+        None, 0, None, None, 0, 0, None, T, _ptr(node_token), _ptr(node_parent), _ptr(node_depth),
+        _ptr(node_pool_idx), _ptr(dev_status), _stream()))
+    return node_token, node_parent, node_depth, node_pool_idx
+
+
+def eagle_accept(mode, node_token, node_parent, target_top1=None, target_logits=None,
+                 temperature=1.0, uniforms=None, max_path=None, path=None, n_accepted=None,
+                 bonus_token=None, workspace=None, dev_status=None):
+    """Returns (path int32[max_path], n_accepted int32[1], bonus int32[1])."""
+    T = node_token.shape[0]
+    dev = node_token.device
+    max_path = T if max_path is None else max_path
+    path = torch.empty(max_path, dtype=torch.int32, device=dev) if path is None else path
+    n_accepted = torch.empty(1, dtype=torch.int32, device=dev) if n_accepted is None else n_accepted
+    bonus_token = torch.empty(1, dtype=torch.int32, device=dev) if bonus_token is None else bonus_token
+    V = target_logits.shape[1] if target_logits is not None else 0
+    nb = lib().eagle_accept_workspace(T, V) if mode == EAGLE_SAMPLE else 0
+    ws = _workspace(nb, dev, workspace) if mode == EAGLE_SAMPLE else None
+    _check("eagle_accept", lib().eagle_accept(
+        mode, T, _ptr(node_token), _ptr(node_parent), _ptr(target_top1), _ptr(target_logits), V,
+        temperature, _ptr(uniforms), max_path, _ptr(path), _ptr(n_accepted), _ptr(bonus_token),
+        _ptr(ws), nb, _ptr(dev_status), _stream()))
+    return path, n_accepted, bonus_token

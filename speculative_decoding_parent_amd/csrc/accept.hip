@@ -1,0 +1,333 @@
+// Acceptance of the longest verified path through the draft tree.
+//
+// Sources: "EAGLE-2: Feature-Level Speculative Decoding Guide", Key
+// Architectural Mechanics 3 - a greedy or sampling verifier walks the tree
+// from the root and accepts matching tokens until the first discrepancy;
+// The Problem 1 and "Support Eagle-3 Speculative Decoding in llama.cpp"
+// (opening post) - speculative sampling's accept/reject rule.
+//
+// GREEDY: one thread per node walks to the root checking that every step holds
+// the target's choice; the deepest fully matching node (lowest index on ties)
+// ends the path.
+//
+// SAMPLE: the walk itself is sequential and touches at most depth+1 rows, but
+// each row needs fp64 softmax mass over the whole vocabulary.  A grid kernel
+// first reduces every row in 4096-token chunks (chunk max and fp64
+// sum of exp((l - chunk max) / temperature)), so the single-workgroup walk
+// only combines ~32 chunk sums per visited node and rescans one 4096-token
+// chunk for the inverse-CDF draw.
+#include "common.h"
+
+namespace eagle {
+
+constexpr int kAcceptChunk = 4096;
+
+// ---------------------------------------------------------------- greedy
+
+__global__ __launch_bounds__(256) void accept_greedy_kernel(
+    int T, const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ top1, int max_path, int32_t* __restrict__ path,
+    int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
+  __shared__ int32_t par[EAGLE_MAX_TREE];
+  __shared__ int32_t tk[EAGLE_MAX_TREE];
+  __shared__ int32_t t1[EAGLE_MAX_TREE];
+  __shared__ int32_t key[EAGLE_MAX_TREE];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < T; i += blockDim.x) {
+    par[i] = parent[i];
+    tk[i] = token[i];
+    t1[i] = top1[i];
+  }
+  __syncthreads();
+  for (int i = tid; i < T; i += blockDim.x) {
+    // key = depth * 256 + (255 - i) for accepted nodes, -1 otherwise: the
+    // largest key is the deepest accepted node with the lowest index.
+    int ok = 1;
+    int d = 0;
+    int j = i;
+    if (i == 0 && par[0] != -1) set_status(status, EAGLE_DEV_BAD_ROOT);
+    while (j != 0) {
+      const int p = par[j];
+      if (p < 0 || p >= j) {
+        set_status(status, p == -1 ? EAGLE_DEV_BAD_ROOT : EAGLE_DEV_BAD_PARENT);
+        ok = 0;
+        break;
+      }
+      if (tk[j] != t1[p]) ok = 0;
+      ++d;
+      j = p;
+    }
+    key[i] = ok ? d * 256 + (255 - i) : -1;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    int best = -1;
+    for (int i = tid; i < T; i += 64) best = max(best, key[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
+    if (tid == 0) {
+      const int end = best < 0 ? 0 : 255 - (best & 255);
+      const int depth = best < 0 ? 0 : (best >> 8);
+      // path[0..depth] from the root; cut if it does not fit
+      int u = end;
+      for (int s = depth; s >= 0; --s) {
+        if (s < max_path) path[s] = u;
+        u = s > 0 ? par[u] : u;
+      }
+      for (int s = depth + 1; s < max_path; ++s) path[s] = -1;
+      if (depth + 1 > max_path) set_status(status, EAGLE_DEV_PATH_TRUNC);
+      *n_acc = min(depth, max_path - 1);
+      *bonus = t1[end];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- sampling
+
+// Per (row, chunk): chunk max m_c (fp32, exact) and s_c = sum over the chunk of
+// exp(((double)l - m_c) / temperature) in fp64.
+__global__ __launch_bounds__(256) void accept_row_stats_kernel(
+    const float* __restrict__ logits, int V, double temp, int nchunk, double* __restrict__ ws) {
+  const int c = blockIdx.x;
+  const int t = blockIdx.y;
+  const float* row = logits + (size_t)t * V;
+  const int lo = c * kAcceptChunk;
+  const int hi = min(V, lo + kAcceptChunk);
+  __shared__ float smax[4];
+  __shared__ double ssum[4];
+  float m = -INFINITY;
+  for (int v = lo + threadIdx.x; v < hi; v += blockDim.x) m = fmaxf(m, row[v]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  double s = 0.0;
+  const double md = (double)m;
+  for (int v = lo + threadIdx.x; v < hi; v += blockDim.x) s += exp(((double)row[v] - md) / temp);
+  s = wave_sum_d(s);
+  if ((threadIdx.x & 63) == 0) ssum[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double* o = ws + ((size_t)t * nchunk + c) * 2;
+    o[0] = md;
+    o[1] = ((ssum[0] + ssum[1]) + ssum[2]) + ssum[3];
+  }
+}
+
+// Block-wide reduction; `red` holds one slot per wave.  The leading barrier
+// lets the same `red` be reused by back-to-back calls.
+template <typename V, typename Op>
+__device__ __forceinline__ V block_reduce(V v, V* red, Op op) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  V r = red[0];
+  const int nw = blockDim.x >> 6;
+  for (int i = 1; i < nw; ++i) r = op(r, red[i]);
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void accept_sample_kernel(
+    int T, const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
+    const float* __restrict__ logits, int V, double temp, const float* __restrict__ U,
+    int nchunk, const double* __restrict__ ws, int max_path, int32_t* __restrict__ path,
+    int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
+  __shared__ int32_t par[EAGLE_MAX_TREE];
+  __shared__ int32_t tk[EAGLE_MAX_TREE];
+  __shared__ int32_t rej[EAGLE_MAX_TREE];
+  __shared__ double dred[16];
+  __shared__ int ired[16];
+  __shared__ double sh_m, sh_target, sh_run;
+  __shared__ int sh_u, sh_nrej, sh_moved, sh_chunk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  for (int i = tid; i < T; i += blockDim.x) {
+    int p = parent[i];
+    const int x = token[i];
+    if (i == 0 ? p != -1 : (p < 0 || p >= i)) {
+      set_status(status, (i == 0 || p == -1) ? EAGLE_DEV_BAD_ROOT : EAGLE_DEV_BAD_PARENT);
+      p = i == 0 ? -1 : 0;
+    }
+    if (x < 0 || x >= V) set_status(status, EAGLE_DEV_BAD_TOKEN);
+    par[i] = p;
+    tk[i] = min(max(x, 0), V - 1);
+  }
+  if (tid == 0) sh_u = 0;
+  __syncthreads();
+
+  // ---- the walk: one accept/reject pass over the children of each node
+  int depth = 0;
+  for (;;) {
+    if (tid == 0) {
+      const int u = sh_u;
+      const float* row = logits + (size_t)u * V;
+      const double* st = ws + (size_t)u * nchunk * 2;
+      double m = st[0];
+      for (int c = 1; c < nchunk; ++c) m = fmax(m, st[2 * c]);
+      double z = 0.0;
+      for (int c = 0; c < nchunk; ++c) z += st[2 * c + 1] * exp((st[2 * c] - m) / temp);
+      double zres = z;
+      int nrej = 0;
+      int moved = 0;
+      for (int c = u + 1; c < T && !moved; ++c) {
+        if (par[c] != u) continue;
+        const int x = tk[c];
+        bool seen = false;
+        for (int r = 0; r < nrej; ++r) seen |= rej[r] == x;
+        if (seen) continue;
+        const double px = exp(((double)row[x] - m) / temp);
+        if ((double)U[c] * zres < px) {
+          moved = 1;
+          sh_u = c;
+        } else {
+          rej[nrej++] = x;
+          zres = zres - px;
+        }
+      }
+      sh_m = m;
+      sh_nrej = nrej;
+      sh_moved = moved;
+      if (!moved) {
+        // the residual draw starts in the first chunk whose running
+        // non-rejected mass passes the target
+        const double target = (double)U[T + u] * zres;
+        double run = 0.0;
+        int chunk = nchunk - 1;
+        double before = 0.0;
+        for (int c = 0; c < nchunk; ++c) {
+          double mass = st[2 * c + 1] * exp((st[2 * c] - m) / temp);
+          for (int r = 0; r < nrej; ++r)
+            if (rej[r] / kAcceptChunk == c) mass -= exp(((double)row[rej[r]] - m) / temp);
+          before = run;
+          if (run + mass > target) {
+            chunk = c;
+            break;
+          }
+          run += mass;
+        }
+        sh_target = target;
+        sh_chunk = chunk;
+        sh_run = before;
+      }
+    }
+    __syncthreads();
+    if (!sh_moved) break;
+    ++depth;
+    if (tid == 0 && depth < max_path) path[depth] = sh_u;
+    __syncthreads();
+  }
+
+  // ---- residual draw at the last node: inverse CDF in token order
+  const int u = sh_u;
+  const float* row = logits + (size_t)u * V;
+  const double m = sh_m;
+  const double target = sh_target;
+  const int nrej = sh_nrej;
+  double run = sh_run;
+  int found = INT_MAX;
+  int lastpos = -1;
+  for (int c = sh_chunk; c < nchunk; ++c) {
+    const int lo = c * kAcceptChunk;
+    const int hi = min(V, lo + kAcceptChunk);
+    const int v0 = lo + tid * 4;          // 1024 threads x 4 tokens = one chunk
+    double q[4];
+    double mine = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = v0 + e;
+      double pv = 0.0;
+      if (v < hi) {
+        bool r = false;
+        for (int j = 0; j < nrej; ++j) r |= rej[j] == v;
+        pv = r ? 0.0 : exp(((double)row[v] - m) / temp);
+      }
+      q[e] = pv;
+      mine += pv;
+    }
+    double incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) dred[tid >> 6] = incl;
+    __syncthreads();
+    double off = run;
+    for (int w = 0; w < (tid >> 6); ++w) off += dred[w];
+    double total = 0.0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) total += dred[w];
+    double cum = off + (incl - mine);
+    int hit = INT_MAX;
+    int last = -1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (q[e] > 0.0) {
+        last = v0 + e;
+        cum += q[e];
+        if (hit == INT_MAX && cum > target) hit = v0 + e;
+      }
+    }
+    hit = block_reduce(hit, ired, [](int a, int b) { return min(a, b); });
+    last = block_reduce(last, ired, [](int a, int b) { return max(a, b); });
+    lastpos = max(lastpos, last);
+    if (hit != INT_MAX) {
+      found = hit;
+      break;
+    }
+    run = run + total;
+  }
+  if (tid == 0) {
+    const int b = found != INT_MAX ? found : max(lastpos, 0);
+    for (int s = depth + 1; s < max_path; ++s) path[s] = -1;
+    path[0] = 0;
+    if (depth + 1 > max_path) set_status(status, EAGLE_DEV_PATH_TRUNC);
+    *n_acc = min(depth, max_path - 1);
+    *bonus = b;
+  }
+}
+
+}  // namespace eagle
+
+extern "C" size_t eagle_accept_workspace(int32_t T, int32_t V) {
+  if (T < 1 || V < 1) return 0;
+  const size_t nchunk = ((size_t)V + eagle::kAcceptChunk - 1) / eagle::kAcceptChunk;
+  return (size_t)T * nchunk * 2 * sizeof(double);
+}
+
+extern "C" int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
+                            const int32_t* node_parent, const int32_t* target_top1,
+                            const float* target_logits, int32_t V, float temperature,
+                            const float* uniforms, int32_t max_path, int32_t* path,
+                            int32_t* n_accepted, int32_t* bonus_token, void* workspace,
+                            size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+  EAGLE_REQUIRE(node_token && node_parent && path && n_accepted && bonus_token, EAGLE_EINVAL);
+  EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && max_path >= 1, EAGLE_EINVAL);
+  if (mode == EAGLE_GREEDY) {
+    EAGLE_REQUIRE(target_top1, EAGLE_EINVAL);
+    hipLaunchKernelGGL(eagle::accept_greedy_kernel, dim3(1), dim3(256), 0, stream, T, node_token,
+                       node_parent, target_top1, max_path, path, n_accepted, bonus_token,
+                       dev_status);
+  } else if (mode == EAGLE_SAMPLE) {
+    EAGLE_REQUIRE(target_logits && uniforms && V >= 1, EAGLE_EINVAL);
+    EAGLE_REQUIRE(temperature > 0.0f && temperature <= 3.0e38f, EAGLE_EINVAL);
+    EAGLE_REQUIRE(workspace && ((uintptr_t)workspace & 7) == 0, EAGLE_EINVAL);
+    EAGLE_REQUIRE(ws_bytes >= eagle_accept_workspace(T, V), EAGLE_EWORKSPACE);
+    const int nchunk = (V + eagle::kAcceptChunk - 1) / eagle::kAcceptChunk;
+    const double temp = (double)temperature;
+    hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, T), dim3(256), 0, stream,
+                       target_logits, V, temp, nchunk, (double*)workspace);
+    EAGLE_LAUNCH_CHECK();
+    hipLaunchKernelGGL(eagle::accept_sample_kernel, dim3(1), dim3(1024), 0, stream, T,
+                       node_token, node_parent, target_logits, V, temp, uniforms, nchunk,
+                       (const double*)workspace, max_path, path, n_accepted, bonus_token,
+                       dev_status);
+  } else {
+    return EAGLE_EINVAL;
+  }
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}

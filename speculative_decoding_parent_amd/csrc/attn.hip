@@ -1,0 +1,507 @@
+// Tree-masked attention of draft-tree nodes against a KV prefix.
+//
+// Sources: "EAGLE-2: Feature-Level Speculative Decoding Guide", Key
+// Architectural Mechanics 3 - every tree node is scored in one batched pass
+// under the tree mask (ancestors only); "Support Eagle-3 Speculative Decoding
+// in llama.cpp" printout - grouped-query attention, 32 query / 8 KV heads of
+// 128 dims.
+//
+// bf16 path, one workgroup = (KV head g, one slice of the positions, one group
+// of <= 64 NTW query rows).  The query rows of a KV head are all (node i, head
+// h) pairs with h / G = g, so every K/V tile fetched from HBM serves the G
+// heads that share it (GQA) and all tree nodes at once.  The prefix is cut
+// into splits of whole 64-position tiles; the tree is one more split, masked
+// by the node's ancestor bits (64 tree positions per tile = one mask word).
+// Each split writes unnormalised partials (row max, row sum, O) and a second
+// kernel combines the splits (log-sum-exp merge).
+//
+// Per 64-position tile, per wave (16 NTW rows):
+//   S^T = K Q^T   v_mfma_f32_16x16x32_bf16, K from LDS as the A operand
+//                 (positions = M), Q^T held in registers as the B operand;
+//   online softmax in the exp2 domain (scale * log2 e folded into one FMA);
+//   O^T += V^T P^T  with P^T taken straight from the S^T accumulators: a lane
+//                 holds 4 consecutive positions of one query row per 16-row
+//                 tile, so two tiles give the 8 k-values of a B operand once
+//                 the k order is permuted; V^T comes from a transposed LDS
+//                 copy with the same permutation.
+// K and V of the next tile are fetched into registers (16-byte loads,
+// coalesced along the head dimension) while the current tile computes.
+//
+// fp32 path (small workloads): one workgroup per (query row, head, split)
+// computes the scores into LDS in fp32 and reduces them directly; same
+// partial layout and merge.
+#include "common.h"
+
+namespace eagle {
+
+constexpr int kAtTile = 64;
+constexpr int kAtF32Chunk = 1024;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+
+struct AttnParams {
+  const bf16_t* q;
+  const bf16_t* kc;
+  const bf16_t* vc;
+  const bf16_t* kt;
+  const bf16_t* vt;
+  int64_t L, ldc;
+  int Tk, ldt;
+  const uint64_t* mask;
+  int words, mask_rows;
+  const int32_t* qmap;
+  int Tq, Hq, Hkv, G;
+  float c;               // scale * log2(e)
+  int n_split;           // prefix splits; split index n_split is the tree
+  int tiles_per_split;
+  float* part_o;         // [n_split + 1][Tq * Hq][HD]
+  float2* part_ml;       // [n_split + 1][Tq * Hq]
+  int32_t* status;
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int HD, int NTW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p) {
+  constexpr int NTH = 64 * NW;
+  constexpr int KB = HD / 32;
+  constexpr int MTV = HD / 16;
+  constexpr int KS = HD + 8;
+  constexpr int VS = kAtTile + 8;
+  constexpr int CPR = HD / 8;
+  constexpr int NCH = kAtTile * CPR / NTH;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[kAtTile * KS];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VS];
+
+  const int split = blockIdx.x;
+  const int gkv = blockIdx.y;
+  const int qg = blockIdx.z;
+  const bool is_tree = split == p.n_split;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int R = p.Tq * p.G;
+  const int RT = p.Tq * p.Hq;
+
+  int grow[NTW];
+  bool valid[NTW];
+  int mrow[NTW];
+  u32x4 qf[NTW][KB];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int r = qg * (16 * NTW * NW) + wave * 16 * NTW + nt * 16 + r16;
+    valid[nt] = r < R;
+    const int i = valid[nt] ? r / p.G : 0;
+    const int h = gkv * p.G + (valid[nt] ? r % p.G : 0);
+    grow[nt] = i * p.Hq + h;
+    int mr = p.qmap ? p.qmap[i] : i;
+    if (mr < 0 || mr >= p.mask_rows) {
+      if (valid[nt] && is_tree && g == 0) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+      mr = -1;
+    }
+    mrow[nt] = mr;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qf[nt][kb] = valid[nt] ? *(const u32x4*)(p.q + (size_t)grow[nt] * HD + kb * 32 + 8 * g)
+                             : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  int64_t pos0;
+  int64_t npos;
+  const bf16_t* kb_ptr;
+  const bf16_t* vb_ptr;
+  if (!is_tree) {
+    pos0 = (int64_t)split * p.tiles_per_split * kAtTile;
+    npos = p.L - pos0;
+    if (npos > (int64_t)p.tiles_per_split * kAtTile) npos = (int64_t)p.tiles_per_split * kAtTile;
+    kb_ptr = p.kc + ((size_t)gkv * p.ldc + pos0) * HD;
+    vb_ptr = p.vc + ((size_t)gkv * p.ldc + pos0) * HD;
+  } else {
+    pos0 = 0;
+    npos = p.Tk;
+    kb_ptr = p.kt + (size_t)gkv * p.ldt * HD;
+    vb_ptr = p.vt + (size_t)gkv * p.ldt * HD;
+  }
+  const int ntiles = npos > 0 ? (int)((npos + kAtTile - 1) / kAtTile) : 0;
+
+  float m[NTW], l[NTW];
+  f32x4 o[MTV][NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    m[nt] = kNegBig;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int mv = 0; mv < MTV; ++mv) o[mv][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  u32x4 kr[NCH], vr[NCH];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + NTH * j;
+      const int pr = c / CPR;
+      const int cc = c - pr * CPR;
+      const int64_t pos = (int64_t)t * kAtTile + pr;
+      const bool ok = pos < npos;
+      kr[j] = ok ? *(const u32x4*)(kb_ptr + pos * HD + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      vr[j] = ok ? *(const u32x4*)(vb_ptr + pos * HD + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = tid + NTH * j;
+      const int pr = c / CPR;
+      const int cc = c - pr * CPR;
+      *(u32x4*)(&Ks[pr * KS + cc * 8]) = kr[j];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        Vt[(cc * 8 + 2 * w) * VS + pr] = (bf16_t)(vr[j][w] & 0xffffu);
+        Vt[(cc * 8 + 2 * w + 1) * VS + pr] = (bf16_t)(vr[j][w] >> 16);
+      }
+    }
+  };
+
+  if (ntiles > 0) load_tile(0);
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (t + 1 < ntiles) load_tile(t + 1);
+
+    // S^T = K Q^T over 4 position tiles of 16
+    f32x4 s[4][NTW];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 a = *(const bf16x8*)(&Ks[(mt * 16 + r16) * KS + kb * 32 + 8 * g]);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[nt][kb]), s[mt][nt],
+                                                              0, 0, 0);
+      }
+    }
+
+    // visibility: positions past the slice end, and non-ancestors in the tree
+    const int64_t tile_pos = (int64_t)t * kAtTile;
+    const bool tail = tile_pos + kAtTile > npos;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      uint64_t bits = ~0ull;
+      if (is_tree) bits = mrow[nt] >= 0 ? p.mask[(size_t)mrow[nt] * p.words + t] : 0ull;
+      if (is_tree || tail) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int pl = mt * 16 + 4 * g + j;
+            if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
+          }
+      }
+    }
+
+    // online softmax (exp2 domain) and P^T packing
+    u32x4 pb[2][NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mt][nt][j]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[nt], mx);
+      const float alpha = exp2f((m[nt] - mnew) * p.c);
+      m[nt] = mnew;
+      const float nmc = -mnew * p.c;
+      float ps = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pv = exp2f(fmaf(s[mt][nt][j], p.c, nmc));
+          s[mt][nt][j] = pv;
+          ps += pv;
+        }
+      l[nt] = fmaf(l[nt], alpha, ps);
+#pragma unroll
+      for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
+                            pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
+                            pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
+                            pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int mv = 0; mv < MTV; ++mv) {
+        const bf16_t* vrow = &Vt[(mv * 16 + r16) * VS + kb2 * 32 + 4 * g];
+        const u32x2 lo = *(const u32x2*)(vrow);
+        const u32x2 hi = *(const u32x2*)(vrow + 16);
+        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          o[mv][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kb2][nt]), o[mv][nt],
+                                                              0, 0, 0);
+      }
+    }
+  }
+
+  // partials: lane (g, r16) holds O^T[hd = 16 mv + 4 g + j][row 16 nt + r16]
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    float lt = l[nt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!valid[nt]) continue;
+    const size_t prow = (size_t)split * RT + grow[nt];
+    if (g == 0) p.part_ml[prow] = make_float2(m[nt], lt);
+    float* po = p.part_o + prow * HD;
+#pragma unroll
+    for (int mv = 0; mv < MTV; ++mv) *(f32x4*)(po + mv * 16 + 4 * g) = o[mv][nt];
+  }
+}
+
+// fp32 path: one workgroup per (split, query row, head).
+__global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnParams p, int hd) {
+  __shared__ float sc[kAtF32Chunk];
+  __shared__ float qs[256];
+  __shared__ float red[4];
+  const int split = blockIdx.x;
+  const int grow = blockIdx.y;
+  const bool is_tree = split == p.n_split;
+  const int i = grow / p.Hq;
+  const int h = grow - i * p.Hq;
+  const int gkv = h / p.G;
+  const float* q = (const float*)p.q;
+  const int RT = p.Tq * p.Hq;
+  for (int d = threadIdx.x; d < hd; d += 256) qs[d] = q[(size_t)grow * hd + d];
+  int64_t pos0, npos;
+  const float* kp;
+  const float* vp;
+  int mr = -1;
+  if (!is_tree) {
+    pos0 = (int64_t)split * kAtF32Chunk;
+    npos = p.L - pos0;
+    if (npos > kAtF32Chunk) npos = kAtF32Chunk;
+    kp = (const float*)p.kc + ((size_t)gkv * p.ldc + pos0) * hd;
+    vp = (const float*)p.vc + ((size_t)gkv * p.ldc + pos0) * hd;
+  } else {
+    pos0 = 0;
+    npos = p.Tk;
+    kp = (const float*)p.kt + (size_t)gkv * p.ldt * hd;
+    vp = (const float*)p.vt + (size_t)gkv * p.ldt * hd;
+    mr = p.qmap ? p.qmap[i] : i;
+    if (mr < 0 || mr >= p.mask_rows) {
+      if (threadIdx.x == 0 && h == 0) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+      mr = -1;
+    }
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j < npos; j += 256) {
+    bool vis = true;
+    if (is_tree) vis = mr >= 0 && ((p.mask[(size_t)mr * p.words + (j >> 6)] >> (j & 63)) & 1ull);
+    float s = -INFINITY;
+    if (vis) {
+      s = 0.f;
+      const float* kr = kp + (size_t)j * hd;
+      for (int d = 0; d < hd; ++d) s = fmaf(qs[d], kr[d], s);
+    }
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), kNegBig);
+  float ls = 0.f;
+  for (int j = threadIdx.x; j < npos; j += 256) {
+    const float pv = exp2f((sc[j] - M) * p.c);
+    sc[j] = pv;
+    ls += pv;
+  }
+  ls = wave_sum(ls);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ls;
+  __syncthreads();
+  const float lt = ((red[0] + red[1]) + red[2]) + red[3];
+  const size_t prow = (size_t)split * RT + grow;
+  for (int d = threadIdx.x; d < hd; d += 256) {
+    float a = 0.f;
+    for (int j = 0; j < npos; ++j) a = fmaf(sc[j], vp[(size_t)j * hd + d], a);
+    p.part_o[prow * hd + d] = a;
+  }
+  if (threadIdx.x == 0) p.part_ml[prow] = make_float2(M, lt);
+}
+
+// Combine the splits of each (query row, head): out = sum_s w_s O_s / sum_s w_s l_s
+// with w_s = exp2((m_s - M) c).
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                         const float2* __restrict__ part_ml,
+                                                         int nsplit, int RT, int hd, float c,
+                                                         void* out, int out_bf16) {
+  const int row = blockIdx.x;
+  float M = kNegBig;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(size_t)s * RT + row].x);
+  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float2 ml = part_ml[(size_t)s * RT + row];
+      const float w = exp2f((ml.x - M) * c);
+      den = fmaf(ml.y, w, den);
+      num = fmaf(part_o[((size_t)s * RT + row) * hd + d], w, num);
+    }
+    const float v = num / den;
+    if (out_bf16)
+      ((bf16_t*)out)[(size_t)row * hd + d] = (bf16_t)f32_to_bf16_bits(v);
+    else
+      ((float*)out)[(size_t)row * hd + d] = v;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+struct AttnPlan {
+  int ntw, nw, qgroups, n_split, tiles_per_split;
+  size_t o_off, ml_off, total;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static AttnPlan attn_plan(int Tq, int Hq, int Hkv, int hd, int64_t L, eagle_dtype dt) {
+  AttnPlan pl{};
+  const int G = Hq / Hkv;
+  const int R = Tq * G;
+  if (dt == EAGLE_BF16) {
+    // rows per workgroup: 64 (4 waves x 16), 128 (4 x 32) or 256 (8 x 32)
+    pl.ntw = R <= 64 ? 1 : 2;
+    pl.nw = R <= 128 ? 4 : 8;
+    const int rows = 16 * pl.ntw * pl.nw;
+    pl.qgroups = (R + rows - 1) / rows;
+    const int64_t tiles = (L + kAtTile - 1) / kAtTile;
+    if (tiles == 0) {
+      pl.n_split = 0;
+      pl.tiles_per_split = 1;
+    } else {
+      const int64_t per_split_blocks = (int64_t)Hkv * pl.qgroups;
+      int64_t want = (256 + per_split_blocks - 1) / per_split_blocks;
+      if (want < 1) want = 1;
+      if (want > tiles) want = tiles;
+      pl.tiles_per_split = (int)((tiles + want - 1) / want);
+      pl.n_split = (int)((tiles + pl.tiles_per_split - 1) / pl.tiles_per_split);
+    }
+  } else {
+    pl.ntw = 0;
+    pl.nw = 4;
+    pl.qgroups = 1;
+    pl.n_split = (int)((L + kAtF32Chunk - 1) / kAtF32Chunk);
+    pl.tiles_per_split = 0;
+  }
+  const size_t RT = (size_t)Tq * Hq;
+  const size_t ns = (size_t)pl.n_split + 1;
+  pl.o_off = 0;
+  pl.ml_off = align256(ns * RT * hd * sizeof(float));
+  pl.total = pl.ml_off + align256(ns * RT * sizeof(float2));
+  return pl;
+}
+
+template <int HD, int NTW, int NW>
+static void launch_attn(const AttnParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((tree_attn_bf16_kernel<HD, NTW, NW>), grid, dim3(64 * NW), 0, s, p);
+}
+
+}  // namespace eagle
+
+extern "C" size_t eagle_tree_attn_workspace(int32_t Tq, int32_t Hq, int32_t Hkv, int32_t hd,
+                                            int64_t L, int32_t Tk, eagle_dtype in_dt) {
+  (void)Tk;
+  if (Tq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || hd < 1 || L < 0) return 0;
+  return eagle::attn_plan(Tq, Hq, Hkv, hd, L, in_dt).total;
+}
+
+extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v_cache, int64_t L,
+                               int64_t ld_cache, const void* k_tree, const void* v_tree,
+                               int32_t Tk, int32_t ld_tree, const uint64_t* mask, int32_t words,
+                               int32_t mask_rows, const int32_t* q_mask_row, int32_t Tq,
+                               int32_t Hq, int32_t Hkv, int32_t hd, float scale,
+                               eagle_dtype in_dt, eagle_dtype out_dt, void* out, void* workspace,
+                               size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+  using namespace eagle;
+  EAGLE_REQUIRE(q && k_tree && v_tree && mask && out && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(L >= 0 && (L == 0 || (k_cache && v_cache && ld_cache >= L)), EAGLE_EINVAL);
+  EAGLE_REQUIRE(Tq >= 1 && Tq <= EAGLE_MAX_TREE && Tk >= 1 && Tk <= EAGLE_MAX_TREE, EAGLE_EINVAL);
+  EAGLE_REQUIRE(ld_tree >= Tk && words >= (Tk + 63) / 64 && words <= 4 && mask_rows >= 1,
+                EAGLE_EINVAL);
+  EAGLE_REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(scale > 0.0f && scale < 3.0e38f, EAGLE_EINVAL);
+  EAGLE_REQUIRE(in_dt == EAGLE_BF16 || in_dt == EAGLE_F32, EAGLE_EINVAL);
+  EAGLE_REQUIRE(out_dt == EAGLE_BF16 || out_dt == EAGLE_F32, EAGLE_EINVAL);
+  EAGLE_REQUIRE(hd == 64 || hd == 128, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k_tree | (uintptr_t)v_tree | (uintptr_t)out |
+                       (uintptr_t)k_cache | (uintptr_t)v_cache;
+  EAGLE_REQUIRE((al & 15) == 0 && ((uintptr_t)mask & 7) == 0, EAGLE_EINVAL);
+  const AttnPlan pl = attn_plan(Tq, Hq, Hkv, hd, L, in_dt);
+  EAGLE_REQUIRE(ws_bytes >= pl.total, EAGLE_EWORKSPACE);
+  char* ws = (char*)workspace;
+  AttnParams p{};
+  p.q = (const bf16_t*)q;
+  p.kc = (const bf16_t*)k_cache;
+  p.vc = (const bf16_t*)v_cache;
+  p.kt = (const bf16_t*)k_tree;
+  p.vt = (const bf16_t*)v_tree;
+  p.L = L;
+  p.ldc = ld_cache;
+  p.Tk = Tk;
+  p.ldt = ld_tree;
+  p.mask = mask;
+  p.words = words;
+  p.mask_rows = mask_rows;
+  p.qmap = q_mask_row;
+  p.Tq = Tq;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.c = scale * kLog2e;
+  p.n_split = pl.n_split;
+  p.tiles_per_split = pl.tiles_per_split;
+  p.part_o = (float*)(ws + pl.o_off);
+  p.part_ml = (float2*)(ws + pl.ml_off);
+  p.status = dev_status;
+  if (in_dt == EAGLE_BF16) {
+    const dim3 grid(pl.n_split + 1, Hkv, pl.qgroups);
+    if (hd == 128) {
+      if (pl.ntw == 1) launch_attn<128, 1, 4>(p, grid, stream);
+      else if (pl.nw == 4) launch_attn<128, 2, 4>(p, grid, stream);
+      else launch_attn<128, 2, 8>(p, grid, stream);
+    } else {
+      if (pl.ntw == 1) launch_attn<64, 1, 4>(p, grid, stream);
+      else if (pl.nw == 4) launch_attn<64, 2, 4>(p, grid, stream);
+      else launch_attn<64, 2, 8>(p, grid, stream);
+    }
+  } else {
+    hipLaunchKernelGGL(tree_attn_f32_kernel, dim3(pl.n_split + 1, Tq * Hq), dim3(256), 0, stream,
+                       p, hd);
+  }
+  EAGLE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(Tq * Hq), dim3(128), 0, stream, p.part_o, p.part_ml,
+                     pl.n_split + 1, Tq * Hq, hd, p.c, out, out_dt == EAGLE_BF16 ? 1 : 0);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}

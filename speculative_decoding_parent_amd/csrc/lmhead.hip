@@ -1,0 +1,437 @@
+// LM head, softmax statistics and top-k.
+//
+// Sources: "EAGLE-2: Feature-Level Speculative Decoding Guide", Key
+// Architectural Mechanics 1 - P = softmax(W_LM f) through the target's own LM
+// head; section 2 - the confidence ratio of the two most likely tokens;
+// "Support Eagle-3 Speculative Decoding in llama.cpp" printout - no bias.
+//
+// bf16 path (the hot one).  logits[t][v] = sum_k f[t][k] W[v][k] with T <= 256
+// feature rows and V up to ~152K vocabulary rows of d <= 8192: at T <= 128 the
+// work is ~T flop per weight byte, so the kernel is bound by streaming W from
+// HBM once.  Design:
+//   * MFMA v_mfma_f32_16x16x32_bf16 with W rows as the M dimension (16 rows per
+//     tile, 4 tiles = 64 rows per wave, 256 rows per 4-wave workgroup) and the
+//     feature rows as N (16 per tile, NT tiles).  W goes straight from HBM into
+//     MFMA A operands: each lane loads 4 x 16 bytes per tile per 128-wide k
+//     step, and the k order inside a step is permuted so those 4 loads are 64
+//     contiguous bytes (a row's 256 bytes are read by 4 lanes).  The permuted
+//     order is applied to both operands, so the contraction is unchanged.
+//   * f is shared by all workgroups (<= 512 KB at T = 64): each 128-wide k
+//     slice is staged once per workgroup in LDS (double-buffered, rows padded
+//     by 16 bytes so the 16 lanes of a b128 read hit distinct banks).
+//   * W for step k+1 is requested before the MFMAs of step k run.
+//   * Epilogue, per wave and feature row: the 64 logits are reduced to
+//     (max, sum exp(l - max)) and to the wave's top-k by (logit desc,
+//     index asc); optional fp32 logits are written with 16-byte stores.
+//   * A second kernel merges the per-wave partials of each row in a fixed
+//     order: lse = M + log(sum s_w exp(m_w - M)), and the top-k by repeated
+//     selection of the best candidate strictly after the previous pick.
+// fp32 path (small workloads): a plain VALU dot product per logit, then a
+// per-row top-k kernel.
+#include "common.h"
+
+namespace eagle {
+
+constexpr int kLmWaves = 4;
+constexpr int kLmMT = 4;
+constexpr int kLmRowsWave = 16 * kLmMT;
+constexpr int kLmRowsBlock = kLmRowsWave * kLmWaves;
+constexpr int kLmKG = 128;
+constexpr int kLmLds = kLmKG + 8;
+
+struct LmParams {
+  const bf16_t* f;
+  const bf16_t* W;
+  int T, d, V, k;
+  float* logits;
+  float2* part_stat;   // [nwave][T]
+  float* part_val;     // [nwave][T][k]
+  int32_t* part_idx;   // [nwave][T][k]
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int NT>
+__global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void lmhead_bf16_kernel(LmParams p) {
+  constexpr int TP = 16 * NT;
+  __shared__ __attribute__((aligned(16))) bf16_t fs[2][TP * kLmLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int v0 = blockIdx.x * kLmRowsBlock + wave * kLmRowsWave;
+
+  const bf16_t* wrow[kLmMT];
+#pragma unroll
+  for (int mt = 0; mt < kLmMT; ++mt) {
+    const int v = min(v0 + mt * 16 + r16, p.V - 1);
+    wrow[mt] = p.W + (size_t)v * p.d + g * 32;
+  }
+
+  f32x4 acc[kLmMT][NT];
+#pragma unroll
+  for (int mt = 0; mt < kLmMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // f staging: TP rows x 128 columns = TP * 16 chunks of 16 bytes, NT per thread
+  auto load_f = [&](int kk, u32x4 (&fr)[NT]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c >> 4;
+      const int col = (c & 15) * 8;
+      fr[j] = row < p.T ? *(const u32x4*)(p.f + (size_t)row * p.d + kk * kLmKG + col)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_f = [&](int buf, const u32x4 (&fr)[NT]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      *(u32x4*)(&fs[buf][(c >> 4) * kLmLds + (c & 15) * 8]) = fr[j];
+    }
+  };
+  auto load_w = [&](int kk, u32x4 (&wr)[kLmMT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < kLmMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[mt][i] = *(const u32x4*)(wrow[mt] + kk * kLmKG + i * 8);
+  };
+  auto compute = [&](int buf, const u32x4 (&wr)[kLmMT][4]) {
+    const bf16_t* fb = fs[buf];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8 b[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        b[nt] = *(const bf16x8*)(fb + (nt * 16 + r16) * kLmLds + g * 32 + i * 8);
+#pragma unroll
+      for (int mt = 0; mt < kLmMT; ++mt) {
+        const bf16x8 a = as_bf16x8(wr[mt][i]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nk = p.d / kLmKG;
+  u32x4 wa[kLmMT][4], wb[kLmMT][4];
+  u32x4 fr[NT];
+  load_f(0, fr);
+  store_f(0, fr);
+  load_w(0, wa);
+  __syncthreads();
+  for (int kk = 0; kk < nk; kk += 2) {
+    const bool more1 = kk + 1 < nk;
+    if (more1) {
+      load_w(kk + 1, wb);
+      load_f(kk + 1, fr);
+    }
+    compute(0, wa);
+    if (more1) store_f(1, fr);
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = kk + 2 < nk;
+    if (more2) {
+      load_w(kk + 2, wa);
+      load_f(kk + 2, fr);
+    }
+    compute(1, wb);
+    if (more2) store_f(0, fr);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Lane (g, r16) holds, for tile (mt, nt), the logits of
+  // vocabulary rows v0 + 16 mt + 4 g + j (j < 4) for feature row 16 nt + r16.
+  const int T = p.T;
+  const int V = p.V;
+  const int wglob = blockIdx.x * kLmWaves + wave;
+  if (p.logits) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = nt * 16 + r16;
+      if (t >= T) continue;
+      float* out = p.logits + (size_t)t * V;
+#pragma unroll
+      for (int mt = 0; mt < kLmMT; ++mt) {
+        const int vb = v0 + mt * 16 + 4 * g;
+        if ((V & 3) == 0 && vb + 3 < V) {
+          *(f32x4*)(out + vb) = acc[mt][nt];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (vb + j < V) out[vb + j] = acc[mt][nt][j];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int t = nt * 16 + r16;
+    float m = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < kLmMT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (v0 + mt * 16 + 4 * g + j < V) m = fmaxf(m, acc[mt][nt][j]);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float s = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < kLmMT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (v0 + mt * 16 + 4 * g + j < V) s += expf(acc[mt][nt][j] - m);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (g == 0 && t < T) p.part_stat[(size_t)wglob * T + t] = make_float2(m, s);
+
+    // wave top-k of this feature row: k rounds of "best not yet taken"
+    uint32_t taken = 0;
+    for (int r = 0; r < p.k; ++r) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int mt = 0; mt < kLmMT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int v = v0 + mt * 16 + 4 * g + j;
+          const float x = acc[mt][nt][j];
+          if (v < V && !((taken >> (mt * 4 + j)) & 1u) && better(x, v, bv, bi)) {
+            bv = x;
+            bi = v;
+          }
+        }
+      float ov = __shfl_xor(bv, 16);
+      int oi = __shfl_xor(bi, 16);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      ov = __shfl_xor(bv, 32);
+      oi = __shfl_xor(bi, 32);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      const int rel = bi - (v0 + 4 * g);
+      if (bi != INT_MAX && rel >= 0 && (rel & 15) < 4 && (rel >> 4) < kLmMT)
+        taken |= 1u << ((rel >> 4) * 4 + (rel & 3));
+      if (g == 0 && t < T) {
+        const size_t o = ((size_t)wglob * T + t) * p.k + r;
+        p.part_val[o] = bv;
+        p.part_idx[o] = bi;
+      }
+    }
+  }
+}
+
+template <typename V, typename Op>
+__device__ __forceinline__ V block_reduce256(V v, V* red, Op op) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return op(op(red[0], red[1]), op(red[2], red[3]));
+}
+
+__device__ __forceinline__ void block_best256(float& v, int& i, float* rv, int* ri) {
+  wave_best(v, i);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    rv[threadIdx.x >> 6] = v;
+    ri[threadIdx.x >> 6] = i;
+  }
+  __syncthreads();
+  v = rv[0];
+  i = ri[0];
+  for (int w = 1; w < 4; ++w)
+    if (better(rv[w], ri[w], v, i)) { v = rv[w]; i = ri[w]; }
+}
+
+// One workgroup per feature row: combine the per-wave statistics and top-k.
+__global__ __launch_bounds__(256) void lmhead_merge_kernel(
+    const float2* __restrict__ part_stat, const float* __restrict__ part_val,
+    const int32_t* __restrict__ part_idx, int nw, int T, int k, int32_t* __restrict__ topk_id,
+    float* __restrict__ topk_logp, float* __restrict__ lse) {
+  __shared__ float redf[4];
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int t = blockIdx.x;
+  float M = -INFINITY;
+  for (int w = threadIdx.x; w < nw; w += 256) M = fmaxf(M, part_stat[(size_t)w * T + t].x);
+  M = block_reduce256(M, redf, [](float a, float b) { return fmaxf(a, b); });
+  float S = 0.f;
+  for (int w = threadIdx.x; w < nw; w += 256) {
+    const float2 st = part_stat[(size_t)w * T + t];
+    if (st.y > 0.f) S += st.y * expf(st.x - M);
+  }
+  S = block_reduce256(S, redf, [](float a, float b) { return a + b; });
+  const float L = M + logf(S);
+  float lastv = INFINITY;
+  int lasti = -1;
+  const int n = nw * k;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int c = threadIdx.x; c < n; c += 256) {
+      const int w = c / k;
+      const int j = c - w * k;
+      const size_t o = ((size_t)w * T + t) * k + j;
+      const float v = part_val[o];
+      const int i = part_idx[o];
+      if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
+        bv = v;
+        bi = i;
+      }
+    }
+    block_best256(bv, bi, rv, ri);
+    if (threadIdx.x == 0) {
+      topk_id[(size_t)t * k + r] = bi;
+      topk_logp[(size_t)t * k + r] = bv - L;
+    }
+    lastv = bv;
+    lasti = bi;
+  }
+  if (threadIdx.x == 0) lse[t] = L;
+}
+
+// ---------------------------------------------------------------- fp32 path
+
+__global__ __launch_bounds__(256) void lmhead_f32_logits_kernel(
+    const float* __restrict__ f, const float* __restrict__ W, int T, int d, int V,
+    float* __restrict__ logits) {
+  __shared__ float fsm[1024];
+  const int t = blockIdx.y;
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  float acc = 0.f;
+  for (int k0 = 0; k0 < d; k0 += 1024) {
+    const int n = min(1024, d - k0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) fsm[i] = f[(size_t)t * d + k0 + i];
+    __syncthreads();
+    if (v < V) {
+      const float* w = W + (size_t)v * d + k0;
+      for (int i = 0; i < n; ++i) acc = fmaf(fsm[i], w[i], acc);
+    }
+  }
+  if (v < V) logits[(size_t)t * V + v] = acc;
+}
+
+__global__ __launch_bounds__(256) void rows_topk_kernel(
+    const float* __restrict__ logits, int V, int k, int32_t* __restrict__ topk_id,
+    float* __restrict__ topk_logp, float* __restrict__ lse) {
+  __shared__ float redf[4];
+  __shared__ float rv[4];
+  __shared__ int ri[4];
+  const int t = blockIdx.x;
+  const float* row = logits + (size_t)t * V;
+  float M = -INFINITY;
+  for (int v = threadIdx.x; v < V; v += 256) M = fmaxf(M, row[v]);
+  M = block_reduce256(M, redf, [](float a, float b) { return fmaxf(a, b); });
+  float S = 0.f;
+  for (int v = threadIdx.x; v < V; v += 256) S += expf(row[v] - M);
+  S = block_reduce256(S, redf, [](float a, float b) { return a + b; });
+  const float L = M + logf(S);
+  float lastv = INFINITY;
+  int lasti = -1;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int v = threadIdx.x; v < V; v += 256) {
+      const float x = row[v];
+      if (better(lastv, lasti, x, v) && better(x, v, bv, bi)) {
+        bv = x;
+        bi = v;
+      }
+    }
+    block_best256(bv, bi, rv, ri);
+    if (threadIdx.x == 0) {
+      topk_id[(size_t)t * k + r] = bi;
+      topk_logp[(size_t)t * k + r] = bv - L;
+    }
+    lastv = bv;
+    lasti = bi;
+  }
+  if (threadIdx.x == 0) lse[t] = L;
+}
+
+// ---------------------------------------------------------------- host side
+
+struct LmLayout {
+  size_t stat_off, val_off, idx_off, logits_off, total;
+  int nw;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
+  LmLayout l{};
+  if (dt == EAGLE_BF16) {
+    l.nw = ((V + kLmRowsBlock - 1) / kLmRowsBlock) * kLmWaves;
+    l.stat_off = 0;
+    l.val_off = align256((size_t)l.nw * T * sizeof(float2));
+    l.idx_off = l.val_off + align256((size_t)l.nw * T * k * sizeof(float));
+    l.total = l.idx_off + align256((size_t)l.nw * T * k * sizeof(int32_t));
+  } else {
+    l.logits_off = 0;
+    l.total = align256((size_t)T * V * sizeof(float));
+  }
+  return l;
+}
+
+template <int NT>
+static void launch_lm(const LmParams& p, int nblocks, hipStream_t s) {
+  hipLaunchKernelGGL(lmhead_bf16_kernel<NT>, dim3(nblocks), dim3(256), 0, s, p);
+}
+
+}  // namespace eagle
+
+extern "C" size_t eagle_lmhead_topk_workspace(int32_t T, int32_t d, int32_t V, int32_t k,
+                                              eagle_dtype dt) {
+  (void)d;
+  if (T < 1 || V < 1 || k < 1) return 0;
+  return eagle::lm_layout(T, V, k, dt).total;
+}
+
+extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
+                                 int32_t k, eagle_dtype dt, int32_t* topk_id, float* topk_logp,
+                                 float* lse, float* logits, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  using namespace eagle;
+  EAGLE_REQUIRE(f && W && topk_id && topk_logp && lse && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && d >= 1 && V >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(k >= 1 && k <= EAGLE_MAX_TOPK && k <= V, EAGLE_EINVAL);
+  EAGLE_REQUIRE(((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
+  const LmLayout l = lm_layout(T, V, k, dt);
+  EAGLE_REQUIRE(ws_bytes >= l.total, EAGLE_EWORKSPACE);
+  char* ws = (char*)workspace;
+  if (dt == EAGLE_BF16) {
+    EAGLE_REQUIRE(d % kLmKG == 0, EAGLE_EUNSUPPORTED);
+    EAGLE_REQUIRE(((uintptr_t)f & 15) == 0 && ((uintptr_t)W & 15) == 0, EAGLE_EINVAL);
+    EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
+    LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
+               (float2*)(ws + l.stat_off), (float*)(ws + l.val_off), (int32_t*)(ws + l.idx_off)};
+    const int nblocks = (V + kLmRowsBlock - 1) / kLmRowsBlock;
+    const int nt = (T + 15) / 16;
+    if (nt <= 1) launch_lm<1>(p, nblocks, stream);
+    else if (nt <= 2) launch_lm<2>(p, nblocks, stream);
+    else if (nt <= 4) launch_lm<4>(p, nblocks, stream);
+    else if (nt <= 8) launch_lm<8>(p, nblocks, stream);
+    else launch_lm<16>(p, nblocks, stream);
+    EAGLE_LAUNCH_CHECK();
+    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(T), dim3(256), 0, stream, p.part_stat,
+                       p.part_val, p.part_idx, l.nw, T, k, topk_id, topk_logp, lse);
+  } else if (dt == EAGLE_F32) {
+    float* lg = logits ? logits : (float*)(ws + l.logits_off);
+    hipLaunchKernelGGL(lmhead_f32_logits_kernel, dim3((V + 255) / 256, T), dim3(256), 0, stream,
+                       (const float*)f, (const float*)W, T, d, V, lg);
+    EAGLE_LAUNCH_CHECK();
+    hipLaunchKernelGGL(rows_topk_kernel, dim3(T), dim3(256), 0, stream, lg, V, k, topk_id,
+                       topk_logp, lse);
+  } else {
+    return EAGLE_EINVAL;
+  }
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}

@@ -1,0 +1,165 @@
+// Dynamic draft tree: EXPAND (grow by cumulative log-probability) and RERANK
+// (prune to the T best nodes).
+//
+// Sources: "Support Eagle-3 Speculative Decoding in llama.cpp" - confidence
+// approximates acceptance, the tree is grown from it and pruned at the end of
+// drafting; "EAGLE-2: Feature-Level Speculative Decoding Guide", section 2 -
+// the token budget goes where confidence is high.  Reading: value = fp32 sum
+// of log-probabilities along the root path, ties to the lower pool index.
+//
+// Both modes fit one workgroup (<= 4096 appended entries, <= 8192 pool
+// entries).  Selection is by exact rank: an entry is kept when fewer than n
+// entries beat it under (value desc, index asc), a total order, so the result
+// does not depend on thread scheduling.  Values are single IEEE fp32 adds
+// (__fadd_rn), never contracted.
+#include "common.h"
+
+namespace eagle {
+
+__global__ __launch_bounds__(1024) void expand_kernel(
+    int32_t* __restrict__ tok, int32_t* __restrict__ par, int32_t* __restrict__ dep,
+    float* __restrict__ val, int pool_n, const int32_t* __restrict__ frontier, int kf,
+    const int32_t* __restrict__ cid, const float* __restrict__ clogp, int k, int ksel,
+    int32_t* __restrict__ new_frontier, int32_t* __restrict__ status) {
+  __shared__ float vs[EAGLE_MAX_APPEND];
+  __shared__ uint8_t sel[EAGLE_MAX_APPEND];
+  const int n = kf * k;
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    const int s = t / k;
+    int u = frontier[s];
+    if (u < 0 || u >= pool_n) {
+      set_status(status, EAGLE_DEV_BAD_INDEX);
+      u = 0;
+    }
+    const float v = __fadd_rn(val[u], clogp[t]);
+    const int e = pool_n + t;
+    tok[e] = cid[t];
+    par[e] = u;
+    dep[e] = dep[u] + 1;
+    val[e] = v;
+    vs[t] = v;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    const float v = vs[t];
+    int rank = 0;
+    for (int o = 0; o < n; ++o) rank += better(vs[o], o, v, t) ? 1 : 0;
+    sel[t] = rank < ksel ? 1 : 0;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    if (!sel[t]) continue;
+    int pos = 0;
+    for (int o = 0; o < t; ++o) pos += sel[o];
+    // exactly k_select entries rank below k_select unless values are NaN
+    if (pos < ksel) new_frontier[pos] = pool_n + t;
+  }
+}
+
+__global__ __launch_bounds__(1024) void rerank_kernel(
+    const int32_t* __restrict__ tok, const int32_t* __restrict__ par,
+    const int32_t* __restrict__ dep, const float* __restrict__ val, int pool_n, int T,
+    int32_t* __restrict__ node_token, int32_t* __restrict__ node_parent,
+    int32_t* __restrict__ node_depth, int32_t* __restrict__ node_pool_idx,
+    int32_t* __restrict__ status) {
+  __shared__ float vs[EAGLE_MAX_POOL];
+  __shared__ int16_t pos[EAGLE_MAX_POOL];
+  __shared__ int32_t cnt[1024];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < pool_n; i += blockDim.x) vs[i] = val[i];
+  __syncthreads();
+  // keep flag per entry: the root always, others when fewer than T-1 non-root
+  // entries beat them
+  const int per = (pool_n + blockDim.x - 1) / blockDim.x;
+  const int lo = tid * per;
+  const int hi = min(pool_n, lo + per);
+  int mine = 0;
+  for (int i = lo; i < hi; ++i) {
+    bool keep;
+    if (i == 0) {
+      keep = true;
+    } else {
+      const float v = vs[i];
+      int rank = 0;
+      for (int o = 1; o < pool_n && rank < T - 1; ++o) rank += better(vs[o], o, v, i) ? 1 : 0;
+      keep = rank < T - 1;
+    }
+    pos[i] = keep ? 1 : 0;
+    mine += keep ? 1 : 0;
+  }
+  cnt[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < (int)blockDim.x; ++w) {
+      const int c = cnt[w];
+      cnt[w] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  int run = cnt[tid];
+  for (int i = lo; i < hi; ++i) {
+    if (pos[i]) {
+      pos[i] = (int16_t)run;
+      ++run;
+    } else {
+      pos[i] = -1;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < pool_n; i += blockDim.x) {
+    const int p = pos[i];
+    if (p < 0 || p >= T) continue;
+    node_token[p] = tok[i];
+    node_depth[p] = dep[i];
+    node_pool_idx[p] = i;
+    const int pp = par[i];
+    int np = -1;
+    if (pp != -1) {
+      if (pp < 0 || pp >= i) {
+        set_status(status, EAGLE_DEV_BAD_PARENT);
+      } else if (pos[pp] < 0) {
+        set_status(status, EAGLE_DEV_ORPHAN);
+      } else {
+        np = pos[pp];
+      }
+    }
+    node_parent[p] = np;
+  }
+}
+
+}  // namespace eagle
+
+extern "C" int eagle_expand_rerank(int32_t mode, int32_t* pool_token, int32_t* pool_parent,
+                                   int32_t* pool_depth, float* pool_value, int32_t pool_n,
+                                   int32_t pool_cap, const int32_t* frontier, int32_t kf,
+                                   const int32_t* child_id, const float* child_logp, int32_t k,
+                                   int32_t k_select, int32_t* new_frontier, int32_t T,
+                                   int32_t* node_token, int32_t* node_parent,
+                                   int32_t* node_depth, int32_t* node_pool_idx,
+                                   int32_t* dev_status, hipStream_t stream) {
+  EAGLE_REQUIRE(pool_token && pool_parent && pool_depth && pool_value, EAGLE_EINVAL);
+  EAGLE_REQUIRE(pool_n >= 1 && pool_n <= pool_cap, EAGLE_EINVAL);
+  if (mode == EAGLE_EXPAND) {
+    EAGLE_REQUIRE(frontier && child_id && child_logp && new_frontier, EAGLE_EINVAL);
+    EAGLE_REQUIRE(kf >= 1 && k >= 1, EAGLE_EINVAL);
+    EAGLE_REQUIRE((int64_t)kf * k <= EAGLE_MAX_APPEND, EAGLE_EINVAL);
+    EAGLE_REQUIRE((int64_t)pool_n + (int64_t)kf * k <= pool_cap, EAGLE_EINVAL);
+    EAGLE_REQUIRE(k_select >= 1 && k_select <= kf * k, EAGLE_EINVAL);
+    hipLaunchKernelGGL(eagle::expand_kernel, dim3(1), dim3(1024), 0, stream, pool_token,
+                       pool_parent, pool_depth, pool_value, pool_n, frontier, kf, child_id,
+                       child_logp, k, k_select, new_frontier, dev_status);
+  } else if (mode == EAGLE_RERANK) {
+    EAGLE_REQUIRE(node_token && node_parent && node_depth && node_pool_idx, EAGLE_EINVAL);
+    EAGLE_REQUIRE(pool_n <= EAGLE_MAX_POOL, EAGLE_EINVAL);
+    EAGLE_REQUIRE(T >= 1 && T <= pool_n && T <= EAGLE_MAX_TREE, EAGLE_EINVAL);
+    hipLaunchKernelGGL(eagle::rerank_kernel, dim3(1), dim3(1024), 0, stream, pool_token,
+                       pool_parent, pool_depth, pool_value, pool_n, T, node_token, node_parent,
+                       node_depth, node_pool_idx, dev_status);
+  } else {
+    return EAGLE_EINVAL;
+  }
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}

@@ -8,3 +8,16 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(scope="session")
+def dev():
+    """cuda:0 with libeagle.so loaded; fails (not skips) if either is missing."""
+    import torch
+    from speculative_decoding_parent_amd import _lib
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    _lib.lib()
+    return torch.device("cuda:0")

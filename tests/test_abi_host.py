@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol
+eagle.h declares, and rejects bad arguments before enqueuing anything.
+No call here reaches a kernel launch, so these run without a GPU."""
+import ctypes
+
+import pytest
+
+from speculative_decoding_parent_amd import _lib
+
+EINVAL, EUNSUP, EWS = _lib.EAGLE_EINVAL, _lib.EAGLE_EUNSUPPORTED, _lib.EAGLE_EWORKSPACE
+FAKE = 0x100000   # 16-byte aligned non-null "device" address, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _lib.declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib._PROTOS, n
+
+
+def test_version_and_strings(lib):
+    assert lib.eagle_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.eagle_status_string(code)
+
+
+def test_workspace_queries(lib):
+    # LM head: per-wave partial statistics + per-wave top-k lists
+    nw = ((128256 + 255) // 256) * 4
+    want = 0
+    for n in (nw * 64 * 8, nw * 64 * 10 * 4, nw * 64 * 10 * 4):
+        want += (n + 255) // 256 * 256
+    assert lib.eagle_lmhead_topk_workspace(64, 4096, 128256, 10, _lib.EAGLE_BF16) == want
+    assert lib.eagle_lmhead_topk_workspace(15, 256, 1024, 4, _lib.EAGLE_F32) >= 15 * 1024 * 4
+    assert lib.eagle_lmhead_topk_workspace(0, 256, 1024, 4, _lib.EAGLE_F32) == 0
+    # attention: (splits + tree) x rows x (hd + 2) floats
+    ws = lib.eagle_tree_attn_workspace(64, 32, 8, 128, 32768, 64, _lib.EAGLE_BF16)
+    assert ws >= 33 * 64 * 32 * (128 + 2) * 4
+    assert lib.eagle_tree_attn_workspace(64, 30, 8, 128, 100, 64, _lib.EAGLE_BF16) == 0
+    assert lib.eagle_accept_workspace(64, 128256) == 64 * 32 * 16
+    assert lib.eagle_accept_workspace(0, 10) == 0
+
+
+def test_mask_argument_errors(lib):
+    f = lib.eagle_build_tree_mask
+    assert f(None, 4, 1, FAKE, FAKE, None, None) == EINVAL
+    assert f(FAKE, 0, 1, FAKE, FAKE, None, None) == EINVAL
+    assert f(FAKE, 257, 5, FAKE, FAKE, None, None) == EINVAL
+    assert f(FAKE, 65, 1, FAKE, FAKE, None, None) == EINVAL       # too few words
+    assert f(FAKE, 10, 5, FAKE, FAKE, None, None) == EINVAL       # more than 4 words
+    assert f(FAKE, 10, 1, FAKE + 4, FAKE, None, None) == EINVAL   # misaligned mask
+
+
+def attn_args(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, L=100, ldc=100, kt=FAKE, vt=FAKE, Tk=8, ldt=8, mask=FAKE,
+             words=1, mask_rows=8, qmap=None, Tq=8, Hq=8, Hkv=2, hd=128, scale=0.088,
+             in_dt=_lib.EAGLE_BF16, out_dt=_lib.EAGLE_BF16, out=FAKE, ws=FAKE, nb=1 << 30,
+             st=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def test_attn_argument_errors(lib):
+    f = lib.eagle_tree_attn
+    assert f(*attn_args(q=None)) == EINVAL
+    assert f(*attn_args(hd=96)) == EUNSUP
+    assert f(*attn_args(Hq=6, Hkv=4)) == EINVAL
+    assert f(*attn_args(Tq=0)) == EINVAL
+    assert f(*attn_args(Tk=300, ldt=300, words=5)) == EINVAL
+    assert f(*attn_args(ldc=50)) == EINVAL
+    assert f(*attn_args(kc=None)) == EINVAL
+    assert f(*attn_args(q=FAKE + 8)) == EINVAL
+    assert f(*attn_args(ws=FAKE + 16)) == EINVAL
+    assert f(*attn_args(nb=16)) == EWS
+    assert f(*attn_args(scale=0.0)) == EINVAL
+    assert f(*attn_args(in_dt=7)) == EINVAL
+
+
+def test_lmhead_argument_errors(lib):
+    f = lib.eagle_lmhead_topk
+    base = [FAKE, FAKE, 4, 256, 1000, 10, _lib.EAGLE_BF16, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+            None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == EINVAL
+    assert call(a5=0) == EINVAL
+    assert call(a5=65) == EINVAL
+    assert call(a4=5, a5=6) == EINVAL            # k > V
+    assert call(a3=200) == EUNSUP                # d not a multiple of 128 (bf16)
+    assert call(a11=FAKE + 64) == EINVAL         # workspace not 256-aligned
+    assert call(a12=100) == EWS
+    assert call(a6=9) == EINVAL
+
+
+def test_tree_argument_errors(lib):
+    f = lib.eagle_expand_rerank
+    P = [FAKE] * 4
+    # EXPAND: pool overflow, k_select out of range, too many appended entries
+    assert f(0, *P, 10, 50, FAKE, 5, FAKE, FAKE, 10, 3, FAKE, 0, None, None, None, None, None,
+             None) == EINVAL
+    assert f(0, *P, 10, 100, FAKE, 5, FAKE, FAKE, 10, 51, FAKE, 0, None, None, None, None, None,
+             None) == EINVAL
+    assert f(0, *P, 10, 100000, FAKE, 100, FAKE, FAKE, 50, 3, FAKE, 0, None, None, None, None,
+             None, None) == EINVAL
+    # RERANK: T larger than the pool, pool larger than the cap
+    assert f(1, *P, 10, 100, None, 0, None, None, 0, 0, None, 11, FAKE, FAKE, FAKE, FAKE, None,
+             None) == EINVAL
+    assert f(1, *P, 9000, 9000, None, 0, None, None, 0, 0, None, 64, FAKE, FAKE, FAKE, FAKE, None,
+             None) == EINVAL
+    assert f(2, *P, 10, 100, None, 0, None, None, 0, 0, None, 5, FAKE, FAKE, FAKE, FAKE, None,
+             None) == EINVAL
+
+
+def test_accept_argument_errors(lib):
+    f = lib.eagle_accept
+    assert f(0, 5, FAKE, FAKE, None, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
+             None) == EINVAL                                     # greedy without top1
+    assert f(1, 5, FAKE, FAKE, None, FAKE, 100, 0.0, FAKE, 5, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+             None, None) == EINVAL                               # temperature 0
+    assert f(1, 5, FAKE, FAKE, None, FAKE, 100, 1.0, FAKE, 5, FAKE, FAKE, FAKE, FAKE, 8, None,
+             None) == EWS
+    assert f(0, 300, FAKE, FAKE, FAKE, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
+             None) == EINVAL                                     # T > 256
+    assert f(3, 5, FAKE, FAKE, FAKE, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
+             None) == EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        _lib.lib()
