@@ -240,6 +240,88 @@ int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
                  void* workspace, size_t ws_bytes, int32_t* dev_status,
                  hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Decoder-layer support for the draft rounds and the verify pass.
+ *
+ * [G] Key Architectural Mechanics 1: each draft step fuses the previous
+ * feature with the current token's embedding, h = W_fuse [f ; Emb(y)], runs one
+ * transformer decoder layer, f' = TransformerLayer(h), and scores f' with the
+ * target's LM head.  [D] yuhuili/EAGLE3-LLaMA3.1-Instruct-8B printout: the
+ * layer is a Llama decoder layer (RMSNorm eps 1e-5, q/k/v/o projections,
+ * SiLU-gated MLP, rotary embedding, no biases) and the draft shares the
+ * target's embedding table.  Weights are [out][in] bf16 (nn.Linear layout).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * eagle_linear - out[m][n] = sum_k x[m][k] W[n][k] (+ residual[m][n]).
+ *   x [M][K] bf16 (M 1..256, K % 128 == 0), W [N][K] bf16, residual [M][N] f32
+ *   or NULL (may alias out when out_dt is f32), out [M][N] out_dt.
+ */
+int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
+                 const float* residual, void* out, eagle_dtype out_dt, hipStream_t stream);
+
+/*
+ * eagle_linear_swiglu - out[m][n] = silu(x W_gate^T)[m][n] * (x W_up^T)[m][n],
+ * the LlamaMLP hidden activation.  x [M][K] bf16, W_gate/W_up [N][K] bf16,
+ * out [M][N] bf16.
+ */
+int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const void* w_gate,
+                        const void* w_up, int32_t N, void* out, hipStream_t stream);
+
+/*
+ * eagle_rmsnorm - out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gamma.
+ *   x [M][N] f32, gamma [N] f32, out [M][N] bf16.
+ */
+int eagle_rmsnorm(const float* x, const float* gamma, int32_t M, int32_t N, float eps,
+                  void* out, hipStream_t stream);
+
+/*
+ * eagle_rope_qkv - rotary embedding of q and k, and placement of k/v in the
+ * tree K/V buffers.  qkv [M][(Hq + 2 Hkv) hd] f32 (q heads, then k, then v);
+ * row m sits at position pos_base + depth[m] (reading: a tree node's position
+ * is the prefix length plus its depth); dims i and i + hd/2 turn by
+ * position * theta^(-2i/hd).  q_out [M][Hq][hd] bf16; k (rotated) and v go to
+ * k_tree/v_tree [Hkv][ld_tree][hd] bf16 at row row_slot[m] (m when NULL);
+ * a slot outside [0, slot_cap) sets EAGLE_DEV_BAD_INDEX and is skipped.
+ */
+int eagle_rope_qkv(const float* qkv, int32_t M, int32_t Hq, int32_t Hkv, int32_t hd,
+                   const int32_t* depth, int64_t pos_base, float theta, const int32_t* row_slot,
+                   int32_t slot_cap, void* q_out, void* k_tree, void* v_tree, int32_t ld_tree,
+                   int32_t* dev_status, hipStream_t stream);
+
+/*
+ * eagle_draft_rows - bookkeeping for one draft round whose rows are the pool
+ * entries frontier[0..kf).  Row j gets draft slot slot_base + j (the slot
+ * holds its K/V and its output feature); slot_of_pool[frontier[j]] is set to
+ * it and slot_parent[slot] to the slot of the entry's parent (-1 for the
+ * root).  Per row: row_token, row_depth (pool depth), row_slot and row_src =
+ * the parent's slot, whose output feature predicted this row's token and is
+ * paired with it ([G] Reference Implementation: the feature and the token it
+ * produced step together).  slot_of_pool [pool capacity] must hold the slots
+ * of earlier rounds.
+ */
+int eagle_draft_rows(const int32_t* frontier, int32_t kf, const int32_t* pool_token,
+                     const int32_t* pool_parent, const int32_t* pool_depth, int32_t pool_n,
+                     int32_t* slot_of_pool, int32_t slot_base, int32_t slot_cap,
+                     int32_t* slot_parent, int32_t* row_token, int32_t* row_depth,
+                     int32_t* row_slot, int32_t* row_src, int32_t* dev_status,
+                     hipStream_t stream);
+
+/*
+ * eagle_draft_input - the fused input [f ; Emb(y)] of each draft row:
+ * out[m] = [bf16(feat[row_src[m]]) (root_feat when row_src[m] < 0) ;
+ * embed[row_token[m]]].  feat [feat_rows][d] f32, root_feat [d] f32,
+ * embed [V][d] bf16, out [M][2d] bf16.
+ */
+int eagle_draft_input(int32_t M, const int32_t* row_token, const int32_t* row_src,
+                      const float* feat, int32_t feat_rows, const float* root_feat,
+                      const void* embed, int32_t V, int32_t d, void* out, int32_t* dev_status,
+                      hipStream_t stream);
+
+/* eagle_embed - out[m] = embed[token[m]] as f32 ([M][d]); embed [V][d] bf16. */
+int eagle_embed(int32_t M, const int32_t* token, const void* embed, int32_t V, int32_t d,
+                float* out, int32_t* dev_status, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,15 +88,20 @@ def draft_and_verify_cycle(cw: CycleWeights, root_token: int, root_feature, *, h
         z = rms_norm(out, cw.draft_norm, eps)
         lm = lm_head_topk(z, cw.w_lm, k)
         srt = -np.sort(-lm["logits"], axis=1)
-        if srt.shape[1] > k:
-            topk_margin = min(topk_margin, float(np.min(srt[:, k - 1] - srt[:, k])))
+        # smallest gap between consecutive logits among the top k + 1 of each row:
+        # the order of the chosen ids (and the cut after k) is robust to logit
+        # errors below half this gap
+        row_margin = np.min(srt[:, :k] - srt[:, 1:k + 1], axis=1) if srt.shape[1] > k else \
+            np.full(len(rows), np.inf)
+        topk_margin = min(topk_margin, float(np.min(row_margin)))
         logp32 = lm["logp"].astype(np.float32)
         start = len(pool)
         new_frontier = expand(pool, rows, lm["ids"], logp32, k_select)
-        frontier_margin = min(frontier_margin,
-                              selection_margin(pool.value, new_frontier, range(start, len(pool))))
+        fr_margin = selection_margin(pool.value, new_frontier, range(start, len(pool)))
+        frontier_margin = min(frontier_margin, fr_margin)
         rounds_out.append({"rows": rows, "ids": lm["ids"], "logp": logp32, "lse": lm["lse"],
-                           "frontier": new_frontier, "x": x, "out": out})
+                           "frontier": new_frontier, "x": x, "out": out,
+                           "topk_margin": row_margin, "frontier_margin": fr_margin})
         if r < rounds - 1:
             for p in new_frontier:
                 slot_of[p] = len(slot_parent)

@@ -38,6 +38,16 @@ def silu(x) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 
 
+def linear(x, W) -> np.ndarray:
+    """x W^T for W stored [out][in] (nn.Linear without bias)."""
+    return _f64(x) @ _f64(W).T
+
+
+def swiglu_mlp_hidden(x, w_gate, w_up) -> np.ndarray:
+    """LlamaMLP hidden activation silu(x W_gate^T) * (x W_up^T)."""
+    return silu(linear(x, w_gate)) * linear(x, w_up)
+
+
 def rope(x, pos, theta: float = 500000.0) -> np.ndarray:
     """Rotate [rows][H][hd] by position: pair (i, i + hd/2) turns by
     pos * theta^(-2i/hd)."""

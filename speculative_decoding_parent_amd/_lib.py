@@ -49,6 +49,15 @@ _PROTOS = {
     "eagle_accept_workspace": (_SZ, [_I32, _I32]),
     "eagle_accept": (_I32, [_I32, _I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ,
                             _P, _P]),
+    "eagle_linear": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, ctypes.c_int, _P]),
+    "eagle_linear_swiglu": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P, _P]),
+    "eagle_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F32, _P, _P]),
+    "eagle_rope_qkv": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _I64, _F32, _P, _I32, _P, _P, _P,
+                              _I32, _P, _P]),
+    "eagle_draft_rows": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                _P]),
+    "eagle_draft_input": (_I32, [_I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
 }
 
 _lib = None
@@ -220,3 +229,72 @@ def eagle_accept(mode, node_token, node_parent, target_top1=None, target_logits=
         temperature, _ptr(uniforms), max_path, _ptr(path), _ptr(n_accepted), _ptr(bonus_token),
         _ptr(ws), nb, _ptr(dev_status), _stream()))
     return path, n_accepted, bonus_token
+
+
+# ---------------------------------------------------------------- layer support
+
+def eagle_linear(x, W, residual=None, out=None, out_dtype=torch.float32):
+    """out = x W^T (+ residual); x [M][K] bf16, W [N][K] bf16."""
+    M, K = x.shape
+    N = W.shape[0]
+    out = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    _check("eagle_linear", lib().eagle_linear(_ptr(x), M, K, _ptr(W), N, _ptr(residual), _ptr(out),
+                                              _dt(out), _stream()))
+    return out
+
+
+def eagle_linear_swiglu(x, w_gate, w_up, out=None):
+    M, K = x.shape
+    N = w_gate.shape[0]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _check("eagle_linear_swiglu", lib().eagle_linear_swiglu(_ptr(x), M, K, _ptr(w_gate), _ptr(w_up),
+                                                            N, _ptr(out), _stream()))
+    return out
+
+
+def eagle_rmsnorm(x, gamma, eps=1e-5, out=None):
+    M, N = x.shape
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _check("eagle_rmsnorm", lib().eagle_rmsnorm(_ptr(x), _ptr(gamma), M, N, eps, _ptr(out),
+                                                _stream()))
+    return out
+
+
+def eagle_rope_qkv(qkv, Hq, Hkv, hd, depth, pos_base, k_tree, v_tree, row_slot=None,
+                   theta=500000.0, q_out=None, dev_status=None):
+    M = qkv.shape[0]
+    q_out = torch.empty((M, Hq, hd), dtype=torch.bfloat16, device=qkv.device) if q_out is None else q_out
+    ld = k_tree.shape[1]
+    _check("eagle_rope_qkv", lib().eagle_rope_qkv(
+        _ptr(qkv), M, Hq, Hkv, hd, _ptr(depth), pos_base, theta, _ptr(row_slot), ld, _ptr(q_out),
+        _ptr(k_tree), _ptr(v_tree), ld, _ptr(dev_status), _stream()))
+    return q_out
+
+
+def eagle_draft_rows(frontier, pool_token, pool_parent, pool_depth, pool_n, slot_of_pool,
+                     slot_base, slot_parent, rows, dev_status=None):
+    """rows: (row_token, row_depth, row_slot, row_src) int32 tensors of >= kf entries."""
+    kf = frontier.shape[0]
+    _check("eagle_draft_rows", lib().eagle_draft_rows(
+        _ptr(frontier), kf, _ptr(pool_token), _ptr(pool_parent), _ptr(pool_depth), pool_n,
+        _ptr(slot_of_pool), slot_base, slot_parent.shape[0], _ptr(slot_parent), *[_ptr(r) for r in rows],
+        _ptr(dev_status), _stream()))
+
+
+def eagle_draft_input(row_token, row_src, feat, root_feat, embed, M=None, out=None, dev_status=None):
+    M = row_token.shape[0] if M is None else M
+    V, d = embed.shape
+    out = torch.empty((M, 2 * d), dtype=torch.bfloat16, device=embed.device) if out is None else out
+    _check("eagle_draft_input", lib().eagle_draft_input(
+        M, _ptr(row_token), _ptr(row_src), _ptr(feat), feat.shape[0], _ptr(root_feat), _ptr(embed),
+        V, d, _ptr(out), _ptr(dev_status), _stream()))
+    return out
+
+
+def eagle_embed(token, embed, out=None, dev_status=None):
+    M = token.shape[0]
+    V, d = embed.shape
+    out = torch.empty((M, d), dtype=torch.float32, device=embed.device) if out is None else out
+    _check("eagle_embed", lib().eagle_embed(M, _ptr(token), _ptr(embed), V, d, _ptr(out),
+                                            _ptr(dev_status), _stream()))
+    return out

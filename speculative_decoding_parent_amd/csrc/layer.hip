@@ -1,0 +1,358 @@
+// Decoder-layer support for the draft and verify passes of one cycle.
+//
+// Sources: "EAGLE-2: Feature-Level Speculative Decoding Guide", Key
+// Architectural Mechanics 1 - the draft step h = W_fuse [f ; Emb(y)],
+// f' = TransformerLayer(h); "Support Eagle-3 Speculative Decoding in llama.cpp"
+// - the yuhuili/EAGLE3-LLaMA3.1-Instruct-8B printout (q/k/v/o projections, a
+// SiLU-gated MLP 4096 -> 14336 -> 4096, RMSNorms with eps 1e-5, rotary
+// embedding, no biases) and the draft sharing the target's embedding.
+//
+// Projections use the weight-streaming MFMA core (few rows, every weight byte
+// read once from HBM) with two epilogues: plain (+ an fp32 residual) and SwiGLU
+// (each wave streams 32 gate rows and the 32 matching up rows, so silu(g) * u is
+// formed in registers and only the product is written).  The residual stream
+// stays fp32; only MFMA operands (normed activations, attention output, MLP
+// hidden) are bf16.  RoPE angles are formed and rotated in fp64 (positions up
+// to ~37K make fp32 angles lose ~1e-3 rad).
+#include "wstream.h"
+
+namespace eagle {
+
+constexpr int kLinRowsBlock = 256;     // plain: 4 waves x 64 output columns
+constexpr int kGluColsBlock = 128;     // swiglu: 4 waves x 32 output columns
+
+struct LinParams {
+  const bf16_t* x;
+  int M, K;
+  const bf16_t* w0;   // plain: W [N][K]; swiglu: W_gate [N][K]
+  const bf16_t* w1;   // swiglu: W_up [N][K]
+  int N;
+  const float* residual;   // plain, nullable: [M][N]
+  void* out;               // [M][N]
+  int out_bf16;
+};
+
+__device__ __forceinline__ void store4(void* out, int out_bf16, size_t off, int n, int N,
+                                       const float (&y)[4]) {
+  if (out_bf16) {
+    bf16_t* o = (bf16_t*)out + off;
+    if ((N & 3) == 0 && n + 3 < N) {
+      *(u32x2*)o = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (n + j < N) o[j] = (bf16_t)f32_to_bf16_bits(y[j]);
+    }
+  } else {
+    float* o = (float*)out + off;
+    if ((N & 3) == 0 && n + 3 < N) {
+      *(f32x4*)o = f32x4{y[0], y[1], y[2], y[3]};
+    } else {
+      for (int j = 0; j < 4; ++j)
+        if (n + j < N) o[j] = y[j];
+    }
+  }
+}
+
+template <int NT, int SWIGLU>
+__global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void linear_bf16_kernel(LinParams p) {
+  __shared__ __attribute__((aligned(16))) bf16_t fs[ws_lds_elems<NT>()];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int n0 = SWIGLU ? blockIdx.x * kGluColsBlock + wave * 32
+                        : blockIdx.x * kLinRowsBlock + wave * 64;
+  const bf16_t* wrow[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int col = SWIGLU ? n0 + (mt & 1) * 16 + r16 : n0 + mt * 16 + r16;
+    const bf16_t* w = (SWIGLU && mt >= 2) ? p.w1 : p.w0;
+    wrow[mt] = w + (size_t)min(col, p.N - 1) * p.K + g * 32;
+  }
+  f32x4 acc[4][NT];
+  wstream_mfma<NT, 4>(wrow, p.x, p.K, p.M, p.K, fs, acc);
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int m = nt * 16 + r16;
+    if (m >= p.M) continue;
+    if (SWIGLU) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int n = n0 + mt * 16 + 4 * g;
+        if (n >= p.N) continue;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float gt = acc[mt][nt][j];
+          y[j] = gt / (1.0f + expf(-gt)) * acc[mt + 2][nt][j];
+        }
+        store4(p.out, 1, (size_t)m * p.N + n, n, p.N, y);
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int n = n0 + mt * 16 + 4 * g;
+        if (n >= p.N) continue;
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[j] = acc[mt][nt][j];
+          if (p.residual && n + j < p.N) y[j] += p.residual[(size_t)m * p.N + n + j];
+        }
+        store4(p.out, p.out_bf16, (size_t)m * p.N + n, n, p.N, y);
+      }
+    }
+  }
+}
+
+// out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gamma, fp32 in, bf16 out.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+                                                      const float* __restrict__ gamma, int N,
+                                                      float eps, bf16_t* __restrict__ out) {
+  __shared__ float red[4];
+  const float* row = x + (size_t)blockIdx.x * N;
+  float ss = 0.f;
+  for (int n = threadIdx.x; n < N; n += 256) ss = fmaf(row[n], row[n], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)N + eps);
+  bf16_t* o = out + (size_t)blockIdx.x * N;
+  for (int n = threadIdx.x; n < N; n += 256)
+    o[n] = (bf16_t)f32_to_bf16_bits(row[n] * r * gamma[n]);
+}
+
+// qkv [M][(Hq + 2 Hkv) hd] fp32 -> q_out [M][Hq][hd] bf16 (rotated); k (rotated)
+// and v into the tree K/V at slot row_slot[m].  Rotation pairs dims i and
+// i + hd/2 by angle (pos_base + depth[m]) * theta^(-2i/hd).
+__global__ __launch_bounds__(256) void rope_qkv_kernel(
+    const float* __restrict__ qkv, int Hq, int Hkv, int hd, const int32_t* __restrict__ depth,
+    int64_t pos_base, double theta, const int32_t* __restrict__ row_slot, int slot_cap,
+    bf16_t* __restrict__ q_out, bf16_t* __restrict__ k_tree, bf16_t* __restrict__ v_tree,
+    int ld_tree, int32_t* __restrict__ status) {
+  const int m = blockIdx.x;
+  const int half = hd / 2;
+  const int H = Hq + 2 * Hkv;
+  int slot = row_slot ? row_slot[m] : m;
+  if (slot < 0 || slot >= slot_cap) {
+    if (threadIdx.x == 0) set_status(status, EAGLE_DEV_BAD_INDEX);
+    slot = -1;
+  }
+  const double pos = (double)(pos_base + depth[m]);
+  const float* row = qkv + (size_t)m * H * hd;
+  for (int e = threadIdx.x; e < H * half; e += 256) {
+    const int hh = e / half;
+    const int i = e - hh * half;
+    const float x1 = row[hh * hd + i];
+    const float x2 = row[hh * hd + i + half];
+    if (hh < Hq + Hkv) {
+      const double ang = pos * pow(theta, -2.0 * (double)i / (double)hd);
+      double sn, cs;
+      sincos(ang, &sn, &cs);
+      const float y1 = (float)((double)x1 * cs - (double)x2 * sn);
+      const float y2 = (float)((double)x2 * cs + (double)x1 * sn);
+      if (hh < Hq) {
+        bf16_t* q = q_out + ((size_t)m * Hq + hh) * hd;
+        q[i] = (bf16_t)f32_to_bf16_bits(y1);
+        q[i + half] = (bf16_t)f32_to_bf16_bits(y2);
+      } else if (slot >= 0) {
+        bf16_t* k = k_tree + ((size_t)(hh - Hq) * ld_tree + slot) * hd;
+        k[i] = (bf16_t)f32_to_bf16_bits(y1);
+        k[i + half] = (bf16_t)f32_to_bf16_bits(y2);
+      }
+    } else if (slot >= 0) {
+      bf16_t* v = v_tree + ((size_t)(hh - Hq - Hkv) * ld_tree + slot) * hd;
+      v[i] = (bf16_t)f32_to_bf16_bits(x1);
+      v[i + half] = (bf16_t)f32_to_bf16_bits(x2);
+    }
+  }
+}
+
+// Bookkeeping for one draft round: the rows are the frontier's pool entries.
+__global__ __launch_bounds__(256) void draft_rows_kernel(
+    const int32_t* __restrict__ frontier, int kf, const int32_t* __restrict__ pool_token,
+    const int32_t* __restrict__ pool_parent, const int32_t* __restrict__ pool_depth, int pool_n,
+    int32_t* __restrict__ slot_of_pool, int slot_base, int slot_cap,
+    int32_t* __restrict__ slot_parent, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ row_depth, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ status) {
+  const int j = threadIdx.x;
+  if (j >= kf) return;
+  int f = frontier[j];
+  if (f < 0 || f >= pool_n) {
+    set_status(status, EAGLE_DEV_BAD_INDEX);
+    f = 0;
+  }
+  const int par = pool_parent[f];
+  int src = -1;
+  if (par >= 0) {
+    src = par < pool_n ? slot_of_pool[par] : -1;
+    if (src < 0 || src >= slot_cap) {
+      set_status(status, EAGLE_DEV_BAD_INDEX);
+      src = -1;
+    }
+  }
+  const int slot = slot_base + j;
+  slot_of_pool[f] = slot;
+  slot_parent[slot] = src;
+  row_token[j] = pool_token[f];
+  row_depth[j] = pool_depth[f];
+  row_slot[j] = slot;
+  row_src[j] = src;
+}
+
+// out[m] = [ bf16(src >= 0 ? feat[src] : root_feat) ; embed[token] ]  ([M][2d] bf16)
+__global__ __launch_bounds__(256) void draft_input_kernel(
+    const int32_t* __restrict__ row_token, const int32_t* __restrict__ row_src,
+    const float* __restrict__ feat, int feat_rows, const float* __restrict__ root_feat,
+    const bf16_t* __restrict__ embed, int V, int d, bf16_t* __restrict__ out,
+    int32_t* __restrict__ status) {
+  const int m = blockIdx.x;
+  int tok = row_token[m];
+  if (tok < 0 || tok >= V) {
+    if (threadIdx.x == 0) set_status(status, EAGLE_DEV_BAD_TOKEN);
+    tok = 0;
+  }
+  const int src = row_src[m];
+  const float* f = (src >= 0 && src < feat_rows) ? feat + (size_t)src * d : root_feat;
+  bf16_t* o = out + (size_t)m * 2 * d;
+  const bf16_t* e = embed + (size_t)tok * d;
+  for (int n = threadIdx.x; n < d; n += 256) {
+    o[n] = (bf16_t)f32_to_bf16_bits(f[n]);
+    o[d + n] = e[n];
+  }
+}
+
+// out[m] = float(embed[token[m]])
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ token,
+                                                    const bf16_t* __restrict__ embed, int V, int d,
+                                                    float* __restrict__ out,
+                                                    int32_t* __restrict__ status) {
+  const int m = blockIdx.x;
+  int tok = token[m];
+  if (tok < 0 || tok >= V) {
+    if (threadIdx.x == 0) set_status(status, EAGLE_DEV_BAD_TOKEN);
+    tok = 0;
+  }
+  const bf16_t* e = embed + (size_t)tok * d;
+  for (int n = threadIdx.x; n < d; n += 256) out[(size_t)m * d + n] = bf16_bits_to_f32(e[n]);
+}
+
+template <int NT, int SWIGLU>
+static void launch_lin(const LinParams& p, hipStream_t s) {
+  const int cols = SWIGLU ? kGluColsBlock : kLinRowsBlock;
+  hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU>), dim3((p.N + cols - 1) / cols), dim3(256),
+                     0, s, p);
+}
+
+template <int SWIGLU>
+static void dispatch_lin(const LinParams& p, hipStream_t s) {
+  const int nt = (p.M + 15) / 16;
+  if (nt <= 1) launch_lin<1, SWIGLU>(p, s);
+  else if (nt <= 2) launch_lin<2, SWIGLU>(p, s);
+  else if (nt <= 4) launch_lin<4, SWIGLU>(p, s);
+  else if (nt <= 8) launch_lin<8, SWIGLU>(p, s);
+  else launch_lin<16, SWIGLU>(p, s);
+}
+
+}  // namespace eagle
+
+using eagle::bf16_t;
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+extern "C" int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
+                            const float* residual, void* out, eagle_dtype out_dt,
+                            hipStream_t stream) {
+  EAGLE_REQUIRE(x && W && out, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && N >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(out_dt == EAGLE_BF16 || out_dt == EAGLE_F32, EAGLE_EINVAL);
+  EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(aligned16(x) && aligned16(W) && aligned16(out), EAGLE_EINVAL);
+  eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)W, nullptr, N, residual, out,
+                     out_dt == EAGLE_BF16 ? 1 : 0};
+  eagle::dispatch_lin<0>(p, stream);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const void* w_gate,
+                                   const void* w_up, int32_t N, void* out, hipStream_t stream) {
+  EAGLE_REQUIRE(x && w_gate && w_up && out, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && N >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(out),
+                EAGLE_EINVAL);
+  eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)w_gate, (const bf16_t*)w_up, N,
+                     nullptr, out, 1};
+  eagle::dispatch_lin<1>(p, stream);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_rmsnorm(const float* x, const float* gamma, int32_t M, int32_t N, float eps,
+                             void* out, hipStream_t stream) {
+  EAGLE_REQUIRE(x && gamma && out && M >= 1 && N >= 1 && eps >= 0.0f, EAGLE_EINVAL);
+  hipLaunchKernelGGL(eagle::rmsnorm_kernel, dim3(M), dim3(256), 0, stream, x, gamma, N, eps,
+                     (bf16_t*)out);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_rope_qkv(const float* qkv, int32_t M, int32_t Hq, int32_t Hkv, int32_t hd,
+                              const int32_t* depth, int64_t pos_base, float theta,
+                              const int32_t* row_slot, int32_t slot_cap, void* q_out,
+                              void* k_tree, void* v_tree, int32_t ld_tree, int32_t* dev_status,
+                              hipStream_t stream) {
+  EAGLE_REQUIRE(qkv && depth && q_out && k_tree && v_tree, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && Hq >= 1 && Hkv >= 1 && hd >= 2 && hd % 2 == 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(slot_cap >= 1 && ld_tree >= slot_cap && theta > 0.0f && pos_base >= 0,
+                EAGLE_EINVAL);
+  hipLaunchKernelGGL(eagle::rope_qkv_kernel, dim3(M), dim3(256), 0, stream, qkv, Hq, Hkv, hd,
+                     depth, pos_base, (double)theta, row_slot, slot_cap, (bf16_t*)q_out,
+                     (bf16_t*)k_tree, (bf16_t*)v_tree, ld_tree, dev_status);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_draft_rows(const int32_t* frontier, int32_t kf, const int32_t* pool_token,
+                                const int32_t* pool_parent, const int32_t* pool_depth,
+                                int32_t pool_n, int32_t* slot_of_pool, int32_t slot_base,
+                                int32_t slot_cap, int32_t* slot_parent, int32_t* row_token,
+                                int32_t* row_depth, int32_t* row_slot, int32_t* row_src,
+                                int32_t* dev_status, hipStream_t stream) {
+  EAGLE_REQUIRE(frontier && pool_token && pool_parent && pool_depth && slot_of_pool &&
+                    slot_parent && row_token && row_depth && row_slot && row_src,
+                EAGLE_EINVAL);
+  EAGLE_REQUIRE(kf >= 1 && kf <= 256 && pool_n >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(slot_base >= 0 && slot_base + kf <= slot_cap, EAGLE_EINVAL);
+  hipLaunchKernelGGL(eagle::draft_rows_kernel, dim3(1), dim3(256), 0, stream, frontier, kf,
+                     pool_token, pool_parent, pool_depth, pool_n, slot_of_pool, slot_base,
+                     slot_cap, slot_parent, row_token, row_depth, row_slot, row_src, dev_status);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_draft_input(int32_t M, const int32_t* row_token, const int32_t* row_src,
+                                 const float* feat, int32_t feat_rows, const float* root_feat,
+                                 const void* embed, int32_t V, int32_t d, void* out,
+                                 int32_t* dev_status, hipStream_t stream) {
+  EAGLE_REQUIRE(row_token && row_src && feat && root_feat && embed && out, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && V >= 1 && d >= 1 && feat_rows >= 1, EAGLE_EINVAL);
+  hipLaunchKernelGGL(eagle::draft_input_kernel, dim3(M), dim3(256), 0, stream, row_token,
+                     row_src, feat, feat_rows, root_feat, (const bf16_t*)embed, V, d,
+                     (bf16_t*)out, dev_status);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_embed(int32_t M, const int32_t* token, const void* embed, int32_t V,
+                           int32_t d, float* out, int32_t* dev_status, hipStream_t stream) {
+  EAGLE_REQUIRE(token && embed && out && M >= 1 && V >= 1 && d >= 1, EAGLE_EINVAL);
+  hipLaunchKernelGGL(eagle::embed_kernel, dim3(M), dim3(256), 0, stream, token,
+                     (const bf16_t*)embed, V, d, out, dev_status);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}

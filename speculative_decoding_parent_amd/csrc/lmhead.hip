@@ -28,7 +28,7 @@
 //     selection of the best candidate strictly after the previous pick.
 // fp32 path (small workloads): a plain VALU dot product per logit, then a
 // per-row top-k kernel.
-#include "common.h"
+#include "wstream.h"
 
 namespace eagle {
 
@@ -36,8 +36,6 @@ constexpr int kLmWaves = 4;
 constexpr int kLmMT = 4;
 constexpr int kLmRowsWave = 16 * kLmMT;
 constexpr int kLmRowsBlock = kLmRowsWave * kLmWaves;
-constexpr int kLmKG = 128;
-constexpr int kLmLds = kLmKG + 8;
 
 struct LmParams {
   const bf16_t* f;
@@ -49,14 +47,9 @@ struct LmParams {
   int32_t* part_idx;   // [nwave][T][k]
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
-  return __builtin_bit_cast(bf16x8, v);
-}
-
 template <int NT>
 __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void lmhead_bf16_kernel(LmParams p) {
-  constexpr int TP = 16 * NT;
-  __shared__ __attribute__((aligned(16))) bf16_t fs[2][TP * kLmLds];
+  __shared__ __attribute__((aligned(16))) bf16_t fs[ws_lds_elems<NT>()];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -70,81 +63,8 @@ __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void lmhead_bf16_kernel(LmP
     const int v = min(v0 + mt * 16 + r16, p.V - 1);
     wrow[mt] = p.W + (size_t)v * p.d + g * 32;
   }
-
   f32x4 acc[kLmMT][NT];
-#pragma unroll
-  for (int mt = 0; mt < kLmMT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // f staging: TP rows x 128 columns = TP * 16 chunks of 16 bytes, NT per thread
-  auto load_f = [&](int kk, u32x4 (&fr)[NT]) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int c = tid + 256 * j;
-      const int row = c >> 4;
-      const int col = (c & 15) * 8;
-      fr[j] = row < p.T ? *(const u32x4*)(p.f + (size_t)row * p.d + kk * kLmKG + col)
-                        : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_f = [&](int buf, const u32x4 (&fr)[NT]) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int c = tid + 256 * j;
-      *(u32x4*)(&fs[buf][(c >> 4) * kLmLds + (c & 15) * 8]) = fr[j];
-    }
-  };
-  auto load_w = [&](int kk, u32x4 (&wr)[kLmMT][4]) {
-#pragma unroll
-    for (int mt = 0; mt < kLmMT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wr[mt][i] = *(const u32x4*)(wrow[mt] + kk * kLmKG + i * 8);
-  };
-  auto compute = [&](int buf, const u32x4 (&wr)[kLmMT][4]) {
-    const bf16_t* fb = fs[buf];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x8 b[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        b[nt] = *(const bf16x8*)(fb + (nt * 16 + r16) * kLmLds + g * 32 + i * 8);
-#pragma unroll
-      for (int mt = 0; mt < kLmMT; ++mt) {
-        const bf16x8 a = as_bf16x8(wr[mt][i]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nt], acc[mt][nt], 0, 0, 0);
-      }
-    }
-  };
-
-  const int nk = p.d / kLmKG;
-  u32x4 wa[kLmMT][4], wb[kLmMT][4];
-  u32x4 fr[NT];
-  load_f(0, fr);
-  store_f(0, fr);
-  load_w(0, wa);
-  __syncthreads();
-  for (int kk = 0; kk < nk; kk += 2) {
-    const bool more1 = kk + 1 < nk;
-    if (more1) {
-      load_w(kk + 1, wb);
-      load_f(kk + 1, fr);
-    }
-    compute(0, wa);
-    if (more1) store_f(1, fr);
-    __syncthreads();
-    if (!more1) break;
-    const bool more2 = kk + 2 < nk;
-    if (more2) {
-      load_w(kk + 2, wa);
-      load_f(kk + 2, fr);
-    }
-    compute(1, wb);
-    if (more2) store_f(0, fr);
-    __syncthreads();
-  }
+  wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
 
   // ---- epilogue.  Lane (g, r16) holds, for tile (mt, nt), the logits of
   // vocabulary rows v0 + 16 mt + 4 g + j (j < 4) for feature row 16 nt + r16.
@@ -407,7 +327,7 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
   EAGLE_REQUIRE(ws_bytes >= l.total, EAGLE_EWORKSPACE);
   char* ws = (char*)workspace;
   if (dt == EAGLE_BF16) {
-    EAGLE_REQUIRE(d % kLmKG == 0, EAGLE_EUNSUPPORTED);
+    EAGLE_REQUIRE(d % kWsKG == 0, EAGLE_EUNSUPPORTED);
     EAGLE_REQUIRE(((uintptr_t)f & 15) == 0 && ((uintptr_t)W & 15) == 0, EAGLE_EINVAL);
     EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,

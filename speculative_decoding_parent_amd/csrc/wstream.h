@@ -1,0 +1,126 @@
+// Weight-streaming bf16 MFMA core shared by the LM head and the decoder-layer
+// projections: Y[m][n] = sum_k X[m][k] W[n][k] for few rows m (<= 256) and many
+// weight rows n.
+//
+// With few activation rows every weight byte is used <= 256 times, so these
+// products are bound by reading W from HBM once.  A 4-wave workgroup owns
+// 4 x MT x 16 weight rows; each wave issues its W rows' 16-byte loads for the
+// next 128-wide k step before running the MFMAs of the current one.  W rows are
+// the MFMA M dimension (v_mfma_f32_16x16x32_bf16 A operand, straight from
+// registers) and the activation rows are N, staged per k step in LDS
+// (double-buffered; rows padded by 16 bytes so the 16 lanes of one b128 read
+// land on distinct banks).  Within a 128-wide k step a lane group g (lanes
+// 16g..16g+15) covers k = 32g..32g+31 over four MFMAs, so each lane's four
+// 16-byte W loads are one contiguous 64-byte run; the activation operand uses
+// the same k order, which leaves the contraction unchanged.
+//
+// After run(), lane (g = lane / 16, r16 = lane % 16) of a wave holds, for tile
+// (mt, nt), Y[m = 16 nt + r16][n = n(mt) + 4 g + j] in acc[mt][nt][j], where n(mt)
+// is the first weight row of the wave's M tile mt.
+#pragma once
+
+#include "common.h"
+
+namespace eagle {
+
+constexpr int kWsKG = 128;        // k elements per step
+constexpr int kWsLds = kWsKG + 8;  // padded LDS row (bf16 elements)
+
+template <int NT>
+constexpr int ws_lds_elems() {
+  return 2 * 16 * NT * kWsLds;
+}
+
+__device__ __forceinline__ bf16x8 ws_as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// wrow[mt]: pointer to the weight row of this lane for tile mt, already offset
+// by 32 g elements.  X: [M][ldx] bf16 activations (rows >= M read as zero).
+// fs: LDS scratch of ws_lds_elems<NT>() elements.  K % 128 == 0.
+template <int NT, int MT>
+__device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], const bf16_t* X,
+                                             int ldx, int M, int K, bf16_t* fs,
+                                             f32x4 (&acc)[MT][NT]) {
+  constexpr int TP = 16 * NT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  bf16_t* fs0 = fs;
+  bf16_t* fs1 = fs + TP * kWsLds;
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_x = [&](int kk, u32x4 (&fr)[NT]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c >> 4;
+      const int col = (c & 15) * 8;
+      fr[j] = row < M ? *(const u32x4*)(X + (size_t)row * ldx + kk * kWsKG + col)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&](bf16_t* buf, const u32x4 (&fr)[NT]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      *(u32x4*)(&buf[(c >> 4) * kWsLds + (c & 15) * 8]) = fr[j];
+    }
+  };
+  auto load_w = [&](int kk, u32x4 (&wr)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wr[mt][i] = *(const u32x4*)(wrow[mt] + kk * kWsKG + i * 8);
+  };
+  auto compute = [&](const bf16_t* fb, const u32x4 (&wr)[MT][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8 b[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        b[nt] = *(const bf16x8*)(fb + (nt * 16 + r16) * kWsLds + g * 32 + i * 8);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = ws_as_bf16x8(wr[mt][i]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nk = K / kWsKG;
+  u32x4 wa[MT][4], wb[MT][4];
+  u32x4 fr[NT];
+  load_x(0, fr);
+  store_x(fs0, fr);
+  load_w(0, wa);
+  __syncthreads();
+  for (int kk = 0; kk < nk; kk += 2) {
+    const bool more1 = kk + 1 < nk;
+    if (more1) {
+      load_w(kk + 1, wb);
+      load_x(kk + 1, fr);
+    }
+    compute(fs0, wa);
+    if (more1) store_x(fs1, fr);
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = kk + 2 < nk;
+    if (more2) {
+      load_w(kk + 2, wa);
+      load_x(kk + 2, fr);
+    }
+    compute(fs1, wb);
+    if (more2) store_x(fs0, fr);
+    __syncthreads();
+  }
+}
+
+}  // namespace eagle

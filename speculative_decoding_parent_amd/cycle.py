@@ -1,0 +1,202 @@
+"""One EAGLE-2 draft-and-verify cycle on the GPU, driven through the C ABI.
+
+The draft grows a dynamic tree for ``rounds`` rounds: each round fuses every
+frontier row's parent feature with its token embedding, runs one decoder layer
+(attention over the draft's KV prefix and the K/V of every node expanded so
+far, under the slot tree's ancestor mask), scores the rows with the shared LM
+head and appends the top-k children by cumulative log-probability.  The tree is
+then pruned to T nodes, verified by one target layer under the tree mask, and a
+path is accepted by speculative sampling ("EAGLE-2: Feature-Level Speculative
+Decoding Guide", Key Architectural Mechanics 1-3; "Support Eagle-3 Speculative
+Decoding in llama.cpp", the dynamic-tree and KV-cache replies).
+
+Every buffer is allocated once here (torch provides the device memory) and the
+whole cycle is a fixed sequence of launches on one stream whose sizes follow
+from (rounds, k, k_select, T) alone: the host never reads device data inside a
+cycle, so the sequence can be captured into a HIP graph and replayed.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from .inputs import Workload
+
+
+class DraftVerifyCycle:
+    def __init__(self, w: Workload, ci: dict, device, temperature: float = 1.0):
+        self.w = w
+        dev = self.dev = torch.device(device)
+        d, hq, hkv, hd, F, V, L = w.d, w.hq, w.hkv, w.hd, w.ffn, w.vocab, w.L
+        R, k, ks, T = w.rounds, w.topk, w.k_select, w.T
+        self.R, self.k, self.ks, self.T, self.L = R, k, ks, T, L
+        self.temperature = temperature
+        to = lambda t: t.to(dev).contiguous()
+        self.w_fuse = to(ci["w_fuse"])
+        self.draft = {n: to(t) for n, t in ci["draft"].items()}
+        self.target = {n: to(t) for n, t in ci["target"].items()}
+        self.draft_norm = to(ci["draft_norm"])
+        self.target_norm = to(ci["target_norm"])
+        self.embed = to(ci["embed"])
+        self.w_lm = to(ci["w_lm"])
+        self.dkc, self.dvc = to(ci["draft_k_cache"]), to(ci["draft_v_cache"])
+        self.tkc, self.tvc = to(ci["target_k_cache"]), to(ci["target_v_cache"])
+        self.root_feat = to(ci["root_feature"]).float()
+        self.uniforms = torch.as_tensor(ci["uniforms"]).to(dev)
+
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        nqkv = (hq + 2 * hkv) * hd
+        # candidate pool (entry 0 = root, never overwritten) and per-round frontiers
+        self.pool_n = [1] + [1 + k + r * ks * k for r in range(R)]
+        cap = self.pool_n[R]
+        self.pool_token = torch.zeros(cap, **i32)
+        self.pool_parent = torch.full((cap,), -1, **i32)
+        self.pool_depth = torch.zeros(cap, **i32)
+        self.pool_value = torch.zeros(cap, **f32)
+        self.pool_token[0] = int(ci["root_token"])
+        self.frontier = [torch.zeros(1 if r == 0 else ks, **i32) for r in range(R + 1)]
+        # draft slots: one per expanded row (K/V, output feature, mask row)
+        self.S = 1 + (R - 1) * ks
+        self.slot_base = [0] + [1 + r * ks for r in range(R - 1)]
+        self.slot_of_pool = torch.full((cap,), -1, **i32)
+        self.slot_parent = torch.full((self.S,), -1, **i32)
+        self.smask = torch.zeros((self.S, (self.S + 63) // 64), dtype=torch.int64, device=dev)
+        self.sdepth = torch.zeros(self.S, **i32)
+        self.rows = [torch.zeros(ks, **i32) for _ in range(4)]      # token, depth, slot, src
+        self.feat = torch.zeros((self.S, d), **f32)
+        self.dkt = torch.zeros((hkv, self.S, hd), **bf)
+        self.dvt = torch.zeros((hkv, self.S, hd), **bf)
+        m = max(ks, T)
+        self.x_in = torch.zeros((ks, 2 * d), **bf)
+        self.h = torch.zeros((m, d), **f32)
+        self.n1 = torch.zeros((m, d), **bf)
+        self.qkv = torch.zeros((m, nqkv), **f32)
+        self.q = torch.zeros((m, hq, hd), **bf)
+        self.attn = torch.zeros((m, hq, hd), **bf)
+        self.x2 = torch.zeros((m, d), **f32)
+        self.n2 = torch.zeros((m, d), **bf)
+        self.gu = torch.zeros((m, F), **bf)
+        self.z = torch.zeros((m, d), **bf)
+        self.ids = [torch.zeros((1 if r == 0 else ks, k), **i32) for r in range(R)]
+        self.logp = [torch.zeros((1 if r == 0 else ks, k), **f32) for r in range(R)]
+        self.lse = torch.zeros(m, **f32)
+        # verify pass
+        self.node_token = torch.zeros(T, **i32)
+        self.node_parent = torch.zeros(T, **i32)
+        self.node_depth = torch.zeros(T, **i32)
+        self.node_pool_idx = torch.zeros(T, **i32)
+        self.vmask = torch.zeros((T, (T + 63) // 64), dtype=torch.int64, device=dev)
+        self.vdepth = torch.zeros(T, **i32)
+        self.vx = torch.zeros((T, d), **f32)
+        self.vout = torch.zeros((T, d), **f32)
+        self.tkt = torch.zeros((hkv, T, hd), **bf)
+        self.tvt = torch.zeros((hkv, T, hd), **bf)
+        self.v_ids = torch.zeros((T, k), **i32)
+        self.v_logp = torch.zeros((T, k), **f32)
+        self.v_logits = torch.zeros((T, V), **f32)
+        self.path = torch.zeros(T, **i32)
+        self.n_accepted = torch.zeros(1, **i32)
+        self.bonus = torch.zeros(1, **i32)
+        self.status = torch.zeros(1, **i32)
+        lib = _lib.lib()
+        ws_attn = max(lib.eagle_tree_attn_workspace(ks, hq, hkv, hd, L, self.S, _lib.EAGLE_BF16),
+                      lib.eagle_tree_attn_workspace(T, hq, hkv, hd, L, T, _lib.EAGLE_BF16))
+        ws_lm = max(lib.eagle_lmhead_topk_workspace(ks, d, V, k, _lib.EAGLE_BF16),
+                    lib.eagle_lmhead_topk_workspace(T, d, V, k, _lib.EAGLE_BF16))
+        self.ws_attn = torch.empty(ws_attn, dtype=torch.uint8, device=dev)
+        self.ws_lm = torch.empty(ws_lm, dtype=torch.uint8, device=dev)
+        self.ws_acc = torch.empty(lib.eagle_accept_workspace(T, V), dtype=torch.uint8, device=dev)
+        self.graph = None
+
+    # ------------------------------------------------------------ one layer
+    def _layer(self, lw, n, x_res, depth, row_slot, kc, vc, kt, vt, Tk, mask, out, q_mask_row):
+        """Decoder layer on rows 0..n-1 whose fp32 input (residual stream) is
+        x_res; writes the fp32 output to ``out``."""
+        w = self.w
+        _lib.eagle_rmsnorm(x_res, lw["norm1"], w.rms_eps, out=self.n1[:n])
+        _lib.eagle_linear(self.n1[:n], lw["wqkv"], out=self.qkv[:n])
+        _lib.eagle_rope_qkv(self.qkv[:n], w.hq, w.hkv, w.hd, depth, self.L, kt, vt,
+                            row_slot=row_slot, theta=w.rope_theta, q_out=self.q[:n],
+                            dev_status=self.status)
+        _lib.eagle_tree_attn(self.q[:n], kc, vc, self.L, kt, vt, Tk, mask, q_mask_row=q_mask_row,
+                             out=self.attn[:n], workspace=self.ws_attn, dev_status=self.status)
+        _lib.eagle_linear(self.attn[:n].view(n, -1), lw["wo"], residual=x_res, out=self.x2[:n])
+        _lib.eagle_rmsnorm(self.x2[:n], lw["norm2"], w.rms_eps, out=self.n2[:n])
+        _lib.eagle_linear_swiglu(self.n2[:n], lw["wgate"], lw["wup"], out=self.gu[:n])
+        _lib.eagle_linear(self.gu[:n], lw["wdown"], residual=self.x2[:n], out=out)
+
+    # ------------------------------------------------------------ the cycle
+    def draft_round(self, r: int):
+        w = self.w
+        kf = 1 if r == 0 else self.ks
+        base = self.slot_base[r]
+        Sr = base + kf
+        fr = self.frontier[r]
+        tok, depth, slot, src = (t[:kf] for t in self.rows)
+        _lib.eagle_draft_rows(fr, self.pool_token, self.pool_parent, self.pool_depth,
+                              self.pool_n[r], self.slot_of_pool, base, self.slot_parent,
+                              (tok, depth, slot, src), dev_status=self.status)
+        _lib.eagle_draft_input(tok, src, self.feat, self.root_feat, self.embed, out=self.x_in[:kf],
+                               dev_status=self.status)
+        _lib.eagle_linear(self.x_in[:kf], self.w_fuse, out=self.h[:kf])
+        _lib.eagle_build_tree_mask(self.slot_parent[:Sr], words=self.smask.shape[1],
+                                   mask=self.smask[:Sr], depth=self.sdepth[:Sr],
+                                   dev_status=self.status)
+        feat_rows = self.feat[base:base + kf]
+        self._layer(self.draft, kf, self.h[:kf], depth, slot, self.dkc, self.dvc, self.dkt,
+                    self.dvt, Sr, self.smask[:Sr], feat_rows, slot)
+        _lib.eagle_rmsnorm(feat_rows, self.draft_norm, w.rms_eps, out=self.z[:kf])
+        _lib.eagle_lmhead_topk(self.z[:kf], self.w_lm, self.k, topk_id=self.ids[r],
+                               topk_logp=self.logp[r], lse=self.lse[:kf], workspace=self.ws_lm)
+        _lib.eagle_expand_rerank(_lib.EAGLE_EXPAND, self.pool_token, self.pool_parent,
+                                 self.pool_depth, self.pool_value, self.pool_n[r], frontier=fr,
+                                 child_id=self.ids[r], child_logp=self.logp[r], k_select=self.ks,
+                                 new_frontier=self.frontier[r + 1], dev_status=self.status)
+
+    def verify(self):
+        w, T = self.w, self.T
+        _lib.eagle_expand_rerank(_lib.EAGLE_RERANK, self.pool_token, self.pool_parent,
+                                 self.pool_depth, self.pool_value, self.pool_n[self.R], T=T,
+                                 node_token=self.node_token, node_parent=self.node_parent,
+                                 node_depth=self.node_depth, node_pool_idx=self.node_pool_idx,
+                                 dev_status=self.status)
+        _lib.eagle_build_tree_mask(self.node_parent, mask=self.vmask, depth=self.vdepth,
+                                   dev_status=self.status)
+        _lib.eagle_embed(self.node_token, self.embed, out=self.vx, dev_status=self.status)
+        self._layer(self.target, T, self.vx, self.node_depth, None, self.tkc, self.tvc, self.tkt,
+                    self.tvt, T, self.vmask, self.vout, None)
+        _lib.eagle_rmsnorm(self.vout, self.target_norm, w.rms_eps, out=self.z[:T])
+        _lib.eagle_lmhead_topk(self.z[:T], self.w_lm, self.k, topk_id=self.v_ids,
+                               topk_logp=self.v_logp, lse=self.lse[:T], logits=self.v_logits,
+                               workspace=self.ws_lm)
+        _lib.eagle_accept(_lib.EAGLE_SAMPLE, self.node_token, self.node_parent,
+                          target_logits=self.v_logits, temperature=self.temperature,
+                          uniforms=self.uniforms, path=self.path, n_accepted=self.n_accepted,
+                          bonus_token=self.bonus, workspace=self.ws_acc, dev_status=self.status)
+
+    def enqueue(self):
+        """Enqueue one whole cycle on the current stream."""
+        for r in range(self.R):
+            self.draft_round(r)
+        self.verify()
+
+    def capture(self):
+        """Capture one cycle into a HIP graph (buffers stay fixed)."""
+        s = torch.cuda.Stream(device=self.dev)
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.enqueue()          # warm-up outside the graph
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.enqueue()
+        torch.cuda.synchronize()
+
+    def run(self):
+        if self.graph is not None:
+            self.graph.replay()
+        else:
+            self.enqueue()

@@ -284,3 +284,56 @@ def lm_head_weight(w: Workload, vocab: Optional[int] = None, d: Optional[int] = 
     V = w.vocab if vocab is None else vocab
     d = w.d if d is None else d
     return normal(rng(w.cfg, STREAM_W), (V, d), std=float(1.0 / np.sqrt(d)), dtype=torch_dtype(w))
+
+
+# --------------------------------------------------------------------------
+# Synthetic weights of one draft-and-verify cycle
+# --------------------------------------------------------------------------
+
+def _w(w: Workload, idx: int, shape, std: float, dtype=torch.bfloat16) -> torch.Tensor:
+    return normal(rng(w.cfg, STREAM_WEIGHTS + idx), shape, std=std, dtype=dtype)
+
+
+def layer_weights(w: Workload, base: int) -> dict:
+    """One Llama decoder layer: W ~ N(0, 1/fan_in), RMSNorm gains 1.  q/k/v are
+    stored as one [(Hq + 2 Hkv) hd][d] matrix (q rows, then k, then v)."""
+    d, hd, F = w.d, w.hd, w.ffn
+    nq = (w.hq + 2 * w.hkv) * hd
+    return {
+        "norm1": torch.ones(d, dtype=torch.float32),
+        "wqkv": _w(w, base + 0, (nq, d), float(1 / np.sqrt(d))),
+        "wo": _w(w, base + 1, (d, w.hq * hd), float(1 / np.sqrt(w.hq * hd))),
+        "norm2": torch.ones(d, dtype=torch.float32),
+        "wgate": _w(w, base + 2, (F, d), float(1 / np.sqrt(d))),
+        "wup": _w(w, base + 3, (F, d), float(1 / np.sqrt(d))),
+        "wdown": _w(w, base + 4, (d, F), float(1 / np.sqrt(F))),
+    }
+
+
+def cycle_inputs(w: Workload) -> dict:
+    """Every input of one cycle (CPU tensors): the draft's fuse matrix and
+    layer, the target's stand-in layer, the shared embedding and LM head, both
+    KV prefixes, the root token and feature, and the acceptance uniforms."""
+    d, hd = w.d, w.hd
+    g_root = rng(w.cfg, STREAM_F)
+    return {
+        "w_fuse": _w(w, 0, (d, 2 * d), float(1 / np.sqrt(2 * d))),
+        "draft": layer_weights(w, 1),
+        "draft_norm": torch.ones(d, dtype=torch.float32),
+        "target": layer_weights(w, 10),
+        "target_norm": torch.ones(d, dtype=torch.float32),
+        "embed": _w(w, 20, (w.vocab, d), 1.0),
+        "w_lm": lm_head_weight(w),
+        "draft_k_cache": normal(rng(w.cfg, STREAM_KC, 1), (w.hkv, w.L, hd)),
+        "draft_v_cache": normal(rng(w.cfg, STREAM_VC, 1), (w.hkv, w.L, hd)),
+        "target_k_cache": normal(rng(w.cfg, STREAM_KC, 0), (w.hkv, w.L, hd)),
+        "target_v_cache": normal(rng(w.cfg, STREAM_VC, 0), (w.hkv, w.L, hd)),
+        "root_feature": normal(g_root, (d,), dtype=torch.float32),
+        "root_token": int(rng(w.cfg, STREAM_TOK).integers(0, w.vocab)),
+        "uniforms": uniforms(rng(w.cfg, STREAM_U), 2 * w.T),
+    }
+
+
+SMALL_CYCLE = Workload(cfg=13, name="small-cycle", d=256, hq=4, hkv=2, hd=64, vocab=1024, L=64,
+                       T=16, max_depth=4, max_branch=4, topk=4, dtype="bf16", sampling=True,
+                       greedy=False, ffn=512, rounds=4, k_select=4)
