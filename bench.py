@@ -1,0 +1,160 @@
+"""Throughput of one EAGLE-2 draft-and-verify cycle on one MI355X.
+
+A step is the whole hot path over one synthetic Llama-3-8B-shaped cycle:
+6 draft rounds (fuse 8192->4096, one decoder layer with 32/8 heads of 128
+over a 4096-token prefix plus the draft tree, SwiGLU 14336, LM head over a
+128256-token vocabulary with top-10, expansion by cumulative log-probability),
+rerank to 64 nodes, tree mask, one target layer verifying the 64 nodes,
+LM head with logits, and speculative-sampling acceptance.  The cycle is
+replayed from a HIP graph with every input already resident in HBM.
+
+Prints one JSON line: nodes verified per second, the roofline of the dominant
+kernel (the LM head at the draft-round shape, timed with HIP events on its
+launch stream) and the CPU oracle's throughput on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+CORES = len(os.sched_getaffinity(0))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, str(CORES))
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from speculative_decoding_parent_amd import _lib, inputs  # noqa: E402
+from speculative_decoding_parent_amd.cycle import DraftVerifyCycle  # noqa: E402
+
+METRIC = "tree-verify nodes/s + KV/LM-head HBM GB/s (% roofline), Llama-3-8B shape"
+HBM_PEAK_GBS = 8000.0
+
+
+def lmhead_bytes(T, d, V, k):
+    """Algorithmic bytes of one LM-head call: W once, the features once, the
+    top-k ids/log-probs and lse out."""
+    return V * d * 2 + T * d * 2 + T * (8 * k + 4)
+
+
+def time_lmhead(cyc, T, iters):
+    """Average duration (s) of eagle_lmhead_topk at T rows, HIP events on the
+    stream the kernels are launched on."""
+    z = cyc.z[:T]
+    ids = torch.empty((T, cyc.k), dtype=torch.int32, device=cyc.dev)
+    lp = torch.empty((T, cyc.k), dtype=torch.float32, device=cyc.dev)
+    lse = torch.empty(T, dtype=torch.float32, device=cyc.dev)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        a.record(stream)
+        _lib.eagle_lmhead_topk(z, cyc.w_lm, cyc.k, topk_id=ids, topk_logp=lp, lse=lse,
+                               workspace=cyc.ws_lm)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ms)) / 1e3, float(np.min(ms)) / 1e3
+
+
+def cpu_baseline(w, ci):
+    """The oracle's full cycle on the host cores (one cycle: 6 draft rounds,
+    rerank, verify layer, LM head, acceptance)."""
+    import oracle
+    from oracle.cycle import CycleWeights
+    from oracle.layer import LayerWeights
+
+    torch.set_num_threads(CORES)
+
+    def lw(x):
+        nq, nk = w.hq * w.hd, w.hkv * w.hd
+        return LayerWeights(norm1=x["norm1"], wq=x["wqkv"][:nq], wk=x["wqkv"][nq:nq + nk],
+                            wv=x["wqkv"][nq + nk:], wo=x["wo"], norm2=x["norm2"],
+                            wgate=x["wgate"], wup=x["wup"], wdown=x["wdown"])
+    cw = CycleWeights(ci["w_fuse"], lw(ci["draft"]), ci["draft_norm"], ci["embed"], ci["w_lm"],
+                      lw(ci["target"]), ci["target_norm"], ci["draft_k_cache"],
+                      ci["draft_v_cache"], ci["target_k_cache"], ci["target_v_cache"])
+    t0 = time.perf_counter()
+    oracle.draft_and_verify_cycle(cw, ci["root_token"], ci["root_feature"], hq=w.hq, hkv=w.hkv,
+                                  hd=w.hd, L=w.L, rounds=w.rounds, k=w.topk,
+                                  k_select=w.k_select, T=w.T, temperature=w.temperature,
+                                  uniforms=ci["uniforms"], theta=w.rope_theta, eps=w.rms_eps)
+    dt = time.perf_counter() - t0
+    return {"value": w.T / dt, "unit": "nodes/s", "cores": CORES, "kind": "oracle",
+            "sample": "one full cycle of the same workload (6 draft rounds, rerank, verify "
+                      f"layer, LM head with logits, sampling acceptance) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lm-iters", type=int, default=30)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharded design is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    w = inputs.LLAMA3_8B_CYCLE
+    dev = torch.device("cuda:0")
+    print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
+    ci = inputs.cycle_inputs(w)
+    cyc = DraftVerifyCycle(w, ci, dev, temperature=w.temperature)
+    print("[bench] inputs resident; capturing the cycle", file=sys.stderr, flush=True)
+    if not args.no_graph:
+        cyc.capture()
+    for _ in range(args.warmup):
+        cyc.run()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} cycles", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        cyc.run()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    assert int(cyc.status.item()) == 0, "device status reported bad data"
+    ms = dt / args.steps * 1e3
+    value = w.T * args.steps / dt
+
+    # dominant kernel: the LM head at the draft-round shape (6 of the 7 LM-head
+    # passes of a cycle), timed with HIP events on its launch stream
+    Td = w.k_select
+    avg_s, min_s = time_lmhead(cyc, Td, args.lm_iters)
+    nbytes = lmhead_bytes(Td, w.d, w.vocab, w.topk)
+    achieved = nbytes / avg_s / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-cycle: fuse 8192->4096, one decoder layer (32 Q / 8 KV "
+                               "heads, hd 128, SwiGLU 14336) over L=4096 + tree, LM head V=128256, "
+                               "6 rounds of top-10, rerank to T=64, one target verify layer, "
+                               "seeded-sampling accept",
+                   "tree_nodes": w.T, "prefix": w.L, "rounds": w.rounds, "topk": w.topk,
+                   "graph": not args.no_graph},
+        "roofline": {"kernel": "eagle_lmhead_topk (lmhead_bf16_kernel + lmhead_merge_kernel), "
+                               f"T={Td}, d={w.d}, V={w.vocab}, k={w.topk}",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_us": round(avg_s * 1e6, 2), "min_us": round(min_s * 1e6, 2),
+                     "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one cycle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, ci)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -256,17 +256,23 @@ int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
  * eagle_linear - out[m][n] = sum_k x[m][k] W[n][k] (+ residual[m][n]).
  *   x [M][K] bf16 (M 1..256, K % 128 == 0), W [N][K] bf16, residual [M][N] f32
  *   or NULL (may alias out when out_dt is f32), out [M][N] out_dt.
+ *   workspace >= eagle_linear_workspace(M, K, N, 0) bytes (16-byte aligned;
+ *   may be NULL when that is 0): fp32 partial sums when the product is split
+ *   over k to occupy the whole GPU; they are summed in a fixed order.
  */
+size_t eagle_linear_workspace(int32_t M, int32_t K, int32_t N, int32_t swiglu);
 int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
-                 const float* residual, void* out, eagle_dtype out_dt, hipStream_t stream);
+                 const float* residual, void* out, eagle_dtype out_dt, void* workspace,
+                 size_t ws_bytes, hipStream_t stream);
 
 /*
  * eagle_linear_swiglu - out[m][n] = silu(x W_gate^T)[m][n] * (x W_up^T)[m][n],
  * the LlamaMLP hidden activation.  x [M][K] bf16, W_gate/W_up [N][K] bf16,
- * out [M][N] bf16.
+ * out [M][N] bf16, workspace >= eagle_linear_workspace(M, K, N, 1) bytes.
  */
 int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const void* w_gate,
-                        const void* w_up, int32_t N, void* out, hipStream_t stream);
+                        const void* w_up, int32_t N, void* out, void* workspace,
+                        size_t ws_bytes, hipStream_t stream);
 
 /*
  * eagle_rmsnorm - out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gamma.

@@ -49,8 +49,9 @@ _PROTOS = {
     "eagle_accept_workspace": (_SZ, [_I32, _I32]),
     "eagle_accept": (_I32, [_I32, _I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ,
                             _P, _P]),
-    "eagle_linear": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, ctypes.c_int, _P]),
-    "eagle_linear_swiglu": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P, _P]),
+    "eagle_linear_workspace": (_SZ, [_I32, _I32, _I32, _I32]),
+    "eagle_linear": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, ctypes.c_int, _P, _SZ, _P]),
+    "eagle_linear_swiglu": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "eagle_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F32, _P, _P]),
     "eagle_rope_qkv": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _I64, _F32, _P, _I32, _P, _P, _P,
                               _I32, _P, _P]),
@@ -233,22 +234,26 @@ def eagle_accept(mode, node_token, node_parent, target_top1=None, target_logits=
 
 # ---------------------------------------------------------------- layer support
 
-def eagle_linear(x, W, residual=None, out=None, out_dtype=torch.float32):
+def eagle_linear(x, W, residual=None, out=None, out_dtype=torch.float32, workspace=None):
     """out = x W^T (+ residual); x [M][K] bf16, W [N][K] bf16."""
     M, K = x.shape
     N = W.shape[0]
     out = torch.empty((M, N), dtype=out_dtype, device=x.device) if out is None else out
+    nb = lib().eagle_linear_workspace(M, K, N, 0)
+    ws = _workspace(nb, x.device, workspace) if nb else None
     _check("eagle_linear", lib().eagle_linear(_ptr(x), M, K, _ptr(W), N, _ptr(residual), _ptr(out),
-                                              _dt(out), _stream()))
+                                              _dt(out), _ptr(ws), nb, _stream()))
     return out
 
 
-def eagle_linear_swiglu(x, w_gate, w_up, out=None):
+def eagle_linear_swiglu(x, w_gate, w_up, out=None, workspace=None):
     M, K = x.shape
     N = w_gate.shape[0]
     out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    nb = lib().eagle_linear_workspace(M, K, N, 1)
+    ws = _workspace(nb, x.device, workspace) if nb else None
     _check("eagle_linear_swiglu", lib().eagle_linear_swiglu(_ptr(x), M, K, _ptr(w_gate), _ptr(w_up),
-                                                            N, _ptr(out), _stream()))
+                                                            N, _ptr(out), _ptr(ws), nb, _stream()))
     return out
 
 

@@ -30,6 +30,8 @@ struct LinParams {
   const float* residual;   // plain, nullable: [M][N]
   void* out;               // [M][N]
   int out_bf16;
+  int ksplit;              // k slices (blockIdx.y); > 1 writes fp32 partials
+  float* part;             // [ksplit][1 or 2][M][N]
 };
 
 __device__ __forceinline__ void store4(void* out, int out_bf16, size_t off, int n, int N,
@@ -67,10 +69,35 @@ __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void linear_bf16_kernel(Lin
   for (int mt = 0; mt < 4; ++mt) {
     const int col = SWIGLU ? n0 + (mt & 1) * 16 + r16 : n0 + mt * 16 + r16;
     const bf16_t* w = (SWIGLU && mt >= 2) ? p.w1 : p.w0;
-    wrow[mt] = w + (size_t)min(col, p.N - 1) * p.K + g * 32;
+    wrow[mt] = w + (size_t)min(col, p.N - 1) * p.K + g * 8;
   }
+  // k slice of this workgroup
+  const int kc = p.K / p.ksplit;
+  const int k0 = blockIdx.y * kc;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) wrow[mt] += k0;
   f32x4 acc[4][NT];
-  wstream_mfma<NT, 4>(wrow, p.x, p.K, p.M, p.K, fs, acc);
+  wstream_mfma<NT, 4>(wrow, p.x + k0, p.K, p.M, kc, fs, acc);
+
+  if (p.ksplit > 1) {
+    // fp32 partials; tile mt of a SwiGLU wave goes to plane mt / 2
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int m = nt * 16 + r16;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int n = SWIGLU ? n0 + (mt & 1) * 16 + 4 * g : n0 + mt * 16 + 4 * g;
+        if (n >= p.N) continue;
+        const int plane = SWIGLU ? (mt >> 1) : 0;
+        const size_t off =
+            (((size_t)blockIdx.y * (SWIGLU ? 2 : 1) + plane) * p.M + m) * p.N + n;
+        const float y[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
+        store4(p.part, 0, off, n, p.N, y);
+      }
+    }
+    return;
+  }
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -102,6 +129,48 @@ __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void linear_bf16_kernel(Lin
         }
         store4(p.out, p.out_bf16, (size_t)m * p.N + n, n, p.N, y);
       }
+    }
+  }
+}
+
+// Sum the k-slice partials in slice order and apply the epilogue: plain
+// (+ residual) or SwiGLU (silu(sum gate) * sum up).  4 outputs per thread.
+__global__ __launch_bounds__(256) void linear_reduce_kernel(LinParams p, int swiglu) {
+  const size_t MN = (size_t)p.M * p.N;
+  const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= MN) return;
+  const int planes = swiglu ? 2 : 1;
+  float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool vec = (p.N & 3) == 0;
+  for (int s = 0; s < p.ksplit; ++s) {
+    const float* pa = p.part + (size_t)s * planes * MN;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (e0 + j >= MN) break;
+      a[j] += pa[e0 + j];
+      if (swiglu) b[j] += pa[MN + e0 + j];
+    }
+  }
+  float y[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (swiglu) {
+      y[j] = a[j] / (1.0f + expf(-a[j])) * b[j];
+    } else {
+      y[j] = a[j];
+      if (p.residual && e0 + j < MN) y[j] += p.residual[e0 + j];
+    }
+  }
+  const int m = (int)(e0 / p.N);
+  const int n = (int)(e0 - (size_t)m * p.N);
+  if (vec) {
+    store4(p.out, swiglu ? 1 : p.out_bf16, e0, n, p.N, y);
+  } else {
+    for (int j = 0; j < 4 && e0 + j < MN; ++j) {
+      if (swiglu || p.out_bf16)
+        ((bf16_t*)p.out)[e0 + j] = (bf16_t)f32_to_bf16_bits(y[j]);
+      else
+        ((float*)p.out)[e0 + j] = y[j];
     }
   }
 }
@@ -240,11 +309,36 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   for (int n = threadIdx.x; n < d; n += 256) out[(size_t)m * d + n] = bf16_bits_to_f32(e[n]);
 }
 
+// k slices for a projection: enough workgroups to fill the chip (about two per
+// CU) while each slice keeps >= 2 k steps where possible and the fp32 partials
+// stay below a quarter of the weight bytes; the count divides K / 128.
+static int lin_ksplit(int M, int K, int N, int swiglu) {
+  const int cols = swiglu ? kGluColsBlock : kLinRowsBlock;
+  const int nblk = (N + cols - 1) / cols;
+  const int nk = K / kWsKG;
+  const int want = (512 + nblk - 1) / nblk;
+  int best = 1;
+  for (int s = 1; s <= nk; ++s) {
+    if (nk % s) continue;
+    if (s > want) break;
+    const double part = (double)s * (swiglu ? 2 : 1) * M * N * 4;
+    const double wbytes = (double)(swiglu ? 2 : 1) * N * K * 2;
+    if (s > 1 && part > 0.25 * wbytes) break;
+    best = s;
+  }
+  return best;
+}
+
+static size_t lin_workspace(int M, int K, int N, int swiglu) {
+  const int s = lin_ksplit(M, K, N, swiglu);
+  return s > 1 ? (size_t)s * (swiglu ? 2 : 1) * M * N * sizeof(float) : 0;
+}
+
 template <int NT, int SWIGLU>
 static void launch_lin(const LinParams& p, hipStream_t s) {
   const int cols = SWIGLU ? kGluColsBlock : kLinRowsBlock;
-  hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU>), dim3((p.N + cols - 1) / cols), dim3(256),
-                     0, s, p);
+  hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU>),
+                     dim3((p.N + cols - 1) / cols, p.ksplit), dim3(256), 0, s, p);
 }
 
 template <int SWIGLU>
@@ -255,6 +349,11 @@ static void dispatch_lin(const LinParams& p, hipStream_t s) {
   else if (nt <= 4) launch_lin<4, SWIGLU>(p, s);
   else if (nt <= 8) launch_lin<8, SWIGLU>(p, s);
   else launch_lin<16, SWIGLU>(p, s);
+  if (p.ksplit > 1) {
+    const size_t MN = (size_t)p.M * p.N;
+    hipLaunchKernelGGL(linear_reduce_kernel, dim3((unsigned)((MN + 1023) / 1024)), dim3(256), 0, s,
+                       p, SWIGLU);
+  }
 }
 
 }  // namespace eagle
@@ -263,30 +362,44 @@ using eagle::bf16_t;
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+extern "C" size_t eagle_linear_workspace(int32_t M, int32_t K, int32_t N, int32_t swiglu) {
+  if (M < 1 || K < eagle::kWsKG || N < 1 || K % eagle::kWsKG) return 0;
+  return eagle::lin_workspace(M, K, N, swiglu ? 1 : 0);
+}
+
 extern "C" int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
                             const float* residual, void* out, eagle_dtype out_dt,
-                            hipStream_t stream) {
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
   EAGLE_REQUIRE(x && W && out, EAGLE_EINVAL);
   EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && N >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(out_dt == EAGLE_BF16 || out_dt == EAGLE_F32, EAGLE_EINVAL);
   EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(aligned16(x) && aligned16(W) && aligned16(out), EAGLE_EINVAL);
+  const int ks = eagle::lin_ksplit(M, K, N, 0);
+  const size_t need = eagle::lin_workspace(M, K, N, 0);
+  EAGLE_REQUIRE(need == 0 || (workspace && aligned16(workspace)), EAGLE_EINVAL);
+  EAGLE_REQUIRE(ws_bytes >= need, EAGLE_EWORKSPACE);
   eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)W, nullptr, N, residual, out,
-                     out_dt == EAGLE_BF16 ? 1 : 0};
+                     out_dt == EAGLE_BF16 ? 1 : 0, ks, (float*)workspace};
   eagle::dispatch_lin<0>(p, stream);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }
 
 extern "C" int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const void* w_gate,
-                                   const void* w_up, int32_t N, void* out, hipStream_t stream) {
+                                   const void* w_up, int32_t N, void* out, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream) {
   EAGLE_REQUIRE(x && w_gate && w_up && out, EAGLE_EINVAL);
   EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && N >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(out),
                 EAGLE_EINVAL);
+  const int ks = eagle::lin_ksplit(M, K, N, 1);
+  const size_t need = eagle::lin_workspace(M, K, N, 1);
+  EAGLE_REQUIRE(need == 0 || (workspace && aligned16(workspace)), EAGLE_EINVAL);
+  EAGLE_REQUIRE(ws_bytes >= need, EAGLE_EWORKSPACE);
   eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)w_gate, (const bf16_t*)w_up, N,
-                     nullptr, out, 1};
+                     nullptr, out, 1, ks, (float*)workspace};
   eagle::dispatch_lin<1>(p, stream);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;

@@ -12,10 +12,7 @@
 //   * MFMA v_mfma_f32_16x16x32_bf16 with W rows as the M dimension (16 rows per
 //     tile, 4 tiles = 64 rows per wave, 256 rows per 4-wave workgroup) and the
 //     feature rows as N (16 per tile, NT tiles).  W goes straight from HBM into
-//     MFMA A operands: each lane loads 4 x 16 bytes per tile per 128-wide k
-//     step, and the k order inside a step is permuted so those 4 loads are 64
-//     contiguous bytes (a row's 256 bytes are read by 4 lanes).  The permuted
-//     order is applied to both operands, so the contraction is unchanged.
+//     MFMA A operands (the shared weight-streaming core, wstream.h).
 //   * f is shared by all workgroups (<= 512 KB at T = 64): each 128-wide k
 //     slice is staged once per workgroup in LDS (double-buffered, rows padded
 //     by 16 bytes so the 16 lanes of a b128 read hit distinct banks).
@@ -24,8 +21,8 @@
 //     (max, sum exp(l - max)) and to the wave's top-k by (logit desc,
 //     index asc); optional fp32 logits are written with 16-byte stores.
 //   * A second kernel merges the per-wave partials of each row in a fixed
-//     order: lse = M + log(sum s_w exp(m_w - M)), and the top-k by repeated
-//     selection of the best candidate strictly after the previous pick.
+//     order: lse = M + log(sum s_w exp(m_w - M)); for the top-k it keeps only
+//     the list prefixes that can still reach the top k and selects among them.
 // fp32 path (small workloads): a plain VALU dot product per logit, then a
 // per-row top-k kernel.
 #include "wstream.h"
@@ -61,7 +58,7 @@ __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void lmhead_bf16_kernel(LmP
 #pragma unroll
   for (int mt = 0; mt < kLmMT; ++mt) {
     const int v = min(v0 + mt * 16 + r16, p.V - 1);
-    wrow[mt] = p.W + (size_t)v * p.d + g * 32;
+    wrow[mt] = p.W + (size_t)v * p.d + g * 8;
   }
   f32x4 acc[kLmMT][NT];
   wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
@@ -170,6 +167,16 @@ __device__ __forceinline__ void block_best256(float& v, int& i, float* rv, int* 
 }
 
 // One workgroup per feature row: combine the per-wave statistics and top-k.
+//
+// Each wave's list is sorted by (logit desc, index asc).  Let theta be the
+// k-th best of the waves' first entries: those k entries are all at least
+// theta, so every member of the global top-k is too, and in each list only the
+// prefix not worse than theta can contribute.  Those survivors (few, unless
+// many logits tie) are gathered in LDS and the top-k is taken by k rounds of
+// "best candidate strictly after the previous pick".  If more survive than
+// LDS holds, the rounds run over all candidates instead (same result).
+constexpr int kMergeCap = 4096;
+
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(
     const float2* __restrict__ part_stat, const float* __restrict__ part_val,
     const int32_t* __restrict__ part_idx, int nw, int T, int k, int32_t* __restrict__ topk_id,
@@ -177,6 +184,9 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
   __shared__ float redf[4];
   __shared__ float rv[4];
   __shared__ int ri[4];
+  __shared__ float sv[kMergeCap];
+  __shared__ int si[kMergeCap];
+  __shared__ int scount;
   const int t = blockIdx.x;
   float M = -INFINITY;
   for (int w = threadIdx.x; w < nw; w += 256) M = fmaxf(M, part_stat[(size_t)w * T + t].x);
@@ -188,21 +198,75 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
   }
   S = block_reduce256(S, redf, [](float a, float b) { return a + b; });
   const float L = M + logf(S);
+
+  // theta: the k-th best first entry over all wave lists
+  float thv = -INFINITY;
+  int thi = INT_MAX;
+  if (nw >= k) {
+    float lastv = INFINITY;
+    int lasti = -1;
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      for (int w = threadIdx.x; w < nw; w += 256) {
+        const size_t o = ((size_t)w * T + t) * k;
+        const float v = part_val[o];
+        const int i = part_idx[o];
+        if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
+          bv = v;
+          bi = i;
+        }
+      }
+      block_best256(bv, bi, rv, ri);
+      lastv = bv;
+      lasti = bi;
+    }
+    thv = lastv;
+    thi = lasti;
+  }
+  if (threadIdx.x == 0) scount = 0;
+  __syncthreads();
+  for (int w = threadIdx.x; w < nw; w += 256) {
+    const size_t o = ((size_t)w * T + t) * k;
+    for (int j = 0; j < k; ++j) {
+      const float v = part_val[o + j];
+      const int i = part_idx[o + j];
+      if (better(thv, thi, v, i)) break;      // worse than theta: the rest of the list too
+      const int slot = atomicAdd(&scount, 1);
+      if (slot < kMergeCap) {
+        sv[slot] = v;
+        si[slot] = i;
+      }
+    }
+  }
+  __syncthreads();
+  const int ns = scount;
+  const bool fits = ns <= kMergeCap;
   float lastv = INFINITY;
   int lasti = -1;
-  const int n = nw * k;
   for (int r = 0; r < k; ++r) {
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int c = threadIdx.x; c < n; c += 256) {
-      const int w = c / k;
-      const int j = c - w * k;
-      const size_t o = ((size_t)w * T + t) * k + j;
-      const float v = part_val[o];
-      const int i = part_idx[o];
-      if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
-        bv = v;
-        bi = i;
+    if (fits) {
+      for (int c = threadIdx.x; c < ns; c += 256) {
+        const float v = sv[c];
+        const int i = si[c];
+        if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
+          bv = v;
+          bi = i;
+        }
+      }
+    } else {
+      const int n = nw * k;
+      for (int c = threadIdx.x; c < n; c += 256) {
+        const int w = c / k;
+        const size_t o = ((size_t)w * T + t) * k + (c - w * k);
+        const float v = part_val[o];
+        const int i = part_idx[o];
+        if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
+          bv = v;
+          bi = i;
+        }
       }
     }
     block_best256(bv, bi, rv, ri);

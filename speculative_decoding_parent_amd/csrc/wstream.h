@@ -9,10 +9,10 @@
 // the MFMA M dimension (v_mfma_f32_16x16x32_bf16 A operand, straight from
 // registers) and the activation rows are N, staged per k step in LDS
 // (double-buffered; rows padded by 16 bytes so the 16 lanes of one b128 read
-// land on distinct banks).  Within a 128-wide k step a lane group g (lanes
-// 16g..16g+15) covers k = 32g..32g+31 over four MFMAs, so each lane's four
-// 16-byte W loads are one contiguous 64-byte run; the activation operand uses
-// the same k order, which leaves the contraction unchanged.
+// land on distinct banks).  MFMA i of a 128-wide k step covers k = 32i..32i+31
+// with lane group g (lanes 16g..16g+15) holding k = 32i + 8g..+7, so in every
+// 16-byte load instruction the four lanes of a W row read 64 contiguous bytes
+// (16 rows x 64 bytes per instruction).
 //
 // After run(), lane (g = lane / 16, r16 = lane % 16) of a wave holds, for tile
 // (mt, nt), Y[m = 16 nt + r16][n = n(mt) + 4 g + j] in acc[mt][nt][j], where n(mt)
@@ -36,7 +36,7 @@ __device__ __forceinline__ bf16x8 ws_as_bf16x8(u32x4 v) {
 }
 
 // wrow[mt]: pointer to the weight row of this lane for tile mt, already offset
-// by 32 g elements.  X: [M][ldx] bf16 activations (rows >= M read as zero).
+// by 8 g elements.  X: [M][ldx] bf16 activations (rows >= M read as zero).
 // fs: LDS scratch of ws_lds_elems<NT>() elements.  K % 128 == 0.
 template <int NT, int MT>
 __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], const bf16_t* X,
@@ -76,7 +76,7 @@ __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], co
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wr[mt][i] = *(const u32x4*)(wrow[mt] + kk * kWsKG + i * 8);
+      for (int i = 0; i < 4; ++i) wr[mt][i] = *(const u32x4*)(wrow[mt] + kk * kWsKG + i * 32);
   };
   auto compute = [&](const bf16_t* fb, const u32x4 (&wr)[MT][4]) {
 #pragma unroll
@@ -84,7 +84,7 @@ __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], co
       bf16x8 b[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        b[nt] = *(const bf16x8*)(fb + (nt * 16 + r16) * kWsLds + g * 32 + i * 8);
+        b[nt] = *(const bf16x8*)(fb + (nt * 16 + r16) * kWsLds + i * 32 + g * 8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 a = ws_as_bf16x8(wr[mt][i]);

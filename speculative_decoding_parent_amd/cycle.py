@@ -108,6 +108,11 @@ class DraftVerifyCycle:
         self.ws_attn = torch.empty(ws_attn, dtype=torch.uint8, device=dev)
         self.ws_lm = torch.empty(ws_lm, dtype=torch.uint8, device=dev)
         self.ws_acc = torch.empty(lib.eagle_accept_workspace(T, V), dtype=torch.uint8, device=dev)
+        ws_lin = 256
+        for M in (1, ks, T):
+            for (K, N, glu) in ((2 * d, d, 0), (d, nqkv, 0), (hq * hd, d, 0), (d, F, 1), (F, d, 0)):
+                ws_lin = max(ws_lin, lib.eagle_linear_workspace(M, K, N, glu))
+        self.ws_lin = torch.empty(ws_lin, dtype=torch.uint8, device=dev)
         self.graph = None
 
     # ------------------------------------------------------------ one layer
@@ -116,16 +121,19 @@ class DraftVerifyCycle:
         x_res; writes the fp32 output to ``out``."""
         w = self.w
         _lib.eagle_rmsnorm(x_res, lw["norm1"], w.rms_eps, out=self.n1[:n])
-        _lib.eagle_linear(self.n1[:n], lw["wqkv"], out=self.qkv[:n])
+        _lib.eagle_linear(self.n1[:n], lw["wqkv"], out=self.qkv[:n], workspace=self.ws_lin)
         _lib.eagle_rope_qkv(self.qkv[:n], w.hq, w.hkv, w.hd, depth, self.L, kt, vt,
                             row_slot=row_slot, theta=w.rope_theta, q_out=self.q[:n],
                             dev_status=self.status)
         _lib.eagle_tree_attn(self.q[:n], kc, vc, self.L, kt, vt, Tk, mask, q_mask_row=q_mask_row,
                              out=self.attn[:n], workspace=self.ws_attn, dev_status=self.status)
-        _lib.eagle_linear(self.attn[:n].view(n, -1), lw["wo"], residual=x_res, out=self.x2[:n])
+        _lib.eagle_linear(self.attn[:n].view(n, -1), lw["wo"], residual=x_res, out=self.x2[:n],
+                          workspace=self.ws_lin)
         _lib.eagle_rmsnorm(self.x2[:n], lw["norm2"], w.rms_eps, out=self.n2[:n])
-        _lib.eagle_linear_swiglu(self.n2[:n], lw["wgate"], lw["wup"], out=self.gu[:n])
-        _lib.eagle_linear(self.gu[:n], lw["wdown"], residual=self.x2[:n], out=out)
+        _lib.eagle_linear_swiglu(self.n2[:n], lw["wgate"], lw["wup"], out=self.gu[:n],
+                                 workspace=self.ws_lin)
+        _lib.eagle_linear(self.gu[:n], lw["wdown"], residual=self.x2[:n], out=out,
+                          workspace=self.ws_lin)
 
     # ------------------------------------------------------------ the cycle
     def draft_round(self, r: int):
@@ -140,7 +148,7 @@ class DraftVerifyCycle:
                               (tok, depth, slot, src), dev_status=self.status)
         _lib.eagle_draft_input(tok, src, self.feat, self.root_feat, self.embed, out=self.x_in[:kf],
                                dev_status=self.status)
-        _lib.eagle_linear(self.x_in[:kf], self.w_fuse, out=self.h[:kf])
+        _lib.eagle_linear(self.x_in[:kf], self.w_fuse, out=self.h[:kf], workspace=self.ws_lin)
         _lib.eagle_build_tree_mask(self.slot_parent[:Sr], words=self.smask.shape[1],
                                    mask=self.smask[:Sr], depth=self.sdepth[:Sr],
                                    dev_status=self.status)
