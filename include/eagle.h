@@ -275,6 +275,32 @@ int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const void* w_gate,
                         size_t ws_bytes, hipStream_t stream);
 
 /*
+ * eagle_linear_rmsnorm - a projection whose result feeds an RMSNorm, in two
+ * launches: out[m] = x[m] W^T + residual[m] (f32, residual may be NULL or
+ * alias out) and norm_out[m] = out[m] / sqrt(mean(out[m]^2) + eps) * gamma
+ * (bf16).  Used for the layer's residual adds, each of which is followed by a
+ * norm (input, post-attention, final).  N % 4 == 0, N <= 8192.
+ *   workspace >= eagle_linear_rows_workspace(M, K, N) bytes.
+ */
+size_t eagle_linear_rows_workspace(int32_t M, int32_t K, int32_t N);
+int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
+                         const float* residual, float* out, const float* gamma, float eps,
+                         void* norm_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * eagle_linear_rope_qkv - the q/k/v projection followed by eagle_rope_qkv's
+ * rotation and placement, in two launches: x [M][K] bf16, w_qkv
+ * [(Hq + 2 Hkv) hd][K] bf16 (q rows, then k, then v); outputs and the other
+ * arguments as eagle_rope_qkv.  (Hq + 2 Hkv) hd <= 16384, hd % 8 == 0.
+ *   workspace >= eagle_linear_rows_workspace(M, K, (Hq + 2 Hkv) hd) bytes.
+ */
+int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const void* w_qkv, int32_t Hq,
+                          int32_t Hkv, int32_t hd, const int32_t* depth, int64_t pos_base,
+                          float theta, const int32_t* row_slot, int32_t slot_cap, void* q_out,
+                          void* k_tree, void* v_tree, int32_t ld_tree, void* workspace,
+                          size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
+
+/*
  * eagle_rmsnorm - out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gamma.
  *   x [M][N] f32, gamma [N] f32, out [M][N] bf16.
  */
@@ -296,33 +322,32 @@ int eagle_rope_qkv(const float* qkv, int32_t M, int32_t Hq, int32_t Hkv, int32_t
                    int32_t* dev_status, hipStream_t stream);
 
 /*
- * eagle_draft_rows - bookkeeping for one draft round whose rows are the pool
- * entries frontier[0..kf).  Row j gets draft slot slot_base + j (the slot
- * holds its K/V and its output feature); slot_of_pool[frontier[j]] is set to
- * it and slot_parent[slot] to the slot of the entry's parent (-1 for the
- * root).  Per row: row_token, row_depth (pool depth), row_slot and row_src =
- * the parent's slot, whose output feature predicted this row's token and is
- * paired with it ([G] Reference Implementation: the feature and the token it
- * produced step together).  slot_of_pool [pool capacity] must hold the slots
- * of earlier rounds.
+ * eagle_draft_prepare - everything one draft round needs before its layer,
+ * for the rows frontier[0..kf) (pool entries; see eagle_expand_rerank):
+ *   - row j gets draft slot slot_base + j, which holds its K/V, its output
+ *     feature and its mask row; slot_of_pool[frontier[j]] is set to it and
+ *     slot_parent[slot] to the slot of the entry's parent (-1 for the root);
+ *   - row_token, row_depth (pool depth), row_slot and row_src (the parent's
+ *     slot, whose output feature predicted this row's token and is paired with
+ *     it: [G] Reference Implementation, the feature and the token it produced
+ *     step together);
+ *   - slot_mask [slot_cap][words] (or NULL): the slot's ancestor mask row, its
+ *     parent slot's row plus its own bit (eagle_build_tree_mask layout);
+ *   - x_in [kf][2d] bf16 (or NULL): the fused input [f ; Emb(y)] =
+ *     [bf16(feat[row_src]) (root_feat for the root) ; embed[row_token]],
+ *     feat [slot_cap][d] f32, root_feat [d] f32, embed [V][d] bf16.
+ * slot_of_pool [pool capacity] must hold the slots of earlier rounds.  A
+ * frontier entry or parent slot out of range sets EAGLE_DEV_BAD_INDEX, a token
+ * outside [0, V) EAGLE_DEV_BAD_TOKEN.
  */
-int eagle_draft_rows(const int32_t* frontier, int32_t kf, const int32_t* pool_token,
-                     const int32_t* pool_parent, const int32_t* pool_depth, int32_t pool_n,
-                     int32_t* slot_of_pool, int32_t slot_base, int32_t slot_cap,
-                     int32_t* slot_parent, int32_t* row_token, int32_t* row_depth,
-                     int32_t* row_slot, int32_t* row_src, int32_t* dev_status,
-                     hipStream_t stream);
-
-/*
- * eagle_draft_input - the fused input [f ; Emb(y)] of each draft row:
- * out[m] = [bf16(feat[row_src[m]]) (root_feat when row_src[m] < 0) ;
- * embed[row_token[m]]].  feat [feat_rows][d] f32, root_feat [d] f32,
- * embed [V][d] bf16, out [M][2d] bf16.
- */
-int eagle_draft_input(int32_t M, const int32_t* row_token, const int32_t* row_src,
-                      const float* feat, int32_t feat_rows, const float* root_feat,
-                      const void* embed, int32_t V, int32_t d, void* out, int32_t* dev_status,
-                      hipStream_t stream);
+int eagle_draft_prepare(const int32_t* frontier, int32_t kf, const int32_t* pool_token,
+                        const int32_t* pool_parent, const int32_t* pool_depth, int32_t pool_n,
+                        int32_t* slot_of_pool, int32_t slot_base, int32_t slot_cap,
+                        int32_t* slot_parent, uint64_t* slot_mask, int32_t words,
+                        int32_t* row_token, int32_t* row_depth, int32_t* row_slot,
+                        int32_t* row_src, const float* feat, const float* root_feat,
+                        const void* embed, int32_t V, int32_t d, void* x_in,
+                        int32_t* dev_status, hipStream_t stream);
 
 /* eagle_embed - out[m] = embed[token[m]] as f32 ([M][d]); embed [V][d] bf16. */
 int eagle_embed(int32_t M, const int32_t* token, const void* embed, int32_t V, int32_t d,

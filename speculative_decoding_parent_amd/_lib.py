@@ -53,11 +53,14 @@ _PROTOS = {
     "eagle_linear": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, ctypes.c_int, _P, _SZ, _P]),
     "eagle_linear_swiglu": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "eagle_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F32, _P, _P]),
+    "eagle_linear_rows_workspace": (_SZ, [_I32, _I32, _I32]),
+    "eagle_linear_rmsnorm": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _P, _F32, _P, _P, _SZ, _P]),
+    "eagle_linear_rope_qkv": (_I32, [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I64, _F32, _P, _I32,
+                                     _P, _P, _P, _I32, _P, _SZ, _P, _P]),
     "eagle_rope_qkv": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _I64, _F32, _P, _I32, _P, _P, _P,
                               _I32, _P, _P]),
-    "eagle_draft_rows": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P,
-                                _P]),
-    "eagle_draft_input": (_I32, [_I32, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
+                                   _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P]),
     "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
 }
 
@@ -257,6 +260,35 @@ def eagle_linear_swiglu(x, w_gate, w_up, out=None, workspace=None):
     return out
 
 
+def eagle_linear_rmsnorm(x, W, gamma, residual=None, out=None, norm_out=None, eps=1e-5,
+                         workspace=None):
+    """out = x W^T (+ residual) in f32; norm_out = RMSNorm(out) * gamma in bf16."""
+    M, K = x.shape
+    N = W.shape[0]
+    out = torch.empty((M, N), dtype=torch.float32, device=x.device) if out is None else out
+    norm_out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if norm_out is None else norm_out
+    nb = lib().eagle_linear_rows_workspace(M, K, N)
+    ws = _workspace(nb, x.device, workspace)
+    _check("eagle_linear_rmsnorm", lib().eagle_linear_rmsnorm(
+        _ptr(x), M, K, _ptr(W), N, _ptr(residual), _ptr(out), _ptr(gamma), eps, _ptr(norm_out),
+        _ptr(ws), nb, _stream()))
+    return out, norm_out
+
+
+def eagle_linear_rope_qkv(x, w_qkv, Hq, Hkv, hd, depth, pos_base, k_tree, v_tree, row_slot=None,
+                          theta=500000.0, q_out=None, workspace=None, dev_status=None):
+    M, K = x.shape
+    N = (Hq + 2 * Hkv) * hd
+    q_out = torch.empty((M, Hq, hd), dtype=torch.bfloat16, device=x.device) if q_out is None else q_out
+    nb = lib().eagle_linear_rows_workspace(M, K, N)
+    ws = _workspace(nb, x.device, workspace)
+    ld = k_tree.shape[1]
+    _check("eagle_linear_rope_qkv", lib().eagle_linear_rope_qkv(
+        _ptr(x), M, K, _ptr(w_qkv), Hq, Hkv, hd, _ptr(depth), pos_base, theta, _ptr(row_slot), ld,
+        _ptr(q_out), _ptr(k_tree), _ptr(v_tree), ld, _ptr(ws), nb, _ptr(dev_status), _stream()))
+    return q_out
+
+
 def eagle_rmsnorm(x, gamma, eps=1e-5, out=None):
     M, N = x.shape
     out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
@@ -276,24 +308,18 @@ def eagle_rope_qkv(qkv, Hq, Hkv, hd, depth, pos_base, k_tree, v_tree, row_slot=N
     return q_out
 
 
-def eagle_draft_rows(frontier, pool_token, pool_parent, pool_depth, pool_n, slot_of_pool,
-                     slot_base, slot_parent, rows, dev_status=None):
+def eagle_draft_prepare(frontier, pool_token, pool_parent, pool_depth, pool_n, slot_of_pool,
+                        slot_base, slot_parent, rows, slot_mask=None, feat=None, root_feat=None,
+                        embed=None, x_in=None, dev_status=None):
     """rows: (row_token, row_depth, row_slot, row_src) int32 tensors of >= kf entries."""
     kf = frontier.shape[0]
-    _check("eagle_draft_rows", lib().eagle_draft_rows(
+    words = slot_mask.shape[1] if slot_mask is not None else 0
+    V, d = embed.shape if embed is not None else (1, 0)
+    _check("eagle_draft_prepare", lib().eagle_draft_prepare(
         _ptr(frontier), kf, _ptr(pool_token), _ptr(pool_parent), _ptr(pool_depth), pool_n,
-        _ptr(slot_of_pool), slot_base, slot_parent.shape[0], _ptr(slot_parent), *[_ptr(r) for r in rows],
+        _ptr(slot_of_pool), slot_base, slot_parent.shape[0], _ptr(slot_parent), _ptr(slot_mask),
+        words, *[_ptr(r) for r in rows], _ptr(feat), _ptr(root_feat), _ptr(embed), V, d, _ptr(x_in),
         _ptr(dev_status), _stream()))
-
-
-def eagle_draft_input(row_token, row_src, feat, root_feat, embed, M=None, out=None, dev_status=None):
-    M = row_token.shape[0] if M is None else M
-    V, d = embed.shape
-    out = torch.empty((M, 2 * d), dtype=torch.bfloat16, device=embed.device) if out is None else out
-    _check("eagle_draft_input", lib().eagle_draft_input(
-        M, _ptr(row_token), _ptr(row_src), _ptr(feat), feat.shape[0], _ptr(root_feat), _ptr(embed),
-        V, d, _ptr(out), _ptr(dev_status), _stream()))
-    return out
 
 
 def eagle_embed(token, embed, out=None, dev_status=None):

@@ -351,23 +351,39 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnParams p, int hd
 }
 
 // Combine the splits of each (query row, head): out = sum_s w_s O_s / sum_s w_s l_s
-// with w_s = exp2((m_s - M) c).
+// with w_s = exp2((m_s - M) c).  The split weights are formed once per row in
+// LDS; each thread then sums one head-dim element over the splits.
+constexpr int kMergeSplits = 1024;
+
 __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          int nsplit, int RT, int hd, float c,
                                                          void* out, int out_bf16) {
+  __shared__ float wsh[kMergeSplits];
+  __shared__ float red[2];
   const int row = blockIdx.x;
   float M = kNegBig;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[(size_t)s * RT + row].x);
+  for (int s = threadIdx.x; s < nsplit; s += blockDim.x)
+    M = fmaxf(M, part_ml[(size_t)s * RT + row].x);
+  M = wave_max(M);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float den = 0.f;
+  for (int s = threadIdx.x; s < nsplit; s += blockDim.x) {
+    const float2 ml = part_ml[(size_t)s * RT + row];
+    const float w = exp2f((ml.x - M) * c);
+    wsh[s] = w;
+  }
+  __syncthreads();
+  for (int s = 0; s < nsplit; ++s) den = fmaf(part_ml[(size_t)s * RT + row].y, wsh[s], den);
+  const float inv = 1.0f / den;
   for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = part_ml[(size_t)s * RT + row];
-      const float w = exp2f((ml.x - M) * c);
-      den = fmaf(ml.y, w, den);
-      num = fmaf(part_o[((size_t)s * RT + row) * hd + d], w, num);
-    }
-    const float v = num / den;
+    float num = 0.f;
+    const float* po = part_o + (size_t)row * hd + d;
+#pragma unroll 4
+    for (int s = 0; s < nsplit; ++s) num = fmaf(po[(size_t)s * RT * hd], wsh[s], num);
+    const float v = num * inv;
     if (out_bf16)
       ((bf16_t*)out)[(size_t)row * hd + d] = (bf16_t)f32_to_bf16_bits(v);
     else
@@ -458,6 +474,7 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
                        (uintptr_t)k_cache | (uintptr_t)v_cache;
   EAGLE_REQUIRE((al & 15) == 0 && ((uintptr_t)mask & 7) == 0, EAGLE_EINVAL);
   const AttnPlan pl = attn_plan(Tq, Hq, Hkv, hd, L, in_dt);
+  EAGLE_REQUIRE(pl.n_split + 1 <= kMergeSplits, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(ws_bytes >= pl.total, EAGLE_EWORKSPACE);
   char* ws = (char*)workspace;
   AttnParams p{};

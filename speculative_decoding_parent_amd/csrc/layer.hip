@@ -30,8 +30,9 @@ struct LinParams {
   const float* residual;   // plain, nullable: [M][N]
   void* out;               // [M][N]
   int out_bf16;
-  int ksplit;              // k slices (blockIdx.y); > 1 writes fp32 partials
+  int ksplit;              // k slices (blockIdx.y)
   float* part;             // [ksplit][1 or 2][M][N]
+  int to_part;             // write fp32 partials for a separate epilogue kernel
 };
 
 __device__ __forceinline__ void store4(void* out, int out_bf16, size_t off, int n, int N,
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void linear_bf16_kernel(Lin
   f32x4 acc[4][NT];
   wstream_mfma<NT, 4>(wrow, p.x + k0, p.K, p.M, kc, fs, acc);
 
-  if (p.ksplit > 1) {
+  if (p.to_part) {
     // fp32 partials; tile mt of a SwiGLU wave goes to plane mt / 2
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -134,21 +135,38 @@ __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void linear_bf16_kernel(Lin
 }
 
 // Sum the k-slice partials in slice order and apply the epilogue: plain
-// (+ residual) or SwiGLU (silu(sum gate) * sum up).  4 outputs per thread.
+// (+ residual) or SwiGLU (silu(sum gate) * sum up).  4 outputs per thread,
+// 16-byte loads when N % 4 == 0.
 __global__ __launch_bounds__(256) void linear_reduce_kernel(LinParams p, int swiglu) {
   const size_t MN = (size_t)p.M * p.N;
   const size_t e0 = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e0 >= MN) return;
   const int planes = swiglu ? 2 : 1;
+  const size_t stride = (size_t)planes * MN;
   float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
   const bool vec = (p.N & 3) == 0;
-  for (int s = 0; s < p.ksplit; ++s) {
-    const float* pa = p.part + (size_t)s * planes * MN;
+  if (vec) {
+    f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
+    const float* pa = p.part + e0;
+#pragma unroll 8
+    for (int s = 0; s < p.ksplit; ++s) {
+      va += *(const f32x4*)(pa + s * stride);
+      if (swiglu) vb += *(const f32x4*)(pa + s * stride + MN);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (e0 + j >= MN) break;
-      a[j] += pa[e0 + j];
-      if (swiglu) b[j] += pa[MN + e0 + j];
+      a[j] = va[j];
+      b[j] = vb[j];
+    }
+  } else {
+    for (int s = 0; s < p.ksplit; ++s) {
+      const float* pa = p.part + (size_t)s * stride;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (e0 + j >= MN) break;
+        a[j] += pa[e0 + j];
+        if (swiglu) b[j] += pa[MN + e0 + j];
+      }
     }
   }
   float y[4];
@@ -175,122 +193,247 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinParams p, int swi
   }
 }
 
-// out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gamma, fp32 in, bf16 out.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
-                                                      const float* __restrict__ gamma, int N,
-                                                      float eps, bf16_t* __restrict__ out) {
-  __shared__ float red[4];
-  const float* row = x + (size_t)blockIdx.x * N;
+// Row-wise reduce epilogues: one workgroup per row m sums the row's k-slice
+// partials (slice order) so the whole row is available to a row operation.
+constexpr int kRowThreads = 512;
+constexpr int kRowVec = 4;                    // float4 per thread: N <= 8192
+constexpr int kRowMaxN = kRowThreads * 4 * kRowVec;
+
+__device__ __forceinline__ f32x4 sum_slices4(const LinParams& p, size_t off) {
+  const size_t MN = (size_t)p.M * p.N;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = 0; s < p.ksplit; ++s) a += *(const f32x4*)(p.part + s * MN + off);
+  return a;
+}
+
+// out = sum + residual (fp32), then norm_out = RMSNorm(out) * gamma (bf16).
+__global__ __launch_bounds__(kRowThreads) void linear_reduce_norm_kernel(
+    LinParams p, const float* __restrict__ gamma, float eps, bf16_t* __restrict__ norm_out) {
+  __shared__ float red[kRowThreads / 64];
+  const int m = blockIdx.x;
+  const int N = p.N;
+  f32x4 v[kRowVec];
   float ss = 0.f;
-  for (int n = threadIdx.x; n < N; n += 256) ss = fmaf(row[n], row[n], ss);
+#pragma unroll
+  for (int q = 0; q < kRowVec; ++q) {
+    const int n = (threadIdx.x + kRowThreads * q) * 4;
+    v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (n >= N) continue;
+    const size_t off = (size_t)m * N + n;
+    v[q] = sum_slices4(p, off);
+    if (p.residual) v[q] += *(const f32x4*)(p.residual + off);
+    *(f32x4*)((float*)p.out + off) = v[q];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ss = fmaf(v[q][j], v[q][j], ss);
+  }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / 64; ++w) tot += red[w];
   const float r = 1.0f / sqrtf(tot / (float)N + eps);
-  bf16_t* o = out + (size_t)blockIdx.x * N;
-  for (int n = threadIdx.x; n < N; n += 256)
-    o[n] = (bf16_t)f32_to_bf16_bits(row[n] * r * gamma[n]);
+#pragma unroll
+  for (int q = 0; q < kRowVec; ++q) {
+    const int n = (threadIdx.x + kRowThreads * q) * 4;
+    if (n >= N) continue;
+    const f32x4 gm = *(const f32x4*)(gamma + n);
+    *(u32x2*)(norm_out + (size_t)m * N + n) =
+        u32x2{pack_bf16x2(v[q][0] * r * gm[0], v[q][1] * r * gm[1]),
+              pack_bf16x2(v[q][2] * r * gm[2], v[q][3] * r * gm[3])};
+  }
 }
 
-// qkv [M][(Hq + 2 Hkv) hd] fp32 -> q_out [M][Hq][hd] bf16 (rotated); k (rotated)
-// and v into the tree K/V at slot row_slot[m].  Rotation pairs dims i and
-// i + hd/2 by angle (pos_base + depth[m]) * theta^(-2i/hd).
-__global__ __launch_bounds__(256) void rope_qkv_kernel(
-    const float* __restrict__ qkv, int Hq, int Hkv, int hd, const int32_t* __restrict__ depth,
-    int64_t pos_base, double theta, const int32_t* __restrict__ row_slot, int slot_cap,
-    bf16_t* __restrict__ q_out, bf16_t* __restrict__ k_tree, bf16_t* __restrict__ v_tree,
-    int ld_tree, int32_t* __restrict__ status) {
-  const int m = blockIdx.x;
-  const int half = hd / 2;
-  const int H = Hq + 2 * Hkv;
-  int slot = row_slot ? row_slot[m] : m;
-  if (slot < 0 || slot >= slot_cap) {
-    if (threadIdx.x == 0) set_status(status, EAGLE_DEV_BAD_INDEX);
+struct RopeArgs {
+  int Hq, Hkv, hd;
+  const int32_t* depth;
+  int64_t pos_base;
+  double theta;
+  const int32_t* row_slot;
+  int slot_cap;
+  bf16_t* q_out;
+  bf16_t* k_tree;
+  bf16_t* v_tree;
+  int ld_tree;
+  int32_t* status;
+};
+
+// Rotate one row held in LDS (q heads, k heads, v heads of hd) and place it:
+// q -> q_out[m], rotated k and plain v -> tree slot row_slot[m].
+__device__ void rope_place_row(const float* row, int m, const RopeArgs& r, const double* inv) {
+  const int half = r.hd / 2;
+  const int H = r.Hq + 2 * r.Hkv;
+  int slot = r.row_slot ? r.row_slot[m] : m;
+  if (slot < 0 || slot >= r.slot_cap) {
+    if (threadIdx.x == 0) set_status(r.status, EAGLE_DEV_BAD_INDEX);
     slot = -1;
   }
-  const double pos = (double)(pos_base + depth[m]);
-  const float* row = qkv + (size_t)m * H * hd;
-  for (int e = threadIdx.x; e < H * half; e += 256) {
+  const double pos = (double)(r.pos_base + r.depth[m]);
+  for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
     const int hh = e / half;
     const int i = e - hh * half;
-    const float x1 = row[hh * hd + i];
-    const float x2 = row[hh * hd + i + half];
-    if (hh < Hq + Hkv) {
-      const double ang = pos * pow(theta, -2.0 * (double)i / (double)hd);
+    const float x1 = row[hh * r.hd + i];
+    const float x2 = row[hh * r.hd + i + half];
+    if (hh < r.Hq + r.Hkv) {
       double sn, cs;
-      sincos(ang, &sn, &cs);
+      sincos(pos * inv[i], &sn, &cs);
       const float y1 = (float)((double)x1 * cs - (double)x2 * sn);
       const float y2 = (float)((double)x2 * cs + (double)x1 * sn);
-      if (hh < Hq) {
-        bf16_t* q = q_out + ((size_t)m * Hq + hh) * hd;
+      if (hh < r.Hq) {
+        bf16_t* q = r.q_out + ((size_t)m * r.Hq + hh) * r.hd;
         q[i] = (bf16_t)f32_to_bf16_bits(y1);
         q[i + half] = (bf16_t)f32_to_bf16_bits(y2);
       } else if (slot >= 0) {
-        bf16_t* k = k_tree + ((size_t)(hh - Hq) * ld_tree + slot) * hd;
+        bf16_t* k = r.k_tree + ((size_t)(hh - r.Hq) * r.ld_tree + slot) * r.hd;
         k[i] = (bf16_t)f32_to_bf16_bits(y1);
         k[i + half] = (bf16_t)f32_to_bf16_bits(y2);
       }
     } else if (slot >= 0) {
-      bf16_t* v = v_tree + ((size_t)(hh - Hq - Hkv) * ld_tree + slot) * hd;
+      bf16_t* v = r.v_tree + ((size_t)(hh - r.Hq - r.Hkv) * r.ld_tree + slot) * r.hd;
       v[i] = (bf16_t)f32_to_bf16_bits(x1);
       v[i + half] = (bf16_t)f32_to_bf16_bits(x2);
     }
   }
 }
 
-// Bookkeeping for one draft round: the rows are the frontier's pool entries.
-__global__ __launch_bounds__(256) void draft_rows_kernel(
-    const int32_t* __restrict__ frontier, int kf, const int32_t* __restrict__ pool_token,
-    const int32_t* __restrict__ pool_parent, const int32_t* __restrict__ pool_depth, int pool_n,
-    int32_t* __restrict__ slot_of_pool, int slot_base, int slot_cap,
-    int32_t* __restrict__ slot_parent, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ row_depth, int32_t* __restrict__ row_slot,
-    int32_t* __restrict__ row_src, int32_t* __restrict__ status) {
-  const int j = threadIdx.x;
-  if (j >= kf) return;
-  int f = frontier[j];
-  if (f < 0 || f >= pool_n) {
-    set_status(status, EAGLE_DEV_BAD_INDEX);
-    f = 0;
-  }
-  const int par = pool_parent[f];
-  int src = -1;
-  if (par >= 0) {
-    src = par < pool_n ? slot_of_pool[par] : -1;
-    if (src < 0 || src >= slot_cap) {
-      set_status(status, EAGLE_DEV_BAD_INDEX);
-      src = -1;
-    }
-  }
-  const int slot = slot_base + j;
-  slot_of_pool[f] = slot;
-  slot_parent[slot] = src;
-  row_token[j] = pool_token[f];
-  row_depth[j] = pool_depth[f];
-  row_slot[j] = slot;
-  row_src[j] = src;
+constexpr int kRopeMaxHalf = 128;
+
+// qkv projection epilogue: sum the row's partials into LDS, then RoPE + place.
+__global__ __launch_bounds__(kRowThreads) void linear_reduce_rope_kernel(LinParams p, RopeArgs r) {
+  extern __shared__ float row[];
+  __shared__ double inv[kRopeMaxHalf];
+  const int m = blockIdx.x;
+  const int half = r.hd / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x)
+    inv[i] = pow(r.theta, -2.0 * (double)i / (double)r.hd);
+  for (int n = threadIdx.x * 4; n < p.N; n += kRowThreads * 4)
+    *(f32x4*)(row + n) = sum_slices4(p, (size_t)m * p.N + n);
+  __syncthreads();
+  rope_place_row(row, m, r, inv);
 }
 
-// out[m] = [ bf16(src >= 0 ? feat[src] : root_feat) ; embed[token] ]  ([M][2d] bf16)
-__global__ __launch_bounds__(256) void draft_input_kernel(
-    const int32_t* __restrict__ row_token, const int32_t* __restrict__ row_src,
-    const float* __restrict__ feat, int feat_rows, const float* __restrict__ root_feat,
-    const bf16_t* __restrict__ embed, int V, int d, bf16_t* __restrict__ out,
-    int32_t* __restrict__ status) {
-  const int m = blockIdx.x;
-  int tok = row_token[m];
-  if (tok < 0 || tok >= V) {
-    if (threadIdx.x == 0) set_status(status, EAGLE_DEV_BAD_TOKEN);
-    tok = 0;
+// out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gamma, fp32 in, bf16 out.  One
+// workgroup per row; rows of up to 256 * 4 * kNormVec elements stay in
+// registers between the sum of squares and the scaling (one pass over HBM).
+constexpr int kNormVec = 8;
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+                                                      const float* __restrict__ gamma, int N,
+                                                      float eps, bf16_t* __restrict__ out) {
+  __shared__ float red[4];
+  const float* row = x + (size_t)blockIdx.x * N;
+  bf16_t* o = out + (size_t)blockIdx.x * N;
+  const bool inreg = (N & 3) == 0 && N <= 256 * 4 * kNormVec &&
+                     (((uintptr_t)x | (uintptr_t)gamma | (uintptr_t)out) & 15) == 0;
+  f32x4 v[kNormVec];
+  float ss = 0.f;
+  if (inreg) {
+#pragma unroll
+    for (int q = 0; q < kNormVec; ++q) {
+      const int n = (threadIdx.x + 256 * q) * 4;
+      v[q] = n < N ? *(const f32x4*)(row + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss = fmaf(v[q][j], v[q][j], ss);
+    }
+  } else {
+    for (int n = threadIdx.x; n < N; n += 256) ss = fmaf(row[n], row[n], ss);
   }
-  const int src = row_src[m];
-  const float* f = (src >= 0 && src < feat_rows) ? feat + (size_t)src * d : root_feat;
-  bf16_t* o = out + (size_t)m * 2 * d;
-  const bf16_t* e = embed + (size_t)tok * d;
-  for (int n = threadIdx.x; n < d; n += 256) {
-    o[n] = (bf16_t)f32_to_bf16_bits(f[n]);
-    o[d + n] = e[n];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)N + eps);
+  if (inreg) {
+#pragma unroll
+    for (int q = 0; q < kNormVec; ++q) {
+      const int n = (threadIdx.x + 256 * q) * 4;
+      if (n >= N) continue;
+      const f32x4 gm = *(const f32x4*)(gamma + n);
+      *(u32x2*)(o + n) = u32x2{pack_bf16x2(v[q][0] * r * gm[0], v[q][1] * r * gm[1]),
+                               pack_bf16x2(v[q][2] * r * gm[2], v[q][3] * r * gm[3])};
+    }
+  } else {
+    for (int n = threadIdx.x; n < N; n += 256)
+      o[n] = (bf16_t)f32_to_bf16_bits(row[n] * r * gamma[n]);
+  }
+}
+
+// qkv [M][(Hq + 2 Hkv) hd] fp32 -> q_out [M][Hq][hd] bf16 (rotated); k (rotated)
+// and v into the tree K/V at slot row_slot[m].  Rotation pairs dims i and
+// i + hd/2 by angle (pos_base + depth[m]) * theta^(-2i/hd).
+__global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__ qkv, RopeArgs r) {
+  __shared__ double inv[kRopeMaxHalf];
+  const int m = blockIdx.x;
+  const int half = r.hd / 2;
+  for (int i = threadIdx.x; i < half; i += blockDim.x)
+    inv[i] = pow(r.theta, -2.0 * (double)i / (double)r.hd);
+  __syncthreads();
+  rope_place_row(qkv + (size_t)m * (r.Hq + 2 * r.Hkv) * r.hd, m, r, inv);
+}
+
+// One draft round's preparation, one workgroup per row j (frontier entry f):
+// bookkeeping (slot base + j, the parent's slot, token, depth), the slot's
+// ancestor mask row (its parent slot's row plus its own bit) and the fused
+// input row [bf16(feature of the parent slot, or the root feature) ; Emb(token)].
+// Parents belong to earlier rounds, so no row reads what another row writes.
+__global__ __launch_bounds__(256) void draft_prepare_kernel(
+    const int32_t* __restrict__ frontier, const int32_t* __restrict__ pool_token,
+    const int32_t* __restrict__ pool_parent, const int32_t* __restrict__ pool_depth, int pool_n,
+    int32_t* __restrict__ slot_of_pool, int slot_base, int slot_cap,
+    int32_t* __restrict__ slot_parent, uint64_t* __restrict__ slot_mask, int words,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_depth,
+    int32_t* __restrict__ row_slot, int32_t* __restrict__ row_src, const float* __restrict__ feat,
+    const float* __restrict__ root_feat, const bf16_t* __restrict__ embed, int V, int d,
+    bf16_t* __restrict__ x_in, int32_t* __restrict__ status) {
+  __shared__ int sh_src, sh_tok;
+  const int j = blockIdx.x;
+  const int slot = slot_base + j;
+  if (threadIdx.x == 0) {
+    int f = frontier[j];
+    if (f < 0 || f >= pool_n) {
+      set_status(status, EAGLE_DEV_BAD_INDEX);
+      f = 0;
+    }
+    const int par = pool_parent[f];
+    int src = -1;
+    if (par >= 0) {
+      src = par < pool_n ? slot_of_pool[par] : -1;
+      if (src < 0 || src >= slot_base) {
+        set_status(status, EAGLE_DEV_BAD_INDEX);
+        src = -1;
+      }
+    }
+    int tok = pool_token[f];
+    if (tok < 0 || tok >= V) {
+      set_status(status, EAGLE_DEV_BAD_TOKEN);
+      tok = 0;
+    }
+    slot_of_pool[f] = slot;
+    slot_parent[slot] = src;
+    row_token[j] = tok;
+    row_depth[j] = pool_depth[f];
+    row_slot[j] = slot;
+    row_src[j] = src;
+    sh_src = src;
+    sh_tok = tok;
+  }
+  __syncthreads();
+  const int src = sh_src;
+  if (slot_mask && (int)threadIdx.x < words) {
+    const int w = threadIdx.x;
+    uint64_t m = src >= 0 ? slot_mask[(size_t)src * words + w] : 0ull;
+    if ((slot >> 6) == w) m |= 1ull << (slot & 63);
+    slot_mask[(size_t)slot * words + w] = m;
+  }
+  if (x_in) {
+    const float* f = src >= 0 ? feat + (size_t)src * d : root_feat;
+    const bf16_t* e = embed + (size_t)sh_tok * d;
+    bf16_t* o = x_in + (size_t)j * 2 * d;
+    for (int n = threadIdx.x; n < d; n += 256) {
+      o[n] = (bf16_t)f32_to_bf16_bits(f[n]);
+      o[d + n] = e[n];
+    }
   }
 }
 
@@ -341,8 +484,20 @@ static void launch_lin(const LinParams& p, hipStream_t s) {
                      dim3((p.N + cols - 1) / cols, p.ksplit), dim3(256), 0, s, p);
 }
 
+// GEMM only, writing fp32 partials (ksplit >= 1) for a row-wise epilogue.
+static void launch_lin_partials(LinParams p, hipStream_t s) {
+  p.to_part = 1;
+  const int nt = (p.M + 15) / 16;
+  if (nt <= 1) launch_lin<1, 0>(p, s);
+  else if (nt <= 2) launch_lin<2, 0>(p, s);
+  else if (nt <= 4) launch_lin<4, 0>(p, s);
+  else if (nt <= 8) launch_lin<8, 0>(p, s);
+  else launch_lin<16, 0>(p, s);
+}
+
 template <int SWIGLU>
-static void dispatch_lin(const LinParams& p, hipStream_t s) {
+static void dispatch_lin(LinParams p, hipStream_t s) {
+  p.to_part = p.ksplit > 1 ? 1 : 0;
   const int nt = (p.M + 15) / 16;
   if (nt <= 1) launch_lin<1, SWIGLU>(p, s);
   else if (nt <= 2) launch_lin<2, SWIGLU>(p, s);
@@ -421,42 +576,91 @@ extern "C" int eagle_rope_qkv(const float* qkv, int32_t M, int32_t Hq, int32_t H
                               hipStream_t stream) {
   EAGLE_REQUIRE(qkv && depth && q_out && k_tree && v_tree, EAGLE_EINVAL);
   EAGLE_REQUIRE(M >= 1 && Hq >= 1 && Hkv >= 1 && hd >= 2 && hd % 2 == 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(hd / 2 <= eagle::kRopeMaxHalf, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(slot_cap >= 1 && ld_tree >= slot_cap && theta > 0.0f && pos_base >= 0,
                 EAGLE_EINVAL);
-  hipLaunchKernelGGL(eagle::rope_qkv_kernel, dim3(M), dim3(256), 0, stream, qkv, Hq, Hkv, hd,
-                     depth, pos_base, (double)theta, row_slot, slot_cap, (bf16_t*)q_out,
-                     (bf16_t*)k_tree, (bf16_t*)v_tree, ld_tree, dev_status);
+  eagle::RopeArgs r{Hq, Hkv, hd, depth, pos_base, (double)theta, row_slot, slot_cap,
+                    (bf16_t*)q_out, (bf16_t*)k_tree, (bf16_t*)v_tree, ld_tree, dev_status};
+  hipLaunchKernelGGL(eagle::rope_qkv_kernel, dim3(M), dim3(256), 0, stream, qkv, r);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }
 
-extern "C" int eagle_draft_rows(const int32_t* frontier, int32_t kf, const int32_t* pool_token,
-                                const int32_t* pool_parent, const int32_t* pool_depth,
-                                int32_t pool_n, int32_t* slot_of_pool, int32_t slot_base,
-                                int32_t slot_cap, int32_t* slot_parent, int32_t* row_token,
-                                int32_t* row_depth, int32_t* row_slot, int32_t* row_src,
-                                int32_t* dev_status, hipStream_t stream) {
+extern "C" size_t eagle_linear_rows_workspace(int32_t M, int32_t K, int32_t N) {
+  if (M < 1 || K < eagle::kWsKG || N < 1 || K % eagle::kWsKG) return 0;
+  return (size_t)eagle::lin_ksplit(M, K, N, 0) * M * N * sizeof(float);
+}
+
+extern "C" int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
+                                    const float* residual, float* out, const float* gamma,
+                                    float eps, void* norm_out, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  EAGLE_REQUIRE(x && W && out && gamma && norm_out && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && N >= 1 && eps >= 0.0f, EAGLE_EINVAL);
+  EAGLE_REQUIRE(K % eagle::kWsKG == 0 && N % 4 == 0 && N <= eagle::kRowMaxN, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(aligned16(x) && aligned16(W) && aligned16(out) && aligned16(gamma) &&
+                    aligned16(workspace) && (!residual || aligned16(residual)) &&
+                    ((uintptr_t)norm_out & 7) == 0,
+                EAGLE_EINVAL);
+  EAGLE_REQUIRE(ws_bytes >= eagle_linear_rows_workspace(M, K, N), EAGLE_EWORKSPACE);
+  eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)W, nullptr, N, residual, out, 0,
+                     eagle::lin_ksplit(M, K, N, 0), (float*)workspace};
+  p.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
+  eagle::launch_lin_partials(p, stream);
+  hipLaunchKernelGGL(eagle::linear_reduce_norm_kernel, dim3(M), dim3(eagle::kRowThreads), 0,
+                     stream, p, gamma, eps, (bf16_t*)norm_out);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const void* w_qkv,
+                                     int32_t Hq, int32_t Hkv, int32_t hd, const int32_t* depth,
+                                     int64_t pos_base, float theta, const int32_t* row_slot,
+                                     int32_t slot_cap, void* q_out, void* k_tree, void* v_tree,
+                                     int32_t ld_tree, void* workspace, size_t ws_bytes,
+                                     int32_t* dev_status, hipStream_t stream) {
+  EAGLE_REQUIRE(x && w_qkv && depth && q_out && k_tree && v_tree && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && Hq >= 1 && Hkv >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(hd >= 8 && hd % 8 == 0 && hd / 2 <= eagle::kRopeMaxHalf, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(slot_cap >= 1 && ld_tree >= slot_cap && theta > 0.0f && pos_base >= 0,
+                EAGLE_EINVAL);
+  const int N = (Hq + 2 * Hkv) * hd;
+  EAGLE_REQUIRE((size_t)N * sizeof(float) <= 64 * 1024, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(aligned16(x) && aligned16(w_qkv) && aligned16(workspace), EAGLE_EINVAL);
+  EAGLE_REQUIRE(ws_bytes >= eagle_linear_rows_workspace(M, K, N), EAGLE_EWORKSPACE);
+  eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)w_qkv, nullptr, N, nullptr, nullptr,
+                     0, eagle::lin_ksplit(M, K, N, 0), (float*)workspace};
+  eagle::RopeArgs r{Hq, Hkv, hd, depth, pos_base, (double)theta, row_slot, slot_cap,
+                    (bf16_t*)q_out, (bf16_t*)k_tree, (bf16_t*)v_tree, ld_tree, dev_status};
+  eagle::launch_lin_partials(p, stream);
+  hipLaunchKernelGGL(eagle::linear_reduce_rope_kernel, dim3(M), dim3(eagle::kRowThreads),
+                     N * sizeof(float), stream, p, r);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_draft_prepare(const int32_t* frontier, int32_t kf, const int32_t* pool_token,
+                                   const int32_t* pool_parent, const int32_t* pool_depth,
+                                   int32_t pool_n, int32_t* slot_of_pool, int32_t slot_base,
+                                   int32_t slot_cap, int32_t* slot_parent, uint64_t* slot_mask,
+                                   int32_t words, int32_t* row_token, int32_t* row_depth,
+                                   int32_t* row_slot, int32_t* row_src, const float* feat,
+                                   const float* root_feat, const void* embed, int32_t V,
+                                   int32_t d, void* x_in, int32_t* dev_status,
+                                   hipStream_t stream) {
   EAGLE_REQUIRE(frontier && pool_token && pool_parent && pool_depth && slot_of_pool &&
                     slot_parent && row_token && row_depth && row_slot && row_src,
                 EAGLE_EINVAL);
-  EAGLE_REQUIRE(kf >= 1 && kf <= 256 && pool_n >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(kf >= 1 && kf <= EAGLE_MAX_TREE && pool_n >= 1 && V >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(slot_base >= 0 && slot_base + kf <= slot_cap, EAGLE_EINVAL);
-  hipLaunchKernelGGL(eagle::draft_rows_kernel, dim3(1), dim3(256), 0, stream, frontier, kf,
+  EAGLE_REQUIRE(!slot_mask || (words >= (slot_cap + 63) / 64 && words <= 4), EAGLE_EINVAL);
+  EAGLE_REQUIRE(!x_in || (feat && root_feat && embed && d >= 1), EAGLE_EINVAL);
+  hipLaunchKernelGGL(eagle::draft_prepare_kernel, dim3(kf), dim3(256), 0, stream, frontier,
                      pool_token, pool_parent, pool_depth, pool_n, slot_of_pool, slot_base,
-                     slot_cap, slot_parent, row_token, row_depth, row_slot, row_src, dev_status);
-  EAGLE_LAUNCH_CHECK();
-  return EAGLE_OK;
-}
-
-extern "C" int eagle_draft_input(int32_t M, const int32_t* row_token, const int32_t* row_src,
-                                 const float* feat, int32_t feat_rows, const float* root_feat,
-                                 const void* embed, int32_t V, int32_t d, void* out,
-                                 int32_t* dev_status, hipStream_t stream) {
-  EAGLE_REQUIRE(row_token && row_src && feat && root_feat && embed && out, EAGLE_EINVAL);
-  EAGLE_REQUIRE(M >= 1 && V >= 1 && d >= 1 && feat_rows >= 1, EAGLE_EINVAL);
-  hipLaunchKernelGGL(eagle::draft_input_kernel, dim3(M), dim3(256), 0, stream, row_token,
-                     row_src, feat, feat_rows, root_feat, (const bf16_t*)embed, V, d,
-                     (bf16_t*)out, dev_status);
+                     slot_cap, slot_parent, slot_mask, words, row_token, row_depth, row_slot,
+                     row_src, feat, root_feat, (const bf16_t*)embed, V, d, (bf16_t*)x_in,
+                     dev_status);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

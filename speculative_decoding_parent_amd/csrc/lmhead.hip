@@ -10,7 +10,7 @@
 // work is ~T flop per weight byte, so the kernel is bound by streaming W from
 // HBM once.  Design:
 //   * MFMA v_mfma_f32_16x16x32_bf16 with W rows as the M dimension (16 rows per
-//     tile, 4 tiles = 64 rows per wave, 256 rows per 4-wave workgroup) and the
+//     tile, 8 or 4 tiles = 128 or 64 rows per wave, 4 waves per workgroup) and the
 //     feature rows as N (16 per tile, NT tiles).  W goes straight from HBM into
 //     MFMA A operands (the shared weight-streaming core, wstream.h).
 //   * f is shared by all workgroups (<= 512 KB at T = 64): each 128-wide k
@@ -30,9 +30,13 @@
 namespace eagle {
 
 constexpr int kLmWaves = 4;
-constexpr int kLmMT = 4;
-constexpr int kLmRowsWave = 16 * kLmMT;
-constexpr int kLmRowsBlock = kLmRowsWave * kLmWaves;
+
+// W tiles of 16 rows per wave: 8 (128 rows) while the feature rows fit one MFMA
+// tile, which keeps the most weight bytes in flight per wave; fewer as more
+// feature rows need accumulator registers (no spills up to T = 256).
+__host__ __device__ constexpr int lm_mt(int T) {
+  return T <= 16 ? 8 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
+}
 
 struct LmParams {
   const bf16_t* f;
@@ -44,8 +48,11 @@ struct LmParams {
   int32_t* part_idx;   // [nwave][T][k]
 };
 
-template <int NT>
-__global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void lmhead_bf16_kernel(LmParams p) {
+template <int NT, int kLmMT>
+__global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_bf16_kernel(
+    LmParams p) {
+  constexpr int kLmRowsWave = 16 * kLmMT;
+  constexpr int kLmRowsBlock = kLmRowsWave * kLmWaves;
   __shared__ __attribute__((aligned(16))) bf16_t fs[ws_lds_elems<NT>()];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -176,6 +183,7 @@ __device__ __forceinline__ void block_best256(float& v, int& i, float* rv, int* 
 // "best candidate strictly after the previous pick".  If more survive than
 // LDS holds, the rounds run over all candidates instead (same result).
 constexpr int kMergeCap = 4096;
+constexpr int kMergePer = 12;     // wave lists per thread kept in registers
 
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(
     const float2* __restrict__ part_stat, const float* __restrict__ part_val,
@@ -199,22 +207,46 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
   S = block_reduce256(S, redf, [](float a, float b) { return a + b; });
   const float L = M + logf(S);
 
-  // theta: the k-th best first entry over all wave lists
+  // theta: the k-th best first entry over all wave lists (held in registers
+  // when each thread owns at most kMergePer lists)
   float thv = -INFINITY;
   int thi = INT_MAX;
   if (nw >= k) {
+    float hv[kMergePer];
+    int hi[kMergePer];
+    const bool inreg = nw <= 256 * kMergePer;
+#pragma unroll
+    for (int q = 0; q < kMergePer; ++q) {
+      const int w = threadIdx.x + 256 * q;
+      hv[q] = -INFINITY;
+      hi[q] = INT_MAX;
+      if (inreg && w < nw) {
+        const size_t o = ((size_t)w * T + t) * k;
+        hv[q] = part_val[o];
+        hi[q] = part_idx[o];
+      }
+    }
     float lastv = INFINITY;
     int lasti = -1;
     for (int r = 0; r < k; ++r) {
       float bv = -INFINITY;
       int bi = INT_MAX;
-      for (int w = threadIdx.x; w < nw; w += 256) {
-        const size_t o = ((size_t)w * T + t) * k;
-        const float v = part_val[o];
-        const int i = part_idx[o];
-        if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
-          bv = v;
-          bi = i;
+      if (inreg) {
+#pragma unroll
+        for (int q = 0; q < kMergePer; ++q)
+          if (better(lastv, lasti, hv[q], hi[q]) && better(hv[q], hi[q], bv, bi)) {
+            bv = hv[q];
+            bi = hi[q];
+          }
+      } else {
+        for (int w = threadIdx.x; w < nw; w += 256) {
+          const size_t o = ((size_t)w * T + t) * k;
+          const float v = part_val[o];
+          const int i = part_idx[o];
+          if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
+            bv = v;
+            bi = i;
+          }
         }
       }
       block_best256(bv, bi, rv, ri);
@@ -352,7 +384,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   LmLayout l{};
   if (dt == EAGLE_BF16) {
-    l.nw = ((V + kLmRowsBlock - 1) / kLmRowsBlock) * kLmWaves;
+    const int rows_block = 16 * lm_mt(T) * kLmWaves;
+    l.nw = ((V + rows_block - 1) / rows_block) * kLmWaves;
     l.stat_off = 0;
     l.val_off = align256((size_t)l.nw * T * sizeof(float2));
     l.idx_off = l.val_off + align256((size_t)l.nw * T * k * sizeof(float));
@@ -364,9 +397,11 @@ static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   return l;
 }
 
-template <int NT>
-static void launch_lm(const LmParams& p, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL(lmhead_bf16_kernel<NT>, dim3(nblocks), dim3(256), 0, s, p);
+template <int NT, int MT>
+static void launch_lm(const LmParams& p, hipStream_t s) {
+  const int rows_block = 16 * MT * kLmWaves;
+  hipLaunchKernelGGL((lmhead_bf16_kernel<NT, MT>), dim3((p.V + rows_block - 1) / rows_block),
+                     dim3(256), 0, s, p);
 }
 
 }  // namespace eagle
@@ -396,13 +431,14 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
     EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
                (float2*)(ws + l.stat_off), (float*)(ws + l.val_off), (int32_t*)(ws + l.idx_off)};
-    const int nblocks = (V + kLmRowsBlock - 1) / kLmRowsBlock;
     const int nt = (T + 15) / 16;
-    if (nt <= 1) launch_lm<1>(p, nblocks, stream);
-    else if (nt <= 2) launch_lm<2>(p, nblocks, stream);
-    else if (nt <= 4) launch_lm<4>(p, nblocks, stream);
-    else if (nt <= 8) launch_lm<8>(p, nblocks, stream);
-    else launch_lm<16>(p, nblocks, stream);
+    static_assert(lm_mt(16) == 8 && lm_mt(64) == 4 && lm_mt(128) == 2 && lm_mt(129) == 1,
+                  "tile choice");
+    if (nt <= 1) launch_lm<1, 8>(p, stream);
+    else if (nt <= 2) launch_lm<2, 4>(p, stream);
+    else if (nt <= 4) launch_lm<4, 4>(p, stream);
+    else if (nt <= 8) launch_lm<8, 2>(p, stream);
+    else launch_lm<16, 1>(p, stream);
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmhead_merge_kernel, dim3(T), dim3(256), 0, stream, p.part_stat,
                        p.part_val, p.part_idx, l.nw, T, k, topk_id, topk_logp, lse);

@@ -87,18 +87,20 @@ __global__ __launch_bounds__(1024) void rerank_kernel(
     pos[i] = keep ? 1 : 0;
     mine += keep ? 1 : 0;
   }
-  cnt[tid] = mine;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < (int)blockDim.x; ++w) {
-      const int c = cnt[w];
-      cnt[w] = run;
-      run += c;
-    }
+  // exclusive scan of the per-thread counts: within each wave, then over the
+  // wave totals
+  int incl = mine;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
+  if (lane == 63) cnt[tid >> 6] = incl;
   __syncthreads();
-  int run = cnt[tid];
+  int off = 0;
+  for (int w = 0; w < (tid >> 6); ++w) off += cnt[w];
+  int run = off + incl - mine;
   for (int i = lo; i < hi; ++i) {
     if (pos[i]) {
       pos[i] = (int16_t)run;

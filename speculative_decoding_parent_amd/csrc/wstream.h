@@ -5,7 +5,9 @@
 // With few activation rows every weight byte is used <= 256 times, so these
 // products are bound by reading W from HBM once.  A 4-wave workgroup owns
 // 4 x MT x 16 weight rows; each wave issues its W rows' 16-byte loads for the
-// next 128-wide k step before running the MFMAs of the current one.  W rows are
+// next 128-wide k step before running the MFMAs of the current one (the small
+// activation loads are issued first, so staging them in LDS never waits for
+// the weight loads still in flight).  W rows are
 // the MFMA M dimension (v_mfma_f32_16x16x32_bf16 A operand, straight from
 // registers) and the activation rows are N, staged per k step in LDS
 // (double-buffered; rows padded by 16 bytes so the 16 lanes of one b128 read
@@ -105,8 +107,8 @@ __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], co
   for (int kk = 0; kk < nk; kk += 2) {
     const bool more1 = kk + 1 < nk;
     if (more1) {
+      load_x(kk + 1, fr);   // first: the LDS store below waits only for these
       load_w(kk + 1, wb);
-      load_x(kk + 1, fr);
     }
     compute(fs0, wa);
     if (more1) store_x(fs1, fr);
@@ -114,8 +116,8 @@ __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], co
     if (!more1) break;
     const bool more2 = kk + 2 < nk;
     if (more2) {
-      load_w(kk + 2, wa);
       load_x(kk + 2, fr);
+      load_w(kk + 2, wa);
     }
     compute(fs1, wb);
     if (more2) store_x(fs0, fr);

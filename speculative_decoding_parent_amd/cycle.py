@@ -110,30 +110,32 @@ class DraftVerifyCycle:
         self.ws_acc = torch.empty(lib.eagle_accept_workspace(T, V), dtype=torch.uint8, device=dev)
         ws_lin = 256
         for M in (1, ks, T):
-            for (K, N, glu) in ((2 * d, d, 0), (d, nqkv, 0), (hq * hd, d, 0), (d, F, 1), (F, d, 0)):
-                ws_lin = max(ws_lin, lib.eagle_linear_workspace(M, K, N, glu))
+            for (K, N) in ((2 * d, d), (d, nqkv), (hq * hd, d), (F, d)):
+                ws_lin = max(ws_lin, lib.eagle_linear_rows_workspace(M, K, N))
+            ws_lin = max(ws_lin, lib.eagle_linear_workspace(M, d, F, 1))
         self.ws_lin = torch.empty(ws_lin, dtype=torch.uint8, device=dev)
         self.graph = None
 
     # ------------------------------------------------------------ one layer
-    def _layer(self, lw, n, x_res, depth, row_slot, kc, vc, kt, vt, Tk, mask, out, q_mask_row):
-        """Decoder layer on rows 0..n-1 whose fp32 input (residual stream) is
-        x_res; writes the fp32 output to ``out``."""
+    def _layer(self, lw, n, x_res, depth, row_slot, kc, vc, kt, vt, Tk, mask, out, q_mask_row,
+               final_norm):
+        """Decoder layer on rows 0..n-1: self.n1[:n] holds RMSNorm(x_res) (bf16),
+        x_res the fp32 residual stream.  Writes the fp32 output to ``out`` and
+        its final RMSNorm (bf16) to self.z[:n]."""
         w = self.w
-        _lib.eagle_rmsnorm(x_res, lw["norm1"], w.rms_eps, out=self.n1[:n])
-        _lib.eagle_linear(self.n1[:n], lw["wqkv"], out=self.qkv[:n], workspace=self.ws_lin)
-        _lib.eagle_rope_qkv(self.qkv[:n], w.hq, w.hkv, w.hd, depth, self.L, kt, vt,
-                            row_slot=row_slot, theta=w.rope_theta, q_out=self.q[:n],
-                            dev_status=self.status)
+        _lib.eagle_linear_rope_qkv(self.n1[:n], lw["wqkv"], w.hq, w.hkv, w.hd, depth, self.L, kt, vt,
+                                   row_slot=row_slot, theta=w.rope_theta, q_out=self.q[:n],
+                                   workspace=self.ws_lin, dev_status=self.status)
         _lib.eagle_tree_attn(self.q[:n], kc, vc, self.L, kt, vt, Tk, mask, q_mask_row=q_mask_row,
                              out=self.attn[:n], workspace=self.ws_attn, dev_status=self.status)
-        _lib.eagle_linear(self.attn[:n].view(n, -1), lw["wo"], residual=x_res, out=self.x2[:n],
-                          workspace=self.ws_lin)
-        _lib.eagle_rmsnorm(self.x2[:n], lw["norm2"], w.rms_eps, out=self.n2[:n])
+        _lib.eagle_linear_rmsnorm(self.attn[:n].view(n, -1), lw["wo"], lw["norm2"], residual=x_res,
+                                  out=self.x2[:n], norm_out=self.n2[:n], eps=w.rms_eps,
+                                  workspace=self.ws_lin)
         _lib.eagle_linear_swiglu(self.n2[:n], lw["wgate"], lw["wup"], out=self.gu[:n],
                                  workspace=self.ws_lin)
-        _lib.eagle_linear(self.gu[:n], lw["wdown"], residual=self.x2[:n], out=out,
-                          workspace=self.ws_lin)
+        _lib.eagle_linear_rmsnorm(self.gu[:n], lw["wdown"], final_norm, residual=self.x2[:n],
+                                  out=out, norm_out=self.z[:n], eps=w.rms_eps,
+                                  workspace=self.ws_lin)
 
     # ------------------------------------------------------------ the cycle
     def draft_round(self, r: int):
@@ -143,19 +145,16 @@ class DraftVerifyCycle:
         Sr = base + kf
         fr = self.frontier[r]
         tok, depth, slot, src = (t[:kf] for t in self.rows)
-        _lib.eagle_draft_rows(fr, self.pool_token, self.pool_parent, self.pool_depth,
-                              self.pool_n[r], self.slot_of_pool, base, self.slot_parent,
-                              (tok, depth, slot, src), dev_status=self.status)
-        _lib.eagle_draft_input(tok, src, self.feat, self.root_feat, self.embed, out=self.x_in[:kf],
-                               dev_status=self.status)
-        _lib.eagle_linear(self.x_in[:kf], self.w_fuse, out=self.h[:kf], workspace=self.ws_lin)
-        _lib.eagle_build_tree_mask(self.slot_parent[:Sr], words=self.smask.shape[1],
-                                   mask=self.smask[:Sr], depth=self.sdepth[:Sr],
-                                   dev_status=self.status)
+        _lib.eagle_draft_prepare(fr, self.pool_token, self.pool_parent, self.pool_depth,
+                                 self.pool_n[r], self.slot_of_pool, base, self.slot_parent,
+                                 (tok, depth, slot, src), slot_mask=self.smask, feat=self.feat,
+                                 root_feat=self.root_feat, embed=self.embed, x_in=self.x_in[:kf],
+                                 dev_status=self.status)
+        _lib.eagle_linear_rmsnorm(self.x_in[:kf], self.w_fuse, self.draft["norm1"], out=self.h[:kf],
+                                  norm_out=self.n1[:kf], eps=w.rms_eps, workspace=self.ws_lin)
         feat_rows = self.feat[base:base + kf]
         self._layer(self.draft, kf, self.h[:kf], depth, slot, self.dkc, self.dvc, self.dkt,
-                    self.dvt, Sr, self.smask[:Sr], feat_rows, slot)
-        _lib.eagle_rmsnorm(feat_rows, self.draft_norm, w.rms_eps, out=self.z[:kf])
+                    self.dvt, Sr, self.smask[:Sr], feat_rows, slot, self.draft_norm)
         _lib.eagle_lmhead_topk(self.z[:kf], self.w_lm, self.k, topk_id=self.ids[r],
                                topk_logp=self.logp[r], lse=self.lse[:kf], workspace=self.ws_lm)
         _lib.eagle_expand_rerank(_lib.EAGLE_EXPAND, self.pool_token, self.pool_parent,
@@ -173,9 +172,9 @@ class DraftVerifyCycle:
         _lib.eagle_build_tree_mask(self.node_parent, mask=self.vmask, depth=self.vdepth,
                                    dev_status=self.status)
         _lib.eagle_embed(self.node_token, self.embed, out=self.vx, dev_status=self.status)
+        _lib.eagle_rmsnorm(self.vx, self.target["norm1"], w.rms_eps, out=self.n1[:T])
         self._layer(self.target, T, self.vx, self.node_depth, None, self.tkc, self.tvc, self.tkt,
-                    self.tvt, T, self.vmask, self.vout, None)
-        _lib.eagle_rmsnorm(self.vout, self.target_norm, w.rms_eps, out=self.z[:T])
+                    self.tvt, T, self.vmask, self.vout, None, self.target_norm)
         _lib.eagle_lmhead_topk(self.z[:T], self.w_lm, self.k, topk_id=self.v_ids,
                                topk_logp=self.v_logp, lse=self.lse[:T], logits=self.v_logits,
                                workspace=self.ws_lm)

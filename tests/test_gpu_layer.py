@@ -53,6 +53,50 @@ def test_swiglu(dev, M, K, N):
     assert np.all(np.abs(got - ref) <= U * np.abs(ref) + 1e-4 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("M,K,N,res", [(1, 8192, 4096, False), (10, 4096, 4096, True),
+                                       (64, 14336, 4096, True), (7, 256, 8192, True)])
+def test_linear_rmsnorm(dev, M, K, N, res):
+    print(f"linear_rmsnorm M={M} K={K} N={N}", flush=True)
+    g = inputs.rng(707, M, K)
+    x = inputs.normal(g, (M, K))
+    W = inputs.normal(g, (N, K), std=float(1 / np.sqrt(K)))
+    r = inputs.normal(g, (M, N), dtype=torch.float32) if res else None
+    gamma = 1 + 0.1 * inputs.normal(g, (N,), dtype=torch.float32)
+    out, nrm = _lib.eagle_linear_rmsnorm(x.to(dev), W.to(dev), gamma.to(dev),
+                                         residual=None if r is None else r.to(dev))
+    ref = linear(x, W) + (0 if r is None else r.numpy())
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-5
+    rn = oracle.rms_norm(ref, gamma, 1e-5)
+    assert np.all(np.abs(nrm.float().cpu().numpy() - rn) <= U * np.abs(rn) + 1e-4 * np.abs(rn).max())
+
+
+def test_linear_rope_qkv(dev):
+    g = inputs.rng(708, 0)
+    M, K, hq, hkv, hd, cap, L = 10, 4096, 32, 8, 128, 51, 4096
+    x = inputs.normal(g, (M, K))
+    W = inputs.normal(g, ((hq + 2 * hkv) * hd, K), std=float(1 / np.sqrt(K)))
+    depth = g.integers(0, 7, M).astype(np.int32)
+    slots = g.choice(cap, M, replace=False).astype(np.int32)
+    kt = torch.zeros((hkv, cap, hd), dtype=torch.bfloat16, device=dev)
+    vt = torch.zeros_like(kt)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    q = _lib.eagle_linear_rope_qkv(x.to(dev), W.to(dev), hq, hkv, hd, torch.from_numpy(depth).to(dev),
+                                   L, kt, vt, row_slot=torch.from_numpy(slots).to(dev), dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    qkv = linear(x, W).reshape(M, hq + 2 * hkv, hd)
+    pos = L + depth
+    rq, rk = oracle.rope(qkv[:, :hq], pos), oracle.rope(qkv[:, hq:hq + hkv], pos)
+    tol = lambda r: U * np.abs(r) + 1e-4 * np.abs(r).max()
+    assert np.all(np.abs(q.float().cpu().numpy() - rq) <= tol(rq))
+    ktn, vtn = kt.float().cpu().numpy(), vt.float().cpu().numpy()
+    kmax, vmax = np.abs(rk).max(), np.abs(qkv[:, hq + hkv:]).max()
+    for m in range(M):
+        assert np.all(np.abs(ktn[:, slots[m]] - rk[m]) <= U * np.abs(rk[m]) + 1e-4 * kmax)
+        vr = qkv[m, hq + hkv:]
+        assert np.all(np.abs(vtn[:, slots[m]] - vr) <= U * np.abs(vr) + 1e-4 * vmax)
+
+
 def test_rmsnorm(dev):
     g = inputs.rng(702, 0)
     x = inputs.normal(g, (33, 4096), std=3.0, dtype=torch.float32)
@@ -91,8 +135,9 @@ def test_rope_qkv(dev, L, hd):
     assert np.all(ktn[:, untouched] == 0)
 
 
-def test_draft_rows_input_and_embed(dev):
-    """Round bookkeeping is integer work: compared exactly with a hand model."""
+def test_draft_prepare_and_embed(dev):
+    """Round bookkeeping is integer work: compared exactly with a hand model;
+    slot mask rows against the oracle's mask of the slot tree."""
     g = inputs.rng(704, 0)
     V, d, cap, S = 500, 128, 40, 12
     # pool: root, 4 children (round 1), then 8 entries below frontier [1, 3]
@@ -103,32 +148,35 @@ def test_draft_rows_input_and_embed(dev):
     pt, pp, pd = P(tok), P(par, fill=-1), P(dep)
     slot_of = torch.full((cap,), -1, dtype=torch.int32, device=dev)
     slot_parent = torch.full((S,), -1, dtype=torch.int32, device=dev)
+    smask = torch.zeros((S, 1), dtype=torch.int64, device=dev)
     rows = [torch.zeros(4, dtype=torch.int32, device=dev) for _ in range(4)]
+    feat = inputs.normal(g, (S, d), dtype=torch.float32)
+    root = inputs.normal(g, (d,), dtype=torch.float32)
+    emb = inputs.normal(g, (V, d))
+    fd, rd, ed = feat.to(dev), root.to(dev), emb.to(dev)
+    x_in = torch.zeros((4, 2 * d), dtype=torch.bfloat16, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
-    _lib.eagle_draft_rows(torch.tensor([0], dtype=torch.int32, device=dev), pt, pp, pd, 1, slot_of,
-                          0, slot_parent, [r[:1] for r in rows], dev_status=st)
-    _lib.eagle_draft_rows(torch.tensor([1, 3], dtype=torch.int32, device=dev), pt, pp, pd, 5,
-                          slot_of, 1, slot_parent, [r[:2] for r in rows], dev_status=st)
-    _lib.eagle_draft_rows(torch.tensor([6, 9, 12], dtype=torch.int32, device=dev), pt, pp, pd, 13,
-                          slot_of, 3, slot_parent, [r[:3] for r in rows], dev_status=st)
+    for fr, n, base in (([0], 1, 0), ([1, 3], 5, 1), ([6, 9, 12], 13, 3)):
+        _lib.eagle_draft_prepare(torch.tensor(fr, dtype=torch.int32, device=dev), pt, pp, pd, n,
+                                 slot_of, base, slot_parent, [r[:len(fr)] for r in rows],
+                                 slot_mask=smask, feat=fd, root_feat=rd, embed=ed,
+                                 x_in=x_in[:len(fr)], dev_status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    assert slot_parent.cpu().tolist()[:6] == [-1, 0, 0, 1, 2, 2]
+    sp = slot_parent.cpu().tolist()[:6]
+    assert sp == [-1, 0, 0, 1, 2, 2]
     assert slot_of.cpu().tolist()[:13] == [0, 1, -1, 2, -1, -1, 3, -1, -1, 4, -1, -1, 5]
     assert rows[0].cpu().tolist()[:3] == [tok[6], tok[9], tok[12]]
     assert rows[1].cpu().tolist()[:3] == [2, 2, 2]
     assert rows[2].cpu().tolist()[:3] == [3, 4, 5]
     assert rows[3].cpu().tolist()[:3] == [1, 2, 2]
-    feat = inputs.normal(g, (S, d), dtype=torch.float32)
-    root = inputs.normal(g, (d,), dtype=torch.float32)
-    emb = inputs.normal(g, (V, d))
-    src = torch.tensor([-1, 1, 2], dtype=torch.int32, device=dev)
+    ref_mask, _ = oracle.build_tree_mask(np.array(sp, np.int32))
+    assert np.array_equal(smask[:6].cpu().numpy().view(np.uint64), ref_mask)
+    want = torch.stack([torch.cat([feat[s].to(torch.bfloat16), emb[t]]) for s, t in
+                        [(1, tok[6]), (2, tok[9]), (2, tok[12])]])
+    assert torch.equal(x_in[:3].cpu(), want)
     tk = torch.tensor([7, 8, 499], dtype=torch.int32, device=dev)
-    x = _lib.eagle_draft_input(tk, src, feat.to(dev), root.to(dev), emb.to(dev)).cpu()
-    want = torch.stack([torch.cat([f.to(torch.bfloat16), emb[t]]) for f, t in
-                        [(root, 7), (feat[1], 8), (feat[2], 499)]])
-    assert torch.equal(x, want)
-    e = _lib.eagle_embed(tk, emb.to(dev)).cpu()
+    e = _lib.eagle_embed(tk, ed).cpu()
     assert torch.equal(e, emb[[7, 8, 499]].float())
 
 
@@ -150,8 +198,10 @@ def layer_case(dev, w, seed, n, Tk, slots, slot_par):
     mask, _ = _lib.eagle_build_tree_mask(torch.from_numpy(slot_par).to(dev))
     out = torch.zeros((n, w.d), dtype=torch.float32, device=dev)
     sl = torch.from_numpy(slots.astype(np.int32)).to(dev)
-    cyc._layer({k: v.to(dev) for k, v in lw.items()}, n, x.to(dev), torch.from_numpy(depth).to(dev),
-               sl, cyc.dkc, cyc.dvc, kt, vt, Tk, mask, out, sl)
+    lwd = {k: v.to(dev) for k, v in lw.items()}
+    _lib.eagle_rmsnorm(x.to(dev), lwd["norm1"], w.rms_eps, out=cyc.n1[:n])
+    cyc._layer(lwd, n, x.to(dev), torch.from_numpy(depth).to(dev), sl, cyc.dkc, cyc.dvc, kt, vt,
+               Tk, mask, out, sl, cyc.draft_norm)
     torch.cuda.synchronize()
     assert int(cyc.status.item()) == 0
     nq = w.hq * w.hd
