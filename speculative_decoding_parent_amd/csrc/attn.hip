@@ -22,14 +22,22 @@
 //   O^T += V^T P^T  with P^T taken straight from the S^T accumulators: a lane
 //                 holds 4 consecutive positions of one query row per 16-row
 //                 tile, so two tiles give the 8 k-values of a B operand once
-//                 the k order is permuted; V^T comes from a transposed LDS
-//                 copy with the same permutation.
+//                 the k order is permuted.  V stays row-major in LDS (stored
+//                 like K, 16 bytes per lane); its A operand is read with the
+//                 gfx950 transposing LDS read ds_read_b64_tr_b16, which hands
+//                 lane i of a 16-lane group element j of the 8-byte chunk that
+//                 lane 4j + i/4 addressed (position i mod 4 of it): pointing
+//                 lane (g, r16) at V[4g + r16/4][4 (r16 mod 4)] of a 16-dim
+//                 slice gives it V[4g + j][r16] for j < 4, i.e. four positions
+//                 of one head dim, in the permuted k order.
 // K and V of the next tile are fetched into registers (16-byte loads,
 // coalesced along the head dimension) while the current tile computes.
 //
 // fp32 path (small workloads): one workgroup per (query row, head, split)
 // computes the scores into LDS in fp32 and reduces them directly; same
 // partial layout and merge.
+#include <type_traits>
+
 #include "common.h"
 
 namespace eagle {
@@ -63,17 +71,29 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read of 4 bf16 (see the file comment for the lane layout).
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
 template <int HD, int NTW, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p) {
   constexpr int NTH = 64 * NW;
   constexpr int KB = HD / 32;
   constexpr int MTV = HD / 16;
+  // row strides: K rows 8 elements past a bank round (16 lanes of a b128 read
+  // on distinct banks), V rows 16 past (the four rows a 16-lane group reads
+  // with the transposing b64 read on disjoint banks)
   constexpr int KS = HD + 8;
-  constexpr int VS = kAtTile + 8;
+  constexpr int VS = HD + 16;
   constexpr int CPR = HD / 8;
   constexpr int NCH = kAtTile * CPR / NTH;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[kAtTile * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[HD * VS];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[kAtTile * VS];
 
   const int split = blockIdx.x;
   const int gkv = blockIdx.y;
@@ -111,13 +131,13 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
   }
 
   int64_t pos0;
-  int64_t npos;
+  int npos;
   const bf16_t* kb_ptr;
   const bf16_t* vb_ptr;
   if (!is_tree) {
     pos0 = (int64_t)split * p.tiles_per_split * kAtTile;
-    npos = p.L - pos0;
-    if (npos > (int64_t)p.tiles_per_split * kAtTile) npos = (int64_t)p.tiles_per_split * kAtTile;
+    const int64_t rest = p.L - pos0;
+    npos = rest > (int64_t)p.tiles_per_split * kAtTile ? p.tiles_per_split * kAtTile : (int)rest;
     kb_ptr = p.kc + ((size_t)gkv * p.ldc + pos0) * HD;
     vb_ptr = p.vc + ((size_t)gkv * p.ldc + pos0) * HD;
   } else {
@@ -126,7 +146,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     kb_ptr = p.kt + (size_t)gkv * p.ldt * HD;
     vb_ptr = p.vt + (size_t)gkv * p.ldt * HD;
   }
-  const int ntiles = npos > 0 ? (int)((npos + kAtTile - 1) / kAtTile) : 0;
+  const int ntiles = npos > 0 ? (npos + kAtTile - 1) / kAtTile : 0;
 
   float m[NTW], l[NTW];
   f32x4 o[MTV][NTW];
@@ -145,10 +165,11 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
       const int c = tid + NTH * j;
       const int pr = c / CPR;
       const int cc = c - pr * CPR;
-      const int64_t pos = (int64_t)t * kAtTile + pr;
+      const int pos = t * kAtTile + pr;
       const bool ok = pos < npos;
-      kr[j] = ok ? *(const u32x4*)(kb_ptr + pos * HD + cc * 8) : u32x4{0u, 0u, 0u, 0u};
-      vr[j] = ok ? *(const u32x4*)(vb_ptr + pos * HD + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      const int off = pos * HD + cc * 8;
+      kr[j] = ok ? *(const u32x4*)(kb_ptr + off) : u32x4{0u, 0u, 0u, 0u};
+      vr[j] = ok ? *(const u32x4*)(vb_ptr + off) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto store_tile = [&]() {
@@ -158,109 +179,117 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
       const int pr = c / CPR;
       const int cc = c - pr * CPR;
       *(u32x4*)(&Ks[pr * KS + cc * 8]) = kr[j];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        Vt[(cc * 8 + 2 * w) * VS + pr] = (bf16_t)(vr[j][w] & 0xffffu);
-        Vt[(cc * 8 + 2 * w + 1) * VS + pr] = (bf16_t)(vr[j][w] >> 16);
-      }
+      *(u32x4*)(&Vs[pr * VS + cc * 8]) = vr[j];
     }
   };
 
-  if (ntiles > 0) load_tile(0);
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
+  // The prefix and tree slices run separate copies of the tile loop, so the
+  // prefix loop issues no mask loads (and no wait on them) while the next
+  // tile's K/V are in flight.
+  auto run_tiles = [&](auto tree_tag) {
+    constexpr bool TREE = decltype(tree_tag)::value;
+    if (ntiles > 0) load_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+      __syncthreads();
+      store_tile();
+      __syncthreads();
+      if (t + 1 < ntiles) load_tile(t + 1);
 
-    // S^T = K Q^T over 4 position tiles of 16
-    f32x4 s[4][NTW];
+      // S^T = K Q^T over 4 position tiles of 16
+      f32x4 s[4][NTW];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NTW; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = *(const bf16x8*)(&Ks[(mt * 16 + r16) * KS + kb * 32 + 8 * g]);
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8 a = *(const bf16x8*)(&Ks[(mt * 16 + r16) * KS + kb * 32 + 8 * g]);
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[nt][kb]), s[mt][nt],
-                                                              0, 0, 0);
+          for (int nt = 0; nt < NTW; ++nt)
+            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[nt][kb]),
+                                                                s[mt][nt], 0, 0, 0);
+        }
       }
-    }
 
-    // visibility: positions past the slice end, and non-ancestors in the tree
-    const int64_t tile_pos = (int64_t)t * kAtTile;
-    const bool tail = tile_pos + kAtTile > npos;
+      // visibility: positions past the slice end, and non-ancestors in the tree
+      const int tile_pos = t * kAtTile;
+      if (TREE || tile_pos + kAtTile > npos) {
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      uint64_t bits = ~0ull;
-      if (is_tree) bits = mrow[nt] >= 0 ? p.mask[(size_t)mrow[nt] * p.words + t] : 0ull;
-      if (is_tree || tail) {
+        for (int nt = 0; nt < NTW; ++nt) {
+          uint64_t bits = ~0ull;
+          if (TREE) bits = mrow[nt] >= 0 ? p.mask[(size_t)mrow[nt] * p.words + t] : 0ull;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int pl = mt * 16 + 4 * g + j;
+              if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
+            }
+        }
+      }
+
+      // online softmax in the exp2 domain (arguments <= 0: the native v_exp_f32
+      // is exact enough and flushes only values below 2^-126) and P^T packing
+      u32x4 pb[2][NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mt][nt][j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m[nt], mx);
+        const float alpha = __builtin_amdgcn_exp2f((m[nt] - mnew) * p.c);
+        m[nt] = mnew;
+        const float nmc = -mnew * p.c;
+        float ps = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int pl = mt * 16 + 4 * g + j;
-            if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][j], p.c, nmc));
+            s[mt][nt][j] = pv;
+            ps += pv;
           }
-      }
-    }
-
-    // online softmax (exp2 domain) and P^T packing
-    u32x4 pb[2][NTW];
+        l[nt] = fmaf(l[nt], alpha, ps);
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      float mx = -INFINITY;
+        for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mt][nt][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[nt], mx);
-      const float alpha = exp2f((m[nt] - mnew) * p.c);
-      m[nt] = mnew;
-      const float nmc = -mnew * p.c;
-      float ps = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pv = exp2f(fmaf(s[mt][nt][j], p.c, nmc));
-          s[mt][nt][j] = pv;
-          ps += pv;
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
+                              pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
+                              pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
+                              pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
         }
-      l[nt] = fmaf(l[nt], alpha, ps);
-#pragma unroll
-      for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
+      }
+
+      // O^T += V^T P^T
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
-                            pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
-                            pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
-                            pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
+#pragma unroll
+        for (int mv = 0; mv < MTV; ++mv) {
+          // k slots 0-3: positions 32 kb2 + 4 g + j; slots 4-7: 16 further
+          const bf16_t* vp =
+              &Vs[(kb2 * 32 + 4 * g + (r16 >> 2)) * VS + mv * 16 + 4 * (r16 & 3)];
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 16 * VS);
+          const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            o[mv][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kb2][nt]),
+                                                                o[mv][nt], 0, 0, 0);
+        }
       }
     }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int mv = 0; mv < MTV; ++mv) {
-        const bf16_t* vrow = &Vt[(mv * 16 + r16) * VS + kb2 * 32 + 4 * g];
-        const u32x2 lo = *(const u32x2*)(vrow);
-        const u32x2 hi = *(const u32x2*)(vrow + 16);
-        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
-          o[mv][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kb2][nt]), o[mv][nt],
-                                                              0, 0, 0);
-      }
-    }
-  }
+  };
+  if (is_tree)
+    run_tiles(std::true_type{});
+  else
+    run_tiles(std::false_type{});
 
   // partials: lane (g, r16) holds O^T[hd = 16 mv + 4 g + j][row 16 nt + r16]
 #pragma unroll

@@ -32,16 +32,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (lo in bits 0-15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return pack_bf16x2(f, 0.0f) & 0xffffu;
 }
 
 __device__ __forceinline__ void set_status(int32_t* st, int32_t bit) {

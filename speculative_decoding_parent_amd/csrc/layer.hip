@@ -18,8 +18,6 @@
 
 namespace eagle {
 
-constexpr int kLinRowsBlock = 256;     // plain: 4 waves x 64 output columns
-constexpr int kGluColsBlock = 128;     // swiglu: 4 waves x 32 output columns
 
 struct LinParams {
   const bf16_t* x;
@@ -56,41 +54,52 @@ __device__ __forceinline__ void store4(void* out, int out_bf16, size_t off, int 
   }
 }
 
-template <int NT, int SWIGLU>
-__global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void linear_bf16_kernel(LinParams p) {
+// W tiles (16 rows) per wave: fewer as more activation rows need accumulators
+// (no register spills up to M = 256).  A SwiGLU wave pairs MT/2 gate tiles
+// with the MT/2 up tiles of the same output columns.
+__host__ __device__ constexpr int lin_mt(int nt, int swiglu) {
+  return nt <= 2 ? 4 : (nt <= 8 || swiglu ? 2 : 1);
+}
+__host__ __device__ constexpr int lin_cols_block(int mt, int swiglu) {
+  return swiglu ? 4 * 8 * mt : 4 * 16 * mt;
+}
+
+template <int NT, int SWIGLU, int MT>
+__global__ __launch_bounds__(256, (NT * MT <= 8 ? 2 : 1)) void linear_bf16_kernel(LinParams p) {
+  static_assert(!SWIGLU || MT % 2 == 0, "SwiGLU pairs gate and up tiles");
+  constexpr int HALF = SWIGLU ? MT / 2 : MT;      // output tiles per wave
   __shared__ __attribute__((aligned(16))) bf16_t fs[ws_lds_elems<NT>()];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
   const int r16 = lane & 15;
-  const int n0 = SWIGLU ? blockIdx.x * kGluColsBlock + wave * 32
-                        : blockIdx.x * kLinRowsBlock + wave * 64;
-  const bf16_t* wrow[4];
+  const int n0 = blockIdx.x * lin_cols_block(MT, SWIGLU) + wave * 16 * HALF;
+  const bf16_t* wrow[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int col = SWIGLU ? n0 + (mt & 1) * 16 + r16 : n0 + mt * 16 + r16;
-    const bf16_t* w = (SWIGLU && mt >= 2) ? p.w1 : p.w0;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int col = n0 + (mt % HALF) * 16 + r16;
+    const bf16_t* w = (SWIGLU && mt >= HALF) ? p.w1 : p.w0;
     wrow[mt] = w + (size_t)min(col, p.N - 1) * p.K + g * 8;
   }
   // k slice of this workgroup
   const int kc = p.K / p.ksplit;
   const int k0 = blockIdx.y * kc;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) wrow[mt] += k0;
-  f32x4 acc[4][NT];
-  wstream_mfma<NT, 4>(wrow, p.x + k0, p.K, p.M, kc, fs, acc);
+  for (int mt = 0; mt < MT; ++mt) wrow[mt] += k0;
+  f32x4 acc[MT][NT];
+  wstream_mfma<NT, MT>(wrow, p.x + k0, p.K, p.M, kc, fs, acc);
 
   if (p.to_part) {
-    // fp32 partials; tile mt of a SwiGLU wave goes to plane mt / 2
+    // fp32 partials; a SwiGLU wave's up tiles go to plane 1
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int m = nt * 16 + r16;
       if (m >= p.M) continue;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int n = SWIGLU ? n0 + (mt & 1) * 16 + 4 * g : n0 + mt * 16 + 4 * g;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int n = n0 + (mt % HALF) * 16 + 4 * g;
         if (n >= p.N) continue;
-        const int plane = SWIGLU ? (mt >> 1) : 0;
+        const int plane = mt / HALF;
         const size_t off =
             (((size_t)blockIdx.y * (SWIGLU ? 2 : 1) + plane) * p.M + m) * p.N + n;
         const float y[4] = {acc[mt][nt][0], acc[mt][nt][1], acc[mt][nt][2], acc[mt][nt][3]};
@@ -104,32 +113,22 @@ __global__ __launch_bounds__(256, (NT <= 4 ? 2 : 1)) void linear_bf16_kernel(Lin
   for (int nt = 0; nt < NT; ++nt) {
     const int m = nt * 16 + r16;
     if (m >= p.M) continue;
-    if (SWIGLU) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int n = n0 + mt * 16 + 4 * g;
-        if (n >= p.N) continue;
-        float y[4];
+    for (int mt = 0; mt < HALF; ++mt) {
+      const int n = n0 + mt * 16 + 4 * g;
+      if (n >= p.N) continue;
+      float y[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
+        if (SWIGLU) {
           const float gt = acc[mt][nt][j];
-          y[j] = gt / (1.0f + expf(-gt)) * acc[mt + 2][nt][j];
-        }
-        store4(p.out, 1, (size_t)m * p.N + n, n, p.N, y);
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int n = n0 + mt * 16 + 4 * g;
-        if (n >= p.N) continue;
-        float y[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+          y[j] = gt / (1.0f + expf(-gt)) * acc[mt + HALF][nt][j];
+        } else {
           y[j] = acc[mt][nt][j];
           if (p.residual && n + j < p.N) y[j] += p.residual[(size_t)m * p.N + n + j];
         }
-        store4(p.out, p.out_bf16, (size_t)m * p.N + n, n, p.N, y);
       }
+      store4(p.out, SWIGLU ? 1 : p.out_bf16, (size_t)m * p.N + n, n, p.N, y);
     }
   }
 }
@@ -430,9 +429,19 @@ __global__ __launch_bounds__(256) void draft_prepare_kernel(
     const float* f = src >= 0 ? feat + (size_t)src * d : root_feat;
     const bf16_t* e = embed + (size_t)sh_tok * d;
     bf16_t* o = x_in + (size_t)j * 2 * d;
-    for (int n = threadIdx.x; n < d; n += 256) {
-      o[n] = (bf16_t)f32_to_bf16_bits(f[n]);
-      o[d + n] = e[n];
+    if ((d & 7) == 0 && (((uintptr_t)f | (uintptr_t)e | (uintptr_t)o) & 15) == 0) {
+      for (int n = threadIdx.x * 8; n < d; n += 256 * 8) {
+        const f32x4 a = *(const f32x4*)(f + n);
+        const f32x4 b = *(const f32x4*)(f + n + 4);
+        *(u32x4*)(o + n) = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                 pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+        *(u32x4*)(o + d + n) = *(const u32x4*)(e + n);
+      }
+    } else {
+      for (int n = threadIdx.x; n < d; n += 256) {
+        o[n] = (bf16_t)f32_to_bf16_bits(f[n]);
+        o[d + n] = e[n];
+      }
     }
   }
 }
@@ -449,14 +458,25 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     tok = 0;
   }
   const bf16_t* e = embed + (size_t)tok * d;
-  for (int n = threadIdx.x; n < d; n += 256) out[(size_t)m * d + n] = bf16_bits_to_f32(e[n]);
+  float* o = out + (size_t)m * d;
+  if ((d & 7) == 0 && (((uintptr_t)e | (uintptr_t)o) & 15) == 0) {
+    for (int n = threadIdx.x * 8; n < d; n += 256 * 8) {
+      const u32x4 b = *(const u32x4*)(e + n);
+      *(f32x4*)(o + n) = f32x4{bf16_bits_to_f32(b[0] & 0xffffu), bf16_bits_to_f32(b[0] >> 16),
+                               bf16_bits_to_f32(b[1] & 0xffffu), bf16_bits_to_f32(b[1] >> 16)};
+      *(f32x4*)(o + n + 4) = f32x4{bf16_bits_to_f32(b[2] & 0xffffu), bf16_bits_to_f32(b[2] >> 16),
+                                   bf16_bits_to_f32(b[3] & 0xffffu), bf16_bits_to_f32(b[3] >> 16)};
+    }
+  } else {
+    for (int n = threadIdx.x; n < d; n += 256) o[n] = bf16_bits_to_f32(e[n]);
+  }
 }
 
 // k slices for a projection: enough workgroups to fill the chip (about two per
-// CU) while each slice keeps >= 2 k steps where possible and the fp32 partials
-// stay below a quarter of the weight bytes; the count divides K / 128.
+// CU) while the fp32 partials stay below a quarter of the weight bytes; the
+// count divides K / 128.
 static int lin_ksplit(int M, int K, int N, int swiglu) {
-  const int cols = swiglu ? kGluColsBlock : kLinRowsBlock;
+  const int cols = lin_cols_block(lin_mt((M + 15) / 16, swiglu), swiglu);
   const int nblk = (N + cols - 1) / cols;
   const int nk = K / kWsKG;
   const int want = (512 + nblk - 1) / nblk;
@@ -479,8 +499,9 @@ static size_t lin_workspace(int M, int K, int N, int swiglu) {
 
 template <int NT, int SWIGLU>
 static void launch_lin(const LinParams& p, hipStream_t s) {
-  const int cols = SWIGLU ? kGluColsBlock : kLinRowsBlock;
-  hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU>),
+  constexpr int MT = lin_mt(NT, SWIGLU);
+  const int cols = lin_cols_block(MT, SWIGLU);
+  hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU, MT>),
                      dim3((p.N + cols - 1) / cols, p.ksplit), dim3(256), 0, s, p);
 }
 

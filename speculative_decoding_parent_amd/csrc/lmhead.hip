@@ -35,7 +35,7 @@ constexpr int kLmWaves = 4;
 // tile, which keeps the most weight bytes in flight per wave; fewer as more
 // feature rows need accumulator registers (no spills up to T = 256).
 __host__ __device__ constexpr int lm_mt(int T) {
-  return T <= 16 ? 8 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
+  return T <= 16 ? 8 : (T <= 128 ? 2 : 1);
 }
 
 struct LmParams {
@@ -176,26 +176,30 @@ __device__ __forceinline__ void block_best256(float& v, int& i, float* rv, int* 
 // One workgroup per feature row: combine the per-wave statistics and top-k.
 //
 // Each wave's list is sorted by (logit desc, index asc).  Let theta be the
-// k-th best of the waves' first entries: those k entries are all at least
+// k-th best of the lists' first entries: those k entries are all at least
 // theta, so every member of the global top-k is too, and in each list only the
-// prefix not worse than theta can contribute.  Those survivors (few, unless
-// many logits tie) are gathered in LDS and the top-k is taken by k rounds of
-// "best candidate strictly after the previous pick".  If more survive than
-// LDS holds, the rounds run over all candidates instead (same result).
+// prefix not worse than theta can contribute.  The selections run inside
+// single waves (shuffle reductions, no workgroup barriers): each wave finds
+// the top k of the first entries it holds, theta is the k-th best of those
+// 4k candidates, survivors are gathered in LDS, and wave 0 picks the final k
+// by repeated "best candidate strictly after the previous pick".  If more
+// survive than LDS holds, wave 0 rescans every candidate instead (same result).
 constexpr int kMergeCap = 4096;
-constexpr int kMergePer = 12;     // wave lists per thread kept in registers
+constexpr int kMergePer = 12;     // lists per lane kept in registers (nw <= 3072)
 
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(
     const float2* __restrict__ part_stat, const float* __restrict__ part_val,
     const int32_t* __restrict__ part_idx, int nw, int T, int k, int32_t* __restrict__ topk_id,
     float* __restrict__ topk_logp, float* __restrict__ lse) {
   __shared__ float redf[4];
-  __shared__ float rv[4];
-  __shared__ int ri[4];
+  __shared__ float cv[4 * EAGLE_MAX_TOPK];
+  __shared__ int ci[4 * EAGLE_MAX_TOPK];
   __shared__ float sv[kMergeCap];
   __shared__ int si[kMergeCap];
   __shared__ int scount;
   const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   float M = -INFINITY;
   for (int w = threadIdx.x; w < nw; w += 256) M = fmaxf(M, part_stat[(size_t)w * T + t].x);
   M = block_reduce256(M, redf, [](float a, float b) { return fmaxf(a, b); });
@@ -206,26 +210,25 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
   }
   S = block_reduce256(S, redf, [](float a, float b) { return a + b; });
   const float L = M + logf(S);
+  if (threadIdx.x == 0) scount = 0;
 
-  // theta: the k-th best first entry over all wave lists (held in registers
-  // when each thread owns at most kMergePer lists)
-  float thv = -INFINITY;
-  int thi = INT_MAX;
-  if (nw >= k) {
-    float hv[kMergePer];
-    int hi[kMergePer];
-    const bool inreg = nw <= 256 * kMergePer;
+  // each wave: top k of the first entries of its lists (thread q-th list w =
+  // threadIdx.x + 256 q)
+  const bool inreg = nw <= 256 * kMergePer;
+  float hv[kMergePer];
+  int hi[kMergePer];
 #pragma unroll
-    for (int q = 0; q < kMergePer; ++q) {
-      const int w = threadIdx.x + 256 * q;
-      hv[q] = -INFINITY;
-      hi[q] = INT_MAX;
-      if (inreg && w < nw) {
-        const size_t o = ((size_t)w * T + t) * k;
-        hv[q] = part_val[o];
-        hi[q] = part_idx[o];
-      }
+  for (int q = 0; q < kMergePer; ++q) {
+    const int w = threadIdx.x + 256 * q;
+    hv[q] = -INFINITY;
+    hi[q] = INT_MAX;
+    if (inreg && w < nw) {
+      const size_t o = ((size_t)w * T + t) * k;
+      hv[q] = part_val[o];
+      hi[q] = part_idx[o];
     }
+  }
+  {
     float lastv = INFINITY;
     int lasti = -1;
     for (int r = 0; r < k; ++r) {
@@ -249,20 +252,54 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
           }
         }
       }
-      block_best256(bv, bi, rv, ri);
+      wave_best(bv, bi);
+      if (lane == 0) {
+        cv[wave * k + r] = bv;
+        ci[wave * k + r] = bi;
+      }
+      lastv = bv;
+      lasti = bi;
+    }
+  }
+  __syncthreads();
+  // theta = k-th best of the 4k wave candidates (every wave computes it)
+  float thv = -INFINITY;
+  int thi = INT_MAX;
+  if (nw >= k) {
+    const float myv = lane < 4 * k ? cv[lane] : -INFINITY;
+    const int myi = lane < 4 * k ? ci[lane] : INT_MAX;
+    const float myv2 = lane + 64 < 4 * k ? cv[lane + 64] : -INFINITY;
+    const int myi2 = lane + 64 < 4 * k ? ci[lane + 64] : INT_MAX;
+    const float myv3 = lane + 128 < 4 * k ? cv[lane + 128] : -INFINITY;
+    const int myi3 = lane + 128 < 4 * k ? ci[lane + 128] : INT_MAX;
+    const float myv4 = lane + 192 < 4 * k ? cv[lane + 192] : -INFINITY;
+    const int myi4 = lane + 192 < 4 * k ? ci[lane + 192] : INT_MAX;
+    float lastv = INFINITY;
+    int lasti = -1;
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int bi = INT_MAX;
+      if (better(lastv, lasti, myv, myi) && better(myv, myi, bv, bi)) { bv = myv; bi = myi; }
+      if (better(lastv, lasti, myv2, myi2) && better(myv2, myi2, bv, bi)) { bv = myv2; bi = myi2; }
+      if (better(lastv, lasti, myv3, myi3) && better(myv3, myi3, bv, bi)) { bv = myv3; bi = myi3; }
+      if (better(lastv, lasti, myv4, myi4) && better(myv4, myi4, bv, bi)) { bv = myv4; bi = myi4; }
+      wave_best(bv, bi);
       lastv = bv;
       lasti = bi;
     }
     thv = lastv;
     thi = lasti;
   }
-  if (threadIdx.x == 0) scount = 0;
-  __syncthreads();
-  for (int w = threadIdx.x; w < nw; w += 256) {
+  // survivors: the list prefixes not worse than theta (a list whose first
+  // entry, already in registers, is worse than theta is skipped unread)
+#pragma unroll
+  for (int q = 0; q < kMergePer; ++q) {
+    const int w = threadIdx.x + 256 * q;
+    if (!inreg || w >= nw || better(thv, thi, hv[q], hi[q])) continue;
     const size_t o = ((size_t)w * T + t) * k;
     for (int j = 0; j < k; ++j) {
-      const float v = part_val[o + j];
-      const int i = part_idx[o + j];
+      const float v = j == 0 ? hv[q] : part_val[o + j];
+      const int i = j == 0 ? hi[q] : part_idx[o + j];
       if (better(thv, thi, v, i)) break;      // worse than theta: the rest of the list too
       const int slot = atomicAdd(&scount, 1);
       if (slot < kMergeCap) {
@@ -271,7 +308,23 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
       }
     }
   }
+  if (!inreg) {
+    for (int w = threadIdx.x; w < nw; w += 256) {
+      const size_t o = ((size_t)w * T + t) * k;
+      for (int j = 0; j < k; ++j) {
+        const float v = part_val[o + j];
+        const int i = part_idx[o + j];
+        if (better(thv, thi, v, i)) break;
+        const int slot = atomicAdd(&scount, 1);
+        if (slot < kMergeCap) {
+          sv[slot] = v;
+          si[slot] = i;
+        }
+      }
+    }
+  }
   __syncthreads();
+  if (wave != 0) return;
   const int ns = scount;
   const bool fits = ns <= kMergeCap;
   float lastv = INFINITY;
@@ -280,7 +333,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
     float bv = -INFINITY;
     int bi = INT_MAX;
     if (fits) {
-      for (int c = threadIdx.x; c < ns; c += 256) {
+      for (int c = lane; c < ns; c += 64) {
         const float v = sv[c];
         const int i = si[c];
         if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
@@ -290,7 +343,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
       }
     } else {
       const int n = nw * k;
-      for (int c = threadIdx.x; c < n; c += 256) {
+      for (int c = lane; c < n; c += 64) {
         const int w = c / k;
         const size_t o = ((size_t)w * T + t) * k + (c - w * k);
         const float v = part_val[o];
@@ -301,15 +354,15 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
         }
       }
     }
-    block_best256(bv, bi, rv, ri);
-    if (threadIdx.x == 0) {
+    wave_best(bv, bi);
+    if (lane == 0) {
       topk_id[(size_t)t * k + r] = bi;
       topk_logp[(size_t)t * k + r] = bv - L;
     }
     lastv = bv;
     lasti = bi;
   }
-  if (threadIdx.x == 0) lse[t] = L;
+  if (lane == 0) lse[t] = L;
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -432,11 +485,11 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
                (float2*)(ws + l.stat_off), (float*)(ws + l.val_off), (int32_t*)(ws + l.idx_off)};
     const int nt = (T + 15) / 16;
-    static_assert(lm_mt(16) == 8 && lm_mt(64) == 4 && lm_mt(128) == 2 && lm_mt(129) == 1,
+    static_assert(lm_mt(16) == 8 && lm_mt(64) == 2 && lm_mt(128) == 2 && lm_mt(129) == 1,
                   "tile choice");
     if (nt <= 1) launch_lm<1, 8>(p, stream);
-    else if (nt <= 2) launch_lm<2, 4>(p, stream);
-    else if (nt <= 4) launch_lm<4, 4>(p, stream);
+    else if (nt <= 2) launch_lm<2, 2>(p, stream);
+    else if (nt <= 4) launch_lm<4, 2>(p, stream);
     else if (nt <= 8) launch_lm<8, 2>(p, stream);
     else launch_lm<16, 1>(p, stream);
     EAGLE_LAUNCH_CHECK();

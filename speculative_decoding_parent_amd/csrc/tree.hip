@@ -62,11 +62,12 @@ __global__ __launch_bounds__(1024) void rerank_kernel(
     int32_t* __restrict__ node_token, int32_t* __restrict__ node_parent,
     int32_t* __restrict__ node_depth, int32_t* __restrict__ node_pool_idx,
     int32_t* __restrict__ status) {
-  __shared__ float vs[EAGLE_MAX_POOL];
+  __shared__ __attribute__((aligned(16))) float vs[EAGLE_MAX_POOL];
   __shared__ int16_t pos[EAGLE_MAX_POOL];
   __shared__ int32_t cnt[1024];
   const int tid = threadIdx.x;
-  for (int i = tid; i < pool_n; i += blockDim.x) vs[i] = val[i];
+  const int n4 = (pool_n + 3) / 4;
+  for (int i = tid; i < n4 * 4; i += blockDim.x) vs[i] = i < pool_n ? val[i] : -INFINITY;
   __syncthreads();
   // keep flag per entry: the root always, others when fewer than T-1 non-root
   // entries beat them
@@ -79,9 +80,16 @@ __global__ __launch_bounds__(1024) void rerank_kernel(
     if (i == 0) {
       keep = true;
     } else {
+      // rank among non-root entries: count over all entries (four per LDS
+      // read), minus the root's vote; entries past pool_n hold -inf and an
+      // index above every real one, so they never count
       const float v = vs[i];
-      int rank = 0;
-      for (int o = 1; o < pool_n && rank < T - 1; ++o) rank += better(vs[o], o, v, i) ? 1 : 0;
+      int rank = better(vs[0], 0, v, i) ? -1 : 0;
+      for (int o4 = 0; o4 < n4 && rank < T - 1; ++o4) {
+        const f32x4 q = *(const f32x4*)(&vs[4 * o4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rank += better(q[j], 4 * o4 + j, v, i) ? 1 : 0;
+      }
       keep = rank < T - 1;
     }
     pos[i] = keep ? 1 : 0;

@@ -32,7 +32,7 @@ def test_version_and_strings(lib):
 
 def test_workspace_queries(lib):
     # LM head: per-wave partial statistics + per-wave top-k lists
-    nw = ((128256 + 255) // 256) * 4          # T = 64: 64 rows per wave
+    nw = ((128256 + 127) // 128) * 4          # T = 64: 32 rows per wave
     want = 0
     for n in (nw * 64 * 8, nw * 64 * 10 * 4, nw * 64 * 10 * 4):
         want += (n + 255) // 256 * 256
