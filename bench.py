@@ -63,6 +63,64 @@ def time_lmhead(cyc, T, iters):
     return float(np.mean(ms)) / 1e3, float(np.min(ms)) / 1e3
 
 
+def attn_bytes(Tq, hq, hkv, hd, L, Tk):
+    """Algorithmic bytes of one tree-attention call: the prefix K/V, the tree
+    K/V, q in and out (bf16), and the mask rows."""
+    return 2 * hkv * L * hd * 2 + 2 * hkv * Tk * hd * 2 + Tq * hq * hd * 4 + Tq * 8
+
+
+def long_context_verify(dev, steps):
+    """Tree mask + tree attention over 32 distinct layers' KV caches (Llama-3-8B
+    attention shape, L = 32768, T = 64), layer after layer; HIP events around
+    every attention call on its launch stream."""
+    w = inputs.LONG_CONTEXT
+    vi = inputs.verify_inputs(w, L=0, with_lmhead=False)   # tree, q and tree K/V
+    kc = [inputs.device_normal((w.hkv, w.L, w.hd), 4000 + 2 * l, dev) for l in range(w.layers)]
+    vc = [inputs.device_normal((w.hkv, w.L, w.hd), 4001 + 2 * l, dev) for l in range(w.layers)]
+    par = torch.from_numpy(vi.parents).to(dev)
+    q, kt, vt = vi.q.to(dev), vi.k_tree.to(dev), vi.v_tree.to(dev)
+    out = torch.empty_like(q)
+    lib = _lib.lib()
+    ws = torch.empty(lib.eagle_tree_attn_workspace(w.T, w.hq, w.hkv, w.hd, w.L, w.T, 1),
+                     dtype=torch.uint8, device=dev)
+    mask = torch.empty((w.T, 1), dtype=torch.int64, device=dev)
+    depth = torch.empty(w.T, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one_pass(evs=None):
+        _lib.eagle_build_tree_mask(par, mask=mask, depth=depth)
+        for l in range(w.layers):
+            if evs is not None:
+                evs[l][0].record(stream)
+            _lib.eagle_tree_attn(q, kc[l], vc[l], w.L, kt, vt, w.T, mask, out=out, workspace=ws)
+            if evs is not None:
+                evs[l][1].record(stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_pass()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.layers)]
+    one_pass(evs)
+    torch.cuda.synchronize()
+    per = float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+    nb = attn_bytes(w.T, w.hq, w.hkv, w.hd, w.L, w.T)
+    achieved = nb / per / 1e9
+    del kc, vc
+    return {"workload": "llama3-8b-long-verify: tree mask + 32 layers of tree attention, 32 Q / 8 "
+                        "KV heads, hd 128, bf16 KV prefix L=32768 per layer, T=64 depth <= 7",
+            "value": round(w.T / dt, 1), "unit": "nodes/s", "ms_per_step": round(dt * 1e3, 4),
+            "roofline": {"kernel": "eagle_tree_attn (tree_attn_bf16_kernel + attn_merge_kernel), "
+                                   "one layer", "bound": "hbm", "achieved": round(achieved, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "avg_us": round(per * 1e6, 2), "bytes_per_launch": nb}}
+
+
 def cpu_baseline(w, ci):
     """The oracle's full cycle on the host cores (one cycle: 6 draft rounds,
     rerank, verify layer, LM head, acceptance)."""
@@ -99,6 +157,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lm-iters", type=int, default=30)
+    ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="copy 512 MiB device to device first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -106,6 +167,14 @@ def main():
         sys.exit(2)
     w = inputs.LLAMA3_8B_CYCLE
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        src = torch.zeros(256 << 20, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy probe: 536870912 bytes read, 536870912 bytes written",
+              file=sys.stderr, flush=True)
+        del src, dst
     print(f"[bench] drawing inputs for {w.name}", file=sys.stderr, flush=True)
     ci = inputs.cycle_inputs(w)
     cyc = DraftVerifyCycle(w, ci, dev, temperature=w.temperature)
@@ -150,6 +219,11 @@ def main():
                      "avg_us": round(avg_s * 1e6, 2), "min_us": round(min_s * 1e6, 2),
                      "bytes_per_launch": nbytes},
     }
+    if not args.no_long_context:
+        del cyc
+        torch.cuda.empty_cache()
+        print("[bench] long-context verify (32 layers, L=32768)", file=sys.stderr, flush=True)
+        line["long_context_verify"] = long_context_verify(dev, max(1, min(args.steps, 10)))
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one cycle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, ci)

@@ -337,3 +337,13 @@ def cycle_inputs(w: Workload) -> dict:
 SMALL_CYCLE = Workload(cfg=13, name="small-cycle", d=256, hq=4, hkv=2, hd=64, vocab=1024, L=64,
                        T=16, max_depth=4, max_branch=4, topk=4, dtype="bf16", sampling=True,
                        greedy=False, ffn=512, rounds=4, k_select=4)
+
+
+def device_normal(shape, seed: int, device, dtype=torch.bfloat16) -> torch.Tensor:
+    """N(0, 1) drawn on the GPU with torch's seeded Philox generator, rounded
+    once to ``dtype``.  Used where the host draw would dominate the run time
+    (gigabytes of KV cache for throughput measurement); parity cases use the
+    host generators above."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, device=device, generator=g, dtype=torch.float32).to(dtype)
