@@ -170,7 +170,7 @@ def main():
     if args.copy_probe:
         src = torch.zeros(256 << 20, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.neg(src, out=dst)      # one elementwise kernel: reads src once, writes dst once
         torch.cuda.synchronize()
         print("[bench] copy probe: 536870912 bytes read, 536870912 bytes written",
               file=sys.stderr, flush=True)

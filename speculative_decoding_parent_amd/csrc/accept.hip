@@ -63,8 +63,7 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(
   if (tid < 64) {
     int best = -1;
     for (int i = tid; i < T; i += 64) best = max(best, key[i]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) best = max(best, __shfl_xor(best, o));
+    best = wave_max_i(best);
     if (tid == 0) {
       const int end = best < 0 ? 0 : 255 - (best & 255);
       const int depth = best < 0 ? 0 : (best >> 8);
@@ -118,8 +117,7 @@ __global__ __launch_bounds__(256) void accept_row_stats_kernel(
 // lets the same `red` be reused by back-to-back calls.
 template <typename V, typename Op>
 __device__ __forceinline__ V block_reduce(V v, V* red, Op op) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
+  v = wave_reduce(v, op);
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[w] = v;

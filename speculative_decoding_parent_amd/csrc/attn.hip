@@ -240,8 +240,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mt][nt][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = rows_max(mx);
         const float mnew = fmaxf(m[nt], mx);
         const float alpha = __builtin_amdgcn_exp2f((m[nt] - mnew) * p.c);
         m[nt] = mnew;
@@ -295,8 +294,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     float lt = l[nt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = rows_sum(lt);
     if (!valid[nt]) continue;
     const size_t prow = (size_t)split * RT + grow[nt];
     if (g == 0) p.part_ml[prow] = make_float2(m[nt], lt);

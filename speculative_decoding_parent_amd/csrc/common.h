@@ -53,35 +53,232 @@ __device__ __forceinline__ void set_status(int32_t* st, int32_t bit) {
 // Strict ranking order used by every selection: larger value first, then the
 // lower index.  (+0.0 and -0.0 compare equal and fall through to the index.)
 __device__ __forceinline__ bool better(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+  // bitwise, not short-circuit: compiles to compares and selects, no branches
+  return (av > bv) | ((av == bv) & (ai < bi));
+}
+
+// ---- selection keys.  The same order as `better` as one unsigned 64-bit
+// number: the high word maps the value's bits monotonically (-0.0 folded into
+// +0.0, NaN below every number), the low word is the inverted index, so the
+// larger key wins and equal values fall to the lower index.  Key 0 is below
+// every real (value, index) pair and serves as "none".
+typedef unsigned long long selkey_t;
+
+__device__ __forceinline__ uint32_t ord_f32(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = (u == 0x80000000u) ? 0u : u;
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (v != v) ? 0u : o;
+}
+__device__ __forceinline__ selkey_t sel_key(float v, int i) {
+  return ((selkey_t)ord_f32(v) << 32) | (uint32_t)(~(uint32_t)i);
+}
+__device__ __forceinline__ float key_value(selkey_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_index(selkey_t k) { return (int)~(uint32_t)k; }
+
+// ---- cross-lane reductions without the LDS crossbar.
+//
+// Within a row of 16 lanes the butterfly runs on DPP moves (quad swaps, then
+// the half-row and row mirrors); across rows it runs on gfx950's permlane16 /
+// permlane32 swaps, which hand both lanes of a pair the two operands in the
+// same order.  Every operator used here is commutative, so all 64 lanes end
+// with bit-identical results.  All lanes of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(dpp_move<CTRL>(__float_as_int(x)));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppRowMirror = 0x140;   // lane i <-> 15 - i within 16
+
+// (value of the even row, value of the odd row) of the lane's row pair
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(int x, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+// (value of lane l % 32, value of lane 32 + l % 32)
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(int x, int& a, int& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  a = (int)r[0];
+  b = (int)r[1];
+}
+
+// Combine lanes l, l ^ 16 and l ^ 32 (the four 16-lane rows).
+__device__ __forceinline__ float rows_max(float v) {
+  float a, b;
+  swap16(v, a, b);
+  v = fmaxf(a, b);
+  swap32(v, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  float a, b;
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_move<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_move<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_move<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_move<kDppRowMirror>(v));
+  return rows_max(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_move<kDppQuadXor1>(v);
+  v += dpp_move<kDppQuadXor2>(v);
+  v += dpp_move<kDppHalfMirror>(v);
+  v += dpp_move<kDppRowMirror>(v);
+  return rows_sum(v);
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_move<kDppQuadXor1>(v));
+  v = max(v, dpp_move<kDppQuadXor2>(v));
+  v = max(v, dpp_move<kDppHalfMirror>(v));
+  v = max(v, dpp_move<kDppRowMirror>(v));
+  int a, b;
+  swap16(v, a, b);
+  v = max(a, b);
+  swap32(v, a, b);
+  return max(a, b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const int lo = dpp_move<CTRL>((int)(uint32_t)u);
+  const int hi = dpp_move<CTRL>((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ void swap16(double x, double& a, double& b) {
+  const uint64_t u = __double_as_longlong(x);
+  int alo, blo, ahi, bhi;
+  swap16((int)(uint32_t)u, alo, blo);
+  swap16((int)(uint32_t)(u >> 32), ahi, bhi);
+  a = __longlong_as_double((long long)(((uint64_t)(uint32_t)ahi << 32) | (uint32_t)alo));
+  b = __longlong_as_double((long long)(((uint64_t)(uint32_t)bhi << 32) | (uint32_t)blo));
+}
+__device__ __forceinline__ void swap32(double x, double& a, double& b) {
+  const uint64_t u = __double_as_longlong(x);
+  int alo, blo, ahi, bhi;
+  swap32((int)(uint32_t)u, alo, blo);
+  swap32((int)(uint32_t)(u >> 32), ahi, bhi);
+  a = __longlong_as_double((long long)(((uint64_t)(uint32_t)ahi << 32) | (uint32_t)alo));
+  b = __longlong_as_double((long long)(((uint64_t)(uint32_t)bhi << 32) | (uint32_t)blo));
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_move<kDppQuadXor1>(v);
+  v += dpp_move<kDppQuadXor2>(v);
+  v += dpp_move<kDppHalfMirror>(v);
+  v += dpp_move<kDppRowMirror>(v);
+  double a, b;
+  swap16(v, a, b);
+  v = a + b;
+  swap32(v, a, b);
+  return a + b;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+  const float ov = dpp_move<CTRL>(v);
+  const int oi = dpp_move<CTRL>(i);
+  if (better(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Best (value, index) pair of lanes l, l ^ 16 and l ^ 32.
+__device__ __forceinline__ void rows_best(float& v, int& i) {
+  float a, b;
+  int ia, ib;
+  swap16(v, a, b);
+  swap16(i, ia, ib);
+  if (better(b, ib, a, ia)) { a = b; ia = ib; }
+  swap32(a, v, b);
+  swap32(ia, i, ib);
+  if (better(b, ib, v, i)) { v = b; i = ib; }
+}
+
+template <int CTRL>
+__device__ __forceinline__ selkey_t dpp_move(selkey_t x) {
+  const int lo = dpp_move<CTRL>((int)(uint32_t)x);
+  const int hi = dpp_move<CTRL>((int)(uint32_t)(x >> 32));
+  return ((selkey_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ void swap16(selkey_t x, selkey_t& a, selkey_t& b) {
+  int alo, blo, ahi, bhi;
+  swap16((int)(uint32_t)x, alo, blo);
+  swap16((int)(uint32_t)(x >> 32), ahi, bhi);
+  a = ((selkey_t)(uint32_t)ahi << 32) | (uint32_t)alo;
+  b = ((selkey_t)(uint32_t)bhi << 32) | (uint32_t)blo;
+}
+__device__ __forceinline__ void swap32(selkey_t x, selkey_t& a, selkey_t& b) {
+  int alo, blo, ahi, bhi;
+  swap32((int)(uint32_t)x, alo, blo);
+  swap32((int)(uint32_t)(x >> 32), ahi, bhi);
+  a = ((selkey_t)(uint32_t)ahi << 32) | (uint32_t)alo;
+  b = ((selkey_t)(uint32_t)bhi << 32) | (uint32_t)blo;
+}
+__device__ __forceinline__ selkey_t kmax(selkey_t a, selkey_t b) { return a > b ? a : b; }
+
+// Largest key of lanes l, l ^ 16 and l ^ 32.
+__device__ __forceinline__ selkey_t rows_max_key(selkey_t v) {
+  selkey_t a, b;
+  swap16(v, a, b);
+  swap32(kmax(a, b), a, b);
+  return kmax(a, b);
+}
+
+// Generic butterfly for a commutative operator on float, int, double or selkey_t.
+template <typename V, typename Op>
+__device__ __forceinline__ V wave_reduce(V v, Op op) {
+  v = op(v, dpp_move<kDppQuadXor1>(v));
+  v = op(v, dpp_move<kDppQuadXor2>(v));
+  v = op(v, dpp_move<kDppHalfMirror>(v));
+  v = op(v, dpp_move<kDppRowMirror>(v));
+  V a, b;
+  swap16(v, a, b);
+  v = op(a, b);
+  swap32(v, a, b);
+  return op(a, b);
+}
+
+__device__ __forceinline__ selkey_t wave_max_key(selkey_t v) {
+  return wave_reduce(v, [](selkey_t a, selkey_t b) { return kmax(a, b); });
 }
 
 // Best (value, index) pair across the wave under `better`.
 __device__ __forceinline__ void wave_best(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o);
-    int oi = __shfl_xor(i, o);
-    if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  }
+  best_step<kDppQuadXor1>(v, i);
+  best_step<kDppQuadXor2>(v, i);
+  best_step<kDppHalfMirror>(v, i);
+  best_step<kDppRowMirror>(v, i);
+  rows_best(v, i);
 }
 
 }  // namespace eagle

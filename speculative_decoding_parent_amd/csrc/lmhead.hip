@@ -30,6 +30,12 @@
 namespace eagle {
 
 constexpr int kLmWaves = 4;
+// Largest k whose four per-wave lists fit the X staging buffer for the
+// workgroup-level merge: 4 waves x 16 NT rows x (k + 1) x 8 bytes against
+// 2 x 16 NT x 136 x 2 bytes.
+constexpr int kLmBlockK = 16;
+static_assert(2 * 16 * kWsLds * 2 >= 4 * 16 * (kLmBlockK + 1) * 8, "lists exceed staging LDS");
+static_assert(sizeof(selkey_t) == 8, "key size");
 
 // W tiles of 16 rows per wave: 8 (128 rows) while the feature rows fit one MFMA
 // tile, which keeps the most weight bytes in flight per wave; fewer as more
@@ -43,9 +49,8 @@ struct LmParams {
   const bf16_t* W;
   int T, d, V, k;
   float* logits;
-  float2* part_stat;   // [nwave][T]
-  float* part_val;     // [nwave][T][k]
-  int32_t* part_idx;   // [nwave][T][k]
+  float2* part_stat;   // [T][nb] (max, sum exp(l - max))
+  selkey_t* part_key;  // [T][nb][k] sorted selection keys
 };
 
 template <int NT, int kLmMT>
@@ -94,6 +99,17 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
       }
     }
   }
+  // Per wave and feature row: (max, sum exp(l - max)) and the top-k as
+  // selection keys, by k rounds of "largest key below the previous pick".
+  // With k <= kLmBlockK the four waves' sorted lists go to LDS (the X staging
+  // buffer, free after the main loop) and are merged into one list per
+  // workgroup; otherwise every wave writes its own.
+  const bool block_lists = p.k <= kLmBlockK;
+  constexpr int TP = 16 * NT;
+  selkey_t* lk = (selkey_t*)fs;                 // [4][TP][k]
+  float2* ls = (float2*)(lk + 4 * TP * p.k);    // [4][TP]
+  const int nb = block_lists ? gridDim.x : gridDim.x * kLmWaves;
+  const int list = block_lists ? blockIdx.x : wglob;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int t = nt * 16 + r16;
@@ -103,264 +119,230 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (v0 + mt * 16 + 4 * g + j < V) m = fmaxf(m, acc[mt][nt][j]);
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    m = rows_max(m);
     float s = 0.f;
 #pragma unroll
     for (int mt = 0; mt < kLmMT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (v0 + mt * 16 + 4 * g + j < V) s += expf(acc[mt][nt][j] - m);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    if (g == 0 && t < T) p.part_stat[(size_t)wglob * T + t] = make_float2(m, s);
+    s = rows_sum(s);
+    if (g == 0) {
+      if (block_lists) ls[wave * TP + t] = make_float2(m, s);
+      else if (t < T) p.part_stat[(size_t)t * nb + list] = make_float2(m, s);
+    }
 
-    // wave top-k of this feature row: k rounds of "best not yet taken"
-    uint32_t taken = 0;
+    selkey_t last = ~0ull;
     for (int r = 0; r < p.k; ++r) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
+      selkey_t best = 0;
 #pragma unroll
       for (int mt = 0; mt < kLmMT; ++mt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int v = v0 + mt * 16 + 4 * g + j;
-          const float x = acc[mt][nt][j];
-          if (v < V && !((taken >> (mt * 4 + j)) & 1u) && better(x, v, bv, bi)) {
-            bv = x;
-            bi = v;
-          }
+          const selkey_t key = v < V ? sel_key(acc[mt][nt][j], v) : 0ull;
+          best = ((key < last) & (key > best)) ? key : best;
         }
-      float ov = __shfl_xor(bv, 16);
-      int oi = __shfl_xor(bi, 16);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      ov = __shfl_xor(bv, 32);
-      oi = __shfl_xor(bi, 32);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      const int rel = bi - (v0 + 4 * g);
-      if (bi != INT_MAX && rel >= 0 && (rel & 15) < 4 && (rel >> 4) < kLmMT)
-        taken |= 1u << ((rel >> 4) * 4 + (rel & 3));
-      if (g == 0 && t < T) {
-        const size_t o = ((size_t)wglob * T + t) * p.k + r;
-        p.part_val[o] = bv;
-        p.part_idx[o] = bi;
+      best = rows_max_key(best);
+      if (g == 0) {
+        if (block_lists) lk[(wave * TP + t) * p.k + r] = best;
+        else if (t < T) p.part_key[((size_t)t * nb + list) * p.k + r] = best;
       }
+      last = best;
+    }
+  }
+  if (!block_lists) return;
+  __syncthreads();
+  // Workgroup merge: lane (g, r16) of the wave that owns tile nt follows wave
+  // g's sorted list of row 16 nt + r16; each round the largest of the four
+  // heads (lanes r16, r16 + 16, r16 + 32, r16 + 48) wins and its owner
+  // advances (keys of distinct vocabulary rows never tie).
+  for (int nt = wave; nt < NT; nt += kLmWaves) {
+    const int t = nt * 16 + r16;
+    const float2 st = ls[g * TP + t];
+    const float M = rows_max(st.x);
+    const float S = rows_sum(st.y > 0.f ? st.y * expf(st.x - M) : 0.f);
+    if (g == 0 && t < T) p.part_stat[(size_t)t * nb + list] = make_float2(M, S);
+    const selkey_t* my = lk + (g * TP + t) * p.k;
+    int ptr = 0;
+    selkey_t h = my[0];
+    for (int r = 0; r < p.k; ++r) {
+      const selkey_t b = rows_max_key(h);
+      const bool adv = (h == b) & (b != 0ull);
+      ptr += adv ? 1 : 0;
+      const selkey_t nxt = my[min(ptr, p.k - 1)];
+      h = adv ? (ptr < p.k ? nxt : 0ull) : h;
+      if (g == 0 && t < T) p.part_key[((size_t)t * nb + list) * p.k + r] = b;
     }
   }
 }
 
 template <typename V, typename Op>
 __device__ __forceinline__ V block_reduce256(V v, V* red, Op op) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
+  v = wave_reduce(v, op);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return op(op(red[0], red[1]), op(red[2], red[3]));
 }
 
-__device__ __forceinline__ void block_best256(float& v, int& i, float* rv, int* ri) {
-  wave_best(v, i);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    rv[threadIdx.x >> 6] = v;
-    ri[threadIdx.x >> 6] = i;
-  }
-  __syncthreads();
-  v = rv[0];
-  i = ri[0];
-  for (int w = 1; w < 4; ++w)
-    if (better(rv[w], ri[w], v, i)) { v = rv[w]; i = ri[w]; }
+// One workgroup per feature row: combine the nb partial statistics and top-k
+// lists of the row (stored contiguously: stat[t][nb], key[t][nb][k], each
+// list sorted by descending selection key).
+//
+// lse: the (max, sum) pairs are folded with the usual rescaling, in a fixed
+// assignment and reduction order.  Top-k: let theta be the k-th largest of
+// the lists' first keys.  Those k keys are all at least theta, so every member
+// of the row's top k is too, and only lists whose first key is not below
+// theta can contribute: at most k of them (keys never tie).  theta comes from
+// per-wave selections over first keys held in registers; the surviving lists
+// are copied into LDS and wave 0 merges them, one list per lane, in k rounds.
+constexpr int kMergeHeads = 16;   // first keys per thread held in registers
+
+// (m, s) <- the pair for the union of both sets; a pair with s = 0 is empty.
+// Select-based (no branches) and commutative: both orders give the same bits.
+__device__ __forceinline__ void fold_stat(float& m, float& s, float m2, float s2) {
+  const bool h1 = s > 0.f, h2 = s2 > 0.f;
+  const float M = h1 ? (h2 ? fmaxf(m, m2) : m) : m2;
+  const float a = h1 ? s * expf(m - M) : 0.f;
+  const float b = h2 ? s2 * expf(m2 - M) : 0.f;
+  m = (h1 | h2) ? M : m;
+  s = a + b;
 }
 
-// One workgroup per feature row: combine the per-wave statistics and top-k.
-//
-// Each wave's list is sorted by (logit desc, index asc).  Let theta be the
-// k-th best of the lists' first entries: those k entries are all at least
-// theta, so every member of the global top-k is too, and in each list only the
-// prefix not worse than theta can contribute.  The selections run inside
-// single waves (shuffle reductions, no workgroup barriers): each wave finds
-// the top k of the first entries it holds, theta is the k-th best of those
-// 4k candidates, survivors are gathered in LDS, and wave 0 picks the final k
-// by repeated "best candidate strictly after the previous pick".  If more
-// survive than LDS holds, wave 0 rescans every candidate instead (same result).
-constexpr int kMergeCap = 4096;
-constexpr int kMergePer = 12;     // lists per lane kept in registers (nw <= 3072)
+template <int CTRL>
+__device__ __forceinline__ void fold_step(float& m, float& s) {
+  const float m2 = dpp_move<CTRL>(m), s2 = dpp_move<CTRL>(s);
+  fold_stat(m, s, m2, s2);
+}
+
+// fold_stat is commutative, so the butterfly leaves every lane the same pair.
+__device__ __forceinline__ void fold_stat_wave(float& m, float& s) {
+  fold_step<kDppQuadXor1>(m, s);
+  fold_step<kDppQuadXor2>(m, s);
+  fold_step<kDppHalfMirror>(m, s);
+  fold_step<kDppRowMirror>(m, s);
+  float ma, mb, sa, sb;
+  swap16(m, ma, mb);
+  swap16(s, sa, sb);
+  fold_stat(ma, sa, mb, sb);
+  swap32(ma, m, mb);
+  swap32(sa, s, sb);
+  fold_stat(m, s, mb, sb);
+}
 
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(
-    const float2* __restrict__ part_stat, const float* __restrict__ part_val,
-    const int32_t* __restrict__ part_idx, int nw, int T, int k, int32_t* __restrict__ topk_id,
-    float* __restrict__ topk_logp, float* __restrict__ lse) {
-  __shared__ float redf[4];
-  __shared__ float cv[4 * EAGLE_MAX_TOPK];
-  __shared__ int ci[4 * EAGLE_MAX_TOPK];
-  __shared__ float sv[kMergeCap];
-  __shared__ int si[kMergeCap];
-  __shared__ int scount;
+    const float2* __restrict__ part_stat, const selkey_t* __restrict__ part_key, int nb, int T,
+    int k, int32_t* __restrict__ topk_id, float* __restrict__ topk_logp,
+    float* __restrict__ lse) {
+  __shared__ float2 red[4];
+  __shared__ selkey_t ck[4 * EAGLE_MAX_TOPK];
+  __shared__ int slist[EAGLE_MAX_TOPK];
+  __shared__ int nsl;
+  __shared__ selkey_t sk[EAGLE_MAX_TOPK * EAGLE_MAX_TOPK];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  float M = -INFINITY;
-  for (int w = threadIdx.x; w < nw; w += 256) M = fmaxf(M, part_stat[(size_t)w * T + t].x);
-  M = block_reduce256(M, redf, [](float a, float b) { return fmaxf(a, b); });
-  float S = 0.f;
-  for (int w = threadIdx.x; w < nw; w += 256) {
-    const float2 st = part_stat[(size_t)w * T + t];
-    if (st.y > 0.f) S += st.y * expf(st.x - M);
-  }
-  S = block_reduce256(S, redf, [](float a, float b) { return a + b; });
-  const float L = M + logf(S);
-  if (threadIdx.x == 0) scount = 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const float2* st = part_stat + (size_t)t * nb;
+  const selkey_t* pk = part_key + (size_t)t * nb * k;
+  if (tid == 0) nsl = 0;
 
-  // each wave: top k of the first entries of its lists (thread q-th list w =
-  // threadIdx.x + 256 q)
-  const bool inreg = nw <= 256 * kMergePer;
-  float hv[kMergePer];
-  int hi[kMergePer];
+  // first keys (issued before the statistics pass so the loads overlap)
+  const bool inreg = nb <= 256 * kMergeHeads;
+  selkey_t hk[kMergeHeads];
 #pragma unroll
-  for (int q = 0; q < kMergePer; ++q) {
-    const int w = threadIdx.x + 256 * q;
-    hv[q] = -INFINITY;
-    hi[q] = INT_MAX;
-    if (inreg && w < nw) {
-      const size_t o = ((size_t)w * T + t) * k;
-      hv[q] = part_val[o];
-      hi[q] = part_idx[o];
-    }
+  for (int q = 0; q < kMergeHeads; ++q) {
+    const int w = tid + 256 * q;
+    hk[q] = (inreg && w < nb) ? pk[(size_t)w * k] : 0ull;
   }
+
+  float m = -INFINITY, s = 0.f;
+  for (int w = tid; w < nb; w += 256) {
+    const float2 x = st[w];
+    fold_stat(m, s, x.x, x.y);
+  }
+  fold_stat_wave(m, s);
+  if (lane == 0) red[wave] = make_float2(m, s);
+
+  // per wave: the k largest first keys it holds
   {
-    float lastv = INFINITY;
-    int lasti = -1;
+    selkey_t last = ~0ull;
     for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
+      selkey_t b = 0;
       if (inreg) {
 #pragma unroll
-        for (int q = 0; q < kMergePer; ++q)
-          if (better(lastv, lasti, hv[q], hi[q]) && better(hv[q], hi[q], bv, bi)) {
-            bv = hv[q];
-            bi = hi[q];
-          }
+        for (int q = 0; q < kMergeHeads; ++q) b = ((hk[q] < last) & (hk[q] > b)) ? hk[q] : b;
       } else {
-        for (int w = threadIdx.x; w < nw; w += 256) {
-          const size_t o = ((size_t)w * T + t) * k;
-          const float v = part_val[o];
-          const int i = part_idx[o];
-          if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
-            bv = v;
-            bi = i;
-          }
+        for (int w = tid; w < nb; w += 256) {
+          const selkey_t x = pk[(size_t)w * k];
+          b = ((x < last) & (x > b)) ? x : b;
         }
       }
-      wave_best(bv, bi);
-      if (lane == 0) {
-        cv[wave * k + r] = bv;
-        ci[wave * k + r] = bi;
-      }
-      lastv = bv;
-      lasti = bi;
+      b = wave_max_key(b);
+      if (lane == 0) ck[wave * k + r] = b;
+      last = b;
     }
   }
   __syncthreads();
-  // theta = k-th best of the 4k wave candidates (every wave computes it)
-  float thv = -INFINITY;
-  int thi = INT_MAX;
-  if (nw >= k) {
-    const float myv = lane < 4 * k ? cv[lane] : -INFINITY;
-    const int myi = lane < 4 * k ? ci[lane] : INT_MAX;
-    const float myv2 = lane + 64 < 4 * k ? cv[lane + 64] : -INFINITY;
-    const int myi2 = lane + 64 < 4 * k ? ci[lane + 64] : INT_MAX;
-    const float myv3 = lane + 128 < 4 * k ? cv[lane + 128] : -INFINITY;
-    const int myi3 = lane + 128 < 4 * k ? ci[lane + 128] : INT_MAX;
-    const float myv4 = lane + 192 < 4 * k ? cv[lane + 192] : -INFINITY;
-    const int myi4 = lane + 192 < 4 * k ? ci[lane + 192] : INT_MAX;
-    float lastv = INFINITY;
-    int lasti = -1;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-      if (better(lastv, lasti, myv, myi) && better(myv, myi, bv, bi)) { bv = myv; bi = myi; }
-      if (better(lastv, lasti, myv2, myi2) && better(myv2, myi2, bv, bi)) { bv = myv2; bi = myi2; }
-      if (better(lastv, lasti, myv3, myi3) && better(myv3, myi3, bv, bi)) { bv = myv3; bi = myi3; }
-      if (better(lastv, lasti, myv4, myi4) && better(myv4, myi4, bv, bi)) { bv = myv4; bi = myi4; }
-      wave_best(bv, bi);
-      lastv = bv;
-      lasti = bi;
-    }
-    thv = lastv;
-    thi = lasti;
-  }
-  // survivors: the list prefixes not worse than theta (a list whose first
-  // entry, already in registers, is worse than theta is skipped unread)
+  float M = red[0].x, S = red[0].y;
+  for (int w = 1; w < 4; ++w) fold_stat(M, S, red[w].x, red[w].y);
+  const float L = M + logf(S);
+
+  // theta = k-th largest of the 4k wave candidates (0 if fewer exist)
+  selkey_t theta = ~0ull;
+  {
+    selkey_t c4[4];
 #pragma unroll
-  for (int q = 0; q < kMergePer; ++q) {
-    const int w = threadIdx.x + 256 * q;
-    if (!inreg || w >= nw || better(thv, thi, hv[q], hi[q])) continue;
-    const size_t o = ((size_t)w * T + t) * k;
-    for (int j = 0; j < k; ++j) {
-      const float v = j == 0 ? hv[q] : part_val[o + j];
-      const int i = j == 0 ? hi[q] : part_idx[o + j];
-      if (better(thv, thi, v, i)) break;      // worse than theta: the rest of the list too
-      const int slot = atomicAdd(&scount, 1);
-      if (slot < kMergeCap) {
-        sv[slot] = v;
-        si[slot] = i;
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      c4[c] = e < 4 * k ? ck[e] : 0ull;
+    }
+    for (int r = 0; r < k; ++r) {
+      selkey_t b = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b = ((c4[c] < theta) & (c4[c] > b)) ? c4[c] : b;
+      theta = wave_max_key(b);
+    }
+  }
+  // lists whose first key is real and not below theta
+  if (inreg) {
+#pragma unroll
+    for (int q = 0; q < kMergeHeads; ++q)
+      if (hk[q] != 0ull && hk[q] >= theta) {
+        const int slot = atomicAdd(&nsl, 1);
+        if (slot < EAGLE_MAX_TOPK) slist[slot] = tid + 256 * q;
+      }
+  } else {
+    for (int w = tid; w < nb; w += 256) {
+      const selkey_t x = pk[(size_t)w * k];
+      if (x != 0ull && x >= theta) {
+        const int slot = atomicAdd(&nsl, 1);
+        if (slot < EAGLE_MAX_TOPK) slist[slot] = w;
       }
     }
   }
-  if (!inreg) {
-    for (int w = threadIdx.x; w < nw; w += 256) {
-      const size_t o = ((size_t)w * T + t) * k;
-      for (int j = 0; j < k; ++j) {
-        const float v = part_val[o + j];
-        const int i = part_idx[o + j];
-        if (better(thv, thi, v, i)) break;
-        const int slot = atomicAdd(&scount, 1);
-        if (slot < kMergeCap) {
-          sv[slot] = v;
-          si[slot] = i;
-        }
-      }
-    }
+  __syncthreads();
+  const int ns = min(nsl, EAGLE_MAX_TOPK);
+  for (int c = tid; c < ns * k; c += 256) {
+    const int j = c / k;
+    sk[c] = pk[(size_t)slist[j] * k + (c - j * k)];
   }
   __syncthreads();
   if (wave != 0) return;
-  const int ns = scount;
-  const bool fits = ns <= kMergeCap;
-  float lastv = INFINITY;
-  int lasti = -1;
+  // k-way merge: lane j follows surviving list j
+  int ptr = 0;
+  selkey_t h = lane < ns ? sk[lane * k] : 0ull;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    if (fits) {
-      for (int c = lane; c < ns; c += 64) {
-        const float v = sv[c];
-        const int i = si[c];
-        if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
-          bv = v;
-          bi = i;
-        }
-      }
-    } else {
-      const int n = nw * k;
-      for (int c = lane; c < n; c += 64) {
-        const int w = c / k;
-        const size_t o = ((size_t)w * T + t) * k + (c - w * k);
-        const float v = part_val[o];
-        const int i = part_idx[o];
-        if (better(lastv, lasti, v, i) && better(v, i, bv, bi)) {
-          bv = v;
-          bi = i;
-        }
-      }
-    }
-    wave_best(bv, bi);
+    const selkey_t b = wave_max_key(h);
+    const bool adv = (h == b) & (b != 0ull);
+    ptr += adv ? 1 : 0;
+    const selkey_t nxt = lane < ns ? sk[lane * k + min(ptr, k - 1)] : 0ull;
+    h = adv ? (ptr < k ? nxt : 0ull) : h;
     if (lane == 0) {
-      topk_id[(size_t)t * k + r] = bi;
-      topk_logp[(size_t)t * k + r] = bv - L;
+      topk_id[(size_t)t * k + r] = b ? key_index(b) : -1;
+      topk_logp[(size_t)t * k + r] = b ? key_value(b) - L : -INFINITY;
     }
-    lastv = bv;
-    lasti = bi;
   }
   if (lane == 0) lse[t] = L;
 }
@@ -391,8 +373,6 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(
     const float* __restrict__ logits, int V, int k, int32_t* __restrict__ topk_id,
     float* __restrict__ topk_logp, float* __restrict__ lse) {
   __shared__ float redf[4];
-  __shared__ float rv[4];
-  __shared__ int ri[4];
   const int t = blockIdx.x;
   const float* row = logits + (size_t)t * V;
   float M = -INFINITY;
@@ -402,25 +382,20 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(
   for (int v = threadIdx.x; v < V; v += 256) S += expf(row[v] - M);
   S = block_reduce256(S, redf, [](float a, float b) { return a + b; });
   const float L = M + logf(S);
-  float lastv = INFINITY;
-  int lasti = -1;
+  __shared__ selkey_t redk[4];
+  selkey_t last = ~0ull;
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
+    selkey_t b = 0;
     for (int v = threadIdx.x; v < V; v += 256) {
-      const float x = row[v];
-      if (better(lastv, lasti, x, v) && better(x, v, bv, bi)) {
-        bv = x;
-        bi = v;
-      }
+      const selkey_t x = sel_key(row[v], v);
+      b = ((x < last) & (x > b)) ? x : b;
     }
-    block_best256(bv, bi, rv, ri);
+    b = block_reduce256(b, redk, [](selkey_t x, selkey_t y) { return kmax(x, y); });
     if (threadIdx.x == 0) {
-      topk_id[(size_t)t * k + r] = bi;
-      topk_logp[(size_t)t * k + r] = bv - L;
+      topk_id[(size_t)t * k + r] = b ? key_index(b) : -1;
+      topk_logp[(size_t)t * k + r] = b ? key_value(b) - L : -INFINITY;
     }
-    lastv = bv;
-    lasti = bi;
+    last = b;
   }
   if (threadIdx.x == 0) lse[t] = L;
 }
@@ -428,8 +403,8 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(
 // ---------------------------------------------------------------- host side
 
 struct LmLayout {
-  size_t stat_off, val_off, idx_off, logits_off, total;
-  int nw;
+  size_t stat_off, key_off, logits_off, total;
+  int nb;   // partial lists per feature row
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -438,11 +413,10 @@ static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   LmLayout l{};
   if (dt == EAGLE_BF16) {
     const int rows_block = 16 * lm_mt(T) * kLmWaves;
-    l.nw = ((V + rows_block - 1) / rows_block) * kLmWaves;
+    l.nb = ((V + rows_block - 1) / rows_block) * (k <= kLmBlockK ? 1 : kLmWaves);
     l.stat_off = 0;
-    l.val_off = align256((size_t)l.nw * T * sizeof(float2));
-    l.idx_off = l.val_off + align256((size_t)l.nw * T * k * sizeof(float));
-    l.total = l.idx_off + align256((size_t)l.nw * T * k * sizeof(int32_t));
+    l.key_off = align256((size_t)l.nb * T * sizeof(float2));
+    l.total = l.key_off + align256((size_t)l.nb * T * k * sizeof(selkey_t));
   } else {
     l.logits_off = 0;
     l.total = align256((size_t)T * V * sizeof(float));
@@ -483,7 +457,7 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
     EAGLE_REQUIRE(((uintptr_t)f & 15) == 0 && ((uintptr_t)W & 15) == 0, EAGLE_EINVAL);
     EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
-               (float2*)(ws + l.stat_off), (float*)(ws + l.val_off), (int32_t*)(ws + l.idx_off)};
+               (float2*)(ws + l.stat_off), (selkey_t*)(ws + l.key_off)};
     const int nt = (T + 15) / 16;
     static_assert(lm_mt(16) == 8 && lm_mt(64) == 2 && lm_mt(128) == 2 && lm_mt(129) == 1,
                   "tile choice");
@@ -494,7 +468,7 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
     else launch_lm<16, 1>(p, stream);
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmhead_merge_kernel, dim3(T), dim3(256), 0, stream, p.part_stat,
-                       p.part_val, p.part_idx, l.nw, T, k, topk_id, topk_logp, lse);
+                       p.part_key, l.nb, T, k, topk_id, topk_logp, lse);
   } else if (dt == EAGLE_F32) {
     float* lg = logits ? logits : (float*)(ws + l.logits_off);
     hipLaunchKernelGGL(lmhead_f32_logits_kernel, dim3((V + 255) / 256, T), dim3(256), 0, stream,

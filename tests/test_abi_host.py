@@ -31,12 +31,17 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_queries(lib):
-    # LM head: per-wave partial statistics + per-wave top-k lists
-    nw = ((128256 + 127) // 128) * 4          # T = 64: 32 rows per wave
+    # LM head: per-workgroup statistics and top-k key lists (k <= 16), per-wave above
+    nb = (128256 + 127) // 128                # T = 64: 128 vocabulary rows per workgroup
     want = 0
-    for n in (nw * 64 * 8, nw * 64 * 10 * 4, nw * 64 * 10 * 4):
+    for n in (nb * 64 * 8, nb * 64 * 10 * 8):
         want += (n + 255) // 256 * 256
     assert lib.eagle_lmhead_topk_workspace(64, 4096, 128256, 10, _lib.EAGLE_BF16) == want
+    nb = (128256 + 511) // 512 * 4            # T = 10, k = 20: per-wave lists
+    want = 0
+    for n in (nb * 10 * 8, nb * 10 * 20 * 8):
+        want += (n + 255) // 256 * 256
+    assert lib.eagle_lmhead_topk_workspace(10, 4096, 128256, 20, _lib.EAGLE_BF16) == want
     assert lib.eagle_lmhead_topk_workspace(15, 256, 1024, 4, _lib.EAGLE_F32) >= 15 * 1024 * 4
     assert lib.eagle_lmhead_topk_workspace(0, 256, 1024, 4, _lib.EAGLE_F32) == 0
     # attention: (splits + tree) x rows x (hd + 2) floats
