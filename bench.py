@@ -47,6 +47,7 @@ def time_lmhead(cyc, T, iters):
     """Average duration (s) of eagle_lmhead_topk at T rows, HIP events on the
     stream the kernels are launched on."""
     z = cyc.z[:T]
+    in_norm = (cyc._ssq(cyc.sz, T), cyc.w.rms_eps)      # the draft rounds' deferred final norm
     ids = torch.empty((T, cyc.k), dtype=torch.int32, device=cyc.dev)
     lp = torch.empty((T, cyc.k), dtype=torch.float32, device=cyc.dev)
     lse = torch.empty(T, dtype=torch.float32, device=cyc.dev)
@@ -56,7 +57,7 @@ def time_lmhead(cyc, T, iters):
     for a, b in evs:
         a.record(stream)
         _lib.eagle_lmhead_topk(z, cyc.w_lm, cyc.k, topk_id=ids, topk_logp=lp, lse=lse,
-                               workspace=cyc.ws_lm)
+                               workspace=cyc.ws_lm, in_norm=in_norm)
         b.record(stream)
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in evs]

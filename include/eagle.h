@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 1
+#define EAGLE_ABI_VERSION 2
 
 typedef enum {
   EAGLE_OK = 0,
@@ -152,7 +152,9 @@ int eagle_tree_attn(const void* q,
  * likely tokens, which equals exp(topk_logp[t][0] - topk_logp[t][1]).
  * [D] printout: no bias.
  *
- *   f        [T][d] dt, row t is one feature (final norm already applied).
+ *   f        [T][d] dt, row t is one feature: final norm already applied, or
+ *            deferred (in_ssq [in_parts][T] f32 or NULL, in_eps; see the
+ *            decoder-layer section).
  *   W        [V][d] dt, one row per vocabulary entry.
  *   T 1..256, d % 128 == 0 (bf16) or any d >= 1 (f32), 1 <= k <= min(V, 64).
  *   topk_id  int32[T][k] out: the k largest logits of row t, larger first,
@@ -164,9 +166,9 @@ int eagle_tree_attn(const void* q,
  */
 size_t eagle_lmhead_topk_workspace(int32_t T, int32_t d, int32_t V, int32_t k, eagle_dtype dt);
 int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
-                      int32_t k, eagle_dtype dt, int32_t* topk_id, float* topk_logp,
-                      float* lse, float* logits, void* workspace, size_t ws_bytes,
-                      hipStream_t stream);
+                      int32_t k, eagle_dtype dt, const float* in_ssq, int32_t in_parts,
+                      float in_eps, int32_t* topk_id, float* topk_logp, float* lse,
+                      float* logits, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * eagle_expand_rerank - grow the dynamic draft tree and prune it.
@@ -250,15 +252,38 @@ int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
  * layer is a Llama decoder layer (RMSNorm eps 1e-5, q/k/v/o projections,
  * SiLU-gated MLP, rotary embedding, no biases) and the draft shares the
  * target's embedding table.  Weights are [out][in] bf16 (nn.Linear layout).
+ *
+ * Projection workspaces (eagle_linear*, sizes from eagle_linear_workspace and
+ * eagle_linear_rows_workspace): when the product is split over k to occupy the
+ * whole GPU, fp32 partial tiles are kept there and summed in a fixed order.
+ * With M <= 16 the sum and the epilogue run inside the one projection kernel:
+ * the last workgroup to finish a column block (counted in the first 64 KiB of
+ * the workspace) does them.  Those 64 KiB must be zero before the first call
+ * that uses the buffer (allocate it zeroed); every call leaves them zero, so a
+ * buffer can be reused by later calls on the same stream, also under graph
+ * capture.  Calls that run concurrently must not share a workspace.
+ *
+ * Deferred RMSNorm.  Every norm of the layer feeds a product, and the row
+ * scale 1 / sqrt(mean(y[m]^2) + eps) factors out of it:
+ *   RMSNorm(y)[m] W^T = (y[m] * gamma) W^T / sqrt(mean(y[m]^2) + eps).
+ * eagle_linear_rmsnorm_deferred therefore hands over xg = y * gamma (bf16,
+ * elementwise, needs no whole row) and partial sums of squares ssq[p][m]
+ * (p < eagle_linear_norm_parts(M, K, N), each over a disjoint set of columns);
+ * the consumers (eagle_linear_swiglu, eagle_linear_rope_qkv,
+ * eagle_lmhead_topk) take the optional triple (in_ssq, in_parts, in_eps),
+ * add the partials in p order, and scale their fp32 results of row m by
+ * 1 / sqrt(sum_p in_ssq[p][m] / K + in_eps) before their own epilogue.  With
+ * in_ssq NULL the input is used as given.  The only difference from applying
+ * the norm first is where the bf16 rounding of the input falls (relative error
+ * 2^-9 either way).
  * ------------------------------------------------------------------------ */
 
 /*
  * eagle_linear - out[m][n] = sum_k x[m][k] W[n][k] (+ residual[m][n]).
  *   x [M][K] bf16 (M 1..256, K % 128 == 0), W [N][K] bf16, residual [M][N] f32
  *   or NULL (may alias out when out_dt is f32), out [M][N] out_dt.
- *   workspace >= eagle_linear_workspace(M, K, N, 0) bytes (16-byte aligned;
- *   may be NULL when that is 0): fp32 partial sums when the product is split
- *   over k to occupy the whole GPU; they are summed in a fixed order.
+ *   workspace >= eagle_linear_workspace(M, K, N, 0) bytes (16-byte aligned,
+ *   zeroed before first use; may be NULL when that size is 0).
  */
 size_t eagle_linear_workspace(int32_t M, int32_t K, int32_t N, int32_t swiglu);
 int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
@@ -267,19 +292,20 @@ int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
 
 /*
  * eagle_linear_swiglu - out[m][n] = silu(x W_gate^T)[m][n] * (x W_up^T)[m][n],
- * the LlamaMLP hidden activation.  x [M][K] bf16, W_gate/W_up [N][K] bf16,
+ * the LlamaMLP hidden activation.  x [M][K] bf16 (with an optional deferred
+ * RMSNorm: in_ssq [in_parts][M] or NULL, in_eps), W_gate/W_up [N][K] bf16,
  * out [M][N] bf16, workspace >= eagle_linear_workspace(M, K, N, 1) bytes.
  */
-int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const void* w_gate,
-                        const void* w_up, int32_t N, void* out, void* workspace,
-                        size_t ws_bytes, hipStream_t stream);
+int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const float* in_ssq,
+                        int32_t in_parts, float in_eps, const void* w_gate, const void* w_up,
+                        int32_t N, void* out, void* workspace, size_t ws_bytes,
+                        hipStream_t stream);
 
 /*
  * eagle_linear_rmsnorm - a projection whose result feeds an RMSNorm, in two
  * launches: out[m] = x[m] W^T + residual[m] (f32, residual may be NULL or
  * alias out) and norm_out[m] = out[m] / sqrt(mean(out[m]^2) + eps) * gamma
- * (bf16).  Used for the layer's residual adds, each of which is followed by a
- * norm (input, post-attention, final).  N % 4 == 0, N <= 8192.
+ * (bf16).  N % 4 == 0, N <= 8192.
  *   workspace >= eagle_linear_rows_workspace(M, K, N) bytes.
  */
 size_t eagle_linear_rows_workspace(int32_t M, int32_t K, int32_t N);
@@ -288,13 +314,31 @@ int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const void* W, int
                          void* norm_out, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * eagle_linear_rmsnorm_deferred - the same product and residual add, with the
+ * norm deferred to the consumer (one launch for M <= 16, two otherwise):
+ * out[m] = x[m] W^T + residual[m] (f32), xg_out[m] = out[m] * gamma (bf16,
+ * [M][N]) and ssq_out [P][M] f32, P = eagle_linear_norm_parts(M, K, N):
+ * sums of out[m][n]^2 over disjoint column sets.  Used for the layer's
+ * residual adds, each of which is followed by a norm that feeds a product.
+ * N % 4 == 0, N <= 8192; workspace >= eagle_linear_rows_workspace(M, K, N).
+ */
+int32_t eagle_linear_norm_parts(int32_t M, int32_t K, int32_t N);
+int eagle_linear_rmsnorm_deferred(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
+                                  const float* residual, float* out, const float* gamma,
+                                  void* xg_out, float* ssq_out, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/*
  * eagle_linear_rope_qkv - the q/k/v projection followed by eagle_rope_qkv's
- * rotation and placement, in two launches: x [M][K] bf16, w_qkv
+ * rotation and placement (one launch for M <= 16 and hd % 64 == 0, two
+ * otherwise): x [M][K] bf16 (optional deferred RMSNorm: in_ssq, in_parts,
+ * in_eps), w_qkv
  * [(Hq + 2 Hkv) hd][K] bf16 (q rows, then k, then v); outputs and the other
  * arguments as eagle_rope_qkv.  (Hq + 2 Hkv) hd <= 16384, hd % 8 == 0.
  *   workspace >= eagle_linear_rows_workspace(M, K, (Hq + 2 Hkv) hd) bytes.
  */
-int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const void* w_qkv, int32_t Hq,
+int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const float* in_ssq,
+                          int32_t in_parts, float in_eps, const void* w_qkv, int32_t Hq,
                           int32_t Hkv, int32_t hd, const int32_t* depth, int64_t pos_base,
                           float theta, const int32_t* row_slot, int32_t slot_cap, void* q_out,
                           void* k_tree, void* v_tree, int32_t ld_tree, void* workspace,

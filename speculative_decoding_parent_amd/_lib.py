@@ -42,8 +42,8 @@ _PROTOS = {
                                _I32, _I32, _I32, _I32, _F32, ctypes.c_int, ctypes.c_int, _P, _P,
                                _SZ, _P, _P]),
     "eagle_lmhead_topk_workspace": (_SZ, [_I32, _I32, _I32, _I32, ctypes.c_int]),
-    "eagle_lmhead_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _P, _P, _P, _P,
-                                 _SZ, _P]),
+    "eagle_lmhead_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I32, _F32, _P,
+                                 _P, _P, _P, _P, _SZ, _P]),
     "eagle_expand_rerank": (_I32, [_I32, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32,
                                    _P, _I32, _P, _P, _P, _P, _P, _P]),
     "eagle_accept_workspace": (_SZ, [_I32, _I32]),
@@ -51,12 +51,15 @@ _PROTOS = {
                             _P, _P]),
     "eagle_linear_workspace": (_SZ, [_I32, _I32, _I32, _I32]),
     "eagle_linear": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, ctypes.c_int, _P, _SZ, _P]),
-    "eagle_linear_swiglu": (_I32, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "eagle_linear_swiglu": (_I32, [_P, _I32, _I32, _P, _I32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
     "eagle_rmsnorm": (_I32, [_P, _P, _I32, _I32, _F32, _P, _P]),
     "eagle_linear_rows_workspace": (_SZ, [_I32, _I32, _I32]),
     "eagle_linear_rmsnorm": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _P, _F32, _P, _P, _SZ, _P]),
-    "eagle_linear_rope_qkv": (_I32, [_P, _I32, _I32, _P, _I32, _I32, _I32, _P, _I64, _F32, _P, _I32,
-                                     _P, _P, _P, _I32, _P, _SZ, _P, _P]),
+    "eagle_linear_norm_parts": (_I32, [_I32, _I32, _I32]),
+    "eagle_linear_rmsnorm_deferred": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _P, _SZ,
+                                             _P]),
+    "eagle_linear_rope_qkv": (_I32, [_P, _I32, _I32, _P, _I32, _F32, _P, _I32, _I32, _I32, _P, _I64,
+                                     _F32, _P, _I32, _P, _P, _P, _I32, _P, _SZ, _P, _P]),
     "eagle_rope_qkv": (_I32, [_P, _I32, _I32, _I32, _I32, _P, _I64, _F32, _P, _I32, _P, _P, _P,
                               _I32, _P, _P]),
     "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
@@ -123,9 +126,11 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    # zero-filled: the projection entry points keep self-resetting counters at
+    # the start of their workspace, which must be zero before first use
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------- entry points
@@ -169,8 +174,18 @@ def eagle_tree_attn(q, k_cache, v_cache, L, k_tree, v_tree, Tk, mask, q_mask_row
     return out
 
 
+def _norm_args(in_norm):
+    """(in_ssq, in_parts, in_eps) of an optional deferred RMSNorm given as
+    (ssq f32 [P][M], eps), e.g. the last two results of
+    eagle_linear_rmsnorm_deferred and the norm's eps."""
+    if in_norm is None:
+        return None, 0, 0.0
+    ssq, eps = in_norm
+    return _ptr(ssq), ssq.shape[0], float(eps)
+
+
 def eagle_lmhead_topk(f, W, k, want_logits=False, topk_id=None, topk_logp=None, lse=None,
-                      logits=None, workspace=None):
+                      logits=None, workspace=None, in_norm=None):
     """Returns (topk_id int32[T][k], topk_logp f32[T][k], lse f32[T], logits or None)."""
     T, d = f.shape
     V = W.shape[0]
@@ -184,8 +199,8 @@ def eagle_lmhead_topk(f, W, k, want_logits=False, topk_id=None, topk_logp=None, 
     nb = lib().eagle_lmhead_topk_workspace(T, d, V, k, dt)
     ws = _workspace(nb, dev, workspace)
     _check("eagle_lmhead_topk", lib().eagle_lmhead_topk(
-        _ptr(f), _ptr(W), T, d, V, k, dt, _ptr(topk_id), _ptr(topk_logp), _ptr(lse),
-        _ptr(logits), _ptr(ws), nb, _stream()))
+        _ptr(f), _ptr(W), T, d, V, k, dt, *_norm_args(in_norm), _ptr(topk_id), _ptr(topk_logp),
+        _ptr(lse), _ptr(logits), _ptr(ws), nb, _stream()))
     return topk_id, topk_logp, lse, logits
 
 
@@ -249,14 +264,15 @@ def eagle_linear(x, W, residual=None, out=None, out_dtype=torch.float32, workspa
     return out
 
 
-def eagle_linear_swiglu(x, w_gate, w_up, out=None, workspace=None):
+def eagle_linear_swiglu(x, w_gate, w_up, out=None, workspace=None, in_norm=None):
     M, K = x.shape
     N = w_gate.shape[0]
     out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
     nb = lib().eagle_linear_workspace(M, K, N, 1)
     ws = _workspace(nb, x.device, workspace) if nb else None
-    _check("eagle_linear_swiglu", lib().eagle_linear_swiglu(_ptr(x), M, K, _ptr(w_gate), _ptr(w_up),
-                                                            N, _ptr(out), _ptr(ws), nb, _stream()))
+    _check("eagle_linear_swiglu", lib().eagle_linear_swiglu(
+        _ptr(x), M, K, *_norm_args(in_norm), _ptr(w_gate), _ptr(w_up), N, _ptr(out), _ptr(ws), nb,
+        _stream()))
     return out
 
 
@@ -275,8 +291,28 @@ def eagle_linear_rmsnorm(x, W, gamma, residual=None, out=None, norm_out=None, ep
     return out, norm_out
 
 
+def eagle_linear_rmsnorm_deferred(x, W, gamma, residual=None, out=None, xg_out=None, ssq_out=None,
+                                  workspace=None):
+    """out = x W^T (+ residual) in f32; xg = out * gamma in bf16; ssq [P][M] f32
+    partial row sums of out^2 (a deferred RMSNorm for the next product)."""
+    M, K = x.shape
+    N = W.shape[0]
+    P = lib().eagle_linear_norm_parts(M, K, N)
+    out = torch.empty((M, N), dtype=torch.float32, device=x.device) if out is None else out
+    xg_out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if xg_out is None else xg_out
+    ssq_out = torch.empty((P, M), dtype=torch.float32, device=x.device) if ssq_out is None else ssq_out
+    assert ssq_out.is_contiguous() and ssq_out.shape == (P, M), (ssq_out.shape, P, M)
+    nb = lib().eagle_linear_rows_workspace(M, K, N)
+    ws = _workspace(nb, x.device, workspace)
+    _check("eagle_linear_rmsnorm_deferred", lib().eagle_linear_rmsnorm_deferred(
+        _ptr(x), M, K, _ptr(W), N, _ptr(residual), _ptr(out), _ptr(gamma), _ptr(xg_out),
+        _ptr(ssq_out), _ptr(ws), nb, _stream()))
+    return out, xg_out, ssq_out
+
+
 def eagle_linear_rope_qkv(x, w_qkv, Hq, Hkv, hd, depth, pos_base, k_tree, v_tree, row_slot=None,
-                          theta=500000.0, q_out=None, workspace=None, dev_status=None):
+                          theta=500000.0, q_out=None, workspace=None, dev_status=None,
+                          in_norm=None):
     M, K = x.shape
     N = (Hq + 2 * Hkv) * hd
     q_out = torch.empty((M, Hq, hd), dtype=torch.bfloat16, device=x.device) if q_out is None else q_out
@@ -284,7 +320,7 @@ def eagle_linear_rope_qkv(x, w_qkv, Hq, Hkv, hd, depth, pos_base, k_tree, v_tree
     ws = _workspace(nb, x.device, workspace)
     ld = k_tree.shape[1]
     _check("eagle_linear_rope_qkv", lib().eagle_linear_rope_qkv(
-        _ptr(x), M, K, _ptr(w_qkv), Hq, Hkv, hd, _ptr(depth), pos_base, theta, _ptr(row_slot), ld,
+        _ptr(x), M, K, *_norm_args(in_norm), _ptr(w_qkv), Hq, Hkv, hd, _ptr(depth), pos_base, theta, _ptr(row_slot), ld,
         _ptr(q_out), _ptr(k_tree), _ptr(v_tree), ld, _ptr(ws), nb, _ptr(dev_status), _stream()))
     return q_out
 

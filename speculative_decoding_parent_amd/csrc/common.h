@@ -281,4 +281,22 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
   rows_best(v, i);
 }
 
+// Deferred RMSNorm of a product's input rows.  The rows handed over are
+// y * gamma (bf16) and row m is to be scaled by 1 / sqrt(mean(y[m]^2) + eps);
+// since that scale factors out of the product, consumers apply it to their
+// fp32 results.  mean(y^2) arrives as partial sums of squares ssq[p][m]
+// (p < parts), added here in p order over n elements.
+struct RowNorm {
+  const float* ssq;   // [parts][M], or null: no scaling
+  int parts;
+  int n;
+  float eps;
+};
+
+__device__ __forceinline__ float row_norm_scale(const RowNorm& rn, int M, int m) {
+  float tot = 0.f;
+  for (int q = 0; q < rn.parts; ++q) tot += rn.ssq[(size_t)q * M + m];
+  return 1.0f / sqrtf(tot / (float)rn.n + rn.eps);
+}
+
 }  // namespace eagle

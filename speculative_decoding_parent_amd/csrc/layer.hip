@@ -14,6 +14,8 @@
 // stays fp32; only MFMA operands (normed activations, attention output, MLP
 // hidden) are bf16.  RoPE angles are formed and rotated in fp64 (positions up
 // to ~37K make fp32 angles lose ~1e-3 rad).
+#include <algorithm>
+
 #include "wstream.h"
 
 namespace eagle {
@@ -31,6 +33,7 @@ struct LinParams {
   int ksplit;              // k slices (blockIdx.y)
   float* part;             // [ksplit][1 or 2][M][N]
   int to_part;             // write fp32 partials for a separate epilogue kernel
+  RowNorm in;              // deferred RMSNorm of the input rows (in.ssq null: none)
 };
 
 __device__ __forceinline__ void store4(void* out, int out_bf16, size_t off, int n, int N,
@@ -113,6 +116,7 @@ __global__ __launch_bounds__(256, (NT * MT <= 8 ? 2 : 1)) void linear_bf16_kerne
   for (int nt = 0; nt < NT; ++nt) {
     const int m = nt * 16 + r16;
     if (m >= p.M) continue;
+    const float rs = p.in.ssq ? row_norm_scale(p.in, p.M, m) : 1.0f;
 #pragma unroll
     for (int mt = 0; mt < HALF; ++mt) {
       const int n = n0 + mt * 16 + 4 * g;
@@ -121,10 +125,10 @@ __global__ __launch_bounds__(256, (NT * MT <= 8 ? 2 : 1)) void linear_bf16_kerne
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (SWIGLU) {
-          const float gt = acc[mt][nt][j];
-          y[j] = gt / (1.0f + expf(-gt)) * acc[mt + HALF][nt][j];
+          const float gt = acc[mt][nt][j] * rs;
+          y[j] = gt / (1.0f + expf(-gt)) * (acc[mt + HALF][nt][j] * rs);
         } else {
-          y[j] = acc[mt][nt][j];
+          y[j] = acc[mt][nt][j] * rs;
           if (p.residual && n + j < p.N) y[j] += p.residual[(size_t)m * p.N + n + j];
         }
       }
@@ -168,6 +172,15 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinParams p, int swi
       }
     }
   }
+  if (p.in.ssq) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (e0 + j >= MN) break;
+      const float rs = row_norm_scale(p.in, p.M, (int)((e0 + j) / p.N));
+      a[j] *= rs;
+      b[j] *= rs;
+    }
+  }
   float y[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -206,9 +219,13 @@ __device__ __forceinline__ f32x4 sum_slices4(const LinParams& p, size_t off) {
   return a;
 }
 
-// out = sum + residual (fp32), then norm_out = RMSNorm(out) * gamma (bf16).
+// out = sum + residual (fp32), then norm_out = RMSNorm(out) * gamma (bf16), or
+// with DEFER: norm_out = out * gamma (bf16) and ssq_out[m] = sum out[m]^2 (the
+// row scale is left to the consumer).
+template <bool DEFER>
 __global__ __launch_bounds__(kRowThreads) void linear_reduce_norm_kernel(
-    LinParams p, const float* __restrict__ gamma, float eps, bf16_t* __restrict__ norm_out) {
+    LinParams p, const float* __restrict__ gamma, float eps, bf16_t* __restrict__ norm_out,
+    float* __restrict__ ssq_out) {
   __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x;
   const int N = p.N;
@@ -232,7 +249,8 @@ __global__ __launch_bounds__(kRowThreads) void linear_reduce_norm_kernel(
   float tot = 0.f;
 #pragma unroll
   for (int w = 0; w < kRowThreads / 64; ++w) tot += red[w];
-  const float r = 1.0f / sqrtf(tot / (float)N + eps);
+  if (DEFER && threadIdx.x == 0) ssq_out[m] = tot;
+  const float r = DEFER ? 1.0f : 1.0f / sqrtf(tot / (float)N + eps);
 #pragma unroll
   for (int q = 0; q < kRowVec; ++q) {
     const int n = (threadIdx.x + kRowThreads * q) * 4;
@@ -242,6 +260,15 @@ __global__ __launch_bounds__(kRowThreads) void linear_reduce_norm_kernel(
         u32x2{pack_bf16x2(v[q][0] * r * gm[0], v[q][1] * r * gm[1]),
               pack_bf16x2(v[q][2] * r * gm[2], v[q][3] * r * gm[3])};
   }
+}
+
+// cos and sin of the rotary angle pos * inv: the angle is formed and reduced
+// to [-pi, pi] in fp64 (positions reach ~37K, where an fp32 angle would be off
+// by ~1e-3 rad), sin and cos are then taken in fp32 (~1e-7 absolute).
+__device__ __forceinline__ void rope_cs(double pos, double inv, float& c, float& s) {
+  const double a = pos * inv;
+  const double red = a - 6.283185307179586 * rint(a * 0.15915494309189535);
+  sincosf((float)red, &s, &c);
 }
 
 struct RopeArgs {
@@ -275,10 +302,10 @@ __device__ void rope_place_row(const float* row, int m, const RopeArgs& r, const
     const float x1 = row[hh * r.hd + i];
     const float x2 = row[hh * r.hd + i + half];
     if (hh < r.Hq + r.Hkv) {
-      double sn, cs;
-      sincos(pos * inv[i], &sn, &cs);
-      const float y1 = (float)((double)x1 * cs - (double)x2 * sn);
-      const float y2 = (float)((double)x2 * cs + (double)x1 * sn);
+      float cs, sn;
+      rope_cs(pos, inv[i], cs, sn);
+      const float y1 = x1 * cs - x2 * sn;
+      const float y2 = x2 * cs + x1 * sn;
       if (hh < r.Hq) {
         bf16_t* q = r.q_out + ((size_t)m * r.Hq + hh) * r.hd;
         q[i] = (bf16_t)f32_to_bf16_bits(y1);
@@ -306,8 +333,9 @@ __global__ __launch_bounds__(kRowThreads) void linear_reduce_rope_kernel(LinPara
   const int half = r.hd / 2;
   for (int i = threadIdx.x; i < half; i += blockDim.x)
     inv[i] = pow(r.theta, -2.0 * (double)i / (double)r.hd);
+  const float rs = p.in.ssq ? row_norm_scale(p.in, p.M, m) : 1.0f;
   for (int n = threadIdx.x * 4; n < p.N; n += kRowThreads * 4)
-    *(f32x4*)(row + n) = sum_slices4(p, (size_t)m * p.N + n);
+    *(f32x4*)(row + n) = sum_slices4(p, (size_t)m * p.N + n) * rs;
   __syncthreads();
   rope_place_row(row, m, r, inv);
 }
@@ -472,6 +500,345 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- few rows
+//
+// Projections of M <= 16 activation rows (the draft rounds) run as ONE kernel
+// each, epilogue included.  A workgroup owns 64 weight rows (4 MFMA tiles of
+// 16) and a range of 128-wide k steps; its four waves take interleaved steps of
+// that range, each streaming W straight from HBM into MFMA A operands and the
+// activation rows straight from L2 into B operands (no LDS staging and no
+// barrier in the loop), and the four wave tiles are added in LDS.  A column
+// block's k range is split over S workgroups so that ~512 are in flight; each
+// writes its fp32 tile to the workspace and the last one to arrive (a
+// per-column-block counter) sums the S tiles in range order, so the result
+// does not depend on scheduling, and runs the epilogue:
+//   plain   out = y (+ residual), fp32 or bf16
+//   ressq   out = y + residual (fp32), xg = out * gamma (bf16) and the row sums
+//           of squares of its 64 columns: a deferred RMSNorm (RowNorm) whose
+//           row scale the next product applies
+//   rope    the workgroup owns columns i and i + hd/2 of one head, so q and k
+//           are rotated in registers and q, k, v are placed directly
+//   swiglu  the workgroup owns 32 gate rows and the 32 matching up rows
+// Inputs may carry a deferred RMSNorm (p.in): its row scale multiplies the
+// summed tile before the epilogue.  Counters live in the first
+// kSkCounterBytes of the workspace: they must be zero before the first call,
+// and every call leaves them zero.
+constexpr int kSkMT = 4;
+constexpr size_t kSkCounterBytes = 64 * 1024;
+constexpr int kSkMaxBlocks = (int)(kSkCounterBytes / 4);
+constexpr int kSkMaxRows = 16;
+constexpr int kSkMaxS = 16;     // k ranges per column block
+
+enum SkMode { SK_PLAIN = 0, SK_RESSQ = 1, SK_ROPE = 2, SK_SWIGLU = 3 };
+
+struct SkParams {
+  const bf16_t* x;
+  int M, K;
+  const bf16_t* w0;        // W, or W_gate
+  const bf16_t* w1;        // W_up
+  int N;                   // output columns (rope: (Hq + 2 Hkv) hd)
+  int nblk, S;
+  const float* residual;
+  void* out;
+  int out_bf16;
+  const float* gamma;      // ressq
+  bf16_t* xg_out;          // ressq: [M][N]
+  float* ssq_out;          // ressq: [nblk][M]
+  int32_t* ctr;            // [nblk] per column block
+  float* part;             // [S][nblk][M][64]
+  int nsub;                // rope: column blocks per head
+  RopeArgs rope;
+  RowNorm in;
+};
+
+// Hand-off between workgroups without cache-wide write-backs.  Partial tiles
+// are written with device-coherent (sc1) buffer stores, which complete only
+// once visible to every XCD, and read with sc1 buffer loads, which never hit a
+// stale line in this XCD's L2.  arrive_last waits for the workgroup's stores
+// to complete, then counts the arrival with a device-scope atomic; the
+// workgroup that arrives last of `total` therefore finds every other
+// arrival's tile, and resets the counter.  Called by all threads; same answer
+// in all.
+constexpr int kSc1 = 1 << 4;                     // buffer cache policy bit: sc1
+constexpr int kRsrcWord3 = 0x00020000;           // raw 32-bit buffer data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)min(bytes, (size_t)0x7fffffff), kRsrcWord3);
+}
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+
+__device__ __forceinline__ bool arrive_last(int32_t* ctr, int total, int* flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // own stores complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == total - 1;
+    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// First weight row of tile mt (0..3) of column block xb.
+template <int MODE>
+__device__ __forceinline__ int sk_wrow(const SkParams& p, int xb, int mt) {
+  if (MODE == SK_SWIGLU) return xb * 32 + (mt & 1) * 16;
+  if (MODE == SK_ROPE) {
+    const int hd = p.rope.hd;
+    const int h = xb / p.nsub, sub = xb - h * p.nsub;
+    return h * hd + (mt >= 2 ? hd / 2 : 0) + sub * 32 + (mt & 1) * 16;
+  }
+  return xb * 64 + mt * 16;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
+  __shared__ f32x4 red[4][kSkMT][64];
+  __shared__ float ssl[4][kSkMaxRows];
+  __shared__ float rsc[kSkMaxRows];
+  __shared__ double sinv[MODE == SK_ROPE ? kRopeMaxHalf : 1];
+  __shared__ int flag;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int xb = blockIdx.x;
+  const int yb = blockIdx.y;
+  const int M = p.M, K = p.K, N = p.N;
+  if (MODE == SK_ROPE && threadIdx.x < p.rope.hd / 2)   // read after the first barrier
+    sinv[threadIdx.x] = pow(p.rope.theta, -2.0 * (double)threadIdx.x / (double)p.rope.hd);
+  // input row scales: lanes (row rm, q0) add the partials q0, q0 + 16, ... of
+  // row rm; the loads overlap the main loop, the sums are finished after it
+  const int rm = threadIdx.x >> 4, q0 = threadIdx.x & 15;
+  float in_ss = 0.f;
+  if (p.in.ssq && rm < M)
+    for (int q = q0; q < p.in.parts; q += 16) in_ss += p.in.ssq[(size_t)q * M + rm];
+
+  const bf16_t* wr[kSkMT];
+#pragma unroll
+  for (int mt = 0; mt < kSkMT; ++mt) {
+    const bf16_t* w = (MODE == SK_SWIGLU && mt >= 2) ? p.w1 : p.w0;
+    const int row = min(sk_wrow<MODE>(p, xb, mt) + r16, N - 1);   // N rows per matrix
+    wr[mt] = w + (size_t)row * K + g * 8;
+  }
+  const bool xok = r16 < M;
+  const bf16_t* xr = p.x + (size_t)min(r16, M - 1) * K + g * 8;
+  const int nk = K / kWsKG;
+  const int kb = (int)((int64_t)yb * nk / p.S);
+  const int ke = (int)((int64_t)(yb + 1) * nk / p.S);
+
+  f32x4 acc[kSkMT];
+#pragma unroll
+  for (int mt = 0; mt < kSkMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 wa[kSkMT][4], wb[kSkMT][4], xa[4], xbv[4];
+  auto load = [&](int kk, u32x4 (&w)[kSkMT][4], u32x4 (&xv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xv[i] = xok ? *(const u32x4*)(xr + kk * kWsKG + i * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int mt = 0; mt < kSkMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[mt][i] = *(const u32x4*)(wr[mt] + kk * kWsKG + i * 32);
+  };
+  auto compute = [&](const u32x4 (&w)[kSkMT][4], const u32x4 (&xv)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 b = ws_as_bf16x8(xv[i]);
+#pragma unroll
+      for (int mt = 0; mt < kSkMT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws_as_bf16x8(w[mt][i]), b, acc[mt], 0,
+                                                          0, 0);
+    }
+  };
+  int kk = kb + wave;
+  if (kk < ke) load(kk, wa, xa);
+  for (; kk < ke; kk += 8) {
+    if (kk + 4 < ke) load(kk + 4, wb, xbv);
+    compute(wa, xa);
+    if (kk + 4 >= ke) break;
+    if (kk + 8 < ke) load(kk + 8, wa, xa);
+    compute(wb, xbv);
+  }
+  in_ss += dpp_move<kDppQuadXor1>(in_ss);      // the 16 lanes of a row: a DPP row
+  in_ss += dpp_move<kDppQuadXor2>(in_ss);
+  in_ss += dpp_move<kDppHalfMirror>(in_ss);
+  in_ss += dpp_move<kDppRowMirror>(in_ss);
+  if (q0 == 0 && rm < M)
+    rsc[rm] = p.in.ssq ? 1.0f / sqrtf(in_ss / (float)p.in.n + p.in.eps) : 1.0f;
+#pragma unroll
+  for (int mt = 0; mt < kSkMT; ++mt) red[wave][mt][lane] = acc[mt];
+  __syncthreads();
+
+  // tiles finished by this wave: one (plain, ressq) or a (first, second) pair
+  constexpr bool kPair = MODE == SK_ROPE || MODE == SK_SWIGLU;
+  const bool owner = kPair ? wave < 2 : true;
+  const int ta = wave, tb = wave + 2;
+  const int m = r16;
+  f32x4 ya = red[0][ta & 3][lane] + red[1][ta & 3][lane];
+  ya = ya + red[2][ta & 3][lane];
+  ya = ya + red[3][ta & 3][lane];
+  f32x4 yb2 = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kPair) {
+    yb2 = red[0][tb & 3][lane] + red[1][tb & 3][lane];
+    yb2 = yb2 + red[2][tb & 3][lane];
+    yb2 = yb2 + red[3][tb & 3][lane];
+  }
+  if (p.S > 1) {
+    const __amdgpu_buffer_rsrc_t rpart =
+        dev_rsrc(p.part, (size_t)p.S * p.nblk * M * 64 * sizeof(float));
+    // partial tile [yb][xb][m][64] (byte offsets)
+    const uint32_t mine = (uint32_t)((((size_t)yb * p.nblk + xb) * M + m) * 64 * sizeof(float));
+    if (owner && m < M) {
+      st_dev4(rpart, mine + (ta * 16 + 4 * g) * 4, ya);
+      if (kPair) st_dev4(rpart, mine + (tb * 16 + 4 * g) * 4, yb2);
+    }
+    if (!arrive_last(p.ctr + xb, p.S, &flag)) return;
+    if (owner && m < M) {
+      // all S tiles in flight at once, then summed in range order
+      f32x4 ta4[kSkMaxS], tb4[kSkMaxS];
+#pragma unroll
+      for (int s = 0; s < kSkMaxS; ++s) {
+        if (s < p.S) {
+          const uint32_t o = (uint32_t)((((size_t)s * p.nblk + xb) * M + m) * 64 * sizeof(float));
+          ta4[s] = ld_dev4(rpart, o + (ta * 16 + 4 * g) * 4);
+          if (kPair) tb4[s] = ld_dev4(rpart, o + (tb * 16 + 4 * g) * 4);
+        }
+      }
+      ya = f32x4{0.f, 0.f, 0.f, 0.f};
+      yb2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < kSkMaxS; ++s) {
+        if (s < p.S) {
+          ya = ya + ta4[s];
+          if (kPair) yb2 = yb2 + tb4[s];
+        }
+      }
+    }
+  }
+  if (m < M) {
+    const float rs = rsc[m];
+    ya = ya * rs;
+    yb2 = yb2 * rs;
+  }
+
+  if (MODE == SK_PLAIN || MODE == SK_RESSQ) {
+    const int n = xb * 64 + ta * 16 + 4 * g;
+    float ss = 0.f;
+    if (m < M && n < N) {
+      float y[4] = {ya[0], ya[1], ya[2], ya[3]};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (p.residual && n + j < N) y[j] += p.residual[(size_t)m * N + n + j];
+        if (n + j < N) ss = fmaf(y[j], y[j], ss);
+      }
+      store4(p.out, MODE == SK_RESSQ ? 0 : p.out_bf16, (size_t)m * N + n, n, N, y);
+      if (MODE == SK_RESSQ) {   // N % 4 == 0
+        const f32x4 gm = *(const f32x4*)(p.gamma + n);
+        *(u32x2*)(p.xg_out + (size_t)m * N + n) =
+            u32x2{pack_bf16x2(y[0] * gm[0], y[1] * gm[1]), pack_bf16x2(y[2] * gm[2], y[3] * gm[3])};
+      }
+    }
+    if (MODE == SK_RESSQ) {
+      ss = rows_sum(ss);
+      if (g == 0) ssl[wave][r16] = ss;
+      __syncthreads();
+      if (threadIdx.x < M)
+        p.ssq_out[(size_t)xb * M + threadIdx.x] =
+            ((ssl[0][threadIdx.x] + ssl[1][threadIdx.x]) + ssl[2][threadIdx.x]) +
+            ssl[3][threadIdx.x];
+    }
+  } else if (MODE == SK_SWIGLU) {
+    const int n = xb * 32 + ta * 16 + 4 * g;
+    if (owner && m < M && n < N) {
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = ya[j] / (1.0f + expf(-ya[j])) * yb2[j];
+      store4(p.out, 1, (size_t)m * N + n, n, N, y);
+    }
+  } else {   // SK_ROPE
+    const RopeArgs& r = p.rope;
+    if (owner && m < M) {
+      const int half = r.hd / 2;
+      const int h = xb / p.nsub;
+      const int i0 = (xb - h * p.nsub) * 32 + ta * 16 + 4 * g;
+      int slot = r.row_slot ? r.row_slot[m] : m;
+      if (slot < 0 || slot >= r.slot_cap) {
+        set_status(r.status, EAGLE_DEV_BAD_INDEX);
+        slot = -1;
+      }
+      float y1[4], y2[4];
+      if (h < r.Hq + r.Hkv) {
+        const double pos = (double)(r.pos_base + r.depth[m]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float cs, sn;
+          rope_cs(pos, sinv[i0 + j], cs, sn);
+          y1[j] = ya[j] * cs - yb2[j] * sn;
+          y2[j] = yb2[j] * cs + ya[j] * sn;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y1[j] = ya[j];
+          y2[j] = yb2[j];
+        }
+      }
+      bf16_t* dst = nullptr;
+      if (h < r.Hq) dst = r.q_out + ((size_t)m * r.Hq + h) * r.hd;
+      else if (slot >= 0 && h < r.Hq + r.Hkv)
+        dst = r.k_tree + ((size_t)(h - r.Hq) * r.ld_tree + slot) * r.hd;
+      else if (slot >= 0)
+        dst = r.v_tree + ((size_t)(h - r.Hq - r.Hkv) * r.ld_tree + slot) * r.hd;
+      if (dst) {
+        *(u32x2*)(dst + i0) = u32x2{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
+        *(u32x2*)(dst + i0 + half) =
+            u32x2{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
+      }
+    }
+  }
+}
+
+struct SkPlan {
+  int nblk, S;
+  size_t part_off, total;
+};
+
+// Column blocks by mode; k ranges per column block: the smallest power of two
+// that puts >= 512 workgroups in flight (two per CU), with at least four k
+// steps (one per wave) per workgroup.
+static SkPlan sk_plan(int mode, int M, int K, int N, int heads, int hd) {
+  SkPlan pl{};
+  if (mode == SK_SWIGLU) pl.nblk = (N + 31) / 32;
+  else if (mode == SK_ROPE) pl.nblk = heads * ((hd / 2) / 32);
+  else pl.nblk = (N + 63) / 64;
+  const int nk = K / kWsKG;
+  int S = 1;
+  while (S < kSkMaxS && pl.nblk * S < 512 && 2 * S <= nk / 4) S *= 2;
+  pl.S = S;
+  pl.part_off = kSkCounterBytes;
+  pl.total = pl.S > 1
+                 ? pl.part_off + (((size_t)pl.S * pl.nblk * M * 64 * sizeof(float) + 255) & ~(size_t)255)
+                 : 0;
+  return pl;
+}
+
+template <int MODE>
+static void launch_rows(SkParams p, const SkPlan& pl, void* ws, hipStream_t s) {
+  p.nblk = pl.nblk;
+  p.S = pl.S;
+  char* w = (char*)ws;
+  p.ctr = (int32_t*)w;
+  p.part = w ? (float*)(w + pl.part_off) : nullptr;
+  hipLaunchKernelGGL(linear_rows_kernel<MODE>, dim3(pl.nblk, pl.S), dim3(256), 0, s, p);
+}
+
 // k slices for a projection: enough workgroups to fill the chip (about two per
 // CU) while the fp32 partials stay below a quarter of the weight bytes; the
 // count divides K / 128.
@@ -492,10 +859,27 @@ static int lin_ksplit(int M, int K, int N, int swiglu) {
   return best;
 }
 
+// Workspace of the general path: the counter area (kept untouched, so one
+// buffer can serve both paths) followed by the k-slice partials.
 static size_t lin_workspace(int M, int K, int N, int swiglu) {
+  if (M <= kSkMaxRows) return sk_plan(swiglu ? SK_SWIGLU : SK_PLAIN, M, K, N, 0, 0).total;
   const int s = lin_ksplit(M, K, N, swiglu);
-  return s > 1 ? (size_t)s * (swiglu ? 2 : 1) * M * N * sizeof(float) : 0;
+  return s > 1 ? kSkCounterBytes + (size_t)s * (swiglu ? 2 : 1) * M * N * sizeof(float) : 0;
 }
+
+// Row-epilogue products (rmsnorm, deferred rmsnorm, rope): the largest layout
+// any of them uses at this shape.
+static size_t rows_workspace(int M, int K, int N) {
+  size_t w = kSkCounterBytes + (size_t)lin_ksplit(M, K, N, 0) * M * N * sizeof(float);
+  if (M <= kSkMaxRows) w = std::max(w, sk_plan(SK_PLAIN, M, K, N, 0, 0).total);
+  return w;
+}
+
+static RowNorm row_norm(const float* ssq, int parts, int n, float eps) {
+  return RowNorm{ssq, ssq ? parts : 0, n, eps};
+}
+
+static float* lin_partials(void* ws) { return (float*)((char*)ws + kSkCounterBytes); }
 
 template <int NT, int SWIGLU>
 static void launch_lin(const LinParams& p, hipStream_t s) {
@@ -551,31 +935,56 @@ extern "C" int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, 
   EAGLE_REQUIRE(out_dt == EAGLE_BF16 || out_dt == EAGLE_F32, EAGLE_EINVAL);
   EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(aligned16(x) && aligned16(W) && aligned16(out), EAGLE_EINVAL);
-  const int ks = eagle::lin_ksplit(M, K, N, 0);
   const size_t need = eagle::lin_workspace(M, K, N, 0);
   EAGLE_REQUIRE(need == 0 || (workspace && aligned16(workspace)), EAGLE_EINVAL);
   EAGLE_REQUIRE(ws_bytes >= need, EAGLE_EWORKSPACE);
+  if (M <= eagle::kSkMaxRows) {
+    const eagle::SkPlan pl = eagle::sk_plan(eagle::SK_PLAIN, M, K, N, 0, 0);
+    EAGLE_REQUIRE(pl.nblk <= eagle::kSkMaxBlocks, EAGLE_EUNSUPPORTED);
+    eagle::SkParams p{};
+    p.x = (const bf16_t*)x; p.M = M; p.K = K; p.w0 = (const bf16_t*)W; p.N = N;
+    p.residual = residual; p.out = out; p.out_bf16 = out_dt == EAGLE_BF16 ? 1 : 0;
+    eagle::launch_rows<eagle::SK_PLAIN>(p, pl, pl.total ? workspace : nullptr, stream);
+    EAGLE_LAUNCH_CHECK();
+    return EAGLE_OK;
+  }
+  const int ks = eagle::lin_ksplit(M, K, N, 0);
   eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)W, nullptr, N, residual, out,
-                     out_dt == EAGLE_BF16 ? 1 : 0, ks, (float*)workspace};
+                     out_dt == EAGLE_BF16 ? 1 : 0, ks,
+                     ks > 1 ? eagle::lin_partials(workspace) : nullptr};
   eagle::dispatch_lin<0>(p, stream);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }
 
-extern "C" int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const void* w_gate,
+extern "C" int eagle_linear_swiglu(const void* x, int32_t M, int32_t K, const float* in_ssq,
+                                   int32_t in_parts, float in_eps, const void* w_gate,
                                    const void* w_up, int32_t N, void* out, void* workspace,
                                    size_t ws_bytes, hipStream_t stream) {
   EAGLE_REQUIRE(x && w_gate && w_up && out, EAGLE_EINVAL);
+  EAGLE_REQUIRE(!in_ssq || (in_parts >= 1 && in_eps >= 0.0f), EAGLE_EINVAL);
+  const eagle::RowNorm rn = eagle::row_norm(in_ssq, in_parts, K, in_eps);
   EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && N >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(aligned16(x) && aligned16(w_gate) && aligned16(w_up) && aligned16(out),
                 EAGLE_EINVAL);
-  const int ks = eagle::lin_ksplit(M, K, N, 1);
   const size_t need = eagle::lin_workspace(M, K, N, 1);
   EAGLE_REQUIRE(need == 0 || (workspace && aligned16(workspace)), EAGLE_EINVAL);
   EAGLE_REQUIRE(ws_bytes >= need, EAGLE_EWORKSPACE);
+  if (M <= eagle::kSkMaxRows) {
+    const eagle::SkPlan pl = eagle::sk_plan(eagle::SK_SWIGLU, M, K, N, 0, 0);
+    EAGLE_REQUIRE(pl.nblk <= eagle::kSkMaxBlocks, EAGLE_EUNSUPPORTED);
+    eagle::SkParams p{};
+    p.x = (const bf16_t*)x; p.M = M; p.K = K; p.w0 = (const bf16_t*)w_gate;
+    p.w1 = (const bf16_t*)w_up; p.N = N; p.out = out; p.out_bf16 = 1; p.in = rn;
+    eagle::launch_rows<eagle::SK_SWIGLU>(p, pl, pl.total ? workspace : nullptr, stream);
+    EAGLE_LAUNCH_CHECK();
+    return EAGLE_OK;
+  }
+  const int ks = eagle::lin_ksplit(M, K, N, 1);
   eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)w_gate, (const bf16_t*)w_up, N,
-                     nullptr, out, 1, ks, (float*)workspace};
+                     nullptr, out, 1, ks, ks > 1 ? eagle::lin_partials(workspace) : nullptr};
+  p.in = rn;
   eagle::dispatch_lin<1>(p, stream);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
@@ -609,7 +1018,7 @@ extern "C" int eagle_rope_qkv(const float* qkv, int32_t M, int32_t Hq, int32_t H
 
 extern "C" size_t eagle_linear_rows_workspace(int32_t M, int32_t K, int32_t N) {
   if (M < 1 || K < eagle::kWsKG || N < 1 || K % eagle::kWsKG) return 0;
-  return (size_t)eagle::lin_ksplit(M, K, N, 0) * M * N * sizeof(float);
+  return eagle::rows_workspace(M, K, N);
 }
 
 extern "C" int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
@@ -625,22 +1034,65 @@ extern "C" int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const v
                 EAGLE_EINVAL);
   EAGLE_REQUIRE(ws_bytes >= eagle_linear_rows_workspace(M, K, N), EAGLE_EWORKSPACE);
   eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)W, nullptr, N, residual, out, 0,
-                     eagle::lin_ksplit(M, K, N, 0), (float*)workspace};
+                     eagle::lin_ksplit(M, K, N, 0), eagle::lin_partials(workspace)};
   p.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
   eagle::launch_lin_partials(p, stream);
-  hipLaunchKernelGGL(eagle::linear_reduce_norm_kernel, dim3(M), dim3(eagle::kRowThreads), 0,
-                     stream, p, gamma, eps, (bf16_t*)norm_out);
+  hipLaunchKernelGGL(eagle::linear_reduce_norm_kernel<false>, dim3(M), dim3(eagle::kRowThreads),
+                     0, stream, p, gamma, eps, (bf16_t*)norm_out, nullptr);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }
 
-extern "C" int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const void* w_qkv,
+extern "C" int32_t eagle_linear_norm_parts(int32_t M, int32_t K, int32_t N) {
+  (void)K;
+  if (M < 1 || N < 1) return 0;
+  return M <= eagle::kSkMaxRows ? (N + 63) / 64 : 1;
+}
+
+extern "C" int eagle_linear_rmsnorm_deferred(const void* x, int32_t M, int32_t K, const void* W,
+                                             int32_t N, const float* residual, float* out,
+                                             const float* gamma, void* xg_out, float* ssq_out,
+                                             void* workspace, size_t ws_bytes,
+                                             hipStream_t stream) {
+  EAGLE_REQUIRE(x && W && out && gamma && xg_out && ssq_out && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && N >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(K % eagle::kWsKG == 0 && N % 4 == 0 && N <= eagle::kRowMaxN, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(aligned16(x) && aligned16(W) && aligned16(out) && aligned16(gamma) &&
+                    aligned16(workspace) && (!residual || aligned16(residual)) &&
+                    ((uintptr_t)xg_out & 7) == 0 && ((uintptr_t)ssq_out & 3) == 0,
+                EAGLE_EINVAL);
+  EAGLE_REQUIRE(ws_bytes >= eagle_linear_rows_workspace(M, K, N), EAGLE_EWORKSPACE);
+  if (M <= eagle::kSkMaxRows) {
+    const eagle::SkPlan pl = eagle::sk_plan(eagle::SK_RESSQ, M, K, N, 0, 0);
+    EAGLE_REQUIRE(pl.nblk <= eagle::kSkMaxBlocks, EAGLE_EUNSUPPORTED);
+    eagle::SkParams p{};
+    p.x = (const bf16_t*)x; p.M = M; p.K = K; p.w0 = (const bf16_t*)W; p.N = N;
+    p.residual = residual; p.out = out; p.gamma = gamma; p.xg_out = (bf16_t*)xg_out;
+    p.ssq_out = ssq_out;
+    eagle::launch_rows<eagle::SK_RESSQ>(p, pl, workspace, stream);
+    EAGLE_LAUNCH_CHECK();
+    return EAGLE_OK;
+  }
+  eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)W, nullptr, N, residual, out, 0,
+                     eagle::lin_ksplit(M, K, N, 0), eagle::lin_partials(workspace)};
+  p.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
+  eagle::launch_lin_partials(p, stream);
+  hipLaunchKernelGGL(eagle::linear_reduce_norm_kernel<true>, dim3(M), dim3(eagle::kRowThreads), 0,
+                     stream, p, gamma, 0.0f, (bf16_t*)xg_out, ssq_out);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const float* in_ssq,
+                                     int32_t in_parts, float in_eps, const void* w_qkv,
                                      int32_t Hq, int32_t Hkv, int32_t hd, const int32_t* depth,
                                      int64_t pos_base, float theta, const int32_t* row_slot,
                                      int32_t slot_cap, void* q_out, void* k_tree, void* v_tree,
                                      int32_t ld_tree, void* workspace, size_t ws_bytes,
                                      int32_t* dev_status, hipStream_t stream) {
   EAGLE_REQUIRE(x && w_qkv && depth && q_out && k_tree && v_tree && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(!in_ssq || (in_parts >= 1 && in_eps >= 0.0f), EAGLE_EINVAL);
+  const eagle::RowNorm rn = eagle::row_norm(in_ssq, in_parts, K, in_eps);
   EAGLE_REQUIRE(M >= 1 && M <= EAGLE_MAX_TREE && K >= 1 && Hq >= 1 && Hkv >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(hd >= 8 && hd % 8 == 0 && hd / 2 <= eagle::kRopeMaxHalf, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(K % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
@@ -650,10 +1102,24 @@ extern "C" int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const 
   EAGLE_REQUIRE((size_t)N * sizeof(float) <= 64 * 1024, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(aligned16(x) && aligned16(w_qkv) && aligned16(workspace), EAGLE_EINVAL);
   EAGLE_REQUIRE(ws_bytes >= eagle_linear_rows_workspace(M, K, N), EAGLE_EWORKSPACE);
-  eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)w_qkv, nullptr, N, nullptr, nullptr,
-                     0, eagle::lin_ksplit(M, K, N, 0), (float*)workspace};
   eagle::RopeArgs r{Hq, Hkv, hd, depth, pos_base, (double)theta, row_slot, slot_cap,
                     (bf16_t*)q_out, (bf16_t*)k_tree, (bf16_t*)v_tree, ld_tree, dev_status};
+  if (M <= eagle::kSkMaxRows && hd % 64 == 0 && ((uintptr_t)q_out & 7) == 0 &&
+      ((uintptr_t)k_tree & 7) == 0 && ((uintptr_t)v_tree & 7) == 0) {
+    const eagle::SkPlan pl = eagle::sk_plan(eagle::SK_ROPE, M, K, N, Hq + 2 * Hkv, hd);
+    EAGLE_REQUIRE(pl.nblk <= eagle::kSkMaxBlocks, EAGLE_EUNSUPPORTED);
+    eagle::SkParams p{};
+    p.x = (const bf16_t*)x; p.M = M; p.K = K; p.w0 = (const bf16_t*)w_qkv; p.N = N;
+    p.nsub = (hd / 2) / 32;
+    p.rope = r;
+    p.in = rn;
+    eagle::launch_rows<eagle::SK_ROPE>(p, pl, workspace, stream);
+    EAGLE_LAUNCH_CHECK();
+    return EAGLE_OK;
+  }
+  eagle::LinParams p{(const bf16_t*)x, M, K, (const bf16_t*)w_qkv, nullptr, N, nullptr, nullptr,
+                     0, eagle::lin_ksplit(M, K, N, 0), eagle::lin_partials(workspace)};
+  p.in = rn;
   eagle::launch_lin_partials(p, stream);
   hipLaunchKernelGGL(eagle::linear_reduce_rope_kernel, dim3(M), dim3(eagle::kRowThreads),
                      N * sizeof(float), stream, p, r);

@@ -51,6 +51,7 @@ struct LmParams {
   float* logits;
   float2* part_stat;   // [T][nb] (max, sum exp(l - max))
   selkey_t* part_key;  // [T][nb][k] sorted selection keys
+  RowNorm in;          // deferred RMSNorm of the feature rows (in.ssq null: none)
 };
 
 template <int NT, int kLmMT>
@@ -72,8 +73,37 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
     const int v = min(v0 + mt * 16 + r16, p.V - 1);
     wrow[mt] = p.W + (size_t)v * p.d + g * 8;
   }
+  // deferred RMSNorm of the feature rows: partial sums are loaded before the
+  // main loop and finished after it.  T <= 16: lanes (row tid / 16, q0 =
+  // tid % 16) take partials q0, q0 + 16, ...; otherwise thread t takes row t.
+  __shared__ float rsc[EAGLE_MAX_TREE];
+  const bool rows16 = p.T <= 16;
+  const int rm = rows16 ? tid >> 4 : tid;
+  const int q0 = rows16 ? (tid & 15) : 0;
+  float in_ss = 0.f;
+  if (p.in.ssq && rm < p.T)
+    for (int q = q0; q < p.in.parts; q += rows16 ? 16 : 1) in_ss += p.in.ssq[(size_t)q * p.T + rm];
+
   f32x4 acc[kLmMT][NT];
   wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
+
+  if (p.in.ssq) {
+    if (rows16) {
+      in_ss += dpp_move<kDppQuadXor1>(in_ss);
+      in_ss += dpp_move<kDppQuadXor2>(in_ss);
+      in_ss += dpp_move<kDppHalfMirror>(in_ss);
+      in_ss += dpp_move<kDppRowMirror>(in_ss);
+    }
+    if (rm < p.T && q0 == 0) rsc[rm] = 1.0f / sqrtf(in_ss / (float)p.in.n + p.in.eps);
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = nt * 16 + r16;
+      const float r = t < p.T ? rsc[t] : 1.0f;
+#pragma unroll
+      for (int mt = 0; mt < kLmMT; ++mt) acc[mt][nt] = acc[mt][nt] * r;
+    }
+  }
 
   // ---- epilogue.  Lane (g, r16) holds, for tile (mt, nt), the logits of
   // vocabulary rows v0 + 16 mt + 4 g + j (j < 4) for feature row 16 nt + r16.
@@ -350,7 +380,7 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
 // ---------------------------------------------------------------- fp32 path
 
 __global__ __launch_bounds__(256) void lmhead_f32_logits_kernel(
-    const float* __restrict__ f, const float* __restrict__ W, int T, int d, int V,
+    const float* __restrict__ f, const float* __restrict__ W, int T, int d, int V, RowNorm in,
     float* __restrict__ logits) {
   __shared__ float fsm[1024];
   const int t = blockIdx.y;
@@ -366,6 +396,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_logits_kernel(
       for (int i = 0; i < n; ++i) acc = fmaf(fsm[i], w[i], acc);
     }
   }
+  if (in.ssq) acc *= row_norm_scale(in, T, t);
   if (v < V) logits[(size_t)t * V + v] = acc;
 }
 
@@ -441,11 +472,14 @@ extern "C" size_t eagle_lmhead_topk_workspace(int32_t T, int32_t d, int32_t V, i
 }
 
 extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
-                                 int32_t k, eagle_dtype dt, int32_t* topk_id, float* topk_logp,
-                                 float* lse, float* logits, void* workspace, size_t ws_bytes,
+                                 int32_t k, eagle_dtype dt, const float* in_ssq, int32_t in_parts,
+                                 float in_eps, int32_t* topk_id, float* topk_logp, float* lse,
+                                 float* logits, void* workspace, size_t ws_bytes,
                                  hipStream_t stream) {
   using namespace eagle;
   EAGLE_REQUIRE(f && W && topk_id && topk_logp && lse && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(!in_ssq || (in_parts >= 1 && in_eps >= 0.0f), EAGLE_EINVAL);
+  const RowNorm rn{in_ssq, in_ssq ? in_parts : 0, d, in_eps};
   EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && d >= 1 && V >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(k >= 1 && k <= EAGLE_MAX_TOPK && k <= V, EAGLE_EINVAL);
   EAGLE_REQUIRE(((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
@@ -457,7 +491,7 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
     EAGLE_REQUIRE(((uintptr_t)f & 15) == 0 && ((uintptr_t)W & 15) == 0, EAGLE_EINVAL);
     EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
-               (float2*)(ws + l.stat_off), (selkey_t*)(ws + l.key_off)};
+               (float2*)(ws + l.stat_off), (selkey_t*)(ws + l.key_off), rn};
     const int nt = (T + 15) / 16;
     static_assert(lm_mt(16) == 8 && lm_mt(64) == 2 && lm_mt(128) == 2 && lm_mt(129) == 1,
                   "tile choice");
@@ -472,7 +506,7 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
   } else if (dt == EAGLE_F32) {
     float* lg = logits ? logits : (float*)(ws + l.logits_off);
     hipLaunchKernelGGL(lmhead_f32_logits_kernel, dim3((V + 255) / 256, T), dim3(256), 0, stream,
-                       (const float*)f, (const float*)W, T, d, V, lg);
+                       (const float*)f, (const float*)W, T, d, V, rn, lg);
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(rows_topk_kernel, dim3(T), dim3(256), 0, stream, lg, V, k, topk_id,
                        topk_logp, lse);

@@ -79,6 +79,9 @@ class DraftVerifyCycle:
         self.n2 = torch.zeros((m, d), **bf)
         self.gu = torch.zeros((m, F), **bf)
         self.z = torch.zeros((m, d), **bf)
+        # partial row sums of squares of the deferred norms (norm1, norm2, final)
+        P = max(_lib.lib().eagle_linear_norm_parts(mm, d, d) * mm for mm in (1, ks, T))
+        self.s1, self.s2, self.sz = (torch.zeros(P, **f32) for _ in range(3))
         self.ids = [torch.zeros((1 if r == 0 else ks, k), **i32) for r in range(R)]
         self.logp = [torch.zeros((1 if r == 0 else ks, k), **f32) for r in range(R)]
         self.lse = torch.zeros(m, **f32)
@@ -113,29 +116,40 @@ class DraftVerifyCycle:
             for (K, N) in ((2 * d, d), (d, nqkv), (hq * hd, d), (F, d)):
                 ws_lin = max(ws_lin, lib.eagle_linear_rows_workspace(M, K, N))
             ws_lin = max(ws_lin, lib.eagle_linear_workspace(M, d, F, 1))
-        self.ws_lin = torch.empty(ws_lin, dtype=torch.uint8, device=dev)
+        self.ws_lin = torch.zeros(ws_lin, dtype=torch.uint8, device=dev)   # counters start at 0
         self.graph = None
 
     # ------------------------------------------------------------ one layer
-    def _layer(self, lw, n, x_res, depth, row_slot, kc, vc, kt, vt, Tk, mask, out, q_mask_row,
-               final_norm):
-        """Decoder layer on rows 0..n-1: self.n1[:n] holds RMSNorm(x_res) (bf16),
-        x_res the fp32 residual stream.  Writes the fp32 output to ``out`` and
-        its final RMSNorm (bf16) to self.z[:n]."""
+    def _ssq(self, buf, n):
+        """[P][n] view of a partial-sums buffer for n rows of width d."""
+        P = _lib.lib().eagle_linear_norm_parts(n, self.w.d, self.w.d)
+        return buf[:P * n].view(P, n)
+
+    def _layer(self, lw, n, x_in, in1, x_res, depth, row_slot, kc, vc, kt, vt, Tk, mask, out,
+               q_mask_row, final_norm):
+        """Decoder layer on rows 0..n-1.  x_in (bf16) is the attention input:
+        RMSNorm(x_res) itself (in1 None) or x_res * gamma with its deferred row
+        scale in1 = (ssq, eps); x_res is the fp32 residual stream.  Writes the
+        fp32 output to ``out`` and its final norm, deferred, to self.z[:n];
+        returns that norm's partial sums."""
         w = self.w
-        _lib.eagle_linear_rope_qkv(self.n1[:n], lw["wqkv"], w.hq, w.hkv, w.hd, depth, self.L, kt, vt,
+        eps = w.rms_eps
+        _lib.eagle_linear_rope_qkv(x_in, lw["wqkv"], w.hq, w.hkv, w.hd, depth, self.L, kt, vt,
                                    row_slot=row_slot, theta=w.rope_theta, q_out=self.q[:n],
-                                   workspace=self.ws_lin, dev_status=self.status)
+                                   workspace=self.ws_lin, dev_status=self.status, in_norm=in1)
         _lib.eagle_tree_attn(self.q[:n], kc, vc, self.L, kt, vt, Tk, mask, q_mask_row=q_mask_row,
                              out=self.attn[:n], workspace=self.ws_attn, dev_status=self.status)
-        _lib.eagle_linear_rmsnorm(self.attn[:n].view(n, -1), lw["wo"], lw["norm2"], residual=x_res,
-                                  out=self.x2[:n], norm_out=self.n2[:n], eps=w.rms_eps,
-                                  workspace=self.ws_lin)
+        s2 = self._ssq(self.s2, n)
+        _lib.eagle_linear_rmsnorm_deferred(self.attn[:n].view(n, -1), lw["wo"], lw["norm2"],
+                                           residual=x_res, out=self.x2[:n], xg_out=self.n2[:n],
+                                           ssq_out=s2, workspace=self.ws_lin)
         _lib.eagle_linear_swiglu(self.n2[:n], lw["wgate"], lw["wup"], out=self.gu[:n],
-                                 workspace=self.ws_lin)
-        _lib.eagle_linear_rmsnorm(self.gu[:n], lw["wdown"], final_norm, residual=self.x2[:n],
-                                  out=out, norm_out=self.z[:n], eps=w.rms_eps,
-                                  workspace=self.ws_lin)
+                                 workspace=self.ws_lin, in_norm=(s2, eps))
+        sz = self._ssq(self.sz, n)
+        _lib.eagle_linear_rmsnorm_deferred(self.gu[:n], lw["wdown"], final_norm,
+                                           residual=self.x2[:n], out=out, xg_out=self.z[:n],
+                                           ssq_out=sz, workspace=self.ws_lin)
+        return sz
 
     # ------------------------------------------------------------ the cycle
     def draft_round(self, r: int):
@@ -150,13 +164,17 @@ class DraftVerifyCycle:
                                  (tok, depth, slot, src), slot_mask=self.smask, feat=self.feat,
                                  root_feat=self.root_feat, embed=self.embed, x_in=self.x_in[:kf],
                                  dev_status=self.status)
-        _lib.eagle_linear_rmsnorm(self.x_in[:kf], self.w_fuse, self.draft["norm1"], out=self.h[:kf],
-                                  norm_out=self.n1[:kf], eps=w.rms_eps, workspace=self.ws_lin)
+        s1 = self._ssq(self.s1, kf)
+        _lib.eagle_linear_rmsnorm_deferred(self.x_in[:kf], self.w_fuse, self.draft["norm1"],
+                                           out=self.h[:kf], xg_out=self.n1[:kf], ssq_out=s1,
+                                           workspace=self.ws_lin)
         feat_rows = self.feat[base:base + kf]
-        self._layer(self.draft, kf, self.h[:kf], depth, slot, self.dkc, self.dvc, self.dkt,
-                    self.dvt, Sr, self.smask[:Sr], feat_rows, slot, self.draft_norm)
+        sz = self._layer(self.draft, kf, self.n1[:kf], (s1, w.rms_eps), self.h[:kf], depth, slot,
+                         self.dkc, self.dvc, self.dkt, self.dvt, Sr, self.smask[:Sr], feat_rows,
+                         slot, self.draft_norm)
         _lib.eagle_lmhead_topk(self.z[:kf], self.w_lm, self.k, topk_id=self.ids[r],
-                               topk_logp=self.logp[r], lse=self.lse[:kf], workspace=self.ws_lm)
+                               topk_logp=self.logp[r], lse=self.lse[:kf], workspace=self.ws_lm,
+                               in_norm=(sz, w.rms_eps))
         _lib.eagle_expand_rerank(_lib.EAGLE_EXPAND, self.pool_token, self.pool_parent,
                                  self.pool_depth, self.pool_value, self.pool_n[r], frontier=fr,
                                  child_id=self.ids[r], child_logp=self.logp[r], k_select=self.ks,
@@ -173,11 +191,12 @@ class DraftVerifyCycle:
                                    dev_status=self.status)
         _lib.eagle_embed(self.node_token, self.embed, out=self.vx, dev_status=self.status)
         _lib.eagle_rmsnorm(self.vx, self.target["norm1"], w.rms_eps, out=self.n1[:T])
-        self._layer(self.target, T, self.vx, self.node_depth, None, self.tkc, self.tvc, self.tkt,
-                    self.tvt, T, self.vmask, self.vout, None, self.target_norm)
+        sz = self._layer(self.target, T, self.n1[:T], None, self.vx, self.node_depth, None,
+                         self.tkc, self.tvc, self.tkt, self.tvt, T, self.vmask, self.vout, None,
+                         self.target_norm)
         _lib.eagle_lmhead_topk(self.z[:T], self.w_lm, self.k, topk_id=self.v_ids,
                                topk_logp=self.v_logp, lse=self.lse[:T], logits=self.v_logits,
-                               workspace=self.ws_lm)
+                               workspace=self.ws_lm, in_norm=(sz, w.rms_eps))
         _lib.eagle_accept(_lib.EAGLE_SAMPLE, self.node_token, self.node_parent,
                           target_logits=self.v_logits, temperature=self.temperature,
                           uniforms=self.uniforms, path=self.path, n_accepted=self.n_accepted,

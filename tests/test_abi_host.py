@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.eagle_abi_version() == 1
+    assert lib.eagle_abi_version() == 2
     for code in (0, -1, -2, -3, -4, 7):
         assert lib.eagle_status_string(code)
 
@@ -89,8 +89,8 @@ def test_attn_argument_errors(lib):
 
 def test_lmhead_argument_errors(lib):
     f = lib.eagle_lmhead_topk
-    base = [FAKE, FAKE, 4, 256, 1000, 10, _lib.EAGLE_BF16, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
-            None]
+    base = [FAKE, FAKE, 4, 256, 1000, 10, _lib.EAGLE_BF16, None, 0, 0.0, FAKE, FAKE, FAKE, None,
+            FAKE, 1 << 30, None]
 
     def call(**kw):
         a = list(base)
@@ -103,9 +103,11 @@ def test_lmhead_argument_errors(lib):
     assert call(a5=65) == EINVAL
     assert call(a4=5, a5=6) == EINVAL            # k > V
     assert call(a3=200) == EUNSUP                # d not a multiple of 128 (bf16)
-    assert call(a11=FAKE + 64) == EINVAL         # workspace not 256-aligned
-    assert call(a12=100) == EWS
+    assert call(a14=FAKE + 64) == EINVAL         # workspace not 256-aligned
+    assert call(a15=100) == EWS
     assert call(a6=9) == EINVAL
+    assert call(a7=FAKE, a8=0) == EINVAL         # deferred norm without partials
+    assert call(a7=FAKE, a8=4, a9=-1.0) == EINVAL
 
 
 def test_tree_argument_errors(lib):
@@ -139,6 +141,34 @@ def test_accept_argument_errors(lib):
              None) == EINVAL                                     # T > 256
     assert f(3, 5, FAKE, FAKE, FAKE, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
              None) == EINVAL
+
+
+def test_linear_argument_errors(lib):
+    # deferred rmsnorm: N % 4, missing outputs, misaligned xg_out, small workspace
+    f = lib.eagle_linear_rmsnorm_deferred
+    args = [FAKE, 10, 256, FAKE, 512, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a4=510) == EUNSUP
+    assert call(a8=None) == EINVAL
+    assert call(a8=FAKE + 2) == EINVAL
+    assert call(a11=16) == EWS
+    assert call(a2=200) == EUNSUP
+    # partial counts: one per 64 columns for few rows, one otherwise
+    assert lib.eagle_linear_norm_parts(10, 4096, 4096) == 64
+    assert lib.eagle_linear_norm_parts(16, 4096, 100) == 2
+    assert lib.eagle_linear_norm_parts(64, 4096, 4096) == 1
+    # consumers reject a deferred norm without partials
+    sw = lib.eagle_linear_swiglu
+    assert sw(FAKE, 10, 256, FAKE, 0, 1e-5, FAKE, FAKE, 512, FAKE, FAKE, 1 << 30, None) == EINVAL
+    rq = lib.eagle_linear_rope_qkv
+    assert rq(FAKE, 10, 256, FAKE, 0, 1e-5, FAKE, 4, 2, 64, FAKE, 0, 1e4, None, 16, FAKE, FAKE,
+              FAKE, 16, FAKE, 1 << 30, None, None) == EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -25,7 +25,8 @@ def rel_l2(a, b):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 128, 256), (10, 4096, 1000), (17, 512, 6144),
-                                   (64, 4096, 4096), (130, 256, 300)])
+                                   (64, 4096, 4096), (130, 256, 300), (16, 8192, 4096),
+                                   (3, 14336, 4096), (5, 384, 30), (12, 1024, 100)])
 def test_linear(dev, M, K, N):
     print(f"linear M={M} K={K} N={N}", flush=True)
     g = inputs.rng(700, M, N)
@@ -41,7 +42,8 @@ def test_linear(dev, M, K, N):
     assert np.all(np.abs(gb - ref) <= U * np.abs(ref) + 1e-4 * np.abs(ref).max())
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 256, 512), (10, 4096, 14336), (64, 512, 1000)])
+@pytest.mark.parametrize("M,K,N", [(1, 256, 512), (10, 4096, 14336), (64, 512, 1000),
+                                   (16, 384, 100), (7, 14336, 64)])
 def test_swiglu(dev, M, K, N):
     print(f"swiglu M={M} K={K} N={N}", flush=True)
     g = inputs.rng(701, M, N)
@@ -54,7 +56,9 @@ def test_swiglu(dev, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N,res", [(1, 8192, 4096, False), (10, 4096, 4096, True),
-                                       (64, 14336, 4096, True), (7, 256, 8192, True)])
+                                       (64, 14336, 4096, True), (7, 256, 8192, True),
+                                       (16, 14336, 4096, True), (1, 128, 256, False),
+                                       (10, 8192, 4096, True), (3, 512, 100, True)])
 def test_linear_rmsnorm(dev, M, K, N, res):
     print(f"linear_rmsnorm M={M} K={K} N={N}", flush=True)
     g = inputs.rng(707, M, K)
@@ -70,9 +74,13 @@ def test_linear_rmsnorm(dev, M, K, N, res):
     assert np.all(np.abs(nrm.float().cpu().numpy() - rn) <= U * np.abs(rn) + 1e-4 * np.abs(rn).max())
 
 
-def test_linear_rope_qkv(dev):
-    g = inputs.rng(708, 0)
-    M, K, hq, hkv, hd, cap, L = 10, 4096, 32, 8, 128, 51, 4096
+@pytest.mark.parametrize("M,K,hq,hkv,hd", [(10, 4096, 32, 8, 128), (16, 256, 4, 2, 64),
+                                           (20, 256, 4, 2, 64), (3, 256, 2, 1, 96),
+                                           (1, 512, 8, 2, 128)])
+def test_linear_rope_qkv(dev, M, K, hq, hkv, hd):
+    print(f"linear_rope_qkv M={M} K={K} hq={hq} hkv={hkv} hd={hd}", flush=True)
+    g = inputs.rng(708, M, hd)
+    cap, L = 51, 4096
     x = inputs.normal(g, (M, K))
     W = inputs.normal(g, ((hq + 2 * hkv) * hd, K), std=float(1 / np.sqrt(K)))
     depth = g.integers(0, 7, M).astype(np.int32)
@@ -95,6 +103,136 @@ def test_linear_rope_qkv(dev):
         assert np.all(np.abs(ktn[:, slots[m]] - rk[m]) <= U * np.abs(rk[m]) + 1e-4 * kmax)
         vr = qkv[m, hq + hkv:]
         assert np.all(np.abs(vtn[:, slots[m]] - vr) <= U * np.abs(vr) + 1e-4 * vmax)
+
+
+def bf16_round(a):
+    """fp32 -> bf16 -> fp32, round to nearest even (numpy)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+def deferred(dev, M, K, N, seed):
+    g = inputs.rng(seed, M, K * 100003 + N)
+    x = inputs.normal(g, (M, K))
+    W = inputs.normal(g, (N, K), std=float(1 / np.sqrt(K)))
+    res = inputs.normal(g, (M, N), dtype=torch.float32)
+    gamma = 1 + 0.1 * inputs.normal(g, (N,), dtype=torch.float32)
+    out, xg, ssq = _lib.eagle_linear_rmsnorm_deferred(x.to(dev), W.to(dev), gamma.to(dev),
+                                                      residual=res.to(dev))
+    torch.cuda.synchronize()
+    return x, W, res, gamma, out.cpu().numpy(), xg.float().cpu().numpy(), ssq.cpu().numpy()
+
+
+@pytest.mark.parametrize("M,K,N", [(10, 8192, 4096), (1, 4096, 4096), (16, 14336, 4096),
+                                   (3, 256, 100), (64, 4096, 4096), (17, 512, 256)])
+def test_linear_rmsnorm_deferred(dev, M, K, N):
+    """Producer: out = x W^T + residual; xg = bf16(out * gamma) exactly; the
+    partial sums of squares add up to sum out^2."""
+    print(f"linear_rmsnorm_deferred M={M} K={K} N={N}", flush=True)
+    x, W, res, gamma, out, xg, ssq = deferred(dev, M, K, N, 710)
+    ref = linear(x, W) + res.numpy()
+    assert np.abs(out - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-5
+    assert np.array_equal(xg, bf16_round(out * gamma.numpy()))
+    assert ssq.shape == (_lib.lib().eagle_linear_norm_parts(M, K, N), M)
+    want = (out.astype(np.float64) ** 2).sum(1)
+    np.testing.assert_allclose(ssq.astype(np.float64).sum(0), want, rtol=1e-5)
+
+
+def row_scale(out, eps=1e-5):
+    return 1.0 / np.sqrt((out.astype(np.float64) ** 2).mean(1) + eps)
+
+
+@pytest.mark.parametrize("M,K,N", [(10, 4096, 14336), (64, 512, 1000), (1, 256, 512)])
+def test_swiglu_deferred_norm(dev, M, K, N):
+    """Consumer: silu(r x W_g^T) * (r x W_u^T) with the row scale r taken from
+    the producer's partial sums; compared on the producer's own bf16 rows."""
+    print(f"swiglu deferred M={M} K={K} N={N}", flush=True)
+    _, _, _, _, out, xg, ssq = deferred(dev, M, 256, K, 711)
+    g = inputs.rng(712, M, N)
+    wg = inputs.normal(g, (N, K), std=float(1 / np.sqrt(K)))
+    wu = inputs.normal(g, (N, K), std=float(1 / np.sqrt(K)))
+    xgt = torch.from_numpy(xg).to(torch.bfloat16)
+    got = _lib.eagle_linear_swiglu(xgt.to(dev), wg.to(dev), wu.to(dev),
+                                   in_norm=(torch.from_numpy(ssq).to(dev), 1e-5)).float().cpu().numpy()
+    r = row_scale(out)[:, None]
+    gt, up = r * linear(xgt, wg), r * linear(xgt, wu)
+    ref = gt / (1 + np.exp(-gt)) * up
+    assert np.all(np.abs(got - ref) <= U * np.abs(ref) + 1e-4 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("M,hd", [(10, 128), (20, 64)])
+def test_rope_qkv_deferred_norm(dev, M, hd):
+    print(f"rope deferred M={M} hd={hd}", flush=True)
+    hq, hkv, cap, L = 4, 2, 40, 4096
+    N = (hq + 2 * hkv) * hd
+    _, _, _, _, out, xg, ssq = deferred(dev, M, 256, 512, 713)
+    g = inputs.rng(714, M, hd)
+    W = inputs.normal(g, (N, 512), std=float(1 / np.sqrt(512)))
+    depth = g.integers(0, 7, M).astype(np.int32)
+    slots = g.choice(cap, M, replace=False).astype(np.int32)
+    kt = torch.zeros((hkv, cap, hd), dtype=torch.bfloat16, device=dev)
+    vt = torch.zeros_like(kt)
+    xgt = torch.from_numpy(xg).to(torch.bfloat16)
+    q = _lib.eagle_linear_rope_qkv(xgt.to(dev), W.to(dev), hq, hkv, hd,
+                                   torch.from_numpy(depth).to(dev), L, kt, vt,
+                                   row_slot=torch.from_numpy(slots).to(dev),
+                                   in_norm=(torch.from_numpy(ssq).to(dev), 1e-5))
+    qkv = (row_scale(out)[:, None] * linear(xgt, W)).reshape(M, hq + 2 * hkv, hd)
+    rq = oracle.rope(qkv[:, :hq], L + depth)
+    assert np.all(np.abs(q.float().cpu().numpy() - rq) <= U * np.abs(rq) + 1e-4 * np.abs(rq).max())
+    rk = oracle.rope(qkv[:, hq:hq + hkv], L + depth)
+    ktn = kt.float().cpu().numpy()
+    for m in range(M):
+        assert np.all(np.abs(ktn[:, slots[m]] - rk[m]) <= U * np.abs(rk[m]) + 1e-4 * np.abs(rk).max())
+
+
+@pytest.mark.parametrize("T,V,k", [(10, 20000, 10), (64, 5000, 10), (1, 3000, 4)])
+def test_lmhead_deferred_norm(dev, T, V, k):
+    """LM head on deferred-norm rows: logits = r (xg W^T), top-k and lse of
+    those logits."""
+    print(f"lmhead deferred T={T} V={V}", flush=True)
+    d = 512
+    _, _, _, _, out, xg, ssq = deferred(dev, T, 256, d, 715)
+    g = inputs.rng(716, T, V)
+    W = inputs.normal(g, (V, d), std=float(1 / np.sqrt(d)))
+    xgt = torch.from_numpy(xg).to(torch.bfloat16)
+    ids, logp, lse, lg = _lib.eagle_lmhead_topk(xgt.to(dev), W.to(dev), k, want_logits=True,
+                                                in_norm=(torch.from_numpy(ssq).to(dev), 1e-5))
+    torch.cuda.synchronize()
+    ref = row_scale(out)[:, None] * oracle.lm_head_logits(xgt, W)
+    lg = lg.cpu().numpy()
+    assert np.abs(lg - ref).max() <= 1e-4 * np.abs(ref).max() + 1e-5
+    assert np.array_equal(ids.cpu().numpy(), oracle.topk_ids(lg, k))
+    _, _, rlse = oracle.softmax_stats(ref)
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= 1e-3
+
+
+def test_shared_workspace_reuse(dev):
+    """One zeroed workspace serves a sequence of few-row projections of
+    different shapes (and a many-row one); each result matches a fresh call and
+    the counter area is zero again afterwards."""
+    g = inputs.rng(709, 0)
+    shapes = [(10, 8192, 4096), (10, 4096, 4096), (1, 14336, 4096), (64, 4096, 4096),
+              (16, 4096, 6144), (10, 8192, 4096)]
+    nb = max(_lib.lib().eagle_linear_rows_workspace(M, K, N) for M, K, N in shapes)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        for (M, K, N) in shapes:
+            print(f"shared ws rep={rep} M={M} K={K} N={N}", flush=True)
+            x = inputs.normal(g, (M, K)).to(dev)
+            W = inputs.normal(g, (N, K), std=float(1 / np.sqrt(K))).to(dev)
+            gamma = (1 + 0.1 * inputs.normal(g, (N,), dtype=torch.float32)).to(dev)
+            res = inputs.normal(g, (M, N), dtype=torch.float32).to(dev)
+            o1, n1 = _lib.eagle_linear_rmsnorm(x, W, gamma, residual=res, workspace=ws)
+            o2, n2 = _lib.eagle_linear_rmsnorm(x, W, gamma, residual=res)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(n1, n2)
+            y1 = _lib.eagle_linear(x, W, workspace=ws)
+            y2 = _lib.eagle_linear(x, W)
+            assert torch.equal(y1, y2)
+    torch.cuda.synchronize()
+    assert int(ws[:65536].count_nonzero().item()) == 0
 
 
 def test_rmsnorm(dev):
@@ -200,8 +338,8 @@ def layer_case(dev, w, seed, n, Tk, slots, slot_par):
     sl = torch.from_numpy(slots.astype(np.int32)).to(dev)
     lwd = {k: v.to(dev) for k, v in lw.items()}
     _lib.eagle_rmsnorm(x.to(dev), lwd["norm1"], w.rms_eps, out=cyc.n1[:n])
-    cyc._layer(lwd, n, x.to(dev), torch.from_numpy(depth).to(dev), sl, cyc.dkc, cyc.dvc, kt, vt,
-               Tk, mask, out, sl, cyc.draft_norm)
+    cyc._layer(lwd, n, cyc.n1[:n], None, x.to(dev), torch.from_numpy(depth).to(dev), sl, cyc.dkc,
+               cyc.dvc, kt, vt, Tk, mask, out, sl, cyc.draft_norm)
     torch.cuda.synchronize()
     assert int(cyc.status.item()) == 0
     nq = w.hq * w.hd
