@@ -15,6 +15,7 @@ launch stream) and the CPU oracle's throughput on the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +36,27 @@ from speculative_decoding_parent_amd.cycle import DraftVerifyCycle  # noqa: E402
 
 METRIC = "tree-verify nodes/s + KV/LM-head HBM GB/s (% roofline), Llama-3-8B shape"
 HBM_PEAK_GBS = 8000.0
+
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "speculative_decoding_parent_amd",
+                    "csrc")
+
+
+def measured_traffic(key, sources):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/
+    hbm_traffic.json), or None when the kernel sources have changed since."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int(round(rec["fetch_bytes"] + rec["write_bytes"]))
 
 
 def lmhead_bytes(T, d, V, k):
@@ -118,7 +140,9 @@ def long_context_verify(dev, steps):
             "roofline": {"kernel": "eagle_tree_attn (tree_attn_bf16_kernel + attn_merge_kernel), "
                                    "one layer", "bound": "hbm", "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("eagle_tree_attn_c4_layer_L32768_T64",
+                                                     ["attn.hip", "common.h"]),
                          "avg_us": round(per * 1e6, 2), "bytes_per_launch": nb}}
 
 
@@ -216,7 +240,9 @@ def main():
         "roofline": {"kernel": "eagle_lmhead_topk (lmhead_bf16_kernel + lmhead_merge_kernel), "
                                f"T={Td}, d={w.d}, V={w.vocab}, k={w.topk}",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("eagle_lmhead_topk_T10_d4096_V128256_k10",
+                                                 ["lmhead.hip", "wstream.h", "common.h"]),
                      "avg_us": round(avg_s * 1e6, 2), "min_us": round(min_s * 1e6, 2),
                      "bytes_per_launch": nbytes},
     }

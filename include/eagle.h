@@ -20,7 +20,9 @@
  *     all memory; the library never allocates, frees or keeps a pointer after
  *     the call returns.  Workspaces are caller-provided scratch whose size the
  *     matching *_workspace() query returns; their contents need no
- *     initialisation and are garbage afterwards.
+ *     initialisation and are garbage afterwards, except the projection
+ *     workspaces, whose first 64 KiB hold counters that must start at zero
+ *     and are left at zero (decoder-layer section).
  *   - Single sequence (batch 1), as [P] "Implementation Characteristics"
  *     states.
  *   - Arguments are validated on the host before anything is enqueued; a bad
