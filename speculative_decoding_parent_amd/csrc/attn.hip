@@ -7,7 +7,7 @@
 // 128 dims.
 //
 // bf16 path, one workgroup = (KV head g, one slice of the positions, one group
-// of <= 64 NTW query rows).  The query rows of a KV head are all (node i, head
+// of 16 NTW NW query rows).  The query rows of a KV head are all (node i, head
 // h) pairs with h / G = g, so every K/V tile fetched from HBM serves the G
 // heads that share it (GQA) and all tree nodes at once.  The prefix is cut
 // into splits of whole 64-position tiles; the tree is one more split, masked
@@ -30,14 +30,13 @@
 //                 lane (g, r16) at V[4g + r16/4][4 (r16 mod 4)] of a 16-dim
 //                 slice gives it V[4g + j][r16] for j < 4, i.e. four positions
 //                 of one head dim, in the permuted k order.
-// K and V of the next tile are fetched into registers (16-byte loads,
-// coalesced along the head dimension) while the current tile computes.
+// K and V tiles are fetched two ahead into registers (16-byte loads, coalesced
+// along the head dimension) and double-buffered in LDS, one barrier per tile.
+// The running max is raised lazily (see the softmax step).
 //
 // fp32 path (small workloads): one workgroup per (query row, head, split)
 // computes the scores into LDS in fp32 and reduces them directly; same
 // partial layout and merge.
-#include <type_traits>
-
 #include "common.h"
 
 namespace eagle {
@@ -62,8 +61,8 @@ struct AttnParams {
   float c;               // scale * log2(e)
   int n_split;           // prefix splits; split index n_split is the tree
   int tiles_per_split;
-  float* part_o;         // [n_split + 1][Tq * Hq][HD]
-  float2* part_ml;       // [n_split + 1][Tq * Hq]
+  void* part_o;          // [n_split + 1][Tq * Hq][HD]: bf16 O / l (bf16 path), fp32 O (fp32 path)
+  float2* part_ml;       // [n_split + 1][Tq * Hq] (running max, sum of weights)
   int32_t* status;
 };
 
@@ -92,8 +91,8 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
   constexpr int VS = HD + 16;
   constexpr int CPR = HD / 8;
   constexpr int NCH = kAtTile * CPR / NTH;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kAtTile * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[kAtTile * VS];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kAtTile * KS];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][kAtTile * VS];
 
   const int split = blockIdx.x;
   const int gkv = blockIdx.y;
@@ -158,8 +157,10 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     for (int mv = 0; mv < MTV; ++mv) o[mv][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  u32x4 kr[NCH], vr[NCH];
-  auto load_tile = [&](int t) {
+  // K/V tiles go HBM -> registers (two stages: up to two tiles in flight, each
+  // with two tile-times to arrive) -> LDS (two buffers: one barrier per tile).
+  u32x4 kr0[NCH], vr0[NCH], kr1[NCH], vr1[NCH];
+  auto load_tile = [&](int t, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = tid + NTH * j;
@@ -172,125 +173,152 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
       vr[j] = ok ? *(const u32x4*)(vb_ptr + off) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf, const u32x4 (&kr)[NCH], const u32x4 (&vr)[NCH])
+                        __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
       const int c = tid + NTH * j;
       const int pr = c / CPR;
       const int cc = c - pr * CPR;
-      *(u32x4*)(&Ks[pr * KS + cc * 8]) = kr[j];
-      *(u32x4*)(&Vs[pr * VS + cc * 8]) = vr[j];
+      *(u32x4*)(&Ks[buf][pr * KS + cc * 8]) = kr[j];
+      *(u32x4*)(&Vs[buf][pr * VS + cc * 8]) = vr[j];
     }
   };
 
-  // The prefix and tree slices run separate copies of the tile loop, so the
-  // prefix loop issues no mask loads (and no wait on them) while the next
-  // tile's K/V are in flight.
-  auto run_tiles = [&](auto tree_tag) {
-    constexpr bool TREE = decltype(tree_tag)::value;
-    if (ntiles > 0) load_tile(0);
-    for (int t = 0; t < ntiles; ++t) {
-      __syncthreads();
-      store_tile();
-      __syncthreads();
-      if (t + 1 < ntiles) load_tile(t + 1);
-
-      // S^T = K Q^T over 4 position tiles of 16
-      f32x4 s[4][NTW];
+  // One 64-position tile from LDS buffer `buf` (one instance for both kinds of
+  // slice: the mask is read only on tree tiles and the last, partial tile).
+  auto tile = [&](int t, int buf) __attribute__((always_inline)) {
+    const bool TREE = is_tree;
+    const bf16_t* Kb = Ks[buf];
+    const bf16_t* Vb = Vs[buf];
+    // S^T = K Q^T over 4 position tiles of 16
+    f32x4 s[4][NTW];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NTW; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const bf16x8 a = *(const bf16x8*)(&Ks[(mt * 16 + r16) * KS + kb * 32 + 8 * g]);
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 a = *(const bf16x8*)(&Kb[(mt * 16 + r16) * KS + kb * 32 + 8 * g]);
 #pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-            s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[nt][kb]),
-                                                                s[mt][nt], 0, 0, 0);
-        }
+        for (int nt = 0; nt < NTW; ++nt)
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[nt][kb]),
+                                                              s[mt][nt], 0, 0, 0);
       }
+    }
 
-      // visibility: positions past the slice end, and non-ancestors in the tree
-      const int tile_pos = t * kAtTile;
-      if (TREE || tile_pos + kAtTile > npos) {
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          uint64_t bits = ~0ull;
-          if (TREE) bits = mrow[nt] >= 0 ? p.mask[(size_t)mrow[nt] * p.words + t] : 0ull;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int pl = mt * 16 + 4 * g + j;
-              if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
-            }
-        }
-      }
-
-      // online softmax in the exp2 domain (arguments <= 0: the native v_exp_f32
-      // is exact enough and flushes only values below 2^-126) and P^T packing
-      u32x4 pb[2][NTW];
+    // visibility: positions past the slice end, and non-ancestors in the tree
+    const int tile_pos = t * kAtTile;
+    if (TREE || tile_pos + kAtTile > npos) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[mt][nt][j]);
-        mx = rows_max(mx);
-        const float mnew = fmaxf(m[nt], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m[nt] - mnew) * p.c);
-        m[nt] = mnew;
-        const float nmc = -mnew * p.c;
-        float ps = 0.f;
+        uint64_t bits = ~0ull;
+        if (TREE) bits = mrow[nt] >= 0 ? p.mask[(size_t)mrow[nt] * p.words + t] : 0ull;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][j], p.c, nmc));
-            s[mt][nt][j] = pv;
-            ps += pv;
+            const int pl = mt * 16 + 4 * g + j;
+            if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
           }
-        l[nt] = fmaf(l[nt], alpha, ps);
+      }
+    }
+
+    // Online softmax in the exp2 domain with a lazily raised running max: m
+    // only moves when the tile's max exceeds it by more than 2^8 (in exp2
+    // units), so weights stay <= 2^8 and m, l and O always share the same
+    // reference (exact); after the first tile the rescale is almost never
+    // taken.  exp2 arguments are <= 8: the native v_exp_f32 is exact enough.
+    float mx[NTW];
+    bool up_any = false;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v = fmaxf(v, s[mt][nt][j]);
+      mx[nt] = rows_max(v);
+      up_any |= (mx[nt] - m[nt]) * p.c > 8.0f;
+    }
+    if (__builtin_amdgcn_ballot_w64(up_any)) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const bool up = (mx[nt] - m[nt]) * p.c > 8.0f;
+        const float alpha = up ? __builtin_amdgcn_exp2f((m[nt] - mx[nt]) * p.c) : 1.0f;
+        m[nt] = up ? mx[nt] : m[nt];
+        l[nt] *= alpha;
 #pragma unroll
         for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-          pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
-                              pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
-                              pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
-                              pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
-        }
       }
-
-      // O^T += V^T P^T
+    }
+    u32x4 pb[2][NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const float nmc = -m[nt] * p.c;
+      float ps = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][j], p.c, nmc));
+          s[mt][nt][j] = pv;
+          ps += pv;
+        }
+      l[nt] += ps;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
+        pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
+                            pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
+                            pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
+                            pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
+      }
+    }
+
+    // O^T += V^T P^T
 #pragma unroll
-        for (int mv = 0; mv < MTV; ++mv) {
-          // k slots 0-3: positions 32 kb2 + 4 g + j; slots 4-7: 16 further
-          const bf16_t* vp =
-              &Vs[(kb2 * 32 + 4 * g + (r16 >> 2)) * VS + mv * 16 + 4 * (r16 & 3)];
-          const u32x2 lo = lds_read_tr16(vp);
-          const u32x2 hi = lds_read_tr16(vp + 16 * VS);
-          const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
-          for (int nt = 0; nt < NTW; ++nt)
-            o[mv][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kb2][nt]),
-                                                                o[mv][nt], 0, 0, 0);
-        }
+      for (int mv = 0; mv < MTV; ++mv) {
+        // k slots 0-3: positions 32 kb2 + 4 g + j; slots 4-7: 16 further
+        const bf16_t* vp = &Vb[(kb2 * 32 + 4 * g + (r16 >> 2)) * VS + mv * 16 + 4 * (r16 & 3)];
+        const u32x2 lo = lds_read_tr16(vp);
+        const u32x2 hi = lds_read_tr16(vp + 16 * VS);
+        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          o[mv][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kb2][nt]),
+                                                              o[mv][nt], 0, 0, 0);
       }
     }
   };
-  if (is_tree)
-    run_tiles(std::true_type{});
-  else
-    run_tiles(std::false_type{});
 
-  // partials: lane (g, r16) holds O^T[hd = 16 mv + 4 g + j][row 16 nt + r16]
+  auto run_tiles = [&]() __attribute__((always_inline)) {
+    if (ntiles > 0) load_tile(0, kr0, vr0);
+    if (ntiles > 1) load_tile(1, kr1, vr1);
+    if (ntiles > 0) store_tile(0, kr0, vr0);
+    if (ntiles > 2) load_tile(2, kr0, vr0);
+    __syncthreads();
+#pragma clang loop unroll(disable)
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(t, 0);
+      if (t + 1 < ntiles) store_tile(1, kr1, vr1);
+      if (t + 3 < ntiles) load_tile(t + 3, kr1, vr1);
+      __syncthreads();
+      if (t + 1 >= ntiles) break;
+      tile(t + 1, 1);
+      if (t + 2 < ntiles) store_tile(0, kr0, vr0);
+      if (t + 4 < ntiles) load_tile(t + 4, kr0, vr0);
+      __syncthreads();
+    }
+  };
+  run_tiles();
+
+  // partials: lane (g, r16) holds O^T[hd = 16 mv + 4 g + j][row 16 nt + r16];
+  // stored as O / l in bf16 (a convex combination of V rows: V's range, and a
+  // rounding of 2^-9 relative, below the output's own bf16 rounding)
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     float lt = l[nt];
@@ -298,9 +326,13 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     if (!valid[nt]) continue;
     const size_t prow = (size_t)split * RT + grow[nt];
     if (g == 0) p.part_ml[prow] = make_float2(m[nt], lt);
-    float* po = p.part_o + prow * HD;
+    const float il = lt > 0.f ? 1.0f / lt : 0.f;
+    bf16_t* po = (bf16_t*)p.part_o + prow * HD;
 #pragma unroll
-    for (int mv = 0; mv < MTV; ++mv) *(f32x4*)(po + mv * 16 + 4 * g) = o[mv][nt];
+    for (int mv = 0; mv < MTV; ++mv) {
+      const f32x4 v = o[mv][nt] * il;
+      *(u32x2*)(po + mv * 16 + 4 * g) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
   }
 }
 
@@ -372,17 +404,20 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnParams p, int hd
   for (int d = threadIdx.x; d < hd; d += 256) {
     float a = 0.f;
     for (int j = 0; j < npos; ++j) a = fmaf(sc[j], vp[(size_t)j * hd + d], a);
-    p.part_o[prow * hd + d] = a;
+    ((float*)p.part_o)[prow * hd + d] = a;
   }
   if (threadIdx.x == 0) p.part_ml[prow] = make_float2(M, lt);
 }
 
-// Combine the splits of each (query row, head): out = sum_s w_s O_s / sum_s w_s l_s
-// with w_s = exp2((m_s - M) c).  The split weights are formed once per row in
-// LDS; each thread then sums one head-dim element over the splits.
+// Combine the splits of each (query row, head).  With w_s = exp2((m_s - M) c):
+// out = sum_s w_s O_s / sum_s w_s l_s.  The bf16 path stores o_s = O_s / l_s
+// (so O_s = l_s o_s), the fp32 path O_s itself.  The split weights are formed
+// once per row in LDS; each thread then sums one head-dim element over the
+// splits.
 constexpr int kMergeSplits = 1024;
 
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
+template <bool NORMED_BF16>
+__global__ __launch_bounds__(128) void attn_merge_kernel(const void* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          int nsplit, int RT, int hd, float c,
                                                          void* out, int out_bf16) {
@@ -396,20 +431,28 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
   __syncthreads();
   M = fmaxf(red[0], red[1]);
-  float den = 0.f;
   for (int s = threadIdx.x; s < nsplit; s += blockDim.x) {
     const float2 ml = part_ml[(size_t)s * RT + row];
     const float w = exp2f((ml.x - M) * c);
-    wsh[s] = w;
+    wsh[s] = NORMED_BF16 ? w * ml.y : w;
   }
   __syncthreads();
-  for (int s = 0; s < nsplit; ++s) den = fmaf(part_ml[(size_t)s * RT + row].y, wsh[s], den);
-  const float inv = 1.0f / den;
+  float den = 0.f;
+  for (int s = 0; s < nsplit; ++s)
+    den = NORMED_BF16 ? den + wsh[s] : fmaf(part_ml[(size_t)s * RT + row].y, wsh[s], den);
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
   for (int d = threadIdx.x; d < hd; d += blockDim.x) {
     float num = 0.f;
-    const float* po = part_o + (size_t)row * hd + d;
+    if (NORMED_BF16) {
+      const bf16_t* po = (const bf16_t*)part_o + (size_t)row * hd + d;
 #pragma unroll 4
-    for (int s = 0; s < nsplit; ++s) num = fmaf(po[(size_t)s * RT * hd], wsh[s], num);
+      for (int s = 0; s < nsplit; ++s)
+        num = fmaf(bf16_bits_to_f32(po[(size_t)s * RT * hd]), wsh[s], num);
+    } else {
+      const float* po = (const float*)part_o + (size_t)row * hd + d;
+#pragma unroll 4
+      for (int s = 0; s < nsplit; ++s) num = fmaf(po[(size_t)s * RT * hd], wsh[s], num);
+    }
     const float v = num * inv;
     if (out_bf16)
       ((bf16_t*)out)[(size_t)row * hd + d] = (bf16_t)f32_to_bf16_bits(v);
@@ -459,7 +502,7 @@ static AttnPlan attn_plan(int Tq, int Hq, int Hkv, int hd, int64_t L, eagle_dtyp
   const size_t RT = (size_t)Tq * Hq;
   const size_t ns = (size_t)pl.n_split + 1;
   pl.o_off = 0;
-  pl.ml_off = align256(ns * RT * hd * sizeof(float));
+  pl.ml_off = align256(ns * RT * hd * (dt == EAGLE_BF16 ? sizeof(bf16_t) : sizeof(float)));
   pl.total = pl.ml_off + align256(ns * RT * sizeof(float2));
   return pl;
 }
@@ -525,7 +568,7 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
   p.c = scale * kLog2e;
   p.n_split = pl.n_split;
   p.tiles_per_split = pl.tiles_per_split;
-  p.part_o = (float*)(ws + pl.o_off);
+  p.part_o = ws + pl.o_off;
   p.part_ml = (float2*)(ws + pl.ml_off);
   p.status = dev_status;
   if (in_dt == EAGLE_BF16) {
@@ -544,8 +587,14 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
                        p, hd);
   }
   EAGLE_LAUNCH_CHECK();
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(Tq * Hq), dim3(128), 0, stream, p.part_o, p.part_ml,
-                     pl.n_split + 1, Tq * Hq, hd, p.c, out, out_dt == EAGLE_BF16 ? 1 : 0);
+  if (in_dt == EAGLE_BF16)
+    hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(Tq * Hq), dim3(128), 0, stream, p.part_o,
+                       p.part_ml, pl.n_split + 1, Tq * Hq, hd, p.c, out,
+                       out_dt == EAGLE_BF16 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(Tq * Hq), dim3(128), 0, stream, p.part_o,
+                       p.part_ml, pl.n_split + 1, Tq * Hq, hd, p.c, out,
+                       out_dt == EAGLE_BF16 ? 1 : 0);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }
