@@ -158,10 +158,13 @@ int eagle_tree_attn(const void* q,
  *            deferred (in_ssq [in_parts][T] f32 or NULL, in_eps; see the
  *            decoder-layer section).
  *   W        [V][d] dt, one row per vocabulary entry.
- *   T 1..256, d % 128 == 0 (bf16) or any d >= 1 (f32), 1 <= k <= min(V, 64).
+ *   T 1..256, d % 128 == 0 (bf16) or any d >= 1 (f32), 0 <= k <= min(V, 64);
+ *            k = 0 computes lse (and logits) only, e.g. for sampling
+ *            acceptance, which reads the logits.
  *   topk_id  int32[T][k] out: the k largest logits of row t, larger first,
- *            the lower vocabulary index first among equal logits.
- *   topk_logp f32[T][k] out: logit - lse (temperature 1).
+ *            the lower vocabulary index first among equal logits (NULL when
+ *            k = 0).
+ *   topk_logp f32[T][k] out: logit - lse (temperature 1) (NULL when k = 0).
  *   lse      f32[T] out: log sum_v exp(logit[t][v]).
  *   logits   f32[T][V] out, or NULL: the fp32 logits.
  *   workspace >= eagle_lmhead_topk_workspace(...) bytes, 256-byte aligned.

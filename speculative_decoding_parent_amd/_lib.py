@@ -186,13 +186,15 @@ def _norm_args(in_norm):
 
 def eagle_lmhead_topk(f, W, k, want_logits=False, topk_id=None, topk_logp=None, lse=None,
                       logits=None, workspace=None, in_norm=None):
-    """Returns (topk_id int32[T][k], topk_logp f32[T][k], lse f32[T], logits or None)."""
+    """Returns (topk_id int32[T][k], topk_logp f32[T][k], lse f32[T], logits or None);
+    k = 0 computes lse (and logits) only and returns None for the top-k."""
     T, d = f.shape
     V = W.shape[0]
     dt = _dt(f)
     dev = f.device
-    topk_id = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_id is None else topk_id
-    topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_logp is None else topk_logp
+    if k > 0:
+        topk_id = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_id is None else topk_id
+        topk_logp = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_logp is None else topk_logp
     lse = torch.empty(T, dtype=torch.float32, device=dev) if lse is None else lse
     if want_logits and logits is None:
         logits = torch.empty((T, V), dtype=torch.float32, device=dev)

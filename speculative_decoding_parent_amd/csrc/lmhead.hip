@@ -111,20 +111,56 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
   const int V = p.V;
   const int wglob = blockIdx.x * kLmWaves + wave;
   if (p.logits) {
+    // With at most 2 tiles per wave the workgroup's [16 NT][rows] fp32 tile
+    // fits the staging buffer: it goes through LDS so that every store writes
+    // whole 16-byte pieces of contiguous row segments (RB floats per row);
+    // otherwise lanes store their 4-logit pieces directly.
+    constexpr int RB = kLmRowsBlock;
+    constexpr int RBP = RB + 4;     // padded LDS row
+    constexpr bool kStage = 16 * NT * RBP * 4 <= ws_lds_elems<NT>() * 2;
+    if (kStage) {
+      float* lt = (float*)fs;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int t = nt * 16 + r16;
-      if (t >= T) continue;
-      float* out = p.logits + (size_t)t * V;
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < kLmMT; ++mt) {
-        const int vb = v0 + mt * 16 + 4 * g;
-        if ((V & 3) == 0 && vb + 3 < V) {
-          *(f32x4*)(out + vb) = acc[mt][nt];
+        for (int mt = 0; mt < kLmMT; ++mt)
+          *(f32x4*)(lt + (nt * 16 + r16) * RBP + wave * kLmRowsWave + mt * 16 + 4 * g) =
+              acc[mt][nt];
+      __syncthreads();
+      const int vblk = blockIdx.x * RB;
+      const bool vec = (V & 3) == 0;
+      for (int e = tid; e < 16 * NT * (RB / 4); e += 256) {
+        const int t = e / (RB / 4);
+        const int c = e - t * (RB / 4);
+        const int v = vblk + 4 * c;
+        if (t >= T || v >= V) continue;
+        const f32x4 x = *(const f32x4*)(lt + t * RBP + 4 * c);
+        float* out = p.logits + (size_t)t * V + v;
+        if (vec && v + 3 < V) {
+          *(f32x4*)out = x;
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (vb + j < V) out[vb + j] = acc[mt][nt][j];
+            if (v + j < V) out[j] = x[j];
+        }
+      }
+      __syncthreads();   // the staging buffer is reused below
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int t = nt * 16 + r16;
+        if (t >= T) continue;
+        float* out = p.logits + (size_t)t * V;
+#pragma unroll
+        for (int mt = 0; mt < kLmMT; ++mt) {
+          const int vb = v0 + mt * 16 + 4 * g;
+          if ((V & 3) == 0 && vb + 3 < V) {
+            *(f32x4*)(out + vb) = acc[mt][nt];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (vb + j < V) out[vb + j] = acc[mt][nt][j];
+          }
         }
       }
     }
@@ -467,7 +503,7 @@ static void launch_lm(const LmParams& p, hipStream_t s) {
 extern "C" size_t eagle_lmhead_topk_workspace(int32_t T, int32_t d, int32_t V, int32_t k,
                                               eagle_dtype dt) {
   (void)d;
-  if (T < 1 || V < 1 || k < 1) return 0;
+  if (T < 1 || V < 1 || k < 0) return 0;
   return eagle::lm_layout(T, V, k, dt).total;
 }
 
@@ -477,11 +513,11 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
                                  float* logits, void* workspace, size_t ws_bytes,
                                  hipStream_t stream) {
   using namespace eagle;
-  EAGLE_REQUIRE(f && W && topk_id && topk_logp && lse && workspace, EAGLE_EINVAL);
+  EAGLE_REQUIRE(f && W && lse && workspace && (k == 0 || (topk_id && topk_logp)), EAGLE_EINVAL);
   EAGLE_REQUIRE(!in_ssq || (in_parts >= 1 && in_eps >= 0.0f), EAGLE_EINVAL);
   const RowNorm rn{in_ssq, in_ssq ? in_parts : 0, d, in_eps};
   EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && d >= 1 && V >= 1, EAGLE_EINVAL);
-  EAGLE_REQUIRE(k >= 1 && k <= EAGLE_MAX_TOPK && k <= V, EAGLE_EINVAL);
+  EAGLE_REQUIRE(k >= 0 && k <= EAGLE_MAX_TOPK && k <= V, EAGLE_EINVAL);
   EAGLE_REQUIRE(((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
   const LmLayout l = lm_layout(T, V, k, dt);
   EAGLE_REQUIRE(ws_bytes >= l.total, EAGLE_EWORKSPACE);

@@ -96,8 +96,6 @@ class DraftVerifyCycle:
         self.vout = torch.zeros((T, d), **f32)
         self.tkt = torch.zeros((hkv, T, hd), **bf)
         self.tvt = torch.zeros((hkv, T, hd), **bf)
-        self.v_ids = torch.zeros((T, k), **i32)
-        self.v_logp = torch.zeros((T, k), **f32)
         self.v_logits = torch.zeros((T, V), **f32)
         self.path = torch.zeros(T, **i32)
         self.n_accepted = torch.zeros(1, **i32)
@@ -194,8 +192,8 @@ class DraftVerifyCycle:
         sz = self._layer(self.target, T, self.n1[:T], None, self.vx, self.node_depth, None,
                          self.tkc, self.tvc, self.tkt, self.tvt, T, self.vmask, self.vout, None,
                          self.target_norm)
-        _lib.eagle_lmhead_topk(self.z[:T], self.w_lm, self.k, topk_id=self.v_ids,
-                               topk_logp=self.v_logp, lse=self.lse[:T], logits=self.v_logits,
+        # sampling acceptance reads the logits; no top-k is needed (k = 0)
+        _lib.eagle_lmhead_topk(self.z[:T], self.w_lm, 0, lse=self.lse[:T], logits=self.v_logits,
                                workspace=self.ws_lm, in_norm=(sz, w.rms_eps))
         _lib.eagle_accept(_lib.EAGLE_SAMPLE, self.node_token, self.node_parent,
                           target_logits=self.v_logits, temperature=self.temperature,

@@ -100,7 +100,8 @@ def test_lmhead_argument_errors(lib):
         return f(*a)
 
     assert call(a0=None) == EINVAL
-    assert call(a5=0) == EINVAL
+    assert call(a5=-1) == EINVAL
+    assert call(a5=3, a10=None) == EINVAL        # k > 0 needs them
     assert call(a5=65) == EINVAL
     assert call(a4=5, a5=6) == EINVAL            # k > V
     assert call(a3=200) == EUNSUP                # d not a multiple of 128 (bf16)

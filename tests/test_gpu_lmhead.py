@@ -78,6 +78,22 @@ def test_exact_inputs_with_planted_ties(dev, dt):
     assert np.array_equal(lg.astype(np.float64), oracle.lm_head_logits(f, W))
 
 
+@pytest.mark.parametrize("T,d,V", [(64, 512, 5000), (10, 256, 3001), (1, 128, 300)])
+def test_lse_and_logits_only(dev, T, d, V):
+    """k = 0: no top-k, lse and logits as with k > 0."""
+    g = inputs.rng(404, T, V)
+    f = inputs.normal(g, (T, d))
+    W = inputs.normal(g, (V, d), std=float(1 / np.sqrt(d)))
+    print(f"lmhead k=0 T={T} d={d} V={V}", flush=True)
+    ids, logp, lse, lg = _lib.eagle_lmhead_topk(f.to(dev), W.to(dev), 0, want_logits=True)
+    torch.cuda.synchronize()
+    assert ids is None and logp is None
+    ref = oracle.lm_head_logits(f, W)
+    assert np.abs(lg.cpu().numpy() - ref).max() <= 5e-2
+    _, _, rlse = oracle.softmax_stats(ref)
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= 1e-3
+
+
 def test_confidence_ratio(dev):
     g = inputs.rng(403, 0)
     f = inputs.normal(g, (8, 256))
