@@ -881,6 +881,14 @@ static RowNorm row_norm(const float* ssq, int parts, int n, float eps) {
 
 static float* lin_partials(void* ws) { return (float*)((char*)ws + kSkCounterBytes); }
 
+// lin_ksplit sizes the split from lin_mt((M + 15) / 16, ...) while the
+// launches below round the row tiles up to 1, 2, 4, 8 or 16: both give the
+// same W tiles for every M.
+static_assert(lin_mt(3, 0) == lin_mt(4, 0) && lin_mt(5, 0) == lin_mt(8, 0) &&
+                  lin_mt(9, 0) == lin_mt(16, 0) && lin_mt(3, 1) == lin_mt(4, 1) &&
+                  lin_mt(5, 1) == lin_mt(8, 1) && lin_mt(9, 1) == lin_mt(16, 1),
+              "row-tile buckets must not change the W tiling");
+
 template <int NT, int SWIGLU>
 static void launch_lin(const LinParams& p, hipStream_t s) {
   constexpr int MT = lin_mt(NT, SWIGLU);

@@ -39,9 +39,18 @@ static_assert(sizeof(selkey_t) == 8, "key size");
 
 // W tiles of 16 rows per wave: 8 (128 rows) while the feature rows fit one MFMA
 // tile, which keeps the most weight bytes in flight per wave; fewer as more
-// feature rows need accumulator registers (no spills up to T = 256).
+// feature rows need accumulator registers (no spills up to T = 256).  At
+// T <= 64 four tiles give 501 workgroups for V = 128256, one wave of
+// workgroups at two per CU.
 __host__ __device__ constexpr int lm_mt(int T) {
-  return T <= 16 ? 8 : (T <= 128 ? 2 : 1);
+  return T <= 16 ? 8 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
+}
+
+// The feature-row tiles a launch is compiled for (1, 2, 4, 8 or 16 of 16 rows).
+// The launch and the workspace layout both take the tile count from here and
+// the W tiles from lm_mt(16 * lm_nt(T)), so the two can never disagree.
+__host__ __device__ constexpr int lm_nt(int T) {
+  return T <= 16 ? 1 : (T <= 32 ? 2 : (T <= 64 ? 4 : (T <= 128 ? 8 : 16)));
 }
 
 struct LmParams {
@@ -479,7 +488,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   LmLayout l{};
   if (dt == EAGLE_BF16) {
-    const int rows_block = 16 * lm_mt(T) * kLmWaves;
+    const int rows_block = 16 * lm_mt(16 * lm_nt(T)) * kLmWaves;
     l.nb = ((V + rows_block - 1) / rows_block) * (k <= kLmBlockK ? 1 : kLmWaves);
     l.stat_off = 0;
     l.key_off = align256((size_t)l.nb * T * sizeof(float2));
@@ -491,8 +500,9 @@ static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   return l;
 }
 
-template <int NT, int MT>
+template <int NT>
 static void launch_lm(const LmParams& p, hipStream_t s) {
+  constexpr int MT = lm_mt(16 * NT);
   const int rows_block = 16 * MT * kLmWaves;
   hipLaunchKernelGGL((lmhead_bf16_kernel<NT, MT>), dim3((p.V + rows_block - 1) / rows_block),
                      dim3(256), 0, s, p);
@@ -528,14 +538,13 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
     EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
                (float2*)(ws + l.stat_off), (selkey_t*)(ws + l.key_off), rn};
-    const int nt = (T + 15) / 16;
-    static_assert(lm_mt(16) == 8 && lm_mt(64) == 2 && lm_mt(128) == 2 && lm_mt(129) == 1,
-                  "tile choice");
-    if (nt <= 1) launch_lm<1, 8>(p, stream);
-    else if (nt <= 2) launch_lm<2, 2>(p, stream);
-    else if (nt <= 4) launch_lm<4, 2>(p, stream);
-    else if (nt <= 8) launch_lm<8, 2>(p, stream);
-    else launch_lm<16, 1>(p, stream);
+    switch (lm_nt(T)) {
+      case 1: launch_lm<1>(p, stream); break;
+      case 2: launch_lm<2>(p, stream); break;
+      case 4: launch_lm<4>(p, stream); break;
+      case 8: launch_lm<8>(p, stream); break;
+      default: launch_lm<16>(p, stream); break;
+    }
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmhead_merge_kernel, dim3(T), dim3(256), 0, stream, p.part_stat,
                        p.part_key, l.nb, T, k, topk_id, topk_logp, lse);
