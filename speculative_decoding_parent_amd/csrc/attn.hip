@@ -30,8 +30,13 @@
 //                 lane (g, r16) at V[4g + r16/4][4 (r16 mod 4)] of a 16-dim
 //                 slice gives it V[4g + j][r16] for j < 4, i.e. four positions
 //                 of one head dim, in the permuted k order.
-// K and V tiles are fetched two ahead into registers (16-byte loads, coalesced
-// along the head dimension) and double-buffered in LDS, one barrier per tile.
+// K and V tiles are fetched two ahead into registers (16-byte buffer loads,
+// coalesced along the head dimension) and double-buffered in LDS, one barrier
+// per tile.  The loads are unconditional: positions past the slice fall
+// outside the buffer range and read as zero without touching memory, so the
+// number of loads in flight is fixed and the waits before each LDS store let
+// the newer tile stay in flight.  The tree slice's mask words (at most four
+// per row) are staged in LDS before the loop.
 // The running max is raised lazily (see the softmax step).
 //
 // fp32 path (small workloads): one workgroup per (query row, head, split)
@@ -91,8 +96,15 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
   constexpr int VS = HD + 16;
   constexpr int CPR = HD / 8;
   constexpr int NCH = kAtTile * CPR / NTH;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][kAtTile * KS];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][kAtTile * VS];
+  // K and V double buffers; after the last tile the same space stages each
+  // wave's output rows (PS bytes apart) for row-contiguous stores
+  constexpr int PS = HD * 2 + 16;
+  constexpr int SMEM = 2 * kAtTile * (KS + VS);
+  static_assert(NW * 16 * NTW * PS <= SMEM * 2, "output staging fits the K/V buffers");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[SMEM];
+  bf16_t(*Ks)[kAtTile * KS] = (bf16_t(*)[kAtTile * KS])smem;
+  bf16_t(*Vs)[kAtTile * VS] = (bf16_t(*)[kAtTile * VS])(smem + 2 * kAtTile * KS);
+  __shared__ uint64_t Ms[NW][NTW][16][4];  // tree slice: each row's mask words
 
   const int split = blockIdx.x;
   const int gkv = blockIdx.y;
@@ -108,7 +120,6 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
 
   int grow[NTW];
   bool valid[NTW];
-  int mrow[NTW];
   u32x4 qf[NTW][KB];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
@@ -117,12 +128,14 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     const int i = valid[nt] ? r / p.G : 0;
     const int h = gkv * p.G + (valid[nt] ? r % p.G : 0);
     grow[nt] = i * p.Hq + h;
-    int mr = p.qmap ? p.qmap[i] : i;
-    if (mr < 0 || mr >= p.mask_rows) {
-      if (valid[nt] && is_tree && g == 0) set_status(p.status, EAGLE_DEV_BAD_INDEX);
-      mr = -1;
+    if (is_tree && g == 0) {
+      const int mr = p.qmap ? p.qmap[i] : i;
+      const bool ok = mr >= 0 && mr < p.mask_rows;
+      if (valid[nt] && !ok) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        Ms[wave][nt][r16][w] = ok && w < p.words ? p.mask[(size_t)mr * p.words + w] : 0ull;
     }
-    mrow[nt] = mr;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
       qf[nt][kb] = valid[nt] ? *(const u32x4*)(p.q + (size_t)grow[nt] * HD + kb * 32 + 8 * g)
@@ -159,18 +172,16 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
 
   // K/V tiles go HBM -> registers (two stages: up to two tiles in flight, each
   // with two tile-times to arrive) -> LDS (two buffers: one barrier per tile).
+  const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kb_ptr, (size_t)npos * HD * sizeof(bf16_t));
+  const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vb_ptr, (size_t)npos * HD * sizeof(bf16_t));
   u32x4 kr0[NCH], vr0[NCH], kr1[NCH], vr1[NCH];
   auto load_tile = [&](int t, u32x4 (&kr)[NCH], u32x4 (&vr)[NCH]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NCH; ++j) {
-      const int c = tid + NTH * j;
-      const int pr = c / CPR;
-      const int cc = c - pr * CPR;
-      const int pos = t * kAtTile + pr;
-      const bool ok = pos < npos;
-      const int off = pos * HD + cc * 8;
-      kr[j] = ok ? *(const u32x4*)(kb_ptr + off) : u32x4{0u, 0u, 0u, 0u};
-      vr[j] = ok ? *(const u32x4*)(vb_ptr + off) : u32x4{0u, 0u, 0u, 0u};
+      // chunk c = tid + NTH j of the tile: position c / CPR, 8 dims at (c mod CPR) 8
+      const uint32_t off = (uint32_t)(t * kAtTile * HD + (tid + NTH * j) * 8) * sizeof(bf16_t);
+      kr[j] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+      vr[j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
     }
   };
   auto store_tile = [&](int buf, const u32x4 (&kr)[NCH], const u32x4 (&vr)[NCH])
@@ -185,14 +196,9 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     }
   };
 
-  // One 64-position tile from LDS buffer `buf` (one instance for both kinds of
-  // slice: the mask is read only on tree tiles and the last, partial tile).
-  auto tile = [&](int t, int buf) __attribute__((always_inline)) {
-    const bool TREE = is_tree;
+  // S^T = K Q^T over the 4 position tiles of 16 of LDS buffer `buf`
+  auto qk = [&](int buf, f32x4 (&s)[4][NTW]) __attribute__((always_inline)) {
     const bf16_t* Kb = Ks[buf];
-    const bf16_t* Vb = Vs[buf];
-    // S^T = K Q^T over 4 position tiles of 16
-    f32x4 s[4][NTW];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -208,14 +214,19 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
                                                               s[mt][nt], 0, 0, 0);
       }
     }
+  };
 
+  // Online softmax of tile t's scores into bf16 weights pb (B operands of the
+  // V product), updating m, l and, when the running max moves, O.
+  auto softmax = [&](int t, f32x4 (&s)[4][NTW], u32x4 (&pb)[2][NTW])
+                     __attribute__((always_inline)) {
     // visibility: positions past the slice end, and non-ancestors in the tree
     const int tile_pos = t * kAtTile;
-    if (TREE || tile_pos + kAtTile > npos) {
+    if (is_tree || tile_pos + kAtTile > npos) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         uint64_t bits = ~0ull;
-        if (TREE) bits = mrow[nt] >= 0 ? p.mask[(size_t)mrow[nt] * p.words + t] : 0ull;
+        if (is_tree) bits = Ms[wave][nt][r16][t];  // t < words <= 4
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -254,7 +265,6 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
         for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
       }
     }
-    u32x4 pb[2][NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       const float nmc = -m[nt] * p.c;
@@ -276,8 +286,11 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
                             pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
       }
     }
+  };
 
-    // O^T += V^T P^T
+  // O^T += V^T P^T from LDS buffer `buf`
+  auto pv = [&](int buf, const u32x4 (&pb)[2][NTW]) __attribute__((always_inline)) {
+    const bf16_t* Vb = Vs[buf];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -295,43 +308,77 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     }
   };
 
+  // One whole 64-position tile from LDS buffer `buf`.
+  auto tile = [&](int t, int buf) __attribute__((always_inline)) {
+    f32x4 s[4][NTW];
+    u32x4 pb[2][NTW];
+    qk(buf, s);
+    softmax(t, s, pb);
+    pv(buf, pb);
+  };
+
   auto run_tiles = [&]() __attribute__((always_inline)) {
-    if (ntiles > 0) load_tile(0, kr0, vr0);
-    if (ntiles > 1) load_tile(1, kr1, vr1);
-    if (ntiles > 0) store_tile(0, kr0, vr0);
-    if (ntiles > 2) load_tile(2, kr0, vr0);
+    if (ntiles == 0) return;
+    // issue order fixed (tile 0, 1, 2) so that the waits before each store
+    // count the same loads here as in the loop
+    load_tile(0, kr0, vr0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(1, kr1, vr1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile(0, kr0, vr0);
+    load_tile(2, kr0, vr0);
     __syncthreads();
+    // Loads past the last tile read zeros (out of the buffer range), so the
+    // loop issues the same loads every iteration.  Single-exit loop with the
+    // odd tile peeled: with an exit in the middle, the compiler waits for all
+    // loads (the newer tile too) before the first store of each iteration.
+    int t = 0;
 #pragma clang loop unroll(disable)
-    for (int t = 0; t < ntiles; t += 2) {
+    for (; t + 1 < ntiles; t += 2) {
       tile(t, 0);
-      if (t + 1 < ntiles) store_tile(1, kr1, vr1);
-      if (t + 3 < ntiles) load_tile(t + 3, kr1, vr1);
+      store_tile(1, kr1, vr1);
+      load_tile(t + 3, kr1, vr1);
       __syncthreads();
-      if (t + 1 >= ntiles) break;
       tile(t + 1, 1);
-      if (t + 2 < ntiles) store_tile(0, kr0, vr0);
-      if (t + 4 < ntiles) load_tile(t + 4, kr0, vr0);
+      store_tile(0, kr0, vr0);
+      load_tile(t + 4, kr0, vr0);
       __syncthreads();
     }
+    if (t < ntiles) tile(t, 0);
   };
+
   run_tiles();
 
-  // partials: lane (g, r16) holds O^T[hd = 16 mv + 4 g + j][row 16 nt + r16];
-  // stored as O / l in bf16 (a convex combination of V rows: V's range, and a
-  // rounding of 2^-9 relative, below the output's own bf16 rounding)
+  // Partials: O / l in bf16 (a convex combination of V rows: V's range, and a
+  // rounding of 2^-9 relative, below the output's own bf16 rounding) and
+  // (m, l).  Lane (g, r16) holds O^T[hd = 16 mv + 4 g + j][row 16 nt + r16]:
+  // staged in LDS, then stored as whole rows, 16 bytes per lane (4 query heads
+  // of one node are 4 consecutive rows in memory).
+  __syncthreads();  // every wave is done with the K/V buffers
+  char* stg = (char*)smem + wave * (16 * NTW) * PS;
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    float lt = l[nt];
-    lt = rows_sum(lt);
-    if (!valid[nt]) continue;
-    const size_t prow = (size_t)split * RT + grow[nt];
-    if (g == 0) p.part_ml[prow] = make_float2(m[nt], lt);
+    const float lt = rows_sum(l[nt]);
+    if (valid[nt] && g == 0) p.part_ml[(size_t)split * RT + grow[nt]] = make_float2(m[nt], lt);
     const float il = lt > 0.f ? 1.0f / lt : 0.f;
-    bf16_t* po = (bf16_t*)p.part_o + prow * HD;
 #pragma unroll
     for (int mv = 0; mv < MTV; ++mv) {
       const f32x4 v = o[mv][nt] * il;
-      *(u32x2*)(po + mv * 16 + 4 * g) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *(u32x2*)(stg + (nt * 16 + r16) * PS + (mv * 16 + 4 * g) * 2) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+  }
+  constexpr int CH = HD * 2 / 16;  // 16-byte chunks per row
+#pragma unroll
+  for (int k = 0; k < 16 * NTW * CH / 64; ++k) {
+    const int idx = k * 64 + lane;
+    const int rr = idx / CH;
+    const int ch = idx - rr * CH;
+    const int r = qg * (16 * NTW * NW) + wave * 16 * NTW + rr;
+    if (r < R) {
+      const int orow = (r / p.G) * p.Hq + gkv * p.G + r % p.G;
+      *(u32x4*)((char*)p.part_o + ((size_t)split * RT + orow) * HD * 2 + ch * 16) =
+          *(const u32x4*)(stg + rr * PS + ch * 16);
     }
   }
 }
@@ -416,6 +463,8 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnParams p, int hd
 // splits.
 constexpr int kMergeSplits = 1024;
 
+// Combines the splits' partials, one block per output row: weights
+// 2^((m_s - M) c) (times l_s for the bf16 path, whose partials are O / l).
 template <bool NORMED_BF16>
 __global__ __launch_bounds__(128) void attn_merge_kernel(const void* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
@@ -545,6 +594,8 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
   EAGLE_REQUIRE((al & 15) == 0 && ((uintptr_t)mask & 7) == 0, EAGLE_EINVAL);
   const AttnPlan pl = attn_plan(Tq, Hq, Hkv, hd, L, in_dt);
   EAGLE_REQUIRE(pl.n_split + 1 <= kMergeSplits, EAGLE_EUNSUPPORTED);
+  // 32-bit byte offsets within one slice
+  EAGLE_REQUIRE(in_dt != EAGLE_BF16 || pl.tiles_per_split <= 65536, EAGLE_EUNSUPPORTED);
   EAGLE_REQUIRE(ws_bytes >= pl.total, EAGLE_EWORKSPACE);
   char* ws = (char*)workspace;
   AttnParams p{};
@@ -595,6 +646,7 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
     hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(Tq * Hq), dim3(128), 0, stream, p.part_o,
                        p.part_ml, pl.n_split + 1, Tq * Hq, hd, p.c, out,
                        out_dt == EAGLE_BF16 ? 1 : 0);
+
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

@@ -46,6 +46,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return pack_bf16x2(f, 0.0f) & 0xffffu;
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero and touch no memory; the count is clamped to 2^31 - 1 bytes.
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)(bytes < 0x7fffffffull ? bytes : 0x7fffffffull),
+                                           kRsrcWord3);
+}
+
 __device__ __forceinline__ void set_status(int32_t* st, int32_t bit) {
   if (st) atomicOr(st, bit);
 }

@@ -560,11 +560,9 @@ struct SkParams {
 // arrival's tile, and resets the counter.  Called by all threads; same answer
 // in all.
 constexpr int kSc1 = 1 << 4;                     // buffer cache policy bit: sc1
-constexpr int kRsrcWord3 = 0x00020000;           // raw 32-bit buffer data format
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
-                                           (int)min(bytes, (size_t)0x7fffffff), kRsrcWord3);
+  return buf_rsrc(base, bytes);
 }
 __device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
