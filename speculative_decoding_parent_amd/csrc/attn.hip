@@ -36,7 +36,7 @@
 // outside the buffer range and read as zero without touching memory, so the
 // number of loads in flight is fixed and the waits before each LDS store let
 // the newer tile stay in flight.  The tree slice's mask words (at most four
-// per row) are staged in LDS before the loop.
+// per row) are staged in LDS before the loop, behind the first K/V loads.
 // The running max is raised lazily (see the softmax step).
 //
 // fp32 path (small workloads): one workgroup per (query row, head, split)
@@ -120,6 +120,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
 
   int grow[NTW];
   bool valid[NTW];
+  int mrow[NTW];
   u32x4 qf[NTW][KB];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
@@ -128,14 +129,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     const int i = valid[nt] ? r / p.G : 0;
     const int h = gkv * p.G + (valid[nt] ? r % p.G : 0);
     grow[nt] = i * p.Hq + h;
-    if (is_tree && g == 0) {
-      const int mr = p.qmap ? p.qmap[i] : i;
-      const bool ok = mr >= 0 && mr < p.mask_rows;
-      if (valid[nt] && !ok) set_status(p.status, EAGLE_DEV_BAD_INDEX);
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        Ms[wave][nt][r16][w] = ok && w < p.words ? p.mask[(size_t)mr * p.words + w] : 0ull;
-    }
+    mrow[nt] = is_tree ? (p.qmap ? p.qmap[i] : i) : 0;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
       qf[nt][kb] = valid[nt] ? *(const u32x4*)(p.q + (size_t)grow[nt] * HD + kb * 32 + 8 * g)
@@ -327,6 +321,19 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     __builtin_amdgcn_sched_barrier(0);
     store_tile(0, kr0, vr0);
     load_tile(2, kr0, vr0);
+    if (is_tree && g == 0) {
+      // mask words of each row into LDS, read after the first K/V loads are
+      // on their way
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int mr = mrow[nt];
+        const bool ok = mr >= 0 && mr < p.mask_rows;
+        if (valid[nt] && !ok) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          Ms[wave][nt][r16][w] = ok && w < p.words ? p.mask[(size_t)mr * p.words + w] : 0ull;
+      }
+    }
     __syncthreads();
     // Loads past the last tile read zeros (out of the buffer range), so the
     // loop issues the same loads every iteration.  Single-exit loop with the
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
       load_tile(t + 3, kr1, vr1);
       __syncthreads();
       tile(t + 1, 1);
-      store_tile(0, kr0, vr0);
+      if (t + 2 < ntiles) store_tile(0, kr0, vr0);  // (no wait for loads past the end)
       load_tile(t + 4, kr0, vr0);
       __syncthreads();
     }

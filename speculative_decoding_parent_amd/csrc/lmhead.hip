@@ -272,6 +272,7 @@ __device__ __forceinline__ V block_reduce256(V v, V* red, Op op) {
 // theta can contribute: at most k of them (keys never tie).  theta comes from
 // per-wave selections over first keys held in registers; the surviving lists
 // are copied into LDS and wave 0 merges them, one list per lane, in k rounds.
+// Rows with few short lists take a one-pass path (below).
 constexpr int kMergeHeads = 16;   // first keys per thread held in registers
 
 // (m, s) <- the pair for the union of both sets; a pair with s = 0 is empty.
@@ -322,6 +323,56 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
   const float2* st = part_stat + (size_t)t * nb;
   const selkey_t* pk = part_key + (size_t)t * nb * k;
   if (tid == 0) nsl = 0;
+
+  // Short lists (nb <= 256, nb k <= 4096 keys): all keys go to LDS in one
+  // pass and wave 0 merges every list directly, lane l following lists l,
+  // l + 64, l + 128 and l + 192, with each list's next key read ahead.
+  if (nb <= 256 && nb * k <= EAGLE_MAX_TOPK * EAGLE_MAX_TOPK) {
+    for (int c = tid; c < nb * k; c += 256) sk[c] = pk[c];
+    float m = -INFINITY, s = 0.f;
+    for (int w = tid; w < nb; w += 256) {
+      const float2 x = st[w];
+      fold_stat(m, s, x.x, x.y);
+    }
+    fold_stat_wave(m, s);
+    if (lane == 0) red[wave] = make_float2(m, s);
+    __syncthreads();
+    if (wave != 0) return;
+    float M = red[0].x, S = red[0].y;
+    for (int w = 1; w < 4; ++w) fold_stat(M, S, red[w].x, red[w].y);
+    const float L = M + logf(S);
+    selkey_t hq[4], nx[4];
+    int ptr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int w = lane + 64 * q;
+      ptr[q] = 0;
+      hq[q] = w < nb && k > 0 ? sk[w * k] : 0ull;
+      nx[q] = w < nb && k > 1 ? sk[w * k + 1] : 0ull;
+    }
+    for (int r = 0; r < k; ++r) {
+      selkey_t h = hq[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) h = hq[q] > h ? hq[q] : h;
+      const selkey_t b = wave_max_key(h);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int w = lane + 64 * q;
+        const bool adv = (hq[q] == b) & (b != 0ull);
+        ptr[q] += adv ? 1 : 0;
+        hq[q] = adv ? nx[q] : hq[q];
+        const int nxt = ptr[q] + 1;
+        const selkey_t ahead = (w < nb && nxt < k) ? sk[w * k + nxt] : 0ull;
+        nx[q] = adv ? ahead : nx[q];
+      }
+      if (lane == 0) {
+        topk_id[(size_t)t * k + r] = b ? key_index(b) : -1;
+        topk_logp[(size_t)t * k + r] = b ? key_value(b) - L : -INFINITY;
+      }
+    }
+    if (lane == 0) lse[t] = L;
+    return;
+  }
 
   // first keys (issued before the statistics pass so the loads overlap)
   const bool inreg = nb <= 256 * kMergeHeads;

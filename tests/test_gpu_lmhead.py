@@ -49,7 +49,9 @@ def check(ids, logp, lse, lg, f, W, k, exact=False):
                                      (10, 4096, 2000, 10), (128, 1024, 3000, 10),
                                      (17, 512, 777, 64), (3, 256, 20, 20), (200, 256, 1100, 8),
                                      (10, 512, 20000, 16), (64, 256, 9000, 17),
-                                     (16, 256, 70000, 1)])
+                                     (16, 256, 70000, 1),
+                                     # 256 lists of 16 (one-pass merge) and 257 (two-pass merge)
+                                     (4, 128, 131072, 16), (4, 128, 131073, 16)])
 def test_bf16_random(dev, T, d, V, k):
     g = inputs.rng(400, T, V)
     f = inputs.normal(g, (T, d))
