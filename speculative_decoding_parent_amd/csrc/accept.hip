@@ -14,13 +14,43 @@
 // each row needs fp64 softmax mass over the whole vocabulary.  A grid kernel
 // first reduces every row in 4096-token chunks (chunk max and fp64
 // sum of exp((l - chunk max) / temperature)), so the single-workgroup walk
-// only combines ~32 chunk sums per visited node and rescans one 4096-token
-// chunk for the inverse-CDF draw.
+// only combines ~32 chunk sums per visited node (one wave, in parallel) and
+// rescans one 4096-token chunk for the inverse-CDF draw.
 #include "common.h"
 
 namespace eagle {
 
 constexpr int kAcceptChunk = 4096;
+
+// e^x in fp64 for x <= 0 (the exponents here are (l - max) / temperature).
+// Cody-Waite reduction x = k ln2 + r with ln2 split into a head with
+// trailing zero bits and a tail, so k ln2_hi is exact and |r| <= ln2 / 2;
+// e^r by its Taylor series to degree 12 (remainder < 2e-16 on that range),
+// then scaled by 2^k.  Within a few ulp of the correctly rounded value;
+// 0 below -745.2 (and for -inf).
+__device__ __forceinline__ double exp_nonpos(double x) {
+  constexpr double kLn2Hi = 6.93147180369123816490e-01;
+  constexpr double kLn2Lo = 1.90821492927058770002e-10;
+  constexpr double kLog2e = 1.4426950408889634;
+  if (!(x > -745.2)) return 0.0;
+  const double k = rint(x * kLog2e);
+  double r = fma(-k, kLn2Hi, x);
+  r = fma(-k, kLn2Lo, r);
+  double p = 2.08767569878681e-09;
+  p = fma(p, r, 2.505210838544172e-08);
+  p = fma(p, r, 2.755731922398589e-07);
+  p = fma(p, r, 2.7557319223985893e-06);
+  p = fma(p, r, 2.48015873015873e-05);
+  p = fma(p, r, 0.0001984126984126984);
+  p = fma(p, r, 0.001388888888888889);
+  p = fma(p, r, 0.008333333333333333);
+  p = fma(p, r, 0.041666666666666664);
+  p = fma(p, r, 0.16666666666666666);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)k);
+}
 
 // ---------------------------------------------------------------- greedy
 
@@ -84,9 +114,12 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(
 // ---------------------------------------------------------------- sampling
 
 // Per (row, chunk): chunk max m_c (fp32, exact) and s_c = sum over the chunk of
-// exp(((double)l - m_c) / temperature) in fp64.
+// exp(((double)l - m_c) / temperature) in fp64 (the division taken as a
+// product with the fp64 reciprocal: at most one ulp of the exponent, and
+// exact for temperature 1).
 __global__ __launch_bounds__(256) void accept_row_stats_kernel(
-    const float* __restrict__ logits, int V, double temp, int nchunk, double* __restrict__ ws) {
+    const float* __restrict__ logits, int V, double itemp, int nchunk, double* __restrict__ ws) {
+  constexpr int PER = kAcceptChunk / 256;  // logits per thread, held in registers
   const int c = blockIdx.x;
   const int t = blockIdx.y;
   const float* row = logits + (size_t)t * V;
@@ -94,15 +127,25 @@ __global__ __launch_bounds__(256) void accept_row_stats_kernel(
   const int hi = min(V, lo + kAcceptChunk);
   __shared__ float smax[4];
   __shared__ double ssum[4];
+  float x[PER];
   float m = -INFINITY;
-  for (int v = lo + threadIdx.x; v < hi; v += blockDim.x) m = fmaxf(m, row[v]);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int v = lo + (int)threadIdx.x + 256 * j;
+    x[j] = v < hi ? row[v] : -INFINITY;
+    m = fmaxf(m, x[j]);
+  }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
   double s = 0.0;
   const double md = (double)m;
-  for (int v = lo + threadIdx.x; v < hi; v += blockDim.x) s += exp(((double)row[v] - md) / temp);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int v = lo + (int)threadIdx.x + 256 * j;
+    if (v < hi) s += exp_nonpos(((double)x[j] - md) * itemp);
+  }
   s = wave_sum_d(s);
   if ((threadIdx.x & 63) == 0) ssum[threadIdx.x >> 6] = s;
   __syncthreads();
@@ -130,12 +173,13 @@ __device__ __forceinline__ V block_reduce(V v, V* red, Op op) {
 
 __global__ __launch_bounds__(1024) void accept_sample_kernel(
     int T, const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
-    const float* __restrict__ logits, int V, double temp, const float* __restrict__ U,
+    const float* __restrict__ logits, int V, double itemp, const float* __restrict__ U,
     int nchunk, const double* __restrict__ ws, int max_path, int32_t* __restrict__ path,
     int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
   __shared__ int32_t par[EAGLE_MAX_TREE];
   __shared__ int32_t tk[EAGLE_MAX_TREE];
   __shared__ int32_t rej[EAGLE_MAX_TREE];
+  __shared__ double pxs[EAGLE_MAX_TREE];
   __shared__ double dred[16];
   __shared__ int ired[16];
   __shared__ double sh_m, sh_target, sh_run;
@@ -156,59 +200,97 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(
   if (tid == 0) sh_u = 0;
   __syncthreads();
 
-  // ---- the walk: one accept/reject pass over the children of each node
+  // ---- the walk: one accept/reject pass over the children of each node.
+  // Wave 0 combines the node's chunk statistics and weighs every child in
+  // parallel; lane 0 then takes the decisions in child order.
   int depth = 0;
   for (;;) {
-    if (tid == 0) {
+    if (tid < 64) {
       const int u = sh_u;
       const float* row = logits + (size_t)u * V;
       const double* st = ws + (size_t)u * nchunk * 2;
-      double m = st[0];
-      for (int c = 1; c < nchunk; ++c) m = fmax(m, st[2 * c]);
+      double m = -INFINITY;
+      for (int c = lane; c < nchunk; c += 64) m = fmax(m, st[2 * c]);
+      m = wave_max_d(m);
       double z = 0.0;
-      for (int c = 0; c < nchunk; ++c) z += st[2 * c + 1] * exp((st[2 * c] - m) / temp);
-      double zres = z;
-      int nrej = 0;
-      int moved = 0;
-      for (int c = u + 1; c < T && !moved; ++c) {
-        if (par[c] != u) continue;
-        const int x = tk[c];
-        bool seen = false;
-        for (int r = 0; r < nrej; ++r) seen |= rej[r] == x;
-        if (seen) continue;
-        const double px = exp(((double)row[x] - m) / temp);
-        if ((double)U[c] * zres < px) {
-          moved = 1;
-          sh_u = c;
-        } else {
-          rej[nrej++] = x;
-          zres = zres - px;
-        }
+      for (int c = lane; c < nchunk; c += 64) z += st[2 * c + 1] * exp_nonpos((st[2 * c] - m) * itemp);
+      z = wave_sum_d(z);
+      uint64_t kids[EAGLE_MAX_TREE / 64];
+#pragma unroll
+      for (int q = 0; q < EAGLE_MAX_TREE / 64; ++q) {
+        const int c = 64 * q + lane;
+        const bool is = c > u && c < T && par[c] == u;
+        if (is) pxs[c] = exp_nonpos(((double)row[tk[c]] - m) * itemp);
+        kids[q] = __builtin_amdgcn_ballot_w64(is);
       }
-      sh_m = m;
-      sh_nrej = nrej;
-      sh_moved = moved;
-      if (!moved) {
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) {
+        double zres = z;
+        int nrej = 0;
+        int moved = 0;
+        for (int q = 0; q < EAGLE_MAX_TREE / 64 && !moved; ++q) {
+          uint64_t b = kids[q];
+          while (b && !moved) {
+            const int c = 64 * q + __builtin_ctzll(b);
+            b &= b - 1;
+            const int x = tk[c];
+            bool seen = false;
+            for (int r = 0; r < nrej; ++r) seen |= rej[r] == x;
+            if (seen) continue;
+            const double px = pxs[c];
+            if ((double)U[c] * zres < px) {
+              moved = 1;
+              sh_u = c;
+            } else {
+              rej[nrej++] = x;
+              zres = zres - px;
+            }
+          }
+        }
+        sh_m = m;
+        sh_nrej = nrej;
+        sh_moved = moved;
+        sh_target = (double)U[T + u] * zres;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (!sh_moved) {
         // the residual draw starts in the first chunk whose running
         // non-rejected mass passes the target
-        const double target = (double)U[T + u] * zres;
+        const int nrej = sh_nrej;
+        const double target = sh_target;
         double run = 0.0;
         int chunk = nchunk - 1;
-        double before = 0.0;
-        for (int c = 0; c < nchunk; ++c) {
-          double mass = st[2 * c + 1] * exp((st[2 * c] - m) / temp);
-          for (int r = 0; r < nrej; ++r)
-            if (rej[r] / kAcceptChunk == c) mass -= exp(((double)row[rej[r]] - m) / temp);
-          before = run;
-          if (run + mass > target) {
-            chunk = c;
+        double before = run;
+        for (int c0 = 0; c0 < nchunk; c0 += 64) {
+          const int c = c0 + lane;
+          double mass = 0.0;
+          if (c < nchunk) {
+            mass = st[2 * c + 1] * exp_nonpos((st[2 * c] - m) * itemp);
+            for (int r = 0; r < nrej; ++r)
+              if (rej[r] / kAcceptChunk == c) mass -= exp_nonpos(((double)row[rej[r]] - m) * itemp);
+          }
+          double incl = mass;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+          }
+          // (if no chunk passes, the draw starts in the last one)
+          const int lastw = nchunk - 1 - c0;
+          if (lastw < 64) before = run + __shfl(incl - mass, lastw);
+          const uint64_t pass = __builtin_amdgcn_ballot_w64(c < nchunk && run + incl > target);
+          if (pass) {
+            const int w = __builtin_ctzll(pass);
+            chunk = c0 + w;
+            before = run + __shfl(incl - mass, w);
             break;
           }
-          run += mass;
+          run += __shfl(incl, 63);
         }
-        sh_target = target;
-        sh_chunk = chunk;
-        sh_run = before;
+        if (lane == 0) {
+          sh_chunk = chunk;
+          sh_run = before;
+        }
       }
     }
     __syncthreads();
@@ -240,7 +322,7 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(
       if (v < hi) {
         bool r = false;
         for (int j = 0; j < nrej; ++j) r |= rej[j] == v;
-        pv = r ? 0.0 : exp(((double)row[v] - m) / temp);
+        pv = r ? 0.0 : exp_nonpos(((double)row[v] - m) * itemp);
       }
       q[e] = pv;
       mine += pv;
@@ -315,12 +397,12 @@ extern "C" int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
     EAGLE_REQUIRE(workspace && ((uintptr_t)workspace & 7) == 0, EAGLE_EINVAL);
     EAGLE_REQUIRE(ws_bytes >= eagle_accept_workspace(T, V), EAGLE_EWORKSPACE);
     const int nchunk = (V + eagle::kAcceptChunk - 1) / eagle::kAcceptChunk;
-    const double temp = (double)temperature;
+    const double itemp = 1.0 / (double)temperature;
     hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, T), dim3(256), 0, stream,
-                       target_logits, V, temp, nchunk, (double*)workspace);
+                       target_logits, V, itemp, nchunk, (double*)workspace);
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(eagle::accept_sample_kernel, dim3(1), dim3(1024), 0, stream, T,
-                       node_token, node_parent, target_logits, V, temp, uniforms, nchunk,
+                       node_token, node_parent, target_logits, V, itemp, uniforms, nchunk,
                        (const double*)workspace, max_path, path, n_accepted, bonus_token,
                        dev_status);
   } else {

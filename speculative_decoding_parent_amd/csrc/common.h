@@ -202,6 +202,18 @@ __device__ __forceinline__ void swap32(double x, double& a, double& b) {
   b = __longlong_as_double((long long)(((uint64_t)(uint32_t)bhi << 32) | (uint32_t)blo));
 }
 
+__device__ __forceinline__ double wave_max_d(double v) {
+  v = fmax(v, dpp_move<kDppQuadXor1>(v));
+  v = fmax(v, dpp_move<kDppQuadXor2>(v));
+  v = fmax(v, dpp_move<kDppHalfMirror>(v));
+  v = fmax(v, dpp_move<kDppRowMirror>(v));
+  double a, b;
+  swap16(v, a, b);
+  v = fmax(a, b);
+  swap32(v, a, b);
+  return fmax(a, b);
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
   v += dpp_move<kDppQuadXor1>(v);
   v += dpp_move<kDppQuadXor2>(v);

@@ -8,10 +8,12 @@
 // of log-probabilities along the root path, ties to the lower pool index.
 //
 // Both modes fit one workgroup (<= 4096 appended entries, <= 8192 pool
-// entries).  Selection is by exact rank: an entry is kept when fewer than n
-// entries beat it under (value desc, index asc), a total order, so the result
-// does not depend on thread scheduling.  Values are single IEEE fp32 adds
-// (__fadd_rn), never contracted.
+// entries).  Selection follows (value desc, index asc), a total order, so the
+// result does not depend on thread scheduling: EXPAND keeps an entry when
+// fewer than k_select entries beat it; RERANK sorts the pool's selection keys
+// (the same order as one 64-bit number, NaN last) with a bitonic network and
+// keeps the root and the first T-1 other entries.  Values are single IEEE
+// fp32 adds (__fadd_rn), never contracted.
 #include "common.h"
 
 namespace eagle {
@@ -62,39 +64,50 @@ __global__ __launch_bounds__(1024) void rerank_kernel(
     int32_t* __restrict__ node_token, int32_t* __restrict__ node_parent,
     int32_t* __restrict__ node_depth, int32_t* __restrict__ node_pool_idx,
     int32_t* __restrict__ status) {
-  __shared__ __attribute__((aligned(16))) float vs[EAGLE_MAX_POOL];
+  __shared__ selkey_t ks[EAGLE_MAX_POOL];
   __shared__ int16_t pos[EAGLE_MAX_POOL];
   __shared__ int32_t cnt[1024];
+  __shared__ int root_at;
   const int tid = threadIdx.x;
-  const int n4 = (pool_n + 3) / 4;
-  for (int i = tid; i < n4 * 4; i += blockDim.x) vs[i] = i < pool_n ? val[i] : -INFINITY;
+  // Selection keys (value desc, then index asc, as one number; key 0 pads
+  // the power-of-two length), bitonic-sorted into descending order.
+  int N = 2;
+  while (N < pool_n) N <<= 1;
+  for (int i = tid; i < N; i += blockDim.x) {
+    ks[i] = i < pool_n ? sel_key(val[i], i) : 0ull;
+    if (i < pool_n) pos[i] = 0;
+  }
   __syncthreads();
-  // keep flag per entry: the root always, others when fewer than T-1 non-root
-  // entries beat them
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int c = tid; c < N / 2; c += blockDim.x) {
+        const int a = 2 * c - (c & (stride - 1));  // partner a + stride
+        const bool down = (a & size) == 0;          // this run sorts descending
+        const selkey_t x = ks[a], y = ks[a + stride];
+        if (down ? x < y : x > y) {
+          ks[a] = y;
+          ks[a + stride] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // keep: the root always, and the first T-1 non-root entries of the order
+  for (int q = tid; q < pool_n; q += blockDim.x)
+    if (key_index(ks[q]) == 0) root_at = q;
+  __syncthreads();
+  const int r0 = root_at;
+  for (int q = tid; q < T; q += blockDim.x) {
+    const int i = key_index(ks[q]);
+    if (i == 0 || q < T - 1 || r0 < q) pos[i] = 1;
+  }
+  if (tid == 0 && r0 >= T) pos[0] = 1;
+  __syncthreads();
   const int per = (pool_n + blockDim.x - 1) / blockDim.x;
   const int lo = tid * per;
   const int hi = min(pool_n, lo + per);
   int mine = 0;
-  for (int i = lo; i < hi; ++i) {
-    bool keep;
-    if (i == 0) {
-      keep = true;
-    } else {
-      // rank among non-root entries: count over all entries (four per LDS
-      // read), minus the root's vote; entries past pool_n hold -inf and an
-      // index above every real one, so they never count
-      const float v = vs[i];
-      int rank = better(vs[0], 0, v, i) ? -1 : 0;
-      for (int o4 = 0; o4 < n4 && rank < T - 1; ++o4) {
-        const f32x4 q = *(const f32x4*)(&vs[4 * o4]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) rank += better(q[j], 4 * o4 + j, v, i) ? 1 : 0;
-      }
-      keep = rank < T - 1;
-    }
-    pos[i] = keep ? 1 : 0;
-    mine += keep ? 1 : 0;
-  }
+  for (int i = lo; i < hi; ++i) mine += pos[i];
   // exclusive scan of the per-thread counts: within each wave, then over the
   // wave totals
   int incl = mine;
