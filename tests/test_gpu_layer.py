@@ -278,7 +278,7 @@ def test_draft_prepare_and_embed(dev):
     slot mask rows against the oracle's mask of the slot tree."""
     g = inputs.rng(704, 0)
     V, d, cap, S = 500, 128, 40, 12
-    # pool: root, 4 children (round 1), then 8 entries below frontier [1, 3]
+    # pool: root, 4 children (first expansion), then 8 entries below frontier [1, 3]
     par = np.array([-1, 0, 0, 0, 0, 1, 1, 1, 1, 3, 3, 3, 3], np.int32)
     dep = np.array([0, 1, 1, 1, 1, 2, 2, 2, 2, 2, 2, 2, 2], np.int32)
     tok = g.integers(0, V, 13).astype(np.int32)

@@ -117,3 +117,31 @@ def test_bad_frontier_index_sets_status(dev):
                              k_select=1, dev_status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & _lib.DEV_BAD_INDEX
+
+
+@pytest.mark.parametrize("T", [5, 40, 120])
+def test_rerank_ties_signed_zeros_infinities_and_low_root(dev, T):
+    """RERANK over values with exact ties, +0.0 / -0.0, -inf runs and a root
+    that ranks below most of its descendants (kept regardless)."""
+    g = inputs.rng(78, T)
+    n = 150
+    par = [-1] + [int(g.integers(0, i)) for i in range(1, n)]
+    steps = np.array([0.0, -0.0, -0.25, -0.5, -1.0, -np.inf], np.float32)
+    val = [np.float32(-5.0)]
+    for i in range(1, n):
+        base = np.float32(0.0) if par[i] == 0 else val[par[i]]   # the root's own value is low
+        val.append(np.float32(base + steps[int(g.integers(0, len(steps)))]))
+    pool = Pool([int(x) for x in g.integers(0, 1000, n)], par,
+                [0] + [0] * (n - 1), val)
+    for i in range(1, n):
+        pool.depth[i] = pool.depth[par[i]] + 1
+    tok, pa, dep, va = pool.arrays()
+    T_ = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    got = _lib.eagle_expand_rerank(_lib.EAGLE_RERANK, T_(tok), T_(pa), T_(dep), T_(va), n, T=T,
+                                   dev_status=st)
+    want = oracle.rerank(pool, T)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for a, b in zip(got, want):
+        assert np.array_equal(a.cpu().numpy(), b)
