@@ -195,9 +195,10 @@ int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_
  *   (value desc, index asc), in ascending pool index.
  *   Needs pool_n + kf*k <= pool_cap, kf*k <= 4096, 1 <= k_select <= kf*k.
  * RERANK: keep the root and the T-1 best non-root entries by (value desc,
- *   index asc); write them in ascending pool index as node_token,
- *   node_parent (index into this list, -1 for the root), node_depth and
- *   node_pool_idx.  Needs 1 <= T <= min(pool_n, 256), pool_n <= 8192.
+ *   index asc; +0.0 equals -0.0, a NaN value ranks last); write them in
+ *   ascending pool index as node_token, node_parent (index into this list,
+ *   -1 for the root), node_depth and node_pool_idx.  Needs
+ *   1 <= T <= min(pool_n, 256), pool_n <= 8192.
  * Unused pointers of the other mode may be NULL.
  */
 int eagle_expand_rerank(int32_t mode,
@@ -231,7 +232,10 @@ int eagle_expand_rerank(int32_t mode,
  *   otherwise child c with token x is accepted iff uniforms[c] * Z_res < p[x]
  *   (the walk moves to c), else x is rejected.  When all children are
  *   rejected or u is a leaf, bonus = the smallest token i whose running sum of
- *   non-rejected p exceeds uniforms[T + u] * Z_res.
+ *   non-rejected p exceeds uniforms[T + u] * Z_res.  The division by the
+ *   temperature is a product with its fp64 reciprocal (exact at 1) and sums
+ *   run in chunks of 4096 tokens, so results can differ from a sequential
+ *   fp64 evaluation only where a decision's margin is a few ulp of Z.
  *   workspace >= eagle_accept_workspace(T, V) bytes (SAMPLE only).
  * Outputs: path int32[max_path] = node ids from the root (path[0] = 0), the
  *   rest -1; n_accepted int32[1] = accepted draft nodes (path length - 1);
