@@ -84,6 +84,84 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// Online softmax of tile t's scores s (S^T accumulators: lane (g, r16) holds
+// positions 16 mt + 4 g + j of query row 16 nt + r16) into bf16 weights pb
+// (B operands of the V product), updating m, l and, when the running max
+// moves, O.  ms: the wave's mask words per row tile and row (tree slice only).
+template <int NTW, int MTV>
+__device__ __forceinline__ void tile_softmax(int t, int npos, bool is_tree,
+                                             const uint64_t (*ms)[16][4], float c, int g, int r16,
+                                             f32x4 (&s)[4][NTW], u32x4 (&pb)[2][NTW],
+                                             float (&m)[NTW], float (&l)[NTW],
+                                             f32x4 (&o)[MTV][NTW]) {
+  // visibility: positions past the slice end, and non-ancestors in the tree
+  const int tile_pos = t * kAtTile;
+  if (is_tree || tile_pos + kAtTile > npos) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      uint64_t bits = ~0ull;
+      if (is_tree) bits = ms[nt][r16][t];  // t < words <= 4
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pl = mt * 16 + 4 * g + j;
+          if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
+        }
+    }
+  }
+
+  // Online softmax in the exp2 domain with a lazily raised running max: m
+  // only moves when the tile's max exceeds it by more than 2^8 (in exp2
+  // units), so weights stay <= 2^8 and m, l and O always share the same
+  // reference (exact); after the first tile the rescale is almost never
+  // taken.  exp2 arguments are <= 8: the native v_exp_f32 is exact enough.
+  float mx[NTW];
+  bool up_any = false;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    float v = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v = fmaxf(v, s[mt][nt][j]);
+    mx[nt] = rows_max(v);
+    up_any |= (mx[nt] - m[nt]) * c > 8.0f;
+  }
+  if (__builtin_amdgcn_ballot_w64(up_any)) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const bool up = (mx[nt] - m[nt]) * c > 8.0f;
+      const float alpha = up ? __builtin_amdgcn_exp2f((m[nt] - mx[nt]) * c) : 1.0f;
+      m[nt] = up ? mx[nt] : m[nt];
+      l[nt] *= alpha;
+#pragma unroll
+      for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const float nmc = -m[nt] * c;
+    float ps = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][j], c, nmc));
+        s[mt][nt][j] = pv;
+        ps += pv;
+      }
+    l[nt] += ps;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
+                          pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
+                          pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
+                          pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
+    }
+  }
+}
+
 template <int HD, int NTW, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p) {
   constexpr int NTH = 64 * NW;
@@ -210,76 +288,9 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
     }
   };
 
-  // Online softmax of tile t's scores into bf16 weights pb (B operands of the
-  // V product), updating m, l and, when the running max moves, O.
   auto softmax = [&](int t, f32x4 (&s)[4][NTW], u32x4 (&pb)[2][NTW])
                      __attribute__((always_inline)) {
-    // visibility: positions past the slice end, and non-ancestors in the tree
-    const int tile_pos = t * kAtTile;
-    if (is_tree || tile_pos + kAtTile > npos) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        uint64_t bits = ~0ull;
-        if (is_tree) bits = Ms[wave][nt][r16][t];  // t < words <= 4
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int pl = mt * 16 + 4 * g + j;
-            if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
-          }
-      }
-    }
-
-    // Online softmax in the exp2 domain with a lazily raised running max: m
-    // only moves when the tile's max exceeds it by more than 2^8 (in exp2
-    // units), so weights stay <= 2^8 and m, l and O always share the same
-    // reference (exact); after the first tile the rescale is almost never
-    // taken.  exp2 arguments are <= 8: the native v_exp_f32 is exact enough.
-    float mx[NTW];
-    bool up_any = false;
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      float v = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v = fmaxf(v, s[mt][nt][j]);
-      mx[nt] = rows_max(v);
-      up_any |= (mx[nt] - m[nt]) * p.c > 8.0f;
-    }
-    if (__builtin_amdgcn_ballot_w64(up_any)) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const bool up = (mx[nt] - m[nt]) * p.c > 8.0f;
-        const float alpha = up ? __builtin_amdgcn_exp2f((m[nt] - mx[nt]) * p.c) : 1.0f;
-        m[nt] = up ? mx[nt] : m[nt];
-        l[nt] *= alpha;
-#pragma unroll
-        for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const float nmc = -m[nt] * p.c;
-      float ps = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][j], p.c, nmc));
-          s[mt][nt][j] = pv;
-          ps += pv;
-        }
-      l[nt] += ps;
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
-                            pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
-                            pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
-                            pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
-      }
-    }
+    tile_softmax<NTW, MTV>(t, npos, is_tree, Ms[wave], p.c, g, r16, s, pb, m, l, o);
   };
 
   // O^T += V^T P^T from LDS buffer `buf`
@@ -363,6 +374,261 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p
   // of one node are 4 consecutive rows in memory).
   __syncthreads();  // every wave is done with the K/V buffers
   char* stg = (char*)smem + wave * (16 * NTW) * PS;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const float lt = rows_sum(l[nt]);
+    if (valid[nt] && g == 0) p.part_ml[(size_t)split * RT + grow[nt]] = make_float2(m[nt], lt);
+    const float il = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+    for (int mv = 0; mv < MTV; ++mv) {
+      const f32x4 v = o[mv][nt] * il;
+      *(u32x2*)(stg + (nt * 16 + r16) * PS + (mv * 16 + 4 * g) * 2) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+  }
+  constexpr int CH = HD * 2 / 16;  // 16-byte chunks per row
+#pragma unroll
+  for (int k = 0; k < 16 * NTW * CH / 64; ++k) {
+    const int idx = k * 64 + lane;
+    const int rr = idx / CH;
+    const int ch = idx - rr * CH;
+    const int r = qg * (16 * NTW * NW) + wave * 16 * NTW + rr;
+    if (r < R) {
+      const int orow = (r / p.G) * p.Hq + gkv * p.G + r % p.G;
+      *(u32x4*)((char*)p.part_o + ((size_t)split * RT + orow) * HD * 2 + ch * 16) =
+          *(const u32x4*)(stg + rr * PS + ch * 16);
+    }
+  }
+}
+
+// Ring variant for 128-dim heads.  K/V tiles go straight from HBM into LDS
+// (gfx950 16-byte buffer loads with an LDS destination) through NST stages,
+// so NST - 1 tiles are in flight while one is computed, and no registers
+// stage them.  A load instruction fills 1 KB of LDS contiguously (lane l at
+// byte 16 l), so rows cannot be padded; instead 16-byte chunk c of row r is
+// stored at chunk c ^ (r mod 16) for K (the 16 rows one b128 read touches fall
+// on distinct banks) and at c ^ 2 (r mod 8) for V (the 8 rows of a 32-lane
+// half of a transposing read keep their 32-byte column pair whole and apart).
+// The stages are separate LDS objects, so the compiler's own wait before an
+// LDS read covers only the loads into that stage.  Each step waits for the
+// wave's own loads of the current tile; the barrier that follows publishes
+// every wave's part and tells all waves that the stage about to be refilled
+// is no longer read.  Compute per tile is that of tree_attn_bf16_kernel.
+constexpr int kRingHD = 128;
+constexpr int kRingTileBytes = kAtTile * kRingHD * 2;  // one K (or V) tile: 16 KB
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from the buffer at byte offset off into LDS at
+// lds + 16 lane (lds is the same for the whole wave).  The host pass has no
+// such builtin and never runs this.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, bf16_t* lds, uint32_t off) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, off, 0, 0, 0);
+#endif
+}
+
+// s_waitcnt immediate: vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited on
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+template <int NTW, int NW, int NST>
+__global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p) {
+  constexpr int HD = kRingHD;
+  constexpr int KB = HD / 32;
+  constexpr int MTV = HD / 16;
+  constexpr int TB = kRingTileBytes;
+  constexpr int IPT = TB / 1024 / NW;  // 1 KB load instructions per thread per tile, K and V each
+  constexpr int PS = HD * 2 + 16;      // output staging row stride (bytes)
+  static_assert(NST >= 2 && NST <= 4 && IPT >= 1 && TB % (1024 * NW) == 0, "ring shape");
+  static_assert(NW <= 2 * NST && 16 * NTW * PS <= TB, "output staging: half a stage per wave");
+  // stage s: K tile at [0, TB), V tile at [TB, 2 TB)
+  __shared__ __attribute__((aligned(1024))) bf16_t st0[2 * kAtTile * HD];
+  __shared__ __attribute__((aligned(1024))) bf16_t st1[2 * kAtTile * HD];
+  __shared__ __attribute__((aligned(1024))) bf16_t st2[NST > 2 ? 2 * kAtTile * HD : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t st3[NST > 3 ? 2 * kAtTile * HD : 8];
+  __shared__ uint64_t Ms[NW][NTW][16][4];  // tree slice: each row's mask words
+
+  const int split = blockIdx.x;
+  const int gkv = blockIdx.y;
+  const int qg = blockIdx.z;
+  const bool is_tree = split == p.n_split;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const int R = p.Tq * p.G;
+  const int RT = p.Tq * p.Hq;
+
+  int grow[NTW];
+  bool valid[NTW];
+  int mrow[NTW];
+  u32x4 qf[NTW][KB];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int r = qg * (16 * NTW * NW) + wave * 16 * NTW + nt * 16 + r16;
+    valid[nt] = r < R;
+    const int i = valid[nt] ? r / p.G : 0;
+    const int h = gkv * p.G + (valid[nt] ? r % p.G : 0);
+    grow[nt] = i * p.Hq + h;
+    mrow[nt] = is_tree ? (p.qmap ? p.qmap[i] : i) : 0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qf[nt][kb] = valid[nt] ? *(const u32x4*)(p.q + (size_t)grow[nt] * HD + kb * 32 + 8 * g)
+                             : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  int64_t pos0;
+  int npos;
+  const bf16_t* kb_ptr;
+  const bf16_t* vb_ptr;
+  if (!is_tree) {
+    pos0 = (int64_t)split * p.tiles_per_split * kAtTile;
+    const int64_t rest = p.L - pos0;
+    npos = rest > (int64_t)p.tiles_per_split * kAtTile ? p.tiles_per_split * kAtTile : (int)rest;
+    kb_ptr = p.kc + ((size_t)gkv * p.ldc + pos0) * HD;
+    vb_ptr = p.vc + ((size_t)gkv * p.ldc + pos0) * HD;
+  } else {
+    pos0 = 0;
+    npos = p.Tk;
+    kb_ptr = p.kt + (size_t)gkv * p.ldt * HD;
+    vb_ptr = p.vt + (size_t)gkv * p.ldt * HD;
+  }
+  const int ntiles = npos > 0 ? (npos + kAtTile - 1) / kAtTile : 0;
+
+  float m[NTW], l[NTW];
+  f32x4 o[MTV][NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    m[nt] = kNegBig;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int mv = 0; mv < MTV; ++mv) o[mv][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // This thread's chunks of a tile: instruction j of wave w fills LDS chunks
+  // 64 b .. 64 b + 63 (b = j NW + w), i.e. rows 4 b .. 4 b + 3; lane l takes
+  // row 4 b + l / 16, LDS chunk l mod 16, and loads the chunk of the row that
+  // the swizzle puts there.  Byte offsets within tile 0 of the slice.
+  const __amdgpu_buffer_rsrc_t krs = buf_rsrc(kb_ptr, (size_t)npos * HD * sizeof(bf16_t));
+  const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(vb_ptr, (size_t)npos * HD * sizeof(bf16_t));
+  uint32_t koff[IPT], voff[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int r = 4 * (j * NW + wave) + (lane >> 4);
+    const int cl = lane & 15;
+    koff[j] = (uint32_t)(r * 256 + ((cl ^ (r & 15)) << 4));
+    voff[j] = (uint32_t)(r * 256 + ((cl ^ (2 * (r & 7))) << 4));
+  }
+  // LDS read offsets (bytes): K chunk kb 4 + g of row 16 mt + r16; V as the
+  // transposing read of tree_attn_bf16_kernel addresses it, swizzled
+  uint32_t kro[KB], vro[MTV];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    kro[kb] = (uint32_t)(r16 * 256 + ((((kb ^ (r16 >> 2)) << 2) | (g ^ (r16 & 3))) << 4));
+  const int pe = ((g & 1) << 2) | (r16 >> 2);  // row mod 8 of this lane's V rows
+#pragma unroll
+  for (int mv = 0; mv < MTV; ++mv)
+    vro[mv] = (uint32_t)((4 * g + (r16 >> 2)) * 256 + 8 * (r16 & 3) + 32 * (mv ^ pe));
+
+  auto stage = [&](int s) __attribute__((always_inline)) -> bf16_t* {
+    // s is a compile-time constant at every call (unrolled steps)
+    return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3;
+  };
+  auto issue = [&](int t, bf16_t* stg) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)t * TB;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      lds_load16(krs, stg + (j * NW + wave) * 512, base + koff[j]);
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      lds_load16(vrs, stg + kAtTile * HD + (j * NW + wave) * 512, base + voff[j]);
+  };
+
+  auto qk = [&](const bf16_t* stg, f32x4 (&s)[4][NTW]) __attribute__((always_inline)) {
+    const char* Kb = (const char*)stg;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 a = *(const bf16x8*)(Kb + mt * 4096 + kro[kb]);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[nt][kb]),
+                                                              s[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+  auto pv = [&](const bf16_t* stg, const u32x4 (&pb)[2][NTW]) __attribute__((always_inline)) {
+    const char* Vb = (const char*)(stg + kAtTile * HD);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int mv = 0; mv < MTV; ++mv) {
+        const u32x2 lo = lds_read_tr16((const bf16_t*)(Vb + kb2 * 8192 + vro[mv]));
+        const u32x2 hi = lds_read_tr16((const bf16_t*)(Vb + kb2 * 8192 + 4096 + vro[mv]));
+        const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          o[mv][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kb2][nt]),
+                                                              o[mv][nt], 0, 0, 0);
+      }
+    }
+  };
+  auto step = [&](int t, int s) __attribute__((always_inline)) {
+    // this wave's loads of tile t are done (the NST - 2 newer tiles may still
+    // be in flight), then every wave's are, and stage s - 1 is free
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NST - 2) * 2 * IPT, 0));
+    asm volatile("s_barrier" ::: "memory");
+    issue(t + NST - 1, stage((s + NST - 1) % NST));
+    if (t < ntiles) {
+      f32x4 sc[4][NTW];
+      u32x4 pb[2][NTW];
+      qk(stage(s), sc);
+      tile_softmax<NTW, MTV>(t, npos, is_tree, Ms[wave], p.c, g, r16, sc, pb, m, l, o);
+      pv(stage(s), pb);
+    }
+  };
+
+  if (ntiles > 0) {
+    issue(0, st0);
+    if (NST > 2) issue(1, st1);
+    if (NST > 3) issue(2, st2);
+    if (is_tree && g == 0) {
+      // mask words of each row into LDS, behind the first K/V loads
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int mr = mrow[nt];
+        const bool ok = mr >= 0 && mr < p.mask_rows;
+        if (valid[nt] && !ok) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          Ms[wave][nt][r16][w] = ok && w < p.words ? p.mask[(size_t)mr * p.words + w] : 0ull;
+      }
+    }
+    // Whole rounds of NST steps; steps past the last tile only keep the
+    // barrier and load counts uniform (their loads fall outside the buffer
+    // range and read zero without touching memory).
+#pragma clang loop unroll(disable)
+    for (int t0 = 0; t0 < ntiles; t0 += NST) {
+      step(t0, 0);
+      step(t0 + 1, 1);
+      if (NST > 2) step(t0 + 2, 2);
+      if (NST > 3) step(t0 + 3, 3);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  }
+
+  // Partials, as in tree_attn_bf16_kernel: O / l in bf16 and (m, l), O rows
+  // staged in LDS (half a stage per wave) and stored as whole rows.
+  __syncthreads();  // every wave is done with the stages and no load is in flight
+  char* stg = (char*)stage(wave >> 1) + (wave & 1) * TB;
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const float lt = rows_sum(l[nt]);
@@ -568,6 +834,11 @@ static void launch_attn(const AttnParams& p, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((tree_attn_bf16_kernel<HD, NTW, NW>), grid, dim3(64 * NW), 0, s, p);
 }
 
+template <int NTW, int NW, int NST>
+static void launch_ring(const AttnParams& p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((tree_attn_ring_kernel<NTW, NW, NST>), grid, dim3(64 * NW), 0, s, p);
+}
+
 }  // namespace eagle
 
 extern "C" size_t eagle_tree_attn_workspace(int32_t Tq, int32_t Hq, int32_t Hkv, int32_t hd,
@@ -634,7 +905,7 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
     if (hd == 128) {
       if (pl.ntw == 1) launch_attn<128, 1, 4>(p, grid, stream);
       else if (pl.nw == 4) launch_attn<128, 2, 4>(p, grid, stream);
-      else launch_attn<128, 2, 8>(p, grid, stream);
+      else launch_ring<2, 8, 4>(p, grid, stream);
     } else {
       if (pl.ntw == 1) launch_attn<64, 1, 4>(p, grid, stream);
       else if (pl.nw == 4) launch_attn<64, 2, 4>(p, grid, stream);
