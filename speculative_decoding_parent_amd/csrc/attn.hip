@@ -792,6 +792,11 @@ struct AttnPlan {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int64_t kCUs = 256;  // MI355X compute units
+
+// The LDS-ring kernel serves 128-dim heads with 256 query rows per workgroup.
+static bool ring_path(int hd, int nw) { return hd == kRingHD && nw == 8; }
+
 static AttnPlan attn_plan(int Tq, int Hq, int Hkv, int hd, int64_t L, eagle_dtype dt) {
   AttnPlan pl{};
   const int G = Hq / Hkv;
@@ -806,6 +811,26 @@ static AttnPlan attn_plan(int Tq, int Hq, int Hkv, int hd, int64_t L, eagle_dtyp
     if (tiles == 0) {
       pl.n_split = 0;
       pl.tiles_per_split = 1;
+    } else if (ring_path(hd, pl.nw)) {
+      // One workgroup per CU (the LDS ring): pick the slice length whose
+      // grid (prefix slices plus the tree slice) needs the fewest tile-times,
+      // counting whole rounds of kCUs workgroups; ties go to fewer slices.
+      const int64_t per_split_blocks = (int64_t)Hkv * pl.qgroups;
+      const int64_t tps_min = (tiles + kMergeSplits - 2) / (kMergeSplits - 1);
+      int64_t best_cost = -1;
+      pl.tiles_per_split = (int)(tps_min < 65537 ? tps_min : 65537);  // (host checks reject > 65536)
+      pl.n_split = (int)((tiles + pl.tiles_per_split - 1) / pl.tiles_per_split);
+      for (int64_t tps = tps_min; tps <= tiles && tps <= 65536 && tps < tps_min + 4096; ++tps) {
+        const int64_t n = (tiles + tps - 1) / tps;
+        if (n + 1 > kMergeSplits) continue;
+        const int64_t rounds = ((n + 1) * per_split_blocks + kCUs - 1) / kCUs;
+        const int64_t cost = rounds * tps;
+        if (best_cost < 0 || cost <= best_cost) {
+          best_cost = cost;
+          pl.tiles_per_split = (int)tps;
+          pl.n_split = (int)n;
+        }
+      }
     } else {
       const int64_t per_split_blocks = (int64_t)Hkv * pl.qgroups;
       int64_t want = (256 + per_split_blocks - 1) / per_split_blocks;
