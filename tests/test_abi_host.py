@@ -44,9 +44,11 @@ def test_workspace_queries(lib):
     assert lib.eagle_lmhead_topk_workspace(10, 4096, 128256, 20, _lib.EAGLE_BF16) == want
     assert lib.eagle_lmhead_topk_workspace(15, 256, 1024, 4, _lib.EAGLE_F32) >= 15 * 1024 * 4
     assert lib.eagle_lmhead_topk_workspace(0, 256, 1024, 4, _lib.EAGLE_F32) == 0
-    # attention: (splits + tree) x rows x (hd bf16 + 2 floats); fp32 inputs: hd floats
+    # attention: (splits + tree) x rows x (hd bf16 + 2 floats); fp32 inputs: hd floats.
+    # L = 32768 over 8 KV heads: 31 slices of 17 tiles plus the tree slice make
+    # 256 workgroups, one round of the 256 CUs
     ws = lib.eagle_tree_attn_workspace(64, 32, 8, 128, 32768, 64, _lib.EAGLE_BF16)
-    assert ws >= 33 * 64 * 32 * (128 * 2 + 8)
+    assert ws == 32 * 64 * 32 * 128 * 2 + 32 * 64 * 32 * 8
     assert lib.eagle_tree_attn_workspace(15, 4, 1, 64, 128, 15, _lib.EAGLE_F32) >= 2 * 60 * (64 + 2) * 4
     assert lib.eagle_tree_attn_workspace(64, 30, 8, 128, 100, 64, _lib.EAGLE_BF16) == 0
     assert lib.eagle_accept_workspace(64, 128256) == 64 * 32 * 16
