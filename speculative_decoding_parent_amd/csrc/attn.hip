@@ -729,20 +729,143 @@ __global__ __launch_bounds__(256) void tree_attn_f32_kernel(AttnParams p, int hd
   if (threadIdx.x == 0) p.part_ml[prow] = make_float2(M, lt);
 }
 
-// Combine the splits of each (query row, head).  With w_s = exp2((m_s - M) c):
-// out = sum_s w_s O_s / sum_s w_s l_s.  The bf16 path stores o_s = O_s / l_s
-// (so O_s = l_s o_s), the fp32 path O_s itself.  The split weights are formed
-// once per row in LDS; each thread then sums one head-dim element over the
-// splits.
+// Combine the splits of each (query row, head).  With w_s = 2^((m_s - M) c)
+// and M = max_s m_s: out = sum_s w_s O_s / sum_s w_s l_s.  The bf16 path
+// stores o_s = O_s / l_s (so O_s = l_s o_s), the fp32 path O_s itself.
 constexpr int kMergeSplits = 1024;
 
-// Combines the splits' partials, one block per output row: weights
-// 2^((m_s - M) c) (times l_s for the bf16 path, whose partials are O / l).
-template <bool NORMED_BF16>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const void* __restrict__ part_o,
-                                                         const float2* __restrict__ part_ml,
-                                                         int nsplit, int RT, int hd, float c,
-                                                         void* out, int out_bf16) {
+// bf16 partials.  One block of four waves per RPW consecutive rows (4 rows
+// of 128 dims, 8 of 64).  Lane (row rr, chunk ch) of wave v sums 8 head dims
+// of its row over the splits s = v, v + 4, v + 8, ... in ascending order,
+// one 16-byte load per split; its first 16 loads are issued before anything
+// else, so their latency overlaps wave 0's work on the split weights l_s w_s
+// (split s on lane s mod 64, read once into registers while s < 64).  Wave 0
+// then adds the other waves' sums in wave order and writes the row.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_merge_bf16_kernel(const bf16_t* __restrict__ part_o,
+                                                              const float2* __restrict__ part_ml,
+                                                              int nsplit, int RT, float c,
+                                                              void* out, int out_bf16) {
+  constexpr int CPR = HD / 8;    // 16-byte chunks per row
+  constexpr int RPW = 64 / CPR;  // rows per block
+  constexpr int NWV = 4;         // waves per block
+  constexpr int LPB = 16;        // loads in flight per lane
+  __shared__ float wsh[RPW][kMergeSplits];
+  __shared__ float dsh[RPW];
+  __shared__ f32x4 accs[NWV - 1][2][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int row0 = blockIdx.x * RPW;
+  const int rr = lane / CPR;
+  const int ch = lane - rr * CPR;
+  const int row = row0 + rr;
+  const bool live = row < RT;
+  const bf16_t* po = part_o + (size_t)(live ? row : 0) * HD + ch * 8;
+  const size_t stride = (size_t)RT * HD;
+  auto load_batch = [&](int s0, u32x4 (&v)[LPB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LPB; ++u) {
+      const int s = s0 + NWV * u;
+      v[u] = (live && s < nsplit) ? *(const u32x4*)(po + (size_t)s * stride)
+                                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 v[LPB];
+  load_batch(wave, v);
+
+  if (wave == 0) {
+    float2 ml0[RPW];
+    float M[RPW], den[RPW];
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      ml0[q] = (lane < nsplit && row0 + q < RT) ? part_ml[(size_t)lane * RT + row0 + q]
+                                                : make_float2(kNegBig, 0.f);
+      M[q] = ml0[q].x;
+    }
+    for (int s = lane + 64; s < nsplit; s += 64)
+#pragma unroll
+      for (int q = 0; q < RPW; ++q)
+        if (row0 + q < RT) M[q] = fmaxf(M[q], part_ml[(size_t)s * RT + row0 + q].x);
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      M[q] = wave_max(M[q]);
+      const float w = lane < nsplit ? exp2f((ml0[q].x - M[q]) * c) * ml0[q].y : 0.f;
+      if (lane < nsplit) wsh[q][lane] = w;
+      den[q] = w;
+    }
+    for (int s = lane + 64; s < nsplit; s += 64)
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) {
+        float w = 0.f;
+        if (row0 + q < RT) {
+          const float2 ml = part_ml[(size_t)s * RT + row0 + q];
+          w = exp2f((ml.x - M[q]) * c) * ml.y;
+        }
+        wsh[q][s] = w;
+        den[q] += w;
+      }
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+      const float d = wave_sum(den[q]);
+      if (lane == 0) dsh[q] = d;
+    }
+  }
+  __syncthreads();
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s0 = wave;;) {
+#pragma unroll
+    for (int u = 0; u < LPB; ++u) {
+      const int s = s0 + NWV * u;
+      const float w = s < nsplit ? wsh[rr][s] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(__uint_as_float(v[u][e] << 16), w, acc[2 * e]);
+        acc[2 * e + 1] = fmaf(__uint_as_float(v[u][e] & 0xffff0000u), w, acc[2 * e + 1]);
+      }
+    }
+    s0 += NWV * LPB;
+    if (s0 >= nsplit) break;
+    load_batch(s0, v);
+  }
+  if (wave > 0) {
+    accs[wave - 1][0][lane] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    accs[wave - 1][1][lane] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  __syncthreads();
+  if (wave != 0 || !live) return;
+#pragma unroll
+  for (int w = 0; w < NWV - 1; ++w) {
+    const f32x4 a = accs[w][0][lane];
+    const f32x4 b = accs[w][1][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += a[e];
+      acc[4 + e] += b[e];
+    }
+  }
+  const float dsel = dsh[rr];
+  const float inv = dsel > 0.f ? 1.0f / dsel : 0.f;
+  if (out_bf16) {
+    *(u32x4*)((bf16_t*)out + (size_t)row * HD + ch * 8) =
+        u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+              pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+  } else {
+    float* o = (float*)out + (size_t)row * HD + ch * 8;
+    *(f32x4*)o = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *(f32x4*)(o + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  }
+}
+
+// fp32 partials (O_s unnormalised), one block per output row: the split
+// weights are formed once per row in LDS; each thread then sums one head-dim
+// element over the splits.
+__global__ __launch_bounds__(128) void attn_merge_f32_kernel(const float* __restrict__ part_o,
+                                                             const float2* __restrict__ part_ml,
+                                                             int nsplit, int RT, int hd, float c,
+                                                             void* out, int out_bf16) {
   __shared__ float wsh[kMergeSplits];
   __shared__ float red[2];
   const int row = blockIdx.x;
@@ -753,28 +876,17 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const void* __restrict_
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
   __syncthreads();
   M = fmaxf(red[0], red[1]);
-  for (int s = threadIdx.x; s < nsplit; s += blockDim.x) {
-    const float2 ml = part_ml[(size_t)s * RT + row];
-    const float w = exp2f((ml.x - M) * c);
-    wsh[s] = NORMED_BF16 ? w * ml.y : w;
-  }
+  for (int s = threadIdx.x; s < nsplit; s += blockDim.x)
+    wsh[s] = exp2f((part_ml[(size_t)s * RT + row].x - M) * c);
   __syncthreads();
   float den = 0.f;
-  for (int s = 0; s < nsplit; ++s)
-    den = NORMED_BF16 ? den + wsh[s] : fmaf(part_ml[(size_t)s * RT + row].y, wsh[s], den);
+  for (int s = 0; s < nsplit; ++s) den = fmaf(part_ml[(size_t)s * RT + row].y, wsh[s], den);
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   for (int d = threadIdx.x; d < hd; d += blockDim.x) {
     float num = 0.f;
-    if (NORMED_BF16) {
-      const bf16_t* po = (const bf16_t*)part_o + (size_t)row * hd + d;
+    const float* po = part_o + (size_t)row * hd + d;
 #pragma unroll 4
-      for (int s = 0; s < nsplit; ++s)
-        num = fmaf(bf16_bits_to_f32(po[(size_t)s * RT * hd]), wsh[s], num);
-    } else {
-      const float* po = (const float*)part_o + (size_t)row * hd + d;
-#pragma unroll 4
-      for (int s = 0; s < nsplit; ++s) num = fmaf(po[(size_t)s * RT * hd], wsh[s], num);
-    }
+    for (int s = 0; s < nsplit; ++s) num = fmaf(po[(size_t)s * RT * hd], wsh[s], num);
     const float v = num * inv;
     if (out_bf16)
       ((bf16_t*)out)[(size_t)row * hd + d] = (bf16_t)f32_to_bf16_bits(v);
@@ -941,14 +1053,19 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
                        p, hd);
   }
   EAGLE_LAUNCH_CHECK();
-  if (in_dt == EAGLE_BF16)
-    hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(Tq * Hq), dim3(128), 0, stream, p.part_o,
-                       p.part_ml, pl.n_split + 1, Tq * Hq, hd, p.c, out,
-                       out_dt == EAGLE_BF16 ? 1 : 0);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(Tq * Hq), dim3(128), 0, stream, p.part_o,
-                       p.part_ml, pl.n_split + 1, Tq * Hq, hd, p.c, out,
-                       out_dt == EAGLE_BF16 ? 1 : 0);
+  const int RT = Tq * Hq;
+  const int obf = out_dt == EAGLE_BF16 ? 1 : 0;
+  if (in_dt == EAGLE_BF16) {
+    if (hd == 128)
+      hipLaunchKernelGGL(attn_merge_bf16_kernel<128>, dim3((RT + 3) / 4), dim3(256), 0, stream,
+                         (const bf16_t*)p.part_o, p.part_ml, pl.n_split + 1, RT, p.c, out, obf);
+    else
+      hipLaunchKernelGGL(attn_merge_bf16_kernel<64>, dim3((RT + 7) / 8), dim3(256), 0, stream,
+                         (const bf16_t*)p.part_o, p.part_ml, pl.n_split + 1, RT, p.c, out, obf);
+  } else {
+    hipLaunchKernelGGL(attn_merge_f32_kernel, dim3(RT), dim3(128), 0, stream,
+                       (const float*)p.part_o, p.part_ml, pl.n_split + 1, RT, hd, p.c, out, obf);
+  }
 
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;

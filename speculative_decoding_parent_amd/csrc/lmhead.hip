@@ -328,7 +328,21 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
   // pass and wave 0 merges every list directly, lane l following lists l,
   // l + 64, l + 128 and l + 192, with each list's next key read ahead.
   if (nb <= 256 && nb * k <= EAGLE_MAX_TOPK * EAGLE_MAX_TOPK) {
-    for (int c = tid; c < nb * k; c += 256) sk[c] = pk[c];
+    {
+      // every key load of the thread in flight before the first LDS store
+      constexpr int KPT = EAGLE_MAX_TOPK * EAGLE_MAX_TOPK / 256;
+      selkey_t kv[KPT];
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int c = tid + 256 * i;
+        kv[i] = c < nb * k ? pk[c] : 0ull;
+      }
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int c = tid + 256 * i;
+        if (c < nb * k) sk[c] = kv[i];
+      }
+    }
     float m = -INFINITY, s = 0.f;
     for (int w = tid; w < nb; w += 256) {
       const float2 x = st[w];
