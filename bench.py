@@ -137,7 +137,7 @@ def long_context_verify(dev, steps):
     return {"workload": "llama3-8b-long-verify: tree mask + 32 layers of tree attention, 32 Q / 8 "
                         "KV heads, hd 128, bf16 KV prefix L=32768 per layer, T=64 depth <= 7",
             "value": round(w.T / dt, 1), "unit": "nodes/s", "ms_per_step": round(dt * 1e3, 4),
-            "roofline": {"kernel": "eagle_tree_attn (tree_attn_bf16_kernel + attn_merge_kernel), "
+            "roofline": {"kernel": "eagle_tree_attn (tree_attn_ring_kernel + attn_merge_bf16_kernel), "
                                    "one layer", "bound": "hbm", "achieved": round(achieved, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
