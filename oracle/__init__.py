@@ -15,8 +15,8 @@ Sources (the pages):
     Key Architectural Mechanics sections 1-3 and the Reference Implementation
     listing;
   * "Support Eagle-3 Speculative Decoding in llama.cpp" (llama.cpp discussion
-    #15902), the opening post and the yuhuili/EAGLE3-LLaMA3.1-Instruct-8B
-    module printout;
+    #15902), the opening post, the yuhuili/EAGLE3-LLaMA3.1-Instruct-8B
+    module printout and the reply on the draft's KV cache and its eviction;
   * "EAGLE-2 Speculative Decoding Support for llama.cpp - Phase 1" (llama.cpp
     PR #13908), Implementation Characteristics (single-sequence inference).
 
@@ -31,3 +31,4 @@ from .tree import Pool, expand, rerank  # noqa: F401
 from .accept import accept_greedy, accept_sample  # noqa: F401
 from .layer import rms_norm, rope, silu, decoder_layer, LayerWeights  # noqa: F401
 from .cycle import CycleWeights, draft_and_verify_cycle  # noqa: F401
+from .kv import kv_commit, kv_commit_in_place  # noqa: F401
