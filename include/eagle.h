@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 2
+#define EAGLE_ABI_VERSION 3
 
 typedef enum {
   EAGLE_OK = 0,
@@ -250,6 +250,46 @@ int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
                  int32_t* n_accepted, int32_t* bonus_token,
                  void* workspace, size_t ws_bytes, int32_t* dev_status,
                  hipStream_t stream);
+
+/*
+ * eagle_kv_commit - append the accepted path's K/V rows to the caches.
+ *
+ * [D] reply on how large the draft's context grows: the target keeps KV
+ * entries only for accepted tokens, the draft keeps them for every candidate
+ * and needs eviction.  [G] Key Architectural Mechanics 3: the accepted tokens
+ * are the longest verified root path.  After acceptance, source rows
+ * rows[0], rows[1], ... (eagle_accept's path: node ids, root first; or the
+ * draft's slot ids of the same nodes) become cache positions L, L + 1, ...
+ * of every layer and KV head; every other candidate's rows are dropped.
+ *
+ * src_k, src_v:  [layers][Hkv][ld_src][hd] (layer stride src_layer_stride
+ *                elements); valid source rows are [0, src_rows).
+ * rows:          int32[max_rows] device.
+ * n_accepted:    int32[1] device or NULL.  Rows copied: n_accepted[0] + 1
+ *                (the root and the accepted nodes), or max_rows if NULL.  A
+ *                count above max_rows is cut to max_rows and sets
+ *                EAGLE_DEV_PATH_TRUNC; a negative n_accepted sets
+ *                EAGLE_DEV_BAD_INDEX and copies nothing.
+ * cache_k, cache_v: [layers][Hkv][ld_cache][hd] (layer stride
+ *                cache_layer_stride elements); rows L .. L + n - 1 are
+ *                written, nothing else.
+ * Every source row of a (layer, head) is read before any of its cache rows is
+ * written, so the source may lie inside the cache (tree rows stored right
+ * after the prefix: src_k = cache_k + L hd, ld_src = ld_cache); K and V, and
+ * distinct layers and heads, must not overlap.
+ * Host errors: L < 0, L + max_rows > ld_cache, max_rows outside
+ * [1, EAGLE_MAX_TREE], src_rows outside [1, ld_src], layers < 1, a layer
+ * stride below one layer's size when layers > 1, misaligned (16-byte)
+ * pointers -> EAGLE_EINVAL; hd not 64 or 128, or max_rows * hd * element size
+ * above 64 KiB -> EAGLE_EUNSUPPORTED.  Device errors: a source row outside
+ * [0, src_rows) sets EAGLE_DEV_BAD_INDEX and its cache row is left unchanged.
+ */
+int eagle_kv_commit(const void* src_k, const void* src_v, int32_t ld_src, int32_t src_rows,
+                    int64_t src_layer_stride, const int32_t* rows, const int32_t* n_accepted,
+                    int32_t max_rows, void* cache_k, void* cache_v, int64_t L,
+                    int64_t ld_cache, int64_t cache_layer_stride, int32_t layers,
+                    int32_t Hkv, int32_t hd, eagle_dtype dt, int32_t* dev_status,
+                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Decoder-layer support for the draft rounds and the verify pass.

@@ -65,6 +65,8 @@ _PROTOS = {
     "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
                                    _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P]),
     "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "eagle_kv_commit": (_I32, [_P, _P, _I32, _I32, _I64, _P, _P, _I32, _P, _P, _I64, _I64, _I64, _I32,
+                               _I32, _I32, ctypes.c_int, _P, _P]),
 }
 
 _lib = None
@@ -172,6 +174,33 @@ def eagle_tree_attn(q, k_cache, v_cache, L, k_tree, v_tree, Tk, mask, q_mask_row
         k_tree.shape[1], _ptr(mask), mask.shape[1], mask.shape[0], _ptr(q_mask_row), Tq, Hq, Hkv,
         hd, scale, in_dt, _dt(out), _ptr(out), _ptr(ws), nb, _ptr(dev_status), _stream()))
     return out
+
+
+def eagle_kv_commit(k_src, v_src, rows, k_cache, v_cache, L, n_accepted=None, src_rows=None,
+                    max_rows=None, dev_status=None):
+    """Append source rows ``rows[0 .. n)`` to the caches at positions L, L + 1, ...
+
+    Sources and caches are [Hkv][ld][hd] or [layers][Hkv][ld][hd] views whose
+    last two dimensions are contiguous (a source may be a view into the cache
+    itself).  n = n_accepted[0] + 1 (device int32) or max_rows (default
+    ``rows.shape[0]``)."""
+    if k_src.dim() == 3:
+        k_src, v_src, k_cache, v_cache = (t.unsqueeze(0) for t in (k_src, v_src, k_cache, v_cache))
+    layers, Hkv, nsrc, hd = k_src.shape
+    for t in (k_src, v_src, k_cache, v_cache):
+        if t.stride(3) != 1 or t.stride(2) != hd or t.stride(1) % hd or t.stride(1) < t.shape[2] * hd:
+            raise ValueError("sources and caches need [Hkv][ld][hd] blocks with contiguous rows")
+    if v_src.stride(0) != k_src.stride(0) or v_src.stride(1) != k_src.stride(1) or \
+            v_cache.stride(0) != k_cache.stride(0) or v_cache.stride(1) != k_cache.stride(1):
+        raise ValueError("K and V need the same strides")
+    ld_src = k_src.stride(1) // hd          # rows per head block (the cache's, for a view into it)
+    ld_cache = k_cache.stride(1) // hd
+    max_rows = rows.shape[0] if max_rows is None else max_rows
+    src_rows = nsrc if src_rows is None else src_rows
+    _check("eagle_kv_commit", lib().eagle_kv_commit(
+        _ptr(k_src), _ptr(v_src), ld_src, src_rows, k_src.stride(0), _ptr(rows), _ptr(n_accepted),
+        max_rows, _ptr(k_cache), _ptr(v_cache), L, ld_cache, k_cache.stride(0), layers, Hkv, hd,
+        _dt(k_src), _ptr(dev_status), _stream()))
 
 
 def _norm_args(in_norm):

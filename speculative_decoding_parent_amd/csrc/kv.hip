@@ -1,0 +1,150 @@
+// KV commit after acceptance: the accepted path's K/V rows become the next
+// cache positions.
+//
+// Sources: "Support Eagle-3 Speculative Decoding in llama.cpp", the reply on
+// the draft's context - the target keeps KV only for accepted tokens and the
+// draft's candidates need eviction; "EAGLE-2: Feature-Level Speculative
+// Decoding Guide", Key Architectural Mechanics 3 - the accepted tokens are
+// the longest verified root path.
+//
+// One workgroup per (KV head, K or V, layer).  The row count is read on the
+// device (eagle_accept's n_accepted), so the call needs no host round trip.
+// Every source row of the workgroup is loaded into LDS (16-byte loads, all of
+// a thread's loads in flight before the first is used) before any cache row
+// is stored, so the tree rows may sit inside the cache itself.  The count and
+// the source row ids are read together, so a call waits on two dependent
+// memory round trips.  The work is a
+// few KB per layer: the call is bound by launch latency, not bandwidth, and
+// one launch covers every layer.
+#include "common.h"
+
+namespace eagle {
+
+constexpr int kKvThreads = 256;
+constexpr int kKvStageBytes = 65536;
+constexpr int kKvChunks = kKvStageBytes / 16;          // 16-byte chunks staged
+constexpr int kKvPerThread = kKvChunks / kKvThreads;   // 16
+
+struct KvParams {
+  const char* src[2];      // K, V
+  char* dst[2];
+  int64_t src_ld, src_layer;    // bytes
+  int64_t dst_ld, dst_layer;    // bytes
+  int64_t head_src, head_dst;   // bytes per head block
+  int64_t L;
+  int src_rows, max_rows, cpr;  // cpr: 16-byte chunks per row
+  const int32_t* rows;
+  const int32_t* n_acc;
+  int32_t* status;
+};
+
+__global__ __launch_bounds__(kKvThreads) void kv_commit_kernel(KvParams p) {
+  extern __shared__ u32x4 stg[];  // max_rows x cpr chunks
+  const int head = blockIdx.x;
+  const int kv = blockIdx.y;
+  const int layer = blockIdx.z;
+  const int tid = threadIdx.x;
+  const bool reporter = tid == 0 && head == 0 && kv == 0 && layer == 0;
+  const char* src = p.src[kv] + layer * p.src_layer + head * p.head_src;
+  char* dst = p.dst[kv] + layer * p.dst_layer + head * p.head_dst + p.L * p.dst_ld;
+  const int total_max = p.max_rows * p.cpr;
+  // the count and this thread's source rows are read together; the rows
+  // past the count are never used
+  const int a = p.n_acc ? p.n_acc[0] : p.max_rows - 1;
+  int r[kKvPerThread];
+#pragma unroll
+  for (int i = 0; i < kKvPerThread; ++i) {
+    const int c = tid + kKvThreads * i;
+    r[i] = c < total_max ? p.rows[c / p.cpr] : -1;
+  }
+  int n = p.max_rows;
+  if (a < 0) {
+    if (reporter) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+    n = 0;
+  } else if (a + 1 > p.max_rows) {
+    if (reporter) set_status(p.status, EAGLE_DEV_PATH_TRUNC);
+  } else {
+    n = a + 1;
+  }
+  const int total = n * p.cpr;
+  u32x4 v[kKvPerThread];
+  bool ok[kKvPerThread];
+#pragma unroll
+  for (int i = 0; i < kKvPerThread; ++i) {
+    const int c = tid + kKvThreads * i;
+    ok[i] = false;
+    v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (c < total) {
+      const int j = c / p.cpr;
+      const int ch = c - j * p.cpr;
+      ok[i] = r[i] >= 0 && r[i] < p.src_rows;
+      if (ok[i]) v[i] = *(const u32x4*)(src + r[i] * p.src_ld + ch * 16);
+      else if (ch == 0 && head == 0 && kv == 0 && layer == 0) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kKvPerThread; ++i) {
+    const int c = tid + kKvThreads * i;
+    if (c < total) stg[c] = v[i];
+  }
+  __syncthreads();  // every source row of this (layer, head) is read
+#pragma unroll
+  for (int i = 0; i < kKvPerThread; ++i) {
+    const int c = tid + kKvThreads * i;
+    if (c < total && ok[i]) {
+      const int j = c / p.cpr;
+      const int ch = c - j * p.cpr;
+      *(u32x4*)(dst + j * p.dst_ld + ch * 16) = stg[c];
+    }
+  }
+}
+
+}  // namespace eagle
+
+extern "C" int eagle_kv_commit(const void* src_k, const void* src_v, int32_t ld_src,
+                               int32_t src_rows, int64_t src_layer_stride, const int32_t* rows,
+                               const int32_t* n_accepted, int32_t max_rows, void* cache_k,
+                               void* cache_v, int64_t L, int64_t ld_cache,
+                               int64_t cache_layer_stride, int32_t layers, int32_t Hkv,
+                               int32_t hd, eagle_dtype dt, int32_t* dev_status,
+                               hipStream_t stream) {
+  using namespace eagle;
+  EAGLE_REQUIRE(src_k && src_v && rows && cache_k && cache_v, EAGLE_EINVAL);
+  EAGLE_REQUIRE(dt == EAGLE_BF16 || dt == EAGLE_F32, EAGLE_EINVAL);
+  EAGLE_REQUIRE(Hkv >= 1 && layers >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(max_rows >= 1 && max_rows <= EAGLE_MAX_TREE, EAGLE_EINVAL);
+  EAGLE_REQUIRE(src_rows >= 1 && src_rows <= ld_src, EAGLE_EINVAL);
+  EAGLE_REQUIRE(L >= 0 && ld_cache >= 1 && L + max_rows <= ld_cache, EAGLE_EINVAL);
+  EAGLE_REQUIRE(hd == 64 || hd == 128, EAGLE_EUNSUPPORTED);
+  const int64_t es = dt == EAGLE_BF16 ? 2 : 4;
+  EAGLE_REQUIRE((int64_t)max_rows * hd * es <= kKvStageBytes, EAGLE_EUNSUPPORTED);
+  const int64_t src_layer = (int64_t)Hkv * ld_src * hd;
+  const int64_t dst_layer = (int64_t)Hkv * ld_cache * hd;
+  EAGLE_REQUIRE(layers == 1 || (src_layer_stride >= src_layer && cache_layer_stride >= dst_layer),
+                EAGLE_EINVAL);
+  const uintptr_t al = (uintptr_t)src_k | (uintptr_t)src_v | (uintptr_t)cache_k |
+                       (uintptr_t)cache_v;
+  EAGLE_REQUIRE((al & 15) == 0, EAGLE_EINVAL);
+  KvParams p{};
+  p.src[0] = (const char*)src_k;
+  p.src[1] = (const char*)src_v;
+  p.dst[0] = (char*)cache_k;
+  p.dst[1] = (char*)cache_v;
+  p.src_ld = (int64_t)hd * es;
+  p.dst_ld = (int64_t)hd * es;
+  p.head_src = (int64_t)ld_src * hd * es;
+  p.head_dst = ld_cache * hd * es;
+  p.src_layer = (layers == 1 ? src_layer : src_layer_stride) * es;
+  p.dst_layer = (layers == 1 ? dst_layer : cache_layer_stride) * es;
+  p.L = L;
+  p.src_rows = src_rows;
+  p.max_rows = max_rows;
+  p.cpr = (int)(hd * es / 16);
+  p.rows = rows;
+  p.n_acc = n_accepted;
+  p.status = dev_status;
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(Hkv, 2, layers), dim3(kKvThreads),
+                     (size_t)max_rows * hd * es, stream, p);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.eagle_abi_version() == 2
+    assert lib.eagle_abi_version() == 3
     for code in (0, -1, -2, -3, -4, 7):
         assert lib.eagle_status_string(code)
 
@@ -180,3 +180,34 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         _lib.lib()
+
+
+def test_kv_commit_argument_errors(lib):
+    f = lib.eagle_kv_commit
+    BF, F32 = _lib.EAGLE_BF16, _lib.EAGLE_F32
+    names = ["src_k", "src_v", "ld_src", "src_rows", "src_ls", "rows", "n_acc", "max_rows",
+             "cache_k", "cache_v", "L", "ld_cache", "cache_ls", "layers", "Hkv", "hd", "dt",
+             "status", "stream"]
+    good = dict(src_k=FAKE, src_v=FAKE, ld_src=64, src_rows=64, src_ls=0, rows=FAKE, n_acc=None,
+                max_rows=8, cache_k=FAKE, cache_v=FAKE, L=100, ld_cache=200, cache_ls=0, layers=1,
+                Hkv=8, hd=128, dt=BF, status=None, stream=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(*[a[n] for n in names])
+    assert call(L=193) == EINVAL                      # L + max_rows > ld_cache
+    assert call(L=-1) == EINVAL
+    assert call(max_rows=0) == EINVAL
+    assert call(max_rows=257, ld_cache=1000) == EINVAL
+    assert call(src_rows=65) == EINVAL
+    assert call(src_rows=0) == EINVAL
+    assert call(rows=None) == EINVAL
+    assert call(cache_v=None) == EINVAL
+    assert call(src_k=FAKE + 8) == EINVAL             # 16-byte alignment
+    assert call(layers=0) == EINVAL
+    assert call(layers=2) == EINVAL                   # layer strides below one layer
+    assert call(layers=2, src_ls=8 * 64 * 128, cache_ls=8 * 200 * 128 - 1) == EINVAL
+    assert call(Hkv=0) == EINVAL
+    assert call(dt=7) == EINVAL
+    assert call(hd=96) == EUNSUP
+    assert call(dt=F32, max_rows=129, ld_cache=1000) == EUNSUP   # 129 x 128 x 4 > 64 KiB

@@ -1,0 +1,128 @@
+"""GPU parity: eagle_kv_commit against the oracle, byte for byte."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_parent_amd import _lib, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(t):
+    t = t.cpu()
+    return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.view(torch.int32).numpy()
+
+
+def draw(seed, layers, hkv, S, C, hd, dt=torch.bfloat16):
+    g = inputs.rng(700 + seed, inputs.STREAM_Q, S * 1000 + C)
+    return (inputs.normal(g, (layers, hkv, S, hd), dtype=dt), inputs.normal(g, (layers, hkv, S, hd), dtype=dt),
+            inputs.normal(g, (layers, hkv, C, hd), dtype=dt), inputs.normal(g, (layers, hkv, C, hd), dtype=dt))
+
+
+def path_of(par, node):
+    p = []
+    while node != -1:
+        p.append(node)
+        node = int(par[node])
+    return p[::-1]
+
+
+def run(dev, sk, sv, ck, cv, rows, L, n_acc=None, max_rows=None, src_rows=None, squeeze=False):
+    print(f"kv_commit layers={sk.shape[0]} Hkv={sk.shape[1]} S={sk.shape[2]} C={ck.shape[2]} "
+          f"hd={sk.shape[3]} {sk.dtype} L={L} rows={list(rows)[:8]} n_acc={n_acc}", flush=True)
+    dsk, dsv, dck, dcv = (t.to(dev) for t in (sk, sv, ck, cv))
+    if squeeze:
+        dsk, dsv, dck, dcv = (t[0] for t in (dsk, dsv, dck, dcv))
+    r = torch.tensor(list(rows), dtype=torch.int32, device=dev)
+    na = None if n_acc is None else torch.tensor([n_acc], dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    _lib.eagle_kv_commit(dsk, dsv, r, dck, dcv, L, n_accepted=na, max_rows=max_rows,
+                         src_rows=src_rows, dev_status=st)
+    torch.cuda.synchronize()
+    if squeeze:
+        dck, dcv = dck[None], dcv[None]
+    return dck.cpu(), dcv.cpu(), int(st.item())
+
+
+@pytest.mark.parametrize("layers,hkv,hd,T,L,dt", [
+    (1, 8, 128, 64, 4096, torch.bfloat16),     # Llama-3-8B verify layer
+    (32, 8, 128, 64, 300, torch.bfloat16),     # 32 stacked layers in one launch
+    (1, 4, 128, 60, 2048, torch.bfloat16),     # Qwen2-7B heads
+    (2, 1, 64, 15, 128, torch.float32),        # tiny fp32 workload
+    (3, 2, 64, 40, 77, torch.bfloat16),
+])
+def test_accepted_path_matches_oracle(dev, layers, hkv, hd, T, L, dt):
+    par = inputs.random_tree(inputs.rng(710, T, L), T, 7, 4)
+    node = int(np.argmax([len(path_of(par, i)) for i in range(T)]))
+    path = path_of(par, node)
+    max_rows = 8
+    rows = path + [-1] * (max_rows - len(path))          # eagle_accept's padding
+    sk, sv, ck, cv = draw(1, layers, hkv, T, L + max_rows + 5, hd, dt)
+    gk, gv, st = run(dev, sk, sv, ck, cv, rows, L, n_acc=len(path) - 1, max_rows=max_rows)
+    assert st == 0
+    rk, rv = oracle.kv_commit(bits(sk), bits(sv), path, len(path), bits(ck), bits(cv), L)
+    assert np.array_equal(bits(gk), rk) and np.array_equal(bits(gv), rv)
+
+
+def test_full_size_long_context_cache(dev):
+    """Two layers of the long-context cache (L = 32768, 8 KV heads): the
+    committed rows and the rows around them, checked one by one."""
+    layers, hkv, hd, T, L = 2, 8, 128, 64, 32768
+    C = L + T
+    sk, sv, _, _ = draw(2, layers, hkv, T, 1, hd)
+    ck = torch.zeros((layers, hkv, C, hd), dtype=torch.bfloat16)
+    cv = torch.ones((layers, hkv, C, hd), dtype=torch.bfloat16)
+    path = [0, 3, 9, 20, 41, 63]
+    gk, gv, st = run(dev, sk, sv, ck, cv, path, L, n_acc=len(path) - 1, max_rows=len(path))
+    assert st == 0
+    for j, r in enumerate(path):
+        assert torch.equal(gk[:, :, L + j], sk[:, :, r]) and torch.equal(gv[:, :, L + j], sv[:, :, r])
+    assert torch.count_nonzero(gk[:, :, :L]) == 0 and torch.all(gv[:, :, :L] == 1)
+    assert torch.count_nonzero(gk[:, :, L + len(path):]) == 0
+
+
+def test_in_place_layout_with_aliasing(dev):
+    """Tree rows stored right after the prefix; the path skips rows, so
+    destinations overlap sources of later path entries."""
+    layers, hkv, hd, T, L = 2, 8, 128, 30, 100
+    _, _, ck, cv = draw(3, layers, hkv, 1, L + T + 6, hd)
+    path = [0, 2, 5, 6, 11, 29]
+    dck, dcv = ck.to(dev), cv.to(dev)
+    r = torch.tensor(path, dtype=torch.int32, device=dev)
+    na = torch.tensor([len(path) - 1], dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    print("kv_commit in place", flush=True)
+    _lib.eagle_kv_commit(dck[:, :, L:L + T], dcv[:, :, L:L + T], r, dck, dcv, L, n_accepted=na,
+                         dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rk, rv = oracle.kv_commit_in_place(bits(ck), bits(cv), L, path, len(path))
+    assert np.array_equal(bits(dck), rk) and np.array_equal(bits(dcv), rv)
+
+
+def test_counts_and_status(dev):
+    layers, hkv, hd, T, L = 1, 2, 128, 12, 20
+    sk, sv, ck, cv = draw(4, layers, hkv, T, L + 10, hd)
+    rows = [0, 4, 7, 9]
+    # only the root (n_accepted = 0)
+    gk, gv, st = run(dev, sk, sv, ck, cv, rows, L, n_acc=0, max_rows=4)
+    rk, rv = oracle.kv_commit(bits(sk), bits(sv), rows, 1, bits(ck), bits(cv), L)
+    assert st == 0 and np.array_equal(bits(gk), rk) and np.array_equal(bits(gv), rv)
+    # no count: all max_rows rows, with the 3-dimensional (one layer) form
+    gk, gv, st = run(dev, sk, sv, ck, cv, rows, L, squeeze=True)
+    rk, rv = oracle.kv_commit(bits(sk), bits(sv), rows, 4, bits(ck), bits(cv), L)
+    assert st == 0 and np.array_equal(bits(gk), rk) and np.array_equal(bits(gv), rv)
+    # a count above max_rows is cut and flagged
+    gk, gv, st = run(dev, sk, sv, ck, cv, rows, L, n_acc=9, max_rows=4)
+    assert st == _lib.DEV_PATH_TRUNC and np.array_equal(bits(gk), rk) and np.array_equal(bits(gv), rv)
+    # a negative count copies nothing
+    gk, gv, st = run(dev, sk, sv, ck, cv, rows, L, n_acc=-1, max_rows=4)
+    assert st == _lib.DEV_BAD_INDEX and torch.equal(gk, ck) and torch.equal(gv, cv)
+    # a source row outside [0, src_rows) is flagged and its cache row kept
+    bad = [0, 4, 12, 9]
+    gk, gv, st = run(dev, sk, sv, ck, cv, bad, L, n_acc=3, max_rows=4, src_rows=12)
+    assert st == _lib.DEV_BAD_INDEX
+    rk, rv = oracle.kv_commit(bits(sk), bits(sv), [0, 4], 2, bits(ck), bits(cv), L)
+    rk[:, :, L + 3], rv[:, :, L + 3] = bits(sk)[:, :, 9], bits(sv)[:, :, 9]
+    assert np.array_equal(bits(gk), rk) and np.array_equal(bits(gv), rv)
