@@ -86,6 +86,31 @@ def time_lmhead(cyc, T, iters):
     return float(np.mean(ms)) / 1e3, float(np.min(ms)) / 1e3
 
 
+def graph_time_us(fn, n_calls=20, reps=5):
+    """Mean µs per call of a call whose GPU work is shorter than the binding's
+    own host time: n_calls back-to-back calls are captured in a HIP graph
+    and the replays are timed with HIP events on the replay stream."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fn()
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(n_calls):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * n_calls)
+
+
 def attn_bytes(Tq, hq, hkv, hd, L, Tk):
     """Algorithmic bytes of one tree-attention call: the prefix K/V, the tree
     K/V, q in and out (bf16), and the mask rows."""
@@ -154,28 +179,8 @@ def long_context_verify(dev, steps):
     path = path[::-1]
     rows = torch.tensor(path, dtype=torch.int32, device=dev)
     n_acc = torch.tensor([len(path) - 1], dtype=torch.int32, device=dev)
-    # a few µs of GPU work per call, less than the binding's own host time:
-    # 20 calls are captured in a HIP graph and the replay is timed
-    ksrc, vsrc = kc[:, :, w.L:], vc[:, :, w.L:]
-    n_calls = 20
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        _lib.eagle_kv_commit(ksrc, vsrc, rows, kc, vc, w.L, n_accepted=n_acc)
-    stream.wait_stream(side)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(n_calls):
-            _lib.eagle_kv_commit(ksrc, vsrc, rows, kc, vc, w.L, n_accepted=n_acc)
-    graph.replay()
-    torch.cuda.synchronize()
-    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ka.record(stream)
-    for _ in range(5):
-        graph.replay()
-    kb.record(stream)
-    torch.cuda.synchronize()
-    kv_us = ka.elapsed_time(kb) * 1e3 / (5 * n_calls)
+    kv_us = graph_time_us(lambda: _lib.eagle_kv_commit(kc[:, :, w.L:], vc[:, :, w.L:], rows, kc,
+                                                        vc, w.L, n_accepted=n_acc))
     kv_bytes = 2 * 2 * w.layers * w.hkv * len(path) * w.hd * 2       # K and V, read and written
     del kc, vc
     return {"workload": "llama3-8b-long-verify: tree mask + 32 layers of tree attention, 32 Q / 8 "
@@ -299,6 +304,14 @@ def main():
                      "avg_us": round(avg_s * 1e6, 2), "min_us": round(min_s * 1e6, 2),
                      "bytes_per_launch": nbytes},
     }
+    # confidence gate at a draft round's shape (10 nodes x top-10), in place
+    glp = -torch.sort(torch.rand((Td, w.topk), device=dev) * 8, dim=1).values
+    gate_us = graph_time_us(lambda: _lib.eagle_gate_children(glp, 2.0, 4, out=glp))
+    line["gate"] = {"kernel": f"eagle_gate_children (gate_children_kernel), {Td} nodes x top-"
+                              f"{w.topk}, tau 2, up to 4 branches", "avg_us": round(gate_us, 2),
+                    "bytes_per_launch": Td * w.topk * 8 + Td * 8,
+                    "timing": "HIP graph of 20 back-to-back calls, replayed 5 times",
+                    "note": "under 1 KB per launch: launch-latency bound"}
     if not args.no_long_context:
         del cyc
         torch.cuda.empty_cache()

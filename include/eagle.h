@@ -212,6 +212,30 @@ int eagle_expand_rerank(int32_t mode,
                         int32_t* dev_status, hipStream_t stream);
 
 /*
+ * eagle_gate_children - confidence-gated branching of drafted nodes.
+ *
+ * [G] Key Architectural Mechanics 2: a drafted node's confidence is
+ * C = P(y_(1)) / P(y_(2)); above a threshold tau the draft deepens a linear
+ * chain, at or below it the node branches into 2 to 4 children (tau = 2.0 in
+ * [G]'s Reference Implementation).  Reading: child j (logp sorted
+ * descending) is kept while fewer than max_branch are kept and
+ * logp_j - logp_0 >= -ln(tau), i.e. P_j >= P_(1) / tau: one child exactly when
+ * C > tau.  Children not kept get log-probability -inf, so EXPAND gives them
+ * value -inf and they rank below every kept candidate.
+ *
+ * logp f32[rows][k] device (eagle_lmhead_topk's topk_logp) -> out_logp
+ * f32[rows][k] (may be logp itself); kept int32[rows] (nullable): children
+ * kept; confidence f32[rows] (nullable): exp(logp_0 - logp_1), +inf for
+ * k = 1.  The compare is one fp32 subtraction with ln(tau) computed in fp64
+ * and rounded once to fp32.
+ * Errors: rows < 1, k outside [1, EAGLE_MAX_TOPK], max_branch < 1, tau < 1
+ * or not finite, null logp/out_logp -> EAGLE_EINVAL.
+ */
+int eagle_gate_children(const float* logp, int32_t rows, int32_t k, float tau,
+                        int32_t max_branch, float* out_logp, int32_t* kept,
+                        float* confidence, hipStream_t stream);
+
+/*
  * eagle_accept - accept the longest verified path through the tree.
  *
  * [G] Key Architectural Mechanics 3: a greedy or sampling verifier walks the

@@ -65,6 +65,7 @@ _PROTOS = {
     "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
                                    _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P]),
     "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "eagle_gate_children": (_I32, [_P, _I32, _I32, _F32, _I32, _P, _P, _P, _P]),
     "eagle_kv_commit": (_I32, [_P, _P, _I32, _I32, _I64, _P, _P, _I32, _P, _P, _I64, _I64, _I64, _I32,
                                _I32, _I32, ctypes.c_int, _P, _P]),
 }
@@ -174,6 +175,21 @@ def eagle_tree_attn(q, k_cache, v_cache, L, k_tree, v_tree, Tk, mask, q_mask_row
         k_tree.shape[1], _ptr(mask), mask.shape[1], mask.shape[0], _ptr(q_mask_row), Tq, Hq, Hkv,
         hd, scale, in_dt, _dt(out), _ptr(out), _ptr(ws), nb, _ptr(dev_status), _stream()))
     return out
+
+
+def eagle_gate_children(logp, tau=2.0, max_branch=4, out=None, kept=None, confidence=None):
+    """Confidence gate over sorted top-k log-probs f32 [rows][k]; returns
+    (gated log-probs, kept int32 [rows], confidence f32 [rows]).  ``out`` may
+    be ``logp`` itself (in place)."""
+    rows, k = logp.shape
+    dev = logp.device
+    out = torch.empty_like(logp) if out is None else out
+    kept = torch.empty(rows, dtype=torch.int32, device=dev) if kept is None else kept
+    confidence = torch.empty(rows, dtype=torch.float32, device=dev) if confidence is None else confidence
+    _check("eagle_gate_children", lib().eagle_gate_children(
+        _ptr(logp), rows, k, float(tau), max_branch, _ptr(out), _ptr(kept), _ptr(confidence),
+        _stream()))
+    return out, kept, confidence
 
 
 def eagle_kv_commit(k_src, v_src, rows, k_cache, v_cache, L, n_accepted=None, src_rows=None,

@@ -152,6 +152,30 @@ __global__ __launch_bounds__(1024) void rerank_kernel(
   }
 }
 
+// Confidence gate: one thread per drafted node.  Child j is kept while fewer
+// than max_branch are kept and logp_j - logp_0 >= -ln(tau) (one fp32
+// subtraction and compare, as written); the rest become -inf.
+__global__ __launch_bounds__(64) void gate_children_kernel(const float* __restrict__ lp, int rows,
+                                                           int k, float neg_ln_tau,
+                                                           int max_branch, float* out,
+                                                           int32_t* kept, float* conf) {
+  const int r = blockIdx.x * 64 + threadIdx.x;
+  if (r >= rows) return;
+  const float* x = lp + (size_t)r * k;
+  float* y = out + (size_t)r * k;
+  const float l0 = x[0];
+  const float l1 = k > 1 ? x[1] : 0.f;
+  int n = 0;
+  for (int j = 0; j < k; ++j) {
+    const float v = x[j];
+    const bool keep = (n < max_branch) & (__fsub_rn(v, l0) >= neg_ln_tau);
+    n += keep ? 1 : 0;
+    y[j] = keep ? v : -INFINITY;
+  }
+  if (kept) kept[r] = n;
+  if (conf) conf[r] = k > 1 ? expf(__fsub_rn(l0, l1)) : INFINITY;
+}
+
 }  // namespace eagle
 
 extern "C" int eagle_expand_rerank(int32_t mode, int32_t* pool_token, int32_t* pool_parent,
@@ -183,6 +207,20 @@ extern "C" int eagle_expand_rerank(int32_t mode, int32_t* pool_token, int32_t* p
   } else {
     return EAGLE_EINVAL;
   }
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_gate_children(const float* logp, int32_t rows, int32_t k, float tau,
+                                   int32_t max_branch, float* out_logp, int32_t* kept,
+                                   float* confidence, hipStream_t stream) {
+  using namespace eagle;
+  EAGLE_REQUIRE(logp && out_logp, EAGLE_EINVAL);
+  EAGLE_REQUIRE(rows >= 1 && k >= 1 && k <= EAGLE_MAX_TOPK && max_branch >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(tau >= 1.0f && tau < INFINITY, EAGLE_EINVAL);
+  const float neg_ln_tau = (float)(-log((double)tau));
+  hipLaunchKernelGGL(gate_children_kernel, dim3((rows + 63) / 64), dim3(64), 0, stream, logp, rows,
+                     k, neg_ln_tau, max_branch, out_logp, kept, confidence);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

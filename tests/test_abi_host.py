@@ -211,3 +211,16 @@ def test_kv_commit_argument_errors(lib):
     assert call(dt=7) == EINVAL
     assert call(hd=96) == EUNSUP
     assert call(dt=F32, max_rows=129, ld_cache=1000) == EUNSUP   # 129 x 128 x 4 > 64 KiB
+
+
+def test_gate_argument_errors(lib):
+    f = lib.eagle_gate_children
+    assert f(None, 4, 10, 2.0, 4, FAKE, None, None, None) == EINVAL
+    assert f(FAKE, 4, 10, 2.0, 4, None, None, None, None) == EINVAL
+    assert f(FAKE, 0, 10, 2.0, 4, FAKE, None, None, None) == EINVAL
+    assert f(FAKE, 4, 0, 2.0, 4, FAKE, None, None, None) == EINVAL
+    assert f(FAKE, 4, 65, 2.0, 4, FAKE, None, None, None) == EINVAL
+    assert f(FAKE, 4, 10, 2.0, 0, FAKE, None, None, None) == EINVAL
+    assert f(FAKE, 4, 10, 0.5, 4, FAKE, None, None, None) == EINVAL
+    assert f(FAKE, 4, 10, float("inf"), 4, FAKE, None, None, None) == EINVAL
+    assert f(FAKE, 4, 10, float("nan"), 4, FAKE, None, None, None) == EINVAL
