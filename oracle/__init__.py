@@ -33,3 +33,4 @@ from .layer import rms_norm, rope, silu, decoder_layer, LayerWeights  # noqa: F4
 from .cycle import CycleWeights, draft_and_verify_cycle  # noqa: F401
 from .kv import kv_commit, kv_commit_in_place  # noqa: F401
 from .gate import gate_children  # noqa: F401
+from .fusion import fuse3  # noqa: F401
