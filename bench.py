@@ -312,6 +312,23 @@ def main():
                     "bytes_per_launch": Td * w.topk * 8 + Td * 8,
                     "timing": "HIP graph of 20 back-to-back calls, replayed 5 times",
                     "note": "under 1 KB per launch: launch-latency bound"}
+    # Eagle-3 fusion of the accepted path's three recorded hidden states
+    # (8 rows: root + 7 accepted at the tree's depth bound), d = 4096 -> 4096
+    Mf = 8
+    hs = [inputs.device_normal((Mf, w.d), 5000 + i, dev) for i in range(3)]
+    w_fc = inputs.device_normal((w.d, 3 * w.d), 5003, dev) * (1.0 / np.sqrt(3 * w.d))
+    g_out = torch.empty((Mf, w.d), dtype=torch.float32, device=dev)
+    f_ws = torch.zeros(max(_lib.lib().eagle_linear_workspace(Mf, 3 * w.d, w.d, 0), 256),
+                       dtype=torch.uint8, device=dev)
+    fuse_us = graph_time_us(lambda: _lib.eagle_fuse3(*hs, w_fc, out=g_out, workspace=f_ws))
+    fuse_bytes = w.d * 3 * w.d * 2 + Mf * 3 * w.d * 2 + Mf * w.d * 4
+    line["fusion"] = {"kernel": f"eagle_fuse3 (linear_rows_kernel, three input segments), M={Mf}, "
+                                f"3x{w.d} -> {w.d}", "bound": "hbm",
+                      "achieved": round(fuse_bytes / fuse_us / 1e3, 1), "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": round(fuse_bytes / fuse_us / 1e3 / HBM_PEAK_GBS, 4),
+                      "avg_us": round(fuse_us, 2), "bytes_per_launch": fuse_bytes,
+                      "timing": "HIP graph of 20 back-to-back calls, replayed 5 times"}
+    del hs, w_fc
     if not args.no_long_context:
         del cyc
         torch.cuda.empty_cache()

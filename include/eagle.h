@@ -364,6 +364,26 @@ int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, int32_t N,
                  size_t ws_bytes, hipStream_t stream);
 
 /*
+ * eagle_fuse3 - Eagle-3 feature fusion: out[m][n] = sum_k x[m][k] W[n][k] with
+ * x[m] = [h_low[m] ; h_mid[m] ; h_high[m]] (K = 3 d), read from the three
+ * buffers directly.
+ *
+ * [D] opening post: the target's hidden states after its first, middle and
+ * last decoder layers are recorded; [D] replies: a single FC layer maps the
+ * three to one feature g, which feeds the draft's decoder layer.  Reading: the
+ * segments are concatenated in the order low, middle, high.
+ *   h_low, h_mid, h_high [M][d] bf16 (M 1..16, d % 128 == 0), W [N][3 d] bf16,
+ *   out [M][N] out_dt; workspace >= eagle_linear_workspace(M, 3 d, N, 0)
+ *   bytes, with the zeroing rule of the projection workspaces.
+ *   Errors: null or misaligned (16-byte) pointers, M, d or N < 1 ->
+ *   EAGLE_EINVAL; M > 16 or d % 128 != 0 -> EAGLE_EUNSUPPORTED; small
+ *   workspace -> EAGLE_EWORKSPACE.
+ */
+int eagle_fuse3(const void* h_low, const void* h_mid, const void* h_high, int32_t M,
+                int32_t d, const void* W, int32_t N, void* out, eagle_dtype out_dt,
+                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * eagle_linear_swiglu - out[m][n] = silu(x W_gate^T)[m][n] * (x W_up^T)[m][n],
  * the LlamaMLP hidden activation.  x [M][K] bf16 (with an optional deferred
  * RMSNorm: in_ssq [in_parts][M] or NULL, in_eps), W_gate/W_up [N][K] bf16,

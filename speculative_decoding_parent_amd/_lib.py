@@ -65,6 +65,7 @@ _PROTOS = {
     "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
                                    _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P]),
     "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "eagle_fuse3": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, ctypes.c_int, _P, _SZ, _P]),
     "eagle_gate_children": (_I32, [_P, _I32, _I32, _F32, _I32, _P, _P, _P, _P]),
     "eagle_kv_commit": (_I32, [_P, _P, _I32, _I32, _I64, _P, _P, _I32, _P, _P, _I64, _I64, _I64, _I32,
                                _I32, _I32, ctypes.c_int, _P, _P]),
@@ -174,6 +175,20 @@ def eagle_tree_attn(q, k_cache, v_cache, L, k_tree, v_tree, Tk, mask, q_mask_row
         _ptr(q), _ptr(k_cache), _ptr(v_cache), L, ld_cache, _ptr(k_tree), _ptr(v_tree), Tk,
         k_tree.shape[1], _ptr(mask), mask.shape[1], mask.shape[0], _ptr(q_mask_row), Tq, Hq, Hkv,
         hd, scale, in_dt, _dt(out), _ptr(out), _ptr(ws), nb, _ptr(dev_status), _stream()))
+    return out
+
+
+def eagle_fuse3(h_low, h_mid, h_high, W, out=None, out_dtype=torch.float32, workspace=None):
+    """Eagle-3 fusion: [h_low ; h_mid ; h_high] (each [M][d] bf16) times W^T
+    (W [N][3 d] bf16), without forming the concatenation."""
+    M, d = h_low.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=h_low.device)
+    nb = lib().eagle_linear_workspace(M, 3 * d, N, 0)
+    ws = _workspace(nb, h_low.device, workspace)
+    _check("eagle_fuse3", lib().eagle_fuse3(_ptr(h_low), _ptr(h_mid), _ptr(h_high), M, d, _ptr(W),
+                                            N, _ptr(out), _dt(out), _ptr(ws), nb, _stream()))
     return out
 
 

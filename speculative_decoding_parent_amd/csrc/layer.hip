@@ -549,6 +549,8 @@ struct SkParams {
   int nsub;                // rope: column blocks per head
   RopeArgs rope;
   RowNorm in;
+  const bf16_t* xseg[3];   // kseg > 0: x is these three [M][kseg] blocks side by side
+  int kseg;
 };
 
 // Hand-off between workgroups without cache-wide write-backs.  Partial tiles
@@ -627,7 +629,8 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
     wr[mt] = w + (size_t)row * K + g * 8;
   }
   const bool xok = r16 < M;
-  const bf16_t* xr = p.x + (size_t)min(r16, M - 1) * K + g * 8;
+  const int xrow = min(r16, M - 1);
+  const bf16_t* xr = p.x + (size_t)xrow * K + g * 8;
   const int nk = K / kWsKG;
   const int kb = (int)((int64_t)yb * nk / p.S);
   const int ke = (int)((int64_t)(yb + 1) * nk / p.S);
@@ -637,9 +640,15 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
   for (int mt = 0; mt < kSkMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 wa[kSkMT][4], wb[kSkMT][4], xa[4], xbv[4];
   auto load = [&](int kk, u32x4 (&w)[kSkMT][4], u32x4 (&xv)[4]) {
+    const bf16_t* xp = xr + kk * kWsKG;
+    if (p.kseg) {  // a 128-wide k step lies inside one segment (kseg % 128 == 0)
+      const int kel = kk * kWsKG;
+      const int sg = kel / p.kseg;
+      xp = p.xseg[sg] + (size_t)xrow * p.kseg + (kel - sg * p.kseg) + g * 8;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      xv[i] = xok ? *(const u32x4*)(xr + kk * kWsKG + i * 32) : u32x4{0u, 0u, 0u, 0u};
+      xv[i] = xok ? *(const u32x4*)(xp + i * 32) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int mt = 0; mt < kSkMT; ++mt)
 #pragma unroll
@@ -959,6 +968,33 @@ extern "C" int eagle_linear(const void* x, int32_t M, int32_t K, const void* W, 
                      out_dt == EAGLE_BF16 ? 1 : 0, ks,
                      ks > 1 ? eagle::lin_partials(workspace) : nullptr};
   eagle::dispatch_lin<0>(p, stream);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_fuse3(const void* h_low, const void* h_mid, const void* h_high, int32_t M,
+                           int32_t d, const void* W, int32_t N, void* out, eagle_dtype out_dt,
+                           void* workspace, size_t ws_bytes, hipStream_t stream) {
+  EAGLE_REQUIRE(h_low && h_mid && h_high && W && out, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M >= 1 && d >= 1 && N >= 1 && (int64_t)3 * d <= 0x7fffffff, EAGLE_EINVAL);
+  EAGLE_REQUIRE(out_dt == EAGLE_BF16 || out_dt == EAGLE_F32, EAGLE_EINVAL);
+  EAGLE_REQUIRE(M <= eagle::kSkMaxRows && d % eagle::kWsKG == 0, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(aligned16(h_low) && aligned16(h_mid) && aligned16(h_high) && aligned16(W) &&
+                    aligned16(out), EAGLE_EINVAL);
+  const int K = 3 * d;
+  const size_t need = eagle::lin_workspace(M, K, N, 0);
+  EAGLE_REQUIRE(need == 0 || (workspace && aligned16(workspace)), EAGLE_EINVAL);
+  EAGLE_REQUIRE(ws_bytes >= need, EAGLE_EWORKSPACE);
+  const eagle::SkPlan pl = eagle::sk_plan(eagle::SK_PLAIN, M, K, N, 0, 0);
+  EAGLE_REQUIRE(pl.nblk <= eagle::kSkMaxBlocks, EAGLE_EUNSUPPORTED);
+  eagle::SkParams p{};
+  p.x = (const bf16_t*)h_low; p.M = M; p.K = K; p.w0 = (const bf16_t*)W; p.N = N;
+  p.out = out; p.out_bf16 = out_dt == EAGLE_BF16 ? 1 : 0;
+  p.xseg[0] = (const bf16_t*)h_low;
+  p.xseg[1] = (const bf16_t*)h_mid;
+  p.xseg[2] = (const bf16_t*)h_high;
+  p.kseg = d;
+  eagle::launch_rows<eagle::SK_PLAIN>(p, pl, pl.total ? workspace : nullptr, stream);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

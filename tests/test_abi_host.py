@@ -224,3 +224,20 @@ def test_gate_argument_errors(lib):
     assert f(FAKE, 4, 10, 0.5, 4, FAKE, None, None, None) == EINVAL
     assert f(FAKE, 4, 10, float("inf"), 4, FAKE, None, None, None) == EINVAL
     assert f(FAKE, 4, 10, float("nan"), 4, FAKE, None, None, None) == EINVAL
+
+
+def test_fuse3_argument_errors(lib):
+    f = lib.eagle_fuse3
+    BF = _lib.EAGLE_BF16
+    ok = [FAKE, FAKE, FAKE, 8, 4096, FAKE, 4096, FAKE, BF, FAKE, 1 << 30, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(0, None) == EINVAL
+    assert call(2, FAKE + 4) == EINVAL
+    assert call(3, 0) == EINVAL
+    assert call(3, 17) == EUNSUP          # more than 16 rows
+    assert call(4, 4000) == EUNSUP        # d not a multiple of 128
+    assert call(8, 9) == EINVAL
+    assert call(10, 0) == EWS
