@@ -18,7 +18,8 @@ Sources (the pages):
     #15902), the opening post, the yuhuili/EAGLE3-LLaMA3.1-Instruct-8B
     module printout and the reply on the draft's KV cache and its eviction;
   * "EAGLE-2 Speculative Decoding Support for llama.cpp - Phase 1" (llama.cpp
-    PR #13908), Implementation Characteristics (single-sequence inference).
+    PR #13908), Implementation Characteristics (single-sequence inference)
+    and the test setup (mixed sampling: temperature, top_k, top_p).
 
 Parity status: every function here is pinned by tests under ``tests/`` marked
 ``not gpu`` (closed forms, library routines on special cases, brute force on
@@ -34,3 +35,4 @@ from .cycle import CycleWeights, draft_and_verify_cycle  # noqa: F401
 from .kv import kv_commit, kv_commit_in_place  # noqa: F401
 from .gate import gate_children  # noqa: F401
 from .fusion import fuse3  # noqa: F401
+from .sampling import process_logits  # noqa: F401
