@@ -312,6 +312,22 @@ def main():
                     "bytes_per_launch": Td * w.topk * 8 + Td * 8,
                     "timing": "HIP graph of 20 back-to-back calls, replayed 5 times",
                     "note": "under 1 KB per launch: launch-latency bound"}
+    # mixed-sampling processing of the verify pass's logits (64 rows of the
+    # vocabulary; llama.cpp-like settings: temperature 0.8, top-k 40, top-p 0.95)
+    lg = inputs.device_normal((w.T, w.vocab), 5100, dev, dtype=torch.float32) * 2.0
+    lg_out = torch.empty_like(lg)
+    lp_kept = torch.empty(w.T, dtype=torch.int32, device=dev)
+    lp_us = graph_time_us(lambda: _lib.eagle_logits_process(lg, 0.8, 40, 0.95, out=lg_out,
+                                                            kept=lp_kept), n_calls=10)
+    lp_bytes = 2 * w.T * w.vocab * 4
+    line["logits_process"] = {"kernel": f"eagle_logits_process (logits_process_kernel), {w.T} rows x "
+                                        f"V={w.vocab}, temperature 0.8, top-k 40, top-p 0.95",
+                              "bound": "hbm", "achieved": round(lp_bytes / lp_us / 1e3, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(lp_bytes / lp_us / 1e3 / HBM_PEAK_GBS, 4),
+                              "avg_us": round(lp_us, 2), "bytes_per_launch": lp_bytes,
+                              "timing": "HIP graph of 10 back-to-back calls, replayed 5 times"}
+    del lg, lg_out
     # Eagle-3 fusion of the accepted path's three recorded hidden states
     # (8 rows: root + 7 accepted at the tree's depth bound), d = 4096 -> 4096
     Mf = 8

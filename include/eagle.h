@@ -236,6 +236,31 @@ int eagle_gate_children(const float* logp, int32_t rows, int32_t k, float tau,
                         float* confidence, hipStream_t stream);
 
 /*
+ * eagle_logits_process - mixed-sampling processing (temperature, top-k,
+ * top-p) of the target's logits before eagle_accept(SAMPLE).
+ *
+ * [P] test setup: the speedups are measured under mixed sampling
+ * (temperature, top_k, top_p); [G] Key Architectural Mechanics 3: a greedy or
+ * nucleus-sampling verifier walks the tree.  Reading: top-k keeps the
+ * k = min(top_k, V) tokens ranked first by (logit descending, index
+ * ascending), top_k = 0 keeps all V; top-p (top_p < 1) then keeps, in that
+ * order, the shortest prefix whose mass under exp((l - l_max) / temperature)
+ * (fp64, summed in rank order) reaches top_p times the mass of the k; a
+ * token stays while the mass before it is below that.  Removed tokens become
+ * -inf, so eagle_accept(SAMPLE) with the same temperature samples the
+ * renormalised processed distribution.
+ *
+ * logits f32[T][V] device -> out f32[T][V] (may be logits itself); kept
+ * int32[T] device or NULL: tokens kept per row.  Logits must be finite.
+ * Errors: null pointers, T or V < 1, top_k < 0, temperature not in
+ * (0, inf), top_p not in (0, 1] -> EAGLE_EINVAL; top_p < 1 with more than
+ * 1024 tokens left by top-k -> EAGLE_EUNSUPPORTED.
+ */
+int eagle_logits_process(const float* logits, int32_t T, int32_t V, float temperature,
+                         int32_t top_k, float top_p, float* out, int32_t* kept,
+                         hipStream_t stream);
+
+/*
  * eagle_accept - accept the longest verified path through the tree.
  *
  * [G] Key Architectural Mechanics 3: a greedy or sampling verifier walks the

@@ -25,7 +25,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE,
          "-Wall", "-Wno-unused-function"]
 
-SOURCES = ["mask.hip", "tree.hip", "accept.hip", "lmhead.hip", "attn.hip", "layer.hip", "kv.hip",
+SOURCES = ["mask.hip", "tree.hip", "accept.hip", "lmhead.hip", "attn.hip", "layer.hip", "kv.hip", "sampling.hip",
            "status.hip"]
 
 

@@ -241,3 +241,18 @@ def test_fuse3_argument_errors(lib):
     assert call(4, 4000) == EUNSUP        # d not a multiple of 128
     assert call(8, 9) == EINVAL
     assert call(10, 0) == EWS
+
+
+def test_logits_process_argument_errors(lib):
+    f = lib.eagle_logits_process
+    assert f(None, 4, 100, 1.0, 10, 0.9, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, 10, 0.9, None, None, None) == EINVAL
+    assert f(FAKE, 0, 100, 1.0, 10, 0.9, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 0, 1.0, 10, 0.9, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 100, 0.0, 10, 0.9, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 100, float("inf"), 10, 0.9, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, -1, 0.9, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, 10, 0.0, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, 10, 1.5, FAKE, None, None) == EINVAL
+    assert f(FAKE, 4, 5000, 1.0, 0, 0.9, FAKE, None, None) == EUNSUP     # top-p over 5000 tokens
+    assert f(FAKE, 4, 5000, 1.0, 1025, 0.9, FAKE, None, None) == EUNSUP
