@@ -29,7 +29,7 @@ from .mask import build_tree_mask, mask_bits, mask_popcount  # noqa: F401
 from .attention import tree_attention  # noqa: F401
 from .lmhead import lm_head_logits, softmax_stats, topk_ids, lm_head_topk, confidence_ratio  # noqa: F401
 from .tree import Pool, expand, rerank  # noqa: F401
-from .accept import accept_greedy, accept_sample  # noqa: F401
+from .accept import accept_greedy, accept_sample, accept_sample_q  # noqa: F401
 from .layer import rms_norm, rope, silu, decoder_layer, LayerWeights  # noqa: F401
 from .cycle import CycleWeights, draft_and_verify_cycle  # noqa: F401
 from .kv import kv_commit, kv_commit_in_place  # noqa: F401

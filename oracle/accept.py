@@ -153,3 +153,74 @@ def accept_sample(token, parent, logits, temperature: float, U, return_margin: b
         margin = min(margin, abs(target - lo) / Z, abs(cdf[bonus] - target) / Z)
         out = (path, len(path) - 1, bonus)
         return (*out, margin) if return_margin else out
+
+
+def accept_sample_q(token, parent, target_logits, draft_logits, temperature: float, U,
+                    return_margin: bool = False):
+    """Speculative sampling over the tree with the draft's own distribution.
+
+    Source: "EAGLE-2: Feature-Level Speculative Decoding Guide", The Problem 1
+    (speculative sampling accepts or rejects draft tokens against the target's
+    distribution) and Key Architectural Mechanics 3 (the verifier walks the
+    tree from the root).  Reading for a sampled draft: the children of node u
+    are draws from q_u = softmax(draft_logits[u] / temperature) without
+    replacement, and they are verified by recursive rejection sampling:
+    with p_1 = p_u = softmax(target_logits[u] / temperature) and q_1 = q_u,
+    child i (ascending node index) with token x is accepted iff
+    U[c] * q_i(x) < p_i(x), i.e. with probability min(1, p_i(x) / q_i(x)),
+    and the walk moves to it; on rejection p_(i+1) = max(p_i - q_i, 0)
+    renormalised and q_(i+1) = q_i without x, renormalised.  A child whose
+    token was already rejected at u (no draw repeats a token) is skipped.
+    When every child is rejected, or u is a leaf, the bonus is the smallest
+    token whose running sum of the last residual exceeds U[T + u] times its
+    total.  All fp64 from fp32 logits.
+
+    Returns ``(path, n_accepted, bonus)``, plus the smallest decision margin
+    (in probability) when ``return_margin``.
+    """
+    T = len(parent)
+    V = np.asarray(target_logits).shape[1]
+    _validate(token, parent, V)
+    if not (temperature > 0 and np.isfinite(temperature)):
+        raise ValueError("temperature must be positive and finite")
+    U = np.asarray(U, dtype=np.float32).astype(np.float64)
+    temperature = np.float64(np.float32(temperature))
+    kids = _children(parent)
+    u = 0
+    path = [0]
+    margin = np.inf
+    while True:
+        p = _node_probs(target_logits[u], temperature)
+        p = p / p.sum()
+        q = _node_probs(draft_logits[u], temperature)
+        q = q / q.sum()
+        rejected = []
+        moved = False
+        for c in kids[u]:
+            x = int(token[c])
+            if x in rejected:
+                continue
+            thr = U[c] * q[x]
+            margin = min(margin, abs(thr - p[x]))
+            if thr < p[x]:
+                path.append(c)
+                u = c
+                moved = True
+                break
+            rejected.append(x)
+            r = np.maximum(p - q, 0.0)
+            p = r / r.sum()
+            q = q.copy()
+            q[x] = 0.0
+            qs = q.sum()
+            q = q / qs if qs > 0 else q
+        if moved:
+            continue
+        target = U[T + u] * p.sum()
+        cdf = np.cumsum(p)
+        hit = np.nonzero(cdf > target)[0]
+        bonus = int(hit[0]) if hit.size else int(np.nonzero(p > 0)[0][-1])
+        lo = cdf[bonus - 1] if bonus > 0 else 0.0
+        margin = min(margin, abs(target - lo), abs(cdf[bonus] - target))
+        out = (path, len(path) - 1, bonus)
+        return (*out, margin) if return_margin else out
