@@ -328,6 +328,31 @@ def main():
                               "avg_us": round(lp_us, 2), "bytes_per_launch": lp_bytes,
                               "timing": "HIP graph of 10 back-to-back calls, replayed 5 times"}
     del lg, lg_out
+    # speculative sampling with the draft's distribution over the verify tree
+    # (64 nodes, V = 128256, target and draft logits, a planted path)
+    g = inputs.rng(w.cfg, inputs.STREAM_U, 7)
+    par_np = inputs.random_tree(g, w.T, 7, 4)
+    tl = inputs.device_normal((w.T, w.vocab), 5200, dev, dtype=torch.float32) * 2.0
+    dlq = 0.5 * tl + inputs.device_normal((w.T, w.vocab), 5201, dev, dtype=torch.float32)
+    tok_np = inputs.sibling_distinct_tokens(g, par_np, w.vocab)
+    tok_np = inputs.plant_path(tok_np, par_np, tl.argmax(1).int().cpu().numpy(),
+                               inputs.deepest_leaf(g, par_np))
+    tok_q, par_q = torch.from_numpy(tok_np).to(dev), torch.from_numpy(par_np).to(dev)
+    u_q = torch.from_numpy(inputs.uniforms(g, 2 * w.T)).to(dev)
+    q_ws = torch.zeros(_lib.lib().eagle_accept_q_workspace(w.vocab), dtype=torch.uint8, device=dev)
+    q_out = [torch.empty(w.T, dtype=torch.int32, device=dev),
+             torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev)]
+    aq_us = graph_time_us(lambda: _lib.eagle_accept_q(tok_q, par_q, tl, dlq, w.temperature, u_q,
+                                                      path=q_out[0], n_accepted=q_out[1],
+                                                      bonus_token=q_out[2], workspace=q_ws),
+                          n_calls=5, reps=3)
+    line["accept_q"] = {"kernel": f"eagle_accept_q (accept_sample_q_kernel), {w.T} nodes, "
+                                  f"V={w.vocab}, draft distribution from draft logits",
+                        "avg_us": round(aq_us, 1), "accepted": int(q_out[1].item()),
+                        "timing": "HIP graph of 5 back-to-back calls, replayed 3 times",
+                        "note": "one workgroup walks the tree: a pass over the vocabulary per "
+                                "visited node and per rejection"}
+    del tl, dlq
     # Eagle-3 fusion of the accepted path's three recorded hidden states
     # (8 rows: root + 7 accepted at the tree's depth bound), d = 4096 -> 4096
     Mf = 8

@@ -340,6 +340,40 @@ int eagle_kv_commit(const void* src_k, const void* src_v, int32_t ld_src, int32_
                     int32_t Hkv, int32_t hd, eagle_dtype dt, int32_t* dev_status,
                     hipStream_t stream);
 
+/*
+ * eagle_accept_q - speculative sampling over the tree with the draft's own
+ * distribution instead of a point mass.
+ *
+ * [G] The Problem 1 (accept or reject draft tokens against the target's
+ * distribution) and Key Architectural Mechanics 3 (the verifier walks the
+ * tree).  Reading for a sampled draft: the children of node u are draws from
+ * q_u = softmax(draft_logits[u] / temperature) without replacement and are
+ * verified by recursive rejection sampling.  With p_1 = p_u (target, same
+ * temperature) and q_1 = q_u: child i (ascending index) with token x is
+ * accepted iff uniforms[c] * q_i(x) < p_i(x) (probability min(1, p_i / q_i))
+ * and the walk moves to it; on rejection p_(i+1) = max(p_i - q_i, 0)
+ * renormalised and q_(i+1) = q_i without x, renormalised (q counts as 0 once
+ * no draft mass is left).  A child whose token was already rejected at u is
+ * skipped.  When all children are rejected, or u is a leaf, the bonus is the
+ * smallest token whose running sum of the last residual exceeds
+ * uniforms[T + u] times its total.  fp64 from fp32 logits; sums in a fixed
+ * order (results can differ from a sequential fp64 evaluation only where a
+ * decision's margin is a few ulp).  One workgroup walks the tree, with one
+ * pass over the vocabulary per visited node and per rejection.
+ *
+ * target_logits, draft_logits f32[T][V]; uniforms f32[2T] in [0, 1);
+ * workspace >= eagle_accept_q_workspace(V) bytes (8-byte aligned).  Outputs
+ * and device errors as eagle_accept.  Host errors: null pointers, T outside
+ * [1, EAGLE_MAX_TREE], V or max_path < 1, temperature not in (0, 3e38] ->
+ * EAGLE_EINVAL; small workspace -> EAGLE_EWORKSPACE.
+ */
+size_t eagle_accept_q_workspace(int32_t V);
+int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_t* node_parent,
+                   const float* target_logits, const float* draft_logits, int32_t V,
+                   float temperature, const float* uniforms, int32_t max_path, int32_t* path,
+                   int32_t* n_accepted, int32_t* bonus_token, void* workspace, size_t ws_bytes,
+                   int32_t* dev_status, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Decoder-layer support for the draft rounds and the verify pass.
  *

@@ -65,6 +65,9 @@ _PROTOS = {
     "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
                                    _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P]),
     "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "eagle_accept_q_workspace": (_SZ, [_I32]),
+    "eagle_accept_q": (_I32, [_I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ, _P,
+                              _P]),
     "eagle_logits_process": (_I32, [_P, _I32, _I32, _F32, _I32, _F32, _P, _P, _P]),
     "eagle_fuse3": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, ctypes.c_int, _P, _SZ, _P]),
     "eagle_gate_children": (_I32, [_P, _I32, _I32, _F32, _I32, _P, _P, _P, _P]),
@@ -321,6 +324,27 @@ def eagle_accept(mode, node_token, node_parent, target_top1=None, target_logits=
     ws = _workspace(nb, dev, workspace) if mode == EAGLE_SAMPLE else None
     _check("eagle_accept", lib().eagle_accept(
         mode, T, _ptr(node_token), _ptr(node_parent), _ptr(target_top1), _ptr(target_logits), V,
+        temperature, _ptr(uniforms), max_path, _ptr(path), _ptr(n_accepted), _ptr(bonus_token),
+        _ptr(ws), nb, _ptr(dev_status), _stream()))
+    return path, n_accepted, bonus_token
+
+
+def eagle_accept_q(node_token, node_parent, target_logits, draft_logits, temperature, uniforms,
+                   max_path=None, path=None, n_accepted=None, bonus_token=None, workspace=None,
+                   dev_status=None):
+    """Speculative sampling with the draft's distribution; returns
+    (path int32[max_path], n_accepted int32[1], bonus int32[1])."""
+    T = node_token.shape[0]
+    dev = node_token.device
+    V = target_logits.shape[1]
+    max_path = T if max_path is None else max_path
+    path = torch.empty(max_path, dtype=torch.int32, device=dev) if path is None else path
+    n_accepted = torch.empty(1, dtype=torch.int32, device=dev) if n_accepted is None else n_accepted
+    bonus_token = torch.empty(1, dtype=torch.int32, device=dev) if bonus_token is None else bonus_token
+    nb = lib().eagle_accept_q_workspace(V)
+    ws = _workspace(nb, dev, workspace)
+    _check("eagle_accept_q", lib().eagle_accept_q(
+        T, _ptr(node_token), _ptr(node_parent), _ptr(target_logits), _ptr(draft_logits), V,
         temperature, _ptr(uniforms), max_path, _ptr(path), _ptr(n_accepted), _ptr(bonus_token),
         _ptr(ws), nb, _ptr(dev_status), _stream()))
     return path, n_accepted, bonus_token

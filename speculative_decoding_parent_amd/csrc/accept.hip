@@ -370,6 +370,203 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(
   }
 }
 
+// ---------------------------------------------------------------- draft q
+
+// Speculative sampling with the draft's distribution (recursive rejection
+// sampling over the children of each node, drawn from q without
+// replacement).  One workgroup walks the tree.  At each node it writes the
+// unnormalised p = e^((l - max l) / t) and q = e^((d - max d) / t) of the
+// two rows into the workspace (pres, qres) with their sums; child i with
+// token x is accepted iff U[c] (q(x) / Zq) < p(x) / Zp; a rejection turns
+// pres into max(pres / Zp - qres / Zq, 0) (one pass over the vocabulary),
+// drops x from qres and Zq, and the next child is tried.  The bonus is drawn
+// from the last pres by inverse CDF.  Sums are taken in a fixed order (each
+// thread's elements in index order, then a fixed butterfly, then the waves in
+// order), so the result does not depend on timing.
+constexpr int kQThreads = 1024;
+constexpr int kQWaves = kQThreads / 64;
+
+__device__ __forceinline__ double q_block_sum(double v, double* dred) {
+  v = wave_sum_d(v);
+  const int tid = threadIdx.x;
+  __syncthreads();
+  if ((tid & 63) == 0) dred[tid >> 6] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int w = 0; w < kQWaves; ++w) s += dred[w];
+  return s;
+}
+
+__device__ __forceinline__ float q_block_max(float v, float* fred) {
+  v = wave_max(v);
+  const int tid = threadIdx.x;
+  __syncthreads();
+  if ((tid & 63) == 0) fred[tid >> 6] = v;
+  __syncthreads();
+  float m = -INFINITY;
+  for (int w = 0; w < kQWaves; ++w) m = fmaxf(m, fred[w]);
+  return m;
+}
+
+__global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
+    int T, const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
+    const float* __restrict__ tl, const float* __restrict__ dl, int V, double itemp,
+    const float* __restrict__ U, double* pres, double* qres, int max_path,
+    int32_t* __restrict__ path, int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus,
+    int32_t* __restrict__ status) {
+  __shared__ int32_t par[EAGLE_MAX_TREE];
+  __shared__ int32_t tk[EAGLE_MAX_TREE];
+  __shared__ int32_t kid[EAGLE_MAX_TREE];
+  __shared__ int32_t rej[EAGLE_MAX_TREE];
+  __shared__ double dred[kQWaves];
+  __shared__ float fred[kQWaves];
+  __shared__ double csum[kQThreads];
+  __shared__ int sh_nk, sh_hit, sh_acc;
+  __shared__ double sh_qx;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < T; i += kQThreads) {
+    int p = parent[i];
+    const int x = token[i];
+    if (i == 0 ? p != -1 : (p < 0 || p >= i)) {
+      set_status(status, (i == 0 || p == -1) ? EAGLE_DEV_BAD_ROOT : EAGLE_DEV_BAD_PARENT);
+      p = i == 0 ? -1 : 0;
+    }
+    if (x < 0 || x >= V) set_status(status, EAGLE_DEV_BAD_TOKEN);
+    par[i] = p;
+    tk[i] = min(max(x, 0), V - 1);
+  }
+  __syncthreads();
+  int u = 0, depth = 0;
+  if (tid == 0) path[0] = 0;
+  for (;;) {
+    const float* lrow = tl + (size_t)u * V;
+    const float* drow = dl + (size_t)u * V;
+    float ml = -INFINITY, md = -INFINITY;
+    for (int v = tid; v < V; v += kQThreads) {
+      ml = fmaxf(ml, lrow[v]);
+      md = fmaxf(md, drow[v]);
+    }
+    ml = q_block_max(ml, fred);
+    md = q_block_max(md, fred);
+    double sp = 0.0, sq = 0.0;
+    for (int v = tid; v < V; v += kQThreads) {
+      const double p = exp_nonpos(((double)lrow[v] - (double)ml) * itemp);
+      const double q = exp_nonpos(((double)drow[v] - (double)md) * itemp);
+      pres[v] = p;
+      qres[v] = q;
+      sp += p;
+      sq += q;
+    }
+    double zp = q_block_sum(sp, dred);
+    double zq = q_block_sum(sq, dred);
+    if (tid == 0) {
+      int n = 0;
+      for (int c = u + 1; c < T; ++c)
+        if (par[c] == u) kid[n++] = c;
+      sh_nk = n;
+    }
+    __syncthreads();
+    const int nk = sh_nk;
+    int nrej = 0;
+    int next = -1;
+    for (int i = 0; i < nk; ++i) {
+      const int c = kid[i];
+      const int x = tk[c];
+      bool seen = false;
+      for (int r = 0; r < nrej; ++r) seen |= rej[r] == x;
+      if (seen) continue;                 // a draw never repeats a token
+      // thread 0 decides and shares the decision and q(x), so every thread
+      // takes the same branch (the rejection pass below has barriers)
+      if (tid == 0) {
+        const double qx = qres[x];
+        const double qn = zq > 0.0 ? qx / zq : 0.0;   // (no draft mass left: q counts as 0)
+        sh_acc = (double)U[c] * qn < pres[x] / zp;
+        sh_qx = qx;
+      }
+      __syncthreads();
+      const double qx = sh_qx;
+      if (sh_acc) {
+        next = c;
+        break;
+      }
+      // rejected: p <- max(p / Zp - q / Zq, 0), q <- q without x
+      double s = 0.0;
+      for (int v = tid; v < V; v += kQThreads) {
+        const double r = fmax(pres[v] / zp - (zq > 0.0 ? qres[v] / zq : 0.0), 0.0);
+        pres[v] = r;
+        s += r;
+      }
+      zp = q_block_sum(s, dred);        // (its barriers also order the pres stores)
+      if (tid == 0) {
+        qres[x] = 0.0;
+        rej[nrej] = x;
+      }
+      zq = zq - qx;
+      ++nrej;
+      __syncthreads();
+    }
+    if (next >= 0) {
+      ++depth;
+      if (tid == 0) {
+        if (depth < max_path) path[depth] = next;
+        else set_status(status, EAGLE_DEV_PATH_TRUNC);
+      }
+      u = next;
+      __syncthreads();
+      continue;
+    }
+    // bonus: smallest token whose running sum of pres exceeds U[T + u] Zp.
+    // Thread t owns the contiguous tokens [t C, (t + 1) C).
+    const double target = (double)U[T + u] * zp;
+    const int C = (V + kQThreads - 1) / kQThreads;
+    const int v0 = tid * C;
+    const int v1 = min(V, v0 + C);
+    double own = 0.0;
+    for (int v = v0; v < v1; ++v) own += pres[v];
+    csum[tid] = own;
+    if (tid == 0) sh_hit = 0x7fffffff;
+    __syncthreads();
+    if (tid == 0) {
+      double run = 0.0;
+      for (int t = 0; t < kQThreads; ++t) {
+        const double nx = run + csum[t];
+        csum[t] = run;                    // exclusive prefix
+        run = nx;
+      }
+    }
+    __syncthreads();
+    {
+      // the crossing: one token in exact arithmetic; rounding at a chunk
+      // border can show it to two threads, and the lower token wins
+      double run = csum[tid];
+      for (int v = v0; v < v1; ++v) {
+        const double nx = run + pres[v];
+        if (run <= target && nx > target) {
+          atomicMin(&sh_hit, v);
+          break;
+        }
+        run = nx;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int b = sh_hit == 0x7fffffff ? -1 : sh_hit;
+      if (b < 0) {                        // rounding left none: the last token with mass
+        for (int v = V - 1; v >= 0; --v)
+          if (pres[v] > 0.0) {
+            b = v;
+            break;
+          }
+        b = max(b, 0);
+      }
+      bonus[0] = b;
+      n_acc[0] = depth;
+      for (int d = depth + 1; d < max_path; ++d) path[d] = -1;
+    }
+    return;
+  }
+}
+
 }  // namespace eagle
 
 extern "C" size_t eagle_accept_workspace(int32_t T, int32_t V) {
@@ -408,6 +605,31 @@ extern "C" int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
   } else {
     return EAGLE_EINVAL;
   }
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" size_t eagle_accept_q_workspace(int32_t V) {
+  return V >= 1 ? (size_t)2 * (size_t)V * sizeof(double) : 0;
+}
+
+extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_t* node_parent,
+                              const float* target_logits, const float* draft_logits, int32_t V,
+                              float temperature, const float* uniforms, int32_t max_path,
+                              int32_t* path, int32_t* n_accepted, int32_t* bonus_token,
+                              void* workspace, size_t ws_bytes, int32_t* dev_status,
+                              hipStream_t stream) {
+  EAGLE_REQUIRE(node_token && node_parent && target_logits && draft_logits && uniforms, EAGLE_EINVAL);
+  EAGLE_REQUIRE(path && n_accepted && bonus_token, EAGLE_EINVAL);
+  EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && max_path >= 1 && V >= 1, EAGLE_EINVAL);
+  EAGLE_REQUIRE(temperature > 0.0f && temperature <= 3.0e38f, EAGLE_EINVAL);
+  EAGLE_REQUIRE(workspace && ((uintptr_t)workspace & 7) == 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(ws_bytes >= eagle_accept_q_workspace(V), EAGLE_EWORKSPACE);
+  double* pres = (double*)workspace;
+  hipLaunchKernelGGL(eagle::accept_sample_q_kernel, dim3(1), dim3(eagle::kQThreads), 0, stream, T,
+                     node_token, node_parent, target_logits, draft_logits, V,
+                     1.0 / (double)temperature, uniforms, pres, pres + V, max_path, path,
+                     n_accepted, bonus_token, dev_status);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

@@ -256,3 +256,22 @@ def test_logits_process_argument_errors(lib):
     assert f(FAKE, 4, 100, 1.0, 10, 1.5, FAKE, None, None) == EINVAL
     assert f(FAKE, 4, 5000, 1.0, 0, 0.9, FAKE, None, None) == EUNSUP     # top-p over 5000 tokens
     assert f(FAKE, 4, 5000, 1.0, 1025, 0.9, FAKE, None, None) == EUNSUP
+
+
+def test_accept_q_argument_errors(lib):
+    f = lib.eagle_accept_q
+    assert lib.eagle_accept_q_workspace(128256) == 2 * 128256 * 8
+    assert lib.eagle_accept_q_workspace(0) == 0
+    ok = [8, FAKE, FAKE, FAKE, FAKE, 100, 1.0, FAKE, 8, FAKE, FAKE, FAKE, FAKE, 1600, None, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return f(*a)
+    assert call(0, 0) == EINVAL
+    assert call(0, 257) == EINVAL
+    assert call(4, None) == EINVAL            # draft logits
+    assert call(5, 0) == EINVAL
+    assert call(6, 0.0) == EINVAL
+    assert call(8, 0) == EINVAL
+    assert call(12, FAKE + 4) == EINVAL       # workspace alignment
+    assert call(13, 1599) == EWS

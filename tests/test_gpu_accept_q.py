@@ -1,0 +1,68 @@
+"""GPU parity: eagle_accept_q against the oracle's speculative sampling
+with a draft distribution (paths, counts and bonus tokens equal; draws
+whose oracle margin is below 1e-12 would be excluded and are counted)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_parent_amd import _lib, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def to(dev, x, dt=torch.int32):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev, dt)
+
+
+@pytest.mark.parametrize("T,V,temp,close", [(15, 1024, 1.0, 0.0), (64, 128256, 0.8, 0.3),
+                                            (60, 5000, 1.0, 0.6), (9, 300, 1.3, 1.0),
+                                            (1, 50, 1.0, 0.0)])
+def test_matches_oracle(dev, T, V, temp, close):
+    """Draft logits = close * target + noise: close = 1 makes q = p."""
+    ambiguous = 0
+    for seed in range(4):
+        print(f"accept_q T={T} V={V} temp={temp} close={close} seed={seed}", flush=True)
+        g = inputs.rng(960 + seed, inputs.STREAM_LOGITS, T)
+        par = inputs.random_tree(g, T, 7, 4)
+        tl = (g.standard_normal((T, V), dtype=np.float32) * 2.0).astype(np.float32)
+        noise = g.standard_normal((T, V), dtype=np.float32) * 2.0
+        dl = (close * tl + (1.0 - close) * noise).astype(np.float32)
+        tok = inputs.sibling_distinct_tokens(g, par, V)
+        if seed % 2:
+            tok = inputs.plant_path(tok, par, tl.argmax(1).astype(np.int32), inputs.deepest_leaf(g, par))
+        U = inputs.uniforms(g, 2 * T)
+        rp, rn, rb, margin = oracle.accept_sample_q(tok, par, tl, dl, temp, U, return_margin=True)
+        if margin < 1e-12:
+            ambiguous += 1
+            continue
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        path, n, b = _lib.eagle_accept_q(to(dev, tok), to(dev, par), to(dev, tl, torch.float32),
+                                         to(dev, dl, torch.float32), temp,
+                                         to(dev, U, torch.float32), dev_status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert int(n.item()) == rn and int(b.item()) == rb
+        assert path.cpu().numpy()[:rn + 1].tolist() == rp
+    assert ambiguous == 0
+
+
+def test_q_equal_p_accepts_along_the_first_children(dev):
+    T, V = 12, 700
+    g = inputs.rng(970, 0)
+    par = inputs.random_tree(g, T, 5, 3)
+    lg = g.standard_normal((T, V), dtype=np.float32)
+    tok = inputs.sibling_distinct_tokens(g, par, V)
+    U = inputs.uniforms(g, 2 * T)
+    path, n, b = _lib.eagle_accept_q(to(dev, tok), to(dev, par), to(dev, lg, torch.float32),
+                                     to(dev, lg, torch.float32), 1.0, to(dev, U, torch.float32))
+    torch.cuda.synchronize()
+    # every accept test passes (U < 1 = p / q): the walk follows first children to a leaf
+    want, u = [0], 0
+    while True:
+        kids = [c for c in range(u + 1, T) if par[c] == u]
+        if not kids:
+            break
+        u = kids[0]
+        want.append(u)
+    assert path.cpu().numpy()[:len(want)].tolist() == want and int(n.item()) == len(want) - 1
