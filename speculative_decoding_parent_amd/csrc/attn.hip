@@ -162,6 +162,95 @@ __device__ __forceinline__ void tile_softmax(int t, int npos, bool is_tree,
   }
 }
 
+// Visibility of tile t's scores: positions past the slice end, and tree
+// nodes that are not ancestors of the row's node, are set to -inf.
+template <int NTW>
+__device__ __forceinline__ void mask_scores(int t, int npos, bool is_tree,
+                                            const uint64_t (*ms)[16][4], int g, int r16,
+                                            f32x4 (&s)[4][NTW]) {
+  const int tile_pos = t * kAtTile;
+  if (is_tree || tile_pos + kAtTile > npos) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      uint64_t bits = ~0ull;
+      if (is_tree) bits = ms[nt][r16][t];  // t < words <= 4
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int pl = mt * 16 + 4 * g + j;
+          if (tile_pos + pl >= npos || !((bits >> pl) & 1ull)) s[mt][nt][j] = -INFINITY;
+        }
+    }
+  }
+}
+
+// tile_softmax for scores that arrive already scaled by scale * log2(e) (q
+// folded) and shifted: s = score - mi[row], the score MFMAs having started
+// from -mi instead of 0.  m is the running max in the same scaled units.
+// While m stays put and mi == m (every tile after a slice's first, almost
+// always), the weights are exp2(s) with no arithmetic in between; a tile
+// that raises m (or the first, where mi = 0) also subtracts m - mi.  On
+// return mi = m, the offset for the next tile's score MFMAs.
+template <int NTW, int MTV>
+__device__ __forceinline__ void tile_softmax_shifted(int t, int npos, bool is_tree,
+                                                     const uint64_t (*ms)[16][4], int g, int r16,
+                                                     f32x4 (&s)[4][NTW], u32x4 (&pb)[2][NTW],
+                                                     float (&m)[NTW], float (&l)[NTW],
+                                                     f32x4 (&o)[MTV][NTW], float (&mi)[NTW]) {
+  mask_scores<NTW>(t, npos, is_tree, ms, g, r16, s);
+  float mx[NTW];
+  bool up_any = false, shift_any = false;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    float v = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v = fmaxf(v, s[mt][nt][j]);
+    mx[nt] = rows_max(v) + mi[nt];       // the tile's max score
+    up_any |= mx[nt] - m[nt] > 8.0f;
+    shift_any |= m[nt] != mi[nt];
+  }
+  if (__builtin_amdgcn_ballot_w64(up_any | shift_any)) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const bool up = mx[nt] - m[nt] > 8.0f;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m[nt] - mx[nt]) : 1.0f;
+      m[nt] = up ? mx[nt] : m[nt];
+      l[nt] *= alpha;
+#pragma unroll
+      for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
+      const float d = m[nt] - mi[nt];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[mt][nt][j] -= d;
+      mi[nt] = m[nt];
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    float ps = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(s[mt][nt][j]);
+        s[mt][nt][j] = pv;
+        ps += pv;
+      }
+    l[nt] += ps;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
+                          pack_bf16x2(s[2 * kb2][nt][2], s[2 * kb2][nt][3]),
+                          pack_bf16x2(s[2 * kb2 + 1][nt][0], s[2 * kb2 + 1][nt][1]),
+                          pack_bf16x2(s[2 * kb2 + 1][nt][2], s[2 * kb2 + 1][nt][3])};
+    }
+  }
+}
+
 template <int HD, int NTW, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p) {
   constexpr int NTH = 64 * NW;
@@ -479,6 +568,17 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
       qf[nt][kb] = valid[nt] ? *(const u32x4*)(p.q + (size_t)grow[nt] * HD + kb * 32 + 8 * g)
                              : u32x4{0u, 0u, 0u, 0u};
   }
+  // scale * log2(e) folded into q once (one more bf16 rounding, 2^-9
+  // relative): the score MFMAs then deliver exp2 arguments directly
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = qf[nt][kb][e];
+        qf[nt][kb][e] = pack_bf16x2(bf16_bits_to_f32(w & 0xffffu) * p.c, bf16_bits_to_f32(w >> 16) * p.c);
+      }
 
   int64_t pos0;
   int npos;
@@ -498,12 +598,15 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
   }
   const int ntiles = npos > 0 ? (npos + kAtTile - 1) / kAtTile : 0;
 
-  float m[NTW], l[NTW];
+  // m: running max of the scaled scores; mi: the offset the score MFMAs start
+  // from (-mi in every accumulator), 0 until the first tile sets m
+  float m[NTW], l[NTW], mi[NTW];
   f32x4 o[MTV][NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     m[nt] = kNegBig;
     l[nt] = 0.f;
+    mi[nt] = 0.f;
 #pragma unroll
     for (int mv = 0; mv < MTV; ++mv) o[mv][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -548,11 +651,10 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
   };
 
   auto qk = [&](const bf16_t* stg, f32x4 (&s)[4][NTW]) __attribute__((always_inline)) {
+    f32x4 c0[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) c0[nt] = f32x4{-mi[nt], -mi[nt], -mi[nt], -mi[nt]};
     const char* Kb = (const char*)stg;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -560,8 +662,8 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
         const bf16x8 a = *(const bf16x8*)(Kb + mt * 4096 + kro[kb]);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(qf[nt][kb]),
-                                                              s[mt][nt], 0, 0, 0);
+          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, as_bf16x8(qf[nt][kb]), kb == 0 ? c0[nt] : s[mt][nt], 0, 0, 0);
       }
     }
   };
@@ -591,7 +693,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
       f32x4 sc[4][NTW];
       u32x4 pb[2][NTW];
       qk(stage(s), sc);
-      tile_softmax<NTW, MTV>(t, npos, is_tree, Ms[wave], p.c, g, r16, sc, pb, m, l, o);
+      tile_softmax_shifted<NTW, MTV>(t, npos, is_tree, Ms[wave], g, r16, sc, pb, m, l, o, mi);
       pv(stage(s), pb);
     }
   };
@@ -632,7 +734,9 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const float lt = rows_sum(l[nt]);
-    if (valid[nt] && g == 0) p.part_ml[(size_t)split * RT + grow[nt]] = make_float2(m[nt], lt);
+    // (m back in score units for the merge, which scales by scale * log2(e))
+    if (valid[nt] && g == 0)
+      p.part_ml[(size_t)split * RT + grow[nt]] = make_float2(m[nt] / p.c, lt);
     const float il = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
     for (int mv = 0; mv < MTV; ++mv) {
