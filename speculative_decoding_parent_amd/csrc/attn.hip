@@ -196,7 +196,7 @@ template <int NTW, int MTV>
 __device__ __forceinline__ void tile_softmax_shifted(int t, int npos, bool is_tree,
                                                      const uint64_t (*ms)[16][4], int g, int r16,
                                                      f32x4 (&s)[4][NTW], u32x4 (&pb)[2][NTW],
-                                                     float (&m)[NTW], float (&l)[NTW],
+                                                     float (&m)[NTW], f32x4 (&ls)[NTW],
                                                      f32x4 (&o)[MTV][NTW], float (&mi)[NTW]) {
   mask_scores<NTW>(t, npos, is_tree, ms, g, r16, s);
   float mx[NTW];
@@ -218,7 +218,7 @@ __device__ __forceinline__ void tile_softmax_shifted(int t, int npos, bool is_tr
       const bool up = mx[nt] - m[nt] > 8.0f;
       const float alpha = up ? __builtin_amdgcn_exp2f(m[nt] - mx[nt]) : 1.0f;
       m[nt] = up ? mx[nt] : m[nt];
-      l[nt] *= alpha;
+      ls[nt] *= alpha;
 #pragma unroll
       for (int mv = 0; mv < MTV; ++mv) o[mv][nt] *= alpha;
       const float d = m[nt] - mi[nt];
@@ -231,16 +231,10 @@ __device__ __forceinline__ void tile_softmax_shifted(int t, int npos, bool is_tr
   }
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    float ps = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pv = __builtin_amdgcn_exp2f(s[mt][nt][j]);
-        s[mt][nt][j] = pv;
-        ps += pv;
-      }
-    l[nt] += ps;
+      for (int j = 0; j < 4; ++j) s[mt][nt][j] = __builtin_amdgcn_exp2f(s[mt][nt][j]);
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       pb[kb2][nt] = u32x4{pack_bf16x2(s[2 * kb2][nt][0], s[2 * kb2][nt][1]),
@@ -600,12 +594,12 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
 
   // m: running max of the scaled scores; mi: the offset the score MFMAs start
   // from (-mi in every accumulator), 0 until the first tile sets m
-  float m[NTW], l[NTW], mi[NTW];
-  f32x4 o[MTV][NTW];
+  float m[NTW], mi[NTW];
+  f32x4 o[MTV][NTW], ls[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     m[nt] = kNegBig;
-    l[nt] = 0.f;
+    ls[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     mi[nt] = 0.f;
 #pragma unroll
     for (int mv = 0; mv < MTV; ++mv) o[mv][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -681,6 +675,12 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
           o[mv][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(pb[kb2][nt]),
                                                               o[mv][nt], 0, 0, 0);
       }
+      // row sums of the weights: every row of an all-ones A operand
+      const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+        ls[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, as_bf16x8(pb[kb2][nt]), ls[nt], 0,
+                                                         0, 0);
     }
   };
   auto step = [&](int t, int s) __attribute__((always_inline)) {
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
       f32x4 sc[4][NTW];
       u32x4 pb[2][NTW];
       qk(stage(s), sc);
-      tile_softmax_shifted<NTW, MTV>(t, npos, is_tree, Ms[wave], g, r16, sc, pb, m, l, o, mi);
+      tile_softmax_shifted<NTW, MTV>(t, npos, is_tree, Ms[wave], g, r16, sc, pb, m, ls, o, mi);
       pv(stage(s), pb);
     }
   };
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p
   char* stg = (char*)stage(wave >> 1) + (wave & 1) * TB;
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    const float lt = rows_sum(l[nt]);
+    const float lt = ls[nt][0];          // (the four values of a lane are the same sum)
     // (m back in score units for the merge, which scales by scale * log2(e))
     if (valid[nt] && g == 0)
       p.part_ml[(size_t)split * RT + grow[nt]] = make_float2(m[nt] / p.c, lt);
