@@ -339,7 +339,8 @@ def main():
                                inputs.deepest_leaf(g, par_np))
     tok_q, par_q = torch.from_numpy(tok_np).to(dev), torch.from_numpy(par_np).to(dev)
     u_q = torch.from_numpy(inputs.uniforms(g, 2 * w.T)).to(dev)
-    q_ws = torch.zeros(_lib.lib().eagle_accept_q_workspace(w.vocab), dtype=torch.uint8, device=dev)
+    q_ws = torch.zeros(_lib.lib().eagle_accept_q_workspace(w.T, w.vocab), dtype=torch.uint8,
+                       device=dev)
     q_out = [torch.empty(w.T, dtype=torch.int32, device=dev),
              torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev)]
     aq_us = graph_time_us(lambda: _lib.eagle_accept_q(tok_q, par_q, tl, dlq, w.temperature, u_q,
@@ -350,8 +351,9 @@ def main():
                                   f"V={w.vocab}, draft distribution from draft logits",
                         "avg_us": round(aq_us, 1), "accepted": int(q_out[1].item()),
                         "timing": "HIP graph of 5 back-to-back calls, replayed 3 times",
-                        "note": "one workgroup walks the tree: a pass over the vocabulary per "
-                                "visited node and per rejection"}
+                        "note": "row statistics from a many-workgroup prepass; one workgroup "
+                                "walks the tree, passing over the vocabulary only for rejections "
+                                "and the bonus draw"}
     del tl, dlq
     # Eagle-3 fusion of the accepted path's three recorded hidden states
     # (8 rows: root + 7 accepted at the tree's depth bound), d = 4096 -> 4096

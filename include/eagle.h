@@ -358,16 +358,17 @@ int eagle_kv_commit(const void* src_k, const void* src_v, int32_t ld_src, int32_
  * smallest token whose running sum of the last residual exceeds
  * uniforms[T + u] times its total.  fp64 from fp32 logits; sums in a fixed
  * order (results can differ from a sequential fp64 evaluation only where a
- * decision's margin is a few ulp).  One workgroup walks the tree, with one
- * pass over the vocabulary per visited node and per rejection.
+ * decision's margin is a few ulp).  A many-workgroup prepass takes every
+ * row's (max, sum) statistics; one workgroup then walks the tree, passing
+ * over the vocabulary only for rejections and the bonus draw.
  *
  * target_logits, draft_logits f32[T][V]; uniforms f32[2T] in [0, 1);
- * workspace >= eagle_accept_q_workspace(V) bytes (8-byte aligned).  Outputs
+ * workspace >= eagle_accept_q_workspace(T, V) bytes (8-byte aligned).  Outputs
  * and device errors as eagle_accept.  Host errors: null pointers, T outside
  * [1, EAGLE_MAX_TREE], V or max_path < 1, temperature not in (0, 3e38] ->
  * EAGLE_EINVAL; small workspace -> EAGLE_EWORKSPACE.
  */
-size_t eagle_accept_q_workspace(int32_t V);
+size_t eagle_accept_q_workspace(int32_t T, int32_t V);
 int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_t* node_parent,
                    const float* target_logits, const float* draft_logits, int32_t V,
                    float temperature, const float* uniforms, int32_t max_path, int32_t* path,

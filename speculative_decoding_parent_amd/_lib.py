@@ -65,7 +65,7 @@ _PROTOS = {
     "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
                                    _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P]),
     "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
-    "eagle_accept_q_workspace": (_SZ, [_I32]),
+    "eagle_accept_q_workspace": (_SZ, [_I32, _I32]),
     "eagle_accept_q": (_I32, [_I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ, _P,
                               _P]),
     "eagle_logits_process": (_I32, [_P, _I32, _I32, _F32, _I32, _F32, _P, _P, _P]),
@@ -341,7 +341,7 @@ def eagle_accept_q(node_token, node_parent, target_logits, draft_logits, tempera
     path = torch.empty(max_path, dtype=torch.int32, device=dev) if path is None else path
     n_accepted = torch.empty(1, dtype=torch.int32, device=dev) if n_accepted is None else n_accepted
     bonus_token = torch.empty(1, dtype=torch.int32, device=dev) if bonus_token is None else bonus_token
-    nb = lib().eagle_accept_q_workspace(V)
+    nb = lib().eagle_accept_q_workspace(T, V)
     ws = _workspace(nb, dev, workspace)
     _check("eagle_accept_q", lib().eagle_accept_q(
         T, _ptr(node_token), _ptr(node_parent), _ptr(target_logits), _ptr(draft_logits), V,

@@ -374,17 +374,22 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(
 
 // Speculative sampling with the draft's distribution (recursive rejection
 // sampling over the children of each node, drawn from q without
-// replacement).  One workgroup walks the tree.  At each node it writes the
-// unnormalised p = e^((l - max l) / t) and q = e^((d - max d) / t) of the
-// two rows into the workspace (pres, qres) with their sums; child i with
-// token x is accepted iff U[c] (q(x) / Zq) < p(x) / Zp; a rejection turns
-// pres into max(pres / Zp - qres / Zq, 0) (one pass over the vocabulary),
+// replacement).  A prepass over all rows (accept_row_stats_kernel, many
+// workgroups) gives each row's chunk (max, sum); then one workgroup walks
+// the tree.  At a node the row normalisers Zp, Zq come from the chunk
+// statistics and child i with token x is accepted iff U[c] (q(x) / Zq) <
+// p(x) / Zp, with p = e^((l - max l) / t), q = e^((d - max d) / t) evaluated
+// for x alone.  Only a rejection (or the bonus draw) writes the node's
+// unnormalised rows into the workspace (pres, qres); a rejection then turns
+// pres into max(pres / Zp - qres / Zq, 0) (one pass over the vocabulary,
+// with the reciprocals of Zp and Zq),
 // drops x from qres and Zq, and the next child is tried.  The bonus is drawn
 // from the last pres by inverse CDF.  Sums are taken in a fixed order (each
 // thread's elements in index order, then a fixed butterfly, then the waves in
 // order), so the result does not depend on timing.
 constexpr int kQThreads = 1024;
 constexpr int kQWaves = kQThreads / 64;
+constexpr int kQBatch = 8;
 
 __device__ __forceinline__ double q_block_sum(double v, double* dred) {
   v = wave_sum_d(v);
@@ -411,7 +416,8 @@ __device__ __forceinline__ float q_block_max(float v, float* fred) {
 __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
     int T, const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
     const float* __restrict__ tl, const float* __restrict__ dl, int V, double itemp,
-    const float* __restrict__ U, double* pres, double* qres, int max_path,
+    const float* __restrict__ U, const double* __restrict__ pst, const double* __restrict__ qst,
+    int nchunk, double* pres, double* qres, int max_path,
     int32_t* __restrict__ path, int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus,
     int32_t* __restrict__ status) {
   __shared__ int32_t par[EAGLE_MAX_TREE];
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
   __shared__ float fred[kQWaves];
   __shared__ double csum[kQThreads];
   __shared__ int sh_nk, sh_hit, sh_acc;
-  __shared__ double sh_qx;
+  __shared__ double sh_qx, sh_ml, sh_md, sh_zp, sh_zq;
   const int tid = threadIdx.x;
   for (int i = tid; i < T; i += kQThreads) {
     int p = parent[i];
@@ -441,24 +447,59 @@ __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
   for (;;) {
     const float* lrow = tl + (size_t)u * V;
     const float* drow = dl + (size_t)u * V;
-    float ml = -INFINITY, md = -INFINITY;
-    for (int v = tid; v < V; v += kQThreads) {
-      ml = fmaxf(ml, lrow[v]);
-      md = fmaxf(md, drow[v]);
+    // the row's max and normaliser from the prepass's chunk statistics
+    // (combined in chunk order by wave 0); p(x) and q(x) of single tokens
+    // from the logits; the rows are written out over the vocabulary only
+    // when a rejection or the bonus draw needs them
+    if (tid < 64) {
+      double a = -INFINITY, b = -INFINITY;
+      for (int c = tid; c < nchunk; c += 64) {
+        a = fmax(a, pst[((size_t)u * nchunk + c) * 2]);
+        b = fmax(b, qst[((size_t)u * nchunk + c) * 2]);
+      }
+      a = wave_max_d(a);
+      b = wave_max_d(b);
+      double za = 0.0, zb = 0.0;
+      for (int c = tid; c < nchunk; c += 64) {
+        const double* x = pst + ((size_t)u * nchunk + c) * 2;
+        const double* y = qst + ((size_t)u * nchunk + c) * 2;
+        za += x[1] * exp_nonpos((x[0] - a) * itemp);
+        zb += y[1] * exp_nonpos((y[0] - b) * itemp);
+      }
+      za = wave_sum_d(za);
+      zb = wave_sum_d(zb);
+      if (tid == 0) {
+        sh_ml = a;
+        sh_md = b;
+        sh_zp = za;
+        sh_zq = zb;
+      }
     }
-    ml = q_block_max(ml, fred);
-    md = q_block_max(md, fred);
-    double sp = 0.0, sq = 0.0;
-    for (int v = tid; v < V; v += kQThreads) {
-      const double p = exp_nonpos(((double)lrow[v] - (double)ml) * itemp);
-      const double q = exp_nonpos(((double)drow[v] - (double)md) * itemp);
-      pres[v] = p;
-      qres[v] = q;
-      sp += p;
-      sq += q;
-    }
-    double zp = q_block_sum(sp, dred);
-    double zq = q_block_sum(sq, dred);
+    __syncthreads();
+    const double ml = sh_ml, md = sh_md;
+    double zp = sh_zp, zq = sh_zq;
+    bool rows_out = false;   // pres / qres hold this node's rows
+    // writes pres = p (unnormalised) and qres = q over the vocabulary
+    auto rows = [&]() __attribute__((always_inline)) {
+      for (int v0 = tid; v0 < V; v0 += kQThreads * kQBatch) {
+        float a[kQBatch], b[kQBatch];
+#pragma unroll
+        for (int i = 0; i < kQBatch; ++i) {
+          const int v = v0 + i * kQThreads;
+          a[i] = v < V ? lrow[v] : 0.f;
+          b[i] = v < V ? drow[v] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kQBatch; ++i) {
+          const int v = v0 + i * kQThreads;
+          if (v < V) {
+            pres[v] = exp_nonpos(((double)a[i] - ml) * itemp);
+            qres[v] = exp_nonpos(((double)b[i] - md) * itemp);
+          }
+        }
+      }
+      rows_out = true;
+    };
     if (tid == 0) {
       int n = 0;
       for (int c = u + 1; c < T; ++c)
@@ -478,9 +519,10 @@ __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
       // thread 0 decides and shares the decision and q(x), so every thread
       // takes the same branch (the rejection pass below has barriers)
       if (tid == 0) {
-        const double qx = qres[x];
+        const double qx = rows_out ? qres[x] : exp_nonpos(((double)drow[x] - md) * itemp);
+        const double px = rows_out ? pres[x] : exp_nonpos(((double)lrow[x] - ml) * itemp);
         const double qn = zq > 0.0 ? qx / zq : 0.0;   // (no draft mass left: q counts as 0)
-        sh_acc = (double)U[c] * qn < pres[x] / zp;
+        sh_acc = (double)U[c] * qn < px / zp;
         sh_qx = qx;
       }
       __syncthreads();
@@ -490,11 +532,30 @@ __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
         break;
       }
       // rejected: p <- max(p / Zp - q / Zq, 0), q <- q without x
+      if (!rows_out) {
+        rows();
+        __syncthreads();
+      }
       double s = 0.0;
-      for (int v = tid; v < V; v += kQThreads) {
-        const double r = fmax(pres[v] / zp - (zq > 0.0 ? qres[v] / zq : 0.0), 0.0);
-        pres[v] = r;
-        s += r;
+      const double izp = 1.0 / zp;
+      const double izq = zq > 0.0 ? 1.0 / zq : 0.0;
+      for (int v0 = tid; v0 < V; v0 += kQThreads * kQBatch) {
+        double a[kQBatch], b[kQBatch];
+#pragma unroll
+        for (int i = 0; i < kQBatch; ++i) {
+          const int v = v0 + i * kQThreads;
+          a[i] = v < V ? pres[v] : 0.0;
+          b[i] = v < V ? qres[v] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < kQBatch; ++i) {
+          const int v = v0 + i * kQThreads;
+          if (v < V) {
+            const double r = fmax(a[i] * izp - b[i] * izq, 0.0);
+            pres[v] = r;
+            s += r;
+          }
+        }
       }
       zp = q_block_sum(s, dred);        // (its barriers also order the pres stores)
       if (tid == 0) {
@@ -517,12 +578,22 @@ __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
     }
     // bonus: smallest token whose running sum of pres exceeds U[T + u] Zp.
     // Thread t owns the contiguous tokens [t C, (t + 1) C).
+    if (!rows_out) {
+      rows();
+      __syncthreads();
+    }
     const double target = (double)U[T + u] * zp;
     const int C = (V + kQThreads - 1) / kQThreads;
     const int v0 = tid * C;
     const int v1 = min(V, v0 + C);
     double own = 0.0;
-    for (int v = v0; v < v1; ++v) own += pres[v];
+    for (int w0 = v0; w0 < v1; w0 += kQBatch) {
+      double a[kQBatch];
+#pragma unroll
+      for (int i = 0; i < kQBatch; ++i) a[i] = w0 + i < v1 ? pres[w0 + i] : 0.0;
+#pragma unroll
+      for (int i = 0; i < kQBatch; ++i) own += a[i];
+    }
     csum[tid] = own;
     if (tid == 0) sh_hit = 0x7fffffff;
     __syncthreads();
@@ -539,13 +610,21 @@ __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
       // the crossing: one token in exact arithmetic; rounding at a chunk
       // border can show it to two threads, and the lower token wins
       double run = csum[tid];
-      for (int v = v0; v < v1; ++v) {
-        const double nx = run + pres[v];
-        if (run <= target && nx > target) {
-          atomicMin(&sh_hit, v);
-          break;
+      bool found = false;
+      for (int w0 = v0; w0 < v1 && !found; w0 += kQBatch) {
+        double a[kQBatch];
+#pragma unroll
+        for (int i = 0; i < kQBatch; ++i) a[i] = w0 + i < v1 ? pres[w0 + i] : 0.0;
+#pragma unroll
+        for (int i = 0; i < kQBatch; ++i) {
+          const int v = w0 + i;
+          const double nx = run + a[i];
+          if (!found && v < v1 && run <= target && nx > target) {
+            atomicMin(&sh_hit, v);
+            found = true;
+          }
+          run = nx;
         }
-        run = nx;
       }
     }
     __syncthreads();
@@ -609,8 +688,9 @@ extern "C" int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
   return EAGLE_OK;
 }
 
-extern "C" size_t eagle_accept_q_workspace(int32_t V) {
-  return V >= 1 ? (size_t)2 * (size_t)V * sizeof(double) : 0;
+extern "C" size_t eagle_accept_q_workspace(int32_t T, int32_t V) {
+  if (T < 1 || V < 1) return 0;
+  return (size_t)2 * (size_t)V * sizeof(double) + 2 * eagle_accept_workspace(T, V);
 }
 
 extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_t* node_parent,
@@ -624,12 +704,22 @@ extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_
   EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && max_path >= 1 && V >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(temperature > 0.0f && temperature <= 3.0e38f, EAGLE_EINVAL);
   EAGLE_REQUIRE(workspace && ((uintptr_t)workspace & 7) == 0, EAGLE_EINVAL);
-  EAGLE_REQUIRE(ws_bytes >= eagle_accept_q_workspace(V), EAGLE_EWORKSPACE);
+  EAGLE_REQUIRE(ws_bytes >= eagle_accept_q_workspace(T, V), EAGLE_EWORKSPACE);
+  const int nchunk = (V + eagle::kAcceptChunk - 1) / eagle::kAcceptChunk;
+  const double itemp = 1.0 / (double)temperature;
   double* pres = (double*)workspace;
+  double* pst = pres + 2 * (size_t)V;
+  double* qst = pst + (size_t)T * nchunk * 2;
+  hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, T), dim3(256), 0, stream,
+                     target_logits, V, itemp, nchunk, pst);
+  EAGLE_LAUNCH_CHECK();
+  hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, T), dim3(256), 0, stream,
+                     draft_logits, V, itemp, nchunk, qst);
+  EAGLE_LAUNCH_CHECK();
   hipLaunchKernelGGL(eagle::accept_sample_q_kernel, dim3(1), dim3(eagle::kQThreads), 0, stream, T,
-                     node_token, node_parent, target_logits, draft_logits, V,
-                     1.0 / (double)temperature, uniforms, pres, pres + V, max_path, path,
-                     n_accepted, bonus_token, dev_status);
+                     node_token, node_parent, target_logits, draft_logits, V, itemp, uniforms,
+                     pst, qst, nchunk, pres, pres + V, max_path, path, n_accepted, bonus_token,
+                     dev_status);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

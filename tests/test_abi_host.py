@@ -260,9 +260,11 @@ def test_logits_process_argument_errors(lib):
 
 def test_accept_q_argument_errors(lib):
     f = lib.eagle_accept_q
-    assert lib.eagle_accept_q_workspace(128256) == 2 * 128256 * 8
-    assert lib.eagle_accept_q_workspace(0) == 0
-    ok = [8, FAKE, FAKE, FAKE, FAKE, 100, 1.0, FAKE, 8, FAKE, FAKE, FAKE, FAKE, 1600, None, None]
+    nchunk = (128256 + 4095) // 4096
+    assert lib.eagle_accept_q_workspace(64, 128256) == 2 * 128256 * 8 + 2 * 64 * nchunk * 16
+    assert lib.eagle_accept_q_workspace(64, 0) == 0 and lib.eagle_accept_q_workspace(0, 10) == 0
+    need = lib.eagle_accept_q_workspace(8, 100)
+    ok = [8, FAKE, FAKE, FAKE, FAKE, 100, 1.0, FAKE, 8, FAKE, FAKE, FAKE, FAKE, need, None, None]
     def call(i, v):
         a = list(ok)
         a[i] = v
@@ -274,4 +276,4 @@ def test_accept_q_argument_errors(lib):
     assert call(6, 0.0) == EINVAL
     assert call(8, 0) == EINVAL
     assert call(12, FAKE + 4) == EINVAL       # workspace alignment
-    assert call(13, 1599) == EWS
+    assert call(13, need - 1) == EWS
