@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 // that range, each streaming W straight from HBM into MFMA A operands and the
 // activation rows straight from L2 into B operands (no LDS staging and no
 // barrier in the loop), and the four wave tiles are added in LDS.  A column
-// block's k range is split over S workgroups so that ~512 are in flight; each
+// block's k range is split over S workgroups so that ~256 are in flight; each
 // writes its fp32 tile to the workspace and the last one to arrive (a
 // per-column-block counter) sums the S tiles in range order, so the result
 // does not depend on scheduling, and runs the epilogue:
@@ -818,8 +818,10 @@ struct SkPlan {
 };
 
 // Column blocks by mode; k ranges per column block: the smallest power of two
-// that puts >= 512 workgroups in flight (two per CU), with at least four k
-// steps (one per wave) per workgroup.
+// that puts >= 256 workgroups in flight (one per CU), with at least four k
+// steps (one per wave) per workgroup.  (Measured on the Llama-3-8B draft
+// round: 256 beats 512 and 128 - fewer hand-offs of partial tiles, yet every
+// CU busy.)
 static SkPlan sk_plan(int mode, int M, int K, int N, int heads, int hd) {
   SkPlan pl{};
   if (mode == SK_SWIGLU) pl.nblk = (N + 31) / 32;
@@ -827,7 +829,7 @@ static SkPlan sk_plan(int mode, int M, int K, int N, int heads, int hd) {
   else pl.nblk = (N + 63) / 64;
   const int nk = K / kWsKG;
   int S = 1;
-  while (S < kSkMaxS && pl.nblk * S < 512 && 2 * S <= nk / 4) S *= 2;
+  while (S < kSkMaxS && pl.nblk * S < 256 && 2 * S <= nk / 4) S *= 2;
   pl.S = S;
   pl.part_off = kSkCounterBytes;
   pl.total = pl.S > 1
