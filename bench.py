@@ -317,17 +317,20 @@ def main():
     lg = inputs.device_normal((w.T, w.vocab), 5100, dev, dtype=torch.float32) * 2.0
     lg_out = torch.empty_like(lg)
     lp_kept = torch.empty(w.T, dtype=torch.int32, device=dev)
+    lp_ws = torch.empty(max(_lib.lib().eagle_logits_process_workspace(w.T, w.vocab, 40), 256),
+                        dtype=torch.uint8, device=dev)
     lp_us = graph_time_us(lambda: _lib.eagle_logits_process(lg, 0.8, 40, 0.95, out=lg_out,
-                                                            kept=lp_kept), n_calls=10)
+                                                            kept=lp_kept, workspace=lp_ws),
+                          n_calls=10)
     lp_bytes = 2 * w.T * w.vocab * 4
-    line["logits_process"] = {"kernel": f"eagle_logits_process (logits_process_kernel), {w.T} rows x "
+    line["logits_process"] = {"kernel": f"eagle_logits_process (lp_chunk_kernel + lp_merge_kernel), {w.T} rows x "
                                         f"V={w.vocab}, temperature 0.8, top-k 40, top-p 0.95",
                               "bound": "hbm", "achieved": round(lp_bytes / lp_us / 1e3, 1),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(lp_bytes / lp_us / 1e3 / HBM_PEAK_GBS, 4),
                               "avg_us": round(lp_us, 2), "bytes_per_launch": lp_bytes,
                               "timing": "HIP graph of 10 back-to-back calls, replayed 5 times"}
-    del lg, lg_out
+    del lg, lg_out, lp_ws
     # speculative sampling with the draft's distribution over the verify tree
     # (64 nodes, V = 128256, target and draft logits, a planted path)
     g = inputs.rng(w.cfg, inputs.STREAM_U, 7)

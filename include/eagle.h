@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 3
+#define EAGLE_ABI_VERSION 4
 
 typedef enum {
   EAGLE_OK = 0,
@@ -252,13 +252,19 @@ int eagle_gate_children(const float* logp, int32_t rows, int32_t k, float tau,
  *
  * logits f32[T][V] device -> out f32[T][V] (may be logits itself); kept
  * int32[T] device or NULL: tokens kept per row.  Logits must be finite.
+ * workspace >= eagle_logits_process_workspace(T, V, top_k) bytes, 8-byte
+ * aligned (the query returns 0, and workspace may be NULL, when the k kept
+ * by top-k are too many for the chunked path: then one workgroup per row
+ * streams the row once per radix pass).
  * Errors: null pointers, T or V < 1, top_k < 0, temperature not in
  * (0, inf), top_p not in (0, 1] -> EAGLE_EINVAL; top_p < 1 with more than
- * 1024 tokens left by top-k -> EAGLE_EUNSUPPORTED.
+ * 1024 tokens left by top-k -> EAGLE_EUNSUPPORTED; small or null workspace
+ * when one is needed -> EAGLE_EWORKSPACE.
  */
+size_t eagle_logits_process_workspace(int32_t T, int32_t V, int32_t top_k);
 int eagle_logits_process(const float* logits, int32_t T, int32_t V, float temperature,
                          int32_t top_k, float top_p, float* out, int32_t* kept,
-                         hipStream_t stream);
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
  * eagle_accept - accept the longest verified path through the tree.

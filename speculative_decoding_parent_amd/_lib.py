@@ -68,7 +68,8 @@ _PROTOS = {
     "eagle_accept_q_workspace": (_SZ, [_I32, _I32]),
     "eagle_accept_q": (_I32, [_I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ, _P,
                               _P]),
-    "eagle_logits_process": (_I32, [_P, _I32, _I32, _F32, _I32, _F32, _P, _P, _P]),
+    "eagle_logits_process_workspace": (_SZ, [_I32, _I32, _I32]),
+    "eagle_logits_process": (_I32, [_P, _I32, _I32, _F32, _I32, _F32, _P, _P, _P, _SZ, _P]),
     "eagle_fuse3": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, ctypes.c_int, _P, _SZ, _P]),
     "eagle_gate_children": (_I32, [_P, _I32, _I32, _F32, _I32, _P, _P, _P, _P]),
     "eagle_kv_commit": (_I32, [_P, _P, _I32, _I32, _I64, _P, _P, _I32, _P, _P, _I64, _I64, _I64, _I32,
@@ -182,16 +183,19 @@ def eagle_tree_attn(q, k_cache, v_cache, L, k_tree, v_tree, Tk, mask, q_mask_row
     return out
 
 
-def eagle_logits_process(logits, temperature, top_k=0, top_p=1.0, out=None, kept=None):
+def eagle_logits_process(logits, temperature, top_k=0, top_p=1.0, out=None, kept=None,
+                         workspace=None):
     """Temperature / top-k / top-p processing of f32 [T][V] logits; returns
     (processed logits with removed tokens at -inf, kept int32 [T]).  ``out``
     may be ``logits`` itself."""
     T, V = logits.shape
     out = torch.empty_like(logits) if out is None else out
     kept = torch.empty(T, dtype=torch.int32, device=logits.device) if kept is None else kept
+    nb = lib().eagle_logits_process_workspace(T, V, int(top_k))
+    ws = _workspace(nb, logits.device, workspace) if nb else None
     _check("eagle_logits_process", lib().eagle_logits_process(
         _ptr(logits), T, V, float(temperature), int(top_k), float(top_p), _ptr(out), _ptr(kept),
-        _stream()))
+        _ptr(ws), nb, _stream()))
     return out, kept
 
 

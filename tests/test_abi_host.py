@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.eagle_abi_version() == 3
+    assert lib.eagle_abi_version() == 4
     for code in (0, -1, -2, -3, -4, 7):
         assert lib.eagle_status_string(code)
 
@@ -245,17 +245,27 @@ def test_fuse3_argument_errors(lib):
 
 def test_logits_process_argument_errors(lib):
     f = lib.eagle_logits_process
-    assert f(None, 4, 100, 1.0, 10, 0.9, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 100, 1.0, 10, 0.9, None, None, None) == EINVAL
-    assert f(FAKE, 0, 100, 1.0, 10, 0.9, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 0, 1.0, 10, 0.9, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 100, 0.0, 10, 0.9, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 100, float("inf"), 10, 0.9, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 100, 1.0, -1, 0.9, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 100, 1.0, 10, 0.0, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 100, 1.0, 10, 1.5, FAKE, None, None) == EINVAL
-    assert f(FAKE, 4, 5000, 1.0, 0, 0.9, FAKE, None, None) == EUNSUP     # top-p over 5000 tokens
-    assert f(FAKE, 4, 5000, 1.0, 1025, 0.9, FAKE, None, None) == EUNSUP
+    q = lib.eagle_logits_process_workspace
+    # chunks of 16384 tokens; candidate keys (8 bytes) of every chunk when chunks x k <= 4096
+    assert q(64, 128256, 40) == 64 * 8 * 40 * 8
+    assert q(64, 128256, 512) == 64 * 8 * 512 * 8
+    assert q(64, 128256, 513) == 0 and q(9, 128256, 0) == 0     # one workgroup per row
+    assert q(17, 5000, 1024) == 17 * 1024 * 8 and q(20, 900, 0) == 20 * 900 * 8
+    assert q(0, 100, 10) == 0 and q(4, 0, 10) == 0 and q(4, 100, -1) == 0
+    nb = q(4, 100, 10)
+    assert f(None, 4, 100, 1.0, 10, 0.9, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, 10, 0.9, None, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 0, 100, 1.0, 10, 0.9, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 0, 1.0, 10, 0.9, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 100, 0.0, 10, 0.9, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 100, float("inf"), 10, 0.9, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, -1, 0.9, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, 10, 0.0, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 100, 1.0, 10, 1.5, FAKE, None, FAKE, nb, None) == EINVAL
+    assert f(FAKE, 4, 5000, 1.0, 0, 0.9, FAKE, None, None, 0, None) == EUNSUP   # top-p over 5000 tokens
+    assert f(FAKE, 4, 5000, 1.0, 1025, 0.9, FAKE, None, None, 0, None) == EUNSUP
+    assert f(FAKE, 4, 100, 1.0, 10, 0.9, FAKE, None, None, nb, None) == EWS
+    assert f(FAKE, 4, 100, 1.0, 10, 0.9, FAKE, None, FAKE, nb - 1, None) == EWS
 
 
 def test_accept_q_argument_errors(lib):

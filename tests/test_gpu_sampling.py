@@ -41,6 +41,10 @@ def compare(got, gkept, lg, temp, top_k, top_p):
     (20, 900, 1.0, 0, 0.5, 1.0),          # top-p over the whole (small) vocabulary
     (9, 128256, 1.0, 0, 1.0, 1.0),        # no filtering: a copy
     (25, 2000, 0.5, 1, 0.9, 1.0),         # greedy
+    (12, 50001, 1.0, 30, 0.9, 2.0),       # V % 4 != 0: single-token loads, ragged last chunk
+    (8, 16484, 0.9, 200, 0.99, 1.5),      # last chunk (100 tokens) shorter than k
+    (6, 128256, 1.0, 600, 1.0, 2.0),      # 8 chunks x 600 > 4096 candidates: one workgroup per row
+    (5, 65536, 1.2, 1024, 0.7, 1.0),      # 4 chunks x 1024: the largest candidate set sorted
 ])
 def test_matches_oracle(dev, T, V, temp, top_k, top_p, scale):
     g = inputs.rng(950, T, V)
@@ -57,6 +61,16 @@ def test_ties_and_in_place(dev):
     for top_k, top_p in [(30, 0.9), (100, 1.0), (5, 0.5)]:
         got, gkept = run(dev, lg.copy(), 1.0, top_k, top_p, in_place=True)
         compare(got, gkept, lg, 1.0, top_k, top_p)
+
+
+def test_ties_across_chunks_in_place(dev):
+    """Heavily tied logits over several 16384-token chunks, written in place:
+    the cut falls inside a run of equal values spread over every chunk."""
+    g = inputs.rng(953, 0)
+    lg = np.round(g.standard_normal((12, 60000), dtype=np.float32) * 1.5).astype(np.float32)
+    for top_k, top_p in [(300, 1.0), (1000, 0.6), (17, 0.95)]:
+        got, gkept = run(dev, lg.copy(), 0.9, top_k, top_p, in_place=True)
+        compare(got, gkept, lg, 0.9, top_k, top_p)
 
 
 def test_processed_logits_through_sampling_accept(dev):
