@@ -317,13 +317,13 @@ def main():
     lg = inputs.device_normal((w.T, w.vocab), 5100, dev, dtype=torch.float32) * 2.0
     lg_out = torch.empty_like(lg)
     lp_kept = torch.empty(w.T, dtype=torch.int32, device=dev)
-    lp_ws = torch.empty(max(_lib.lib().eagle_logits_process_workspace(w.T, w.vocab, 40), 256),
-                        dtype=torch.uint8, device=dev)
+    lp_ws = torch.zeros(max(_lib.lib().eagle_logits_process_workspace(w.T, w.vocab, 40), 256),
+                        dtype=torch.uint8, device=dev)   # zero: its counters
     lp_us = graph_time_us(lambda: _lib.eagle_logits_process(lg, 0.8, 40, 0.95, out=lg_out,
                                                             kept=lp_kept, workspace=lp_ws),
                           n_calls=10)
     lp_bytes = 2 * w.T * w.vocab * 4
-    line["logits_process"] = {"kernel": f"eagle_logits_process (lp_chunk_kernel + lp_merge_kernel), {w.T} rows x "
+    line["logits_process"] = {"kernel": f"eagle_logits_process (lp_chunk_kernel), {w.T} rows x "
                                         f"V={w.vocab}, temperature 0.8, top-k 40, top-p 0.95",
                               "bound": "hbm", "achieved": round(lp_bytes / lp_us / 1e3, 1),
                               "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -252,10 +252,12 @@ int eagle_gate_children(const float* logp, int32_t rows, int32_t k, float tau,
  *
  * logits f32[T][V] device -> out f32[T][V] (may be logits itself); kept
  * int32[T] device or NULL: tokens kept per row.  Logits must be finite.
- * workspace >= eagle_logits_process_workspace(T, V, top_k) bytes, 8-byte
- * aligned (the query returns 0, and workspace may be NULL, when the k kept
- * by top-k are too many for the chunked path: then one workgroup per row
- * streams the row once per radix pass).
+ * workspace >= eagle_logits_process_workspace(T, V, top_k) bytes, 256-byte
+ * aligned, all zero before its first use (it starts with per-row arrival
+ * counters, which every call leaves zero again; calls that share one
+ * workspace must not overlap).  The query returns 0, and workspace may be
+ * NULL, when the k kept by top-k are too many for the chunked path: then one
+ * workgroup per row streams the row once per radix pass.
  * Errors: null pointers, T or V < 1, top_k < 0, temperature not in
  * (0, inf), top_p not in (0, 1] -> EAGLE_EINVAL; top_p < 1 with more than
  * 1024 tokens left by top-k -> EAGLE_EUNSUPPORTED; small or null workspace

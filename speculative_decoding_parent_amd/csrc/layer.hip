@@ -553,39 +553,6 @@ struct SkParams {
   int kseg;
 };
 
-// Hand-off between workgroups without cache-wide write-backs.  Partial tiles
-// are written with device-coherent (sc1) buffer stores, which complete only
-// once visible to every XCD, and read with sc1 buffer loads, which never hit a
-// stale line in this XCD's L2.  arrive_last waits for the workgroup's stores
-// to complete, then counts the arrival with a device-scope atomic; the
-// workgroup that arrives last of `total` therefore finds every other
-// arrival's tile, and resets the counter.  Called by all threads; same answer
-// in all.
-constexpr int kSc1 = 1 << 4;                     // buffer cache policy bit: sc1
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, size_t bytes) {
-  return buf_rsrc(base, bytes);
-}
-__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
-}
-__device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
-}
-
-__device__ __forceinline__ bool arrive_last(int32_t* ctr, int total, int* flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // own stores complete
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev == total - 1;
-    if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = last;
-  }
-  __syncthreads();
-  return *flag != 0;
-}
-
 // First weight row of tile mt (0..3) of column block xb.
 template <int MODE>
 __device__ __forceinline__ int sk_wrow(const SkParams& p, int xb, int mt) {

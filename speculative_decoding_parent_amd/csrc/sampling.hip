@@ -8,20 +8,21 @@
 // tree.
 //
 // Two launch shapes.  Rows are cut into chunks of 16384 tokens; when the
-// candidates of a row (chunks x k) fit one merge workgroup (<= 4096 keys):
-// - lp_chunk_kernel, one 512-thread workgroup per chunk (32 tokens a
-//   thread): a lower bound tau of the chunk's k-th value comes from the
-//   minimum of group maxima, the elements >= tau (a few percent of a chunk
-//   for small k) are staged in LDS and radix-selected there, and the chunk
-//   is written out once (its top-k as read, the rest at -inf), with the
-//   selection keys of its top-k going to the workspace;
-// - lp_merge_kernel, one workgroup per row: the row's candidate keys (every
-//   token of the row's top-k is in its chunk's top-k) are radix-selected
-//   for the row's k-th key in registers, the candidates below it become -inf;
-//   with top-p the k kept keys are bitonic-sorted, and those past the cut
-//   become -inf too (the key carries the index).
-// So the row is read from memory once and written once.  Otherwise (large k)
-// one workgroup of 1024 threads per row streams the row once per radix pass.
+// candidates of a row (chunks x k) fit one workgroup (<= 4096 keys),
+// lp_chunk_kernel runs one 512-thread workgroup per chunk (32 tokens a
+// thread):
+// - a lower bound tau of the chunk's k-th value comes from the minimum of
+//   group maxima; the elements >= tau (a few percent of a chunk for small k)
+//   are staged in LDS and radix-selected there;
+// - the chunk's top-k (the row's candidates: every token of the row's top-k
+//   is in its chunk's top-k) hand their selection keys to the workspace with
+//   device-coherent stores; every other token of the chunk is written -inf;
+// - the row's last workgroup to arrive (a self-resetting counter) reads the
+//   candidates, radix-selects the row's k-th key, with top-p sorts the k
+//   kept and cuts them, and writes each candidate as read or -inf.
+// So the row is read from memory about once and written once, and no output
+// element is written by two workgroups.  Otherwise (large k) one workgroup
+// of 1024 threads per row streams the row once per radix pass.
 //
 // Selection: a radix select of the k-th best selection key (value order bits,
 // then the inverted index: the order logit descending, index ascending, with
@@ -33,9 +34,9 @@
 // every element taking part shares; the row kernel takes 8-bit digits over
 // 32 histogram copies.  top-p (< 1, with k <= 1024): the k kept keys in rank
 // order are weighted by exp((l - l_max) / temperature) in fp64 and summed in
-// rank order to find the cut.  Every output element is written by the thread
-// that read its input (or, for a candidate past the cut, after the chunk
-// kernel has finished), so the output may be the input.
+// rank order to find the cut.  Every output element is written once, by the
+// thread that read its input (a candidate: the last workgroup's thread that
+// reads it from the input), so the output may be the input.
 #include "common.h"
 
 namespace eagle {
@@ -48,7 +49,7 @@ constexpr int kLcThreads = 512;
 constexpr int kLcPer = 32;                       // chunk elements held by a thread
 constexpr int kLcChunk = kLcThreads * kLcPer;    // 16384 tokens per chunk
 constexpr int kLcMaxCand = 4096;                 // chunks x k sorted by one workgroup
-constexpr int kLmThreads = 256;
+constexpr int kLmPer = kLcMaxCand / kLcThreads;   // candidate keys per thread in the merge
 constexpr int kLcList = 4096;                    // presented elements staged in LDS
 
 // Calls f(value, index) for every element of the row this thread owns, with
@@ -453,17 +454,20 @@ __global__ __launch_bounds__(kLpThreads) void logits_process_kernel(const float*
 // Chunk c of row t (grid chunks x T): tokens [c * kLcChunk, +n).  VEC: the
 // thread's elements are 8 groups of 4 consecutive tokens, group u at
 // 4 * (u * kLcThreads + tid); else 32 single tokens at j * kLcThreads + tid.
-// Writes the chunk (its top-min(k, n) as read, the rest -inf) and the keys
+// Writes -inf over the chunk's tokens outside its top-min(k, n), and the keys
 // of its top-min(k, n) to cand[(t * chunks + c) * k, +min(k, n)) in no
-// particular order.
+// particular order; the row's last workgroup to arrive at ctr[t] then merges
+// the row (and resets ctr[t]).
 template <bool VEC>
 __global__ __launch_bounds__(kLcThreads, 4) void lp_chunk_kernel(const float* in, int V, int k,
-                                                              float* out, selkey_t* cand) {
+                                                                 double inv_t, float top_p,
+                                                                 float* out, int32_t* kept,
+                                                                 selkey_t* cand, int32_t* ctr) {
   __shared__ LeanLds rl;
-  __shared__ int sh_n, sh_m;
+  __shared__ int sh_n, sh_m, sh_flag, sh_cut;
   __shared__ float sh_lo[kLcThreads / 64], sh_hi[kLcThreads / 64];
-  __shared__ float lx[kLcList];
-  __shared__ int lv[kLcList];
+  __shared__ __align__(16) float lx[kLcList];   // reused by the merge: keys, then weights
+  __shared__ __align__(16) int lv[kLcList];
   const int tid = threadIdx.x;
   const int c = blockIdx.x;
   const size_t t = blockIdx.y;
@@ -580,27 +584,12 @@ __global__ __launch_bounds__(kLcThreads, 4) void lp_chunk_kernel(const float* in
   }
   __syncthreads();   // sh_n is cleared
 
-  // the chunk again (just read, so mostly from the caches): the values
-  // need not stay in registers through the select
-  // (an opaque copy of the row pointer, so that the first loads are not
-  // reused in place of these)
-  const float* row2 = row;
-  asm volatile("" : "+s"(row2));
-  if (VEC) {
-#pragma unroll
-    for (int u = 0; u < kLcPer / 4; ++u) {
-      const int off = min(4 * (u * kLcThreads + tid), n - 4);
-      const f32x4 y = *(const f32x4*)(row2 + base + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * u + e] = y[e];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kLcPer; ++j) x[j] = row2[base + min(j * kLcThreads + tid, n - 1)];
-  }
   // one slot reservation per thread for its kept elements (few threads
-  // have any), then the keys in element order from that slot
-  selkey_t* cw = cand + (t * gridDim.x + c) * (size_t)k;
+  // have any), then the keys in element order from that slot, stored
+  // device-coherently for the row's last workgroup
+  const int chunks = gridDim.x;
+  const __amdgpu_buffer_rsrc_t rc =
+      dev_rsrc(cand + t * chunks * (size_t)k, (size_t)chunks * k * sizeof(selkey_t));
   uint32_t km = 0u;   // kept-element bits
 #pragma unroll
   for (int j = 0; j < kLcPer; ++j) {
@@ -612,66 +601,61 @@ __global__ __launch_bounds__(kLcThreads, 4) void lp_chunk_kernel(const float* in
 #pragma unroll
     for (int j = 0; j < kLcPer; ++j)
       if ((km >> j) & 1u) {
-        if (slot < kc) cw[slot] = sel_key(x[j], index(j));
+        if (slot < kc) {
+          const selkey_t key = sel_key(x[j], index(j));
+          st_dev2(rc, (uint32_t)((c * k + slot) * sizeof(selkey_t)),
+                  u32x2{(uint32_t)key, (uint32_t)(key >> 32)});
+        }
         ++slot;
       }
   }
-#pragma unroll
-  for (int j = 0; j < kLcPer; ++j) x[j] = ((km >> j) & 1u) ? x[j] : -INFINITY;
+  // The chunk's output: -inf for every token outside its top-k.  Its top-k
+  // (the row's candidates) are left to the row's last workgroup, which writes
+  // each as read or -inf, so no output element is written by two workgroups.
   if (VEC) {
 #pragma unroll
     for (int u = 0; u < kLcPer / 4; ++u) {
       const int off = 4 * (u * kLcThreads + tid);
-      if (off < n) *(f32x4*)(orow + base + off) = f32x4{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
+      if (off < n) {
+        const uint32_t q = (km >> (4 * u)) & 15u;
+        if (q == 0u) {
+          *(f32x4*)(orow + base + off) = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (!((q >> e) & 1u)) orow[base + off + e] = -INFINITY;
+        }
+      }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < kLcPer; ++j) {
       const int off = j * kLcThreads + tid;
-      if (off < n) orow[base + off] = x[j];
+      if (off < n && !((km >> j) & 1u)) orow[base + off] = -INFINITY;
     }
   }
-}
+  if (!arrive_last(ctr + t, chunks, &sh_flag)) return;
 
-// Row t: the candidates of its `chunks` chunks (<= kLcMaxCand keys, held
-// in registers, kLmPer per thread) are radix-selected for the row's k-th key;
-// the candidates below it become -inf in the output.  With top-p, the k kept
-// keys are sorted in LDS and those past the cut become -inf as well.
-constexpr int kLmPer = kLcMaxCand / kLmThreads;
-
-__global__ __launch_bounds__(kLmThreads) void lp_merge_kernel(const selkey_t* cand, int V,
-                                                              int chunks, int k, double inv_t,
-                                                              float top_p, float* out,
-                                                              int32_t* kept) {
-  __shared__ LeanLds rl;
-  __shared__ selkey_t s[kLpMaxCand];
-  __shared__ double pw[kLpMaxCand];
-  __shared__ int sh_cut, sh_n;
-  __shared__ uint32_t sh_lo[kLmThreads / 64], sh_hi[kLmThreads / 64];
-  const int tid = threadIdx.x;
-  const size_t t = blockIdx.x;
+  // ---- the row's last workgroup: the merge.  The candidates (<= kLcMaxCand
+  // keys, every token of the row's top-k among them) are radix-selected for
+  // the row's k-th key in registers; with top-p the k kept keys are sorted
+  // in LDS (over the staging list) and cut.
+  lean_clear<kLcThreads>(rl, tid);
   const int kf = min(k, kLcChunk);                                   // full chunks
   const int kl = min(k, V - (chunks - 1) * kLcChunk);               // the last chunk
   const int M = (chunks - 1) * kf + kl;
-  const selkey_t* cr = cand + t * chunks * (size_t)k;
-  // candidate i = j * kLmThreads + tid; loads from clamped positions, all
-  // issued before the first is used; key 0 marks "none"
   selkey_t key[kLmPer];
 #pragma unroll
   for (int j = 0; j < kLmPer; ++j) {
-    const int i = min(j * kLmThreads + tid, M - 1);
-    const int c = min(i / kf, chunks - 1);
-    key[j] = cr[(size_t)c * k + (i - c * kf)];
+    const int i = min(j * kLcThreads + tid, M - 1);
+    const int cc = min(i / kf, chunks - 1);
+    const u32x2 w = ld_dev2(rc, (uint32_t)((cc * k + (i - cc * kf)) * sizeof(selkey_t)));
+    key[j] = j * kLcThreads + tid < M ? (((selkey_t)w.y << 32) | w.x) : 0ull;
   }
-#pragma unroll
-  for (int j = 0; j < kLmPer; ++j)
-    if (j * kLmThreads + tid >= M) key[j] = 0ull;
   if (tid == 0) sh_n = 0;
-
-  uint32_t th_hi = 0, th_lo = 0;
+  uint32_t mh = 0u, ml = 0u;
   if (k < M) {
     // [lo, hi]: the order bits of the smallest and largest candidate
-    lean_clear<kLmThreads>(rl, tid);
     uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
     for (int j = 0; j < kLmPer; ++j)
@@ -682,48 +666,51 @@ __global__ __launch_bounds__(kLmThreads) void lp_merge_kernel(const selkey_t* ca
     lo = (uint32_t)wave_reduce((int)lo, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
     hi = (uint32_t)wave_reduce((int)hi, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
     if ((tid & 63) == 0) {
-      sh_lo[tid >> 6] = lo;
-      sh_hi[tid >> 6] = hi;
+      ((uint32_t*)sh_lo)[tid >> 6] = lo;
+      ((uint32_t*)sh_hi)[tid >> 6] = hi;
     }
     __syncthreads();
-    lo = min(min(sh_lo[0], sh_lo[1]), min(sh_lo[2], sh_lo[3]));
-    hi = max(max(sh_hi[0], sh_hi[1]), max(sh_hi[2], sh_hi[3]));
-    radix_select_lean<kLmThreads>(
+#pragma unroll
+    for (int w = 0; w < kLcThreads / 64; ++w) {
+      lo = min(lo, ((uint32_t*)sh_lo)[w]);
+      hi = max(hi, ((uint32_t*)sh_hi)[w]);
+    }
+    radix_select_lean<kLcThreads>(
         rl, tid, k, lo, hi, ~(uint32_t)(V - 1), 0xffffffffu,
         [&](auto&& f) __attribute__((always_inline)) {
 #pragma unroll
           for (int j = 0; j < kLmPer; ++j)
             if (key[j] != 0ull) f(key_value(key[j]), key_index(key[j]));
         },
-        th_hi, th_lo);
+        mh, ml);
   }
   __syncthreads();   // sh_n is cleared
-  const selkey_t th = ((selkey_t)th_hi << 32) | th_lo;
-  float* orow = out + t * V;
+  const selkey_t th = ((selkey_t)mh << 32) | ml;
+  selkey_t cut = th;   // candidates below it become -inf
   int keep = k;
   if (top_p < 1.0f) {
+    selkey_t* sk = (selkey_t*)lx;    // the staging list is free now
+    double* pw = (double*)lv;
 #pragma unroll
     for (int j = 0; j < kLmPer; ++j)
       if (key[j] != 0ull && key[j] >= th) {
         const int slot = atomicAdd(&sh_n, 1);
-        if (slot < kLpMaxCand) s[slot] = key[j];
+        if (slot < kLpMaxCand) sk[slot] = key[j];
       }
     __syncthreads();
     int N = 1;
     while (N < k) N <<= 1;
-    for (int i = k + tid; i < N; i += kLmThreads) s[i] = 0ull;
-    bitonic_desc<kLmThreads>(s, N, tid);
-    keep = top_p_cut<kLmThreads>(s, k, inv_t, top_p, pw, &sh_cut, tid);
-    for (int i = keep + tid; i < k; i += kLmThreads) {
-      const int v = key_index(s[i]);
-      if ((unsigned)v < (unsigned)V) orow[v] = -INFINITY;
-    }
+    for (int i = k + tid; i < N; i += kLcThreads) sk[i] = 0ull;
+    bitonic_desc<kLcThreads>(sk, N, tid);
+    keep = top_p_cut<kLcThreads>(sk, k, inv_t, top_p, pw, &sh_cut, tid);
+    cut = sk[keep - 1];
   }
+  const float* irow = row;
 #pragma unroll
   for (int j = 0; j < kLmPer; ++j)
-    if (key[j] != 0ull && key[j] < th) {
+    if (key[j] != 0ull) {
       const int v = key_index(key[j]);
-      if ((unsigned)v < (unsigned)V) orow[v] = -INFINITY;
+      if ((unsigned)v < (unsigned)V) orow[v] = key[j] >= cut ? irow[v] : -INFINITY;
     }
   if (tid == 0 && kept) kept[t] = keep;
 }
@@ -731,6 +718,7 @@ __global__ __launch_bounds__(kLmThreads) void lp_merge_kernel(const selkey_t* ca
 // Chunks of a row, and whether its candidates fit one merge workgroup.
 static inline int lp_chunks(int V) { return (V + kLcChunk - 1) / kLcChunk; }
 static inline bool lp_chunked(int V, int k) { return (long long)lp_chunks(V) * k <= kLcMaxCand; }
+static inline size_t lp_ctr_bytes(int T) { return ((size_t)T * sizeof(int32_t) + 255) / 256 * 256; }
 
 }  // namespace eagle
 
@@ -739,7 +727,7 @@ extern "C" size_t eagle_logits_process_workspace(int32_t T, int32_t V, int32_t t
   if (T < 1 || V < 1 || top_k < 0) return 0;
   const int k = (top_k == 0 || top_k >= V) ? V : top_k;
   if (!lp_chunked(V, k)) return 0;
-  return (size_t)T * lp_chunks(V) * k * sizeof(selkey_t);
+  return lp_ctr_bytes(T) + (size_t)T * lp_chunks(V) * k * sizeof(selkey_t);
 }
 
 extern "C" int eagle_logits_process(const float* logits, int32_t T, int32_t V, float temperature,
@@ -761,19 +749,17 @@ extern "C" int eagle_logits_process(const float* logits, int32_t T, int32_t V, f
     return EAGLE_OK;
   }
   EAGLE_REQUIRE(workspace && ws_bytes >= need, EAGLE_EWORKSPACE);
-  EAGLE_REQUIRE(((uintptr_t)workspace & 7) == 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
   const int chunks = lp_chunks(V);
-  selkey_t* cand = (selkey_t*)workspace;
+  int32_t* ctr = (int32_t*)workspace;
+  selkey_t* cand = (selkey_t*)((char*)workspace + lp_ctr_bytes(T));
   const bool vec = (V & 3) == 0 && (((uintptr_t)logits | (uintptr_t)out) & 15) == 0;
   if (vec)
     hipLaunchKernelGGL(lp_chunk_kernel<true>, dim3(chunks, T), dim3(kLcThreads), 0, stream, logits,
-                       V, k, out, cand);
+                       V, k, inv_t, top_p, out, kept, cand, ctr);
   else
     hipLaunchKernelGGL(lp_chunk_kernel<false>, dim3(chunks, T), dim3(kLcThreads), 0, stream, logits,
-                       V, k, out, cand);
-  EAGLE_LAUNCH_CHECK();
-  hipLaunchKernelGGL(lp_merge_kernel, dim3(T), dim3(kLmThreads), 0, stream, cand, V, chunks, k,
-                     inv_t, top_p, out, kept);
+                       V, k, inv_t, top_p, out, kept, cand, ctr);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

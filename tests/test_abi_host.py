@@ -246,11 +246,13 @@ def test_fuse3_argument_errors(lib):
 def test_logits_process_argument_errors(lib):
     f = lib.eagle_logits_process
     q = lib.eagle_logits_process_workspace
-    # chunks of 16384 tokens; candidate keys (8 bytes) of every chunk when chunks x k <= 4096
-    assert q(64, 128256, 40) == 64 * 8 * 40 * 8
-    assert q(64, 128256, 512) == 64 * 8 * 512 * 8
+    # chunks of 16384 tokens; per-row counters (256-byte padded), then the
+    # candidate keys (8 bytes) of every chunk, when chunks x k <= 4096
+    ctr = lambda T: (4 * T + 255) // 256 * 256
+    assert q(64, 128256, 40) == ctr(64) + 64 * 8 * 40 * 8
+    assert q(64, 128256, 512) == ctr(64) + 64 * 8 * 512 * 8
     assert q(64, 128256, 513) == 0 and q(9, 128256, 0) == 0     # one workgroup per row
-    assert q(17, 5000, 1024) == 17 * 1024 * 8 and q(20, 900, 0) == 20 * 900 * 8
+    assert q(17, 5000, 1024) == ctr(17) + 17 * 1024 * 8 and q(20, 900, 0) == ctr(20) + 20 * 900 * 8
     assert q(0, 100, 10) == 0 and q(4, 0, 10) == 0 and q(4, 100, -1) == 0
     nb = q(4, 100, 10)
     assert f(None, 4, 100, 1.0, 10, 0.9, FAKE, None, FAKE, nb, None) == EINVAL

@@ -73,6 +73,23 @@ def test_ties_across_chunks_in_place(dev):
         compare(got, gkept, lg, 0.9, top_k, top_p)
 
 
+def test_workspace_reused_across_calls(dev):
+    """One zeroed workspace for several calls of different shapes, as a graph
+    replay or a serving loop would use it: the per-row arrival counters must
+    be left zero by every call."""
+    shapes = [(64, 128256, 0.8, 40, 0.95), (7, 40000, 1.0, 100, 1.0), (64, 128256, 1.1, 12, 0.8),
+              (3, 1000, 1.0, 0, 0.5)]
+    nb = max(_lib.lib().eagle_logits_process_workspace(T, V, k) for T, V, _, k, _ in shapes)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    for i, (T, V, temp, top_k, top_p) in enumerate(shapes * 2):
+        print(f"reuse call {i}: T={T} V={V} top_k={top_k} top_p={top_p}", flush=True)
+        lg = (inputs.rng(954, i).standard_normal((T, V), dtype=np.float32) * 2).astype(np.float32)
+        x = torch.from_numpy(lg).to(dev)
+        out, kept = _lib.eagle_logits_process(x, temp, top_k, top_p, workspace=ws)
+        torch.cuda.synchronize()
+        compare(out.cpu().numpy(), kept.cpu().numpy(), lg, temp, top_k, top_p)
+
+
 def test_processed_logits_through_sampling_accept(dev):
     """logits -> processor -> eagle_accept(SAMPLE) on the GPU against the
     oracle processor -> oracle sampling walk, on planted and random trees."""
