@@ -451,7 +451,8 @@ __global__ __launch_bounds__(kLpThreads) void logits_process_kernel(const float*
   if (tid == 0 && kept) kept[r] = keep;
 }
 
-// Chunk c of row t (grid chunks x T): tokens [c * kLcChunk, +n).  VEC: the
+// Chunk c of row t (grid T x chunks: rows in x, up to 2^31 - 1 of them):
+// tokens [c * kLcChunk, +n).  VEC: the
 // thread's elements are 8 groups of 4 consecutive tokens, group u at
 // 4 * (u * kLcThreads + tid); else 32 single tokens at j * kLcThreads + tid.
 // Writes -inf over the chunk's tokens outside its top-min(k, n), and the keys
@@ -469,8 +470,8 @@ __global__ __launch_bounds__(kLcThreads, 4) void lp_chunk_kernel(const float* in
   __shared__ __align__(16) float lx[kLcList];   // reused by the merge: keys, then weights
   __shared__ __align__(16) int lv[kLcList];
   const int tid = threadIdx.x;
-  const int c = blockIdx.x;
-  const size_t t = blockIdx.y;
+  const int c = blockIdx.y;
+  const size_t t = blockIdx.x;
   const int base = c * kLcChunk;
   const int n = min(kLcChunk, V - base);
   const int kc = min(k, n);
@@ -587,7 +588,7 @@ __global__ __launch_bounds__(kLcThreads, 4) void lp_chunk_kernel(const float* in
   // one slot reservation per thread for its kept elements (few threads
   // have any), then the keys in element order from that slot, stored
   // device-coherently for the row's last workgroup
-  const int chunks = gridDim.x;
+  const int chunks = gridDim.y;
   const __amdgpu_buffer_rsrc_t rc =
       dev_rsrc(cand + t * chunks * (size_t)k, (size_t)chunks * k * sizeof(selkey_t));
   uint32_t km = 0u;   // kept-element bits
@@ -755,10 +756,10 @@ extern "C" int eagle_logits_process(const float* logits, int32_t T, int32_t V, f
   selkey_t* cand = (selkey_t*)((char*)workspace + lp_ctr_bytes(T));
   const bool vec = (V & 3) == 0 && (((uintptr_t)logits | (uintptr_t)out) & 15) == 0;
   if (vec)
-    hipLaunchKernelGGL(lp_chunk_kernel<true>, dim3(chunks, T), dim3(kLcThreads), 0, stream, logits,
+    hipLaunchKernelGGL(lp_chunk_kernel<true>, dim3(T, chunks), dim3(kLcThreads), 0, stream, logits,
                        V, k, inv_t, top_p, out, kept, cand, ctr);
   else
-    hipLaunchKernelGGL(lp_chunk_kernel<false>, dim3(chunks, T), dim3(kLcThreads), 0, stream, logits,
+    hipLaunchKernelGGL(lp_chunk_kernel<false>, dim3(T, chunks), dim3(kLcThreads), 0, stream, logits,
                        V, k, inv_t, top_p, out, kept, cand, ctr);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
