@@ -45,6 +45,9 @@ def compare(got, gkept, lg, temp, top_k, top_p):
     (8, 16484, 0.9, 200, 0.99, 1.5),      # last chunk (100 tokens) shorter than k
     (6, 128256, 1.0, 600, 1.0, 2.0),      # 8 chunks x 600 > 4096 candidates: one workgroup per row
     (5, 65536, 1.2, 1024, 0.7, 1.0),      # 4 chunks x 1024: the largest candidate set sorted
+    (1, 128256, 0.8, 40, 0.95, 2.0),      # one row: its 8 chunk workgroups hand off to the last
+    (4, 1001, 1.0, 20, 0.9, 1.0),         # one unaligned chunk (single-token loads)
+    (3, 3000, 1.0, 0, 1.0, 1.0),          # no filtering on the chunked path: every token a candidate
 ])
 def test_matches_oracle(dev, T, V, temp, top_k, top_p, scale):
     g = inputs.rng(950, T, V)
