@@ -117,12 +117,18 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(
 // exp(((double)l - m_c) / temperature) in fp64 (the division taken as a
 // product with the fp64 reciprocal: at most one ulp of the exponent, and
 // exact for temperature 1).
+// Rows [0, T0) of the grid read logits0 and write ws0, the rest logits1 and
+// ws1 (one launch for the target's and the draft's rows).
 __global__ __launch_bounds__(256) void accept_row_stats_kernel(
-    const float* __restrict__ logits, int V, double itemp, int nchunk, double* __restrict__ ws) {
+    const float* __restrict__ logits0, double* __restrict__ ws0, int T0,
+    const float* __restrict__ logits1, double* __restrict__ ws1, int V, double itemp,
+    int nchunk) {
   constexpr int PER = kAcceptChunk / 256;  // logits per thread, held in registers
   const int c = blockIdx.x;
-  const int t = blockIdx.y;
-  const float* row = logits + (size_t)t * V;
+  const bool second = (int)blockIdx.y >= T0;
+  const int t = second ? (int)blockIdx.y - T0 : (int)blockIdx.y;
+  const float* row = (second ? logits1 : logits0) + (size_t)t * V;
+  double* ws = second ? ws1 : ws0;
   const int lo = c * kAcceptChunk;
   const int hi = min(V, lo + kAcceptChunk);
   __shared__ float smax[4];
@@ -675,7 +681,8 @@ extern "C" int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
     const int nchunk = (V + eagle::kAcceptChunk - 1) / eagle::kAcceptChunk;
     const double itemp = 1.0 / (double)temperature;
     hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, T), dim3(256), 0, stream,
-                       target_logits, V, itemp, nchunk, (double*)workspace);
+                       target_logits, (double*)workspace, T, target_logits, (double*)workspace, V,
+                       itemp, nchunk);
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(eagle::accept_sample_kernel, dim3(1), dim3(1024), 0, stream, T,
                        node_token, node_parent, target_logits, V, itemp, uniforms, nchunk,
@@ -710,11 +717,8 @@ extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_
   double* pres = (double*)workspace;
   double* pst = pres + 2 * (size_t)V;
   double* qst = pst + (size_t)T * nchunk * 2;
-  hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, T), dim3(256), 0, stream,
-                     target_logits, V, itemp, nchunk, pst);
-  EAGLE_LAUNCH_CHECK();
-  hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, T), dim3(256), 0, stream,
-                     draft_logits, V, itemp, nchunk, qst);
+  hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, 2 * T), dim3(256), 0, stream,
+                     target_logits, pst, T, draft_logits, qst, V, itemp, nchunk);
   EAGLE_LAUNCH_CHECK();
   hipLaunchKernelGGL(eagle::accept_sample_q_kernel, dim3(1), dim3(eagle::kQThreads), 0, stream, T,
                      node_token, node_parent, target_logits, draft_logits, V, itemp, uniforms,
