@@ -21,16 +21,18 @@ Sources (the pages):
     PR #13908), Implementation Characteristics (single-sequence inference)
     and the test setup (mixed sampling: temperature, top_k, top_p).
 
-Parity status: every function here is pinned by tests under ``tests/`` marked
-``not gpu`` (closed forms, library routines on special cases, brute force on
-tiny inputs, invariants the pages state).  No function is parity unpinned.
+Parity status: every public function here, the layer's building blocks
+(``linear``, ``swiglu_mlp_hidden``, ``rms_norm``, ``silu``, ``rope``) included,
+is pinned by tests under ``tests/`` that run without a GPU: closed forms,
+library routines on special cases, brute force on tiny integer inputs, and
+invariants the pages state.  No function is parity unpinned.
 """
 from .mask import build_tree_mask, mask_bits, mask_popcount  # noqa: F401
 from .attention import tree_attention  # noqa: F401
 from .lmhead import lm_head_logits, softmax_stats, topk_ids, lm_head_topk, confidence_ratio  # noqa: F401
 from .tree import Pool, expand, rerank  # noqa: F401
 from .accept import accept_greedy, accept_sample, accept_sample_q  # noqa: F401
-from .layer import rms_norm, rope, silu, decoder_layer, LayerWeights  # noqa: F401
+from .layer import rms_norm, rope, silu, linear, swiglu_mlp_hidden, decoder_layer, LayerWeights  # noqa: F401
 from .cycle import CycleWeights, draft_and_verify_cycle  # noqa: F401
 from .kv import kv_commit, kv_commit_in_place  # noqa: F401
 from .gate import gate_children  # noqa: F401

@@ -148,3 +148,22 @@ def test_planted_mistake_is_caught():
     new = [1, 2, 3]
     wrong = sorted(sorted(new, key=lambda i: (-float(pool.value[i]), -i))[:2])
     assert wrong != r["new_frontier"]
+
+
+def test_selection_margin_bruteforce():
+    """The margin of a cut is the smallest chosen value minus the largest
+    unchosen one among the candidates, checked against every pair."""
+    from oracle.tree import selection_margin
+    g = np.random.default_rng(21)
+    for _ in range(50):
+        n = int(g.integers(2, 9))
+        vals = g.standard_normal(n).astype(np.float32)
+        cand = list(range(n))
+        chosen = [i for i in cand if g.random() < 0.5]
+        want = min((float(vals[a]) - float(vals[b]) for a in chosen for b in cand if b not in chosen),
+                   default=float("inf"))
+        assert selection_margin(vals, chosen, cand) == want
+    # a top-k cut has a non-negative margin; swapping one member makes it negative
+    v = np.array([3.0, 1.0, 2.0, 0.5], dtype=np.float32)
+    assert selection_margin(v, [0, 2], range(4)) == 1.0
+    assert selection_margin(v, [0, 1], range(4)) == -1.0
