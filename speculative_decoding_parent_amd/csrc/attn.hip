@@ -511,11 +511,6 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, bf16_t* ld
 #endif
 }
 
-// s_waitcnt immediate: vmcnt <= vm, lgkmcnt <= lgkm, expcnt not waited on
-constexpr int waitcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
-
 template <int NTW, int NW, int NST>
 __global__ __launch_bounds__(64 * NW, 1) void tree_attn_ring_kernel(AttnParams p) {
   constexpr int HD = kRingHD;

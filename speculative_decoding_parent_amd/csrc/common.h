@@ -55,14 +55,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, siz
                                            kRsrcWord3);
 }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt
+// not waited on.  On gfx9 vmcnt counts vector-memory stores as well as loads.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
 // Hand-off between workgroups without cache-wide write-backs.  Partial tiles
-// are written with device-coherent (sc1) buffer stores, which complete only
-// once visible to every XCD, and read with sc1 buffer loads, which never hit a
-// stale line in this XCD's L2.  arrive_last waits for the workgroup's stores
-// to complete, then counts the arrival with a device-scope atomic; the
-// workgroup that arrives last of `total` therefore finds every other
-// arrival's tile, and resets the counter.  Called by all threads; same answer
-// in all.
+// are written with device-coherent (sc1) buffer stores, which are acknowledged
+// only once visible to every XCD, and read with sc1 buffer loads, which never
+// hit a stale line in this XCD's L2.  arrive_last first makes every thread
+// wait (s_waitcnt vmcnt(0)) until its own stores are acknowledged; only then
+// does the barrier let thread 0 count the workgroup's arrival with a
+// device-scope atomic.  The workgroup that arrives last of `total` therefore
+// finds every other arrival's tile complete, and resets the counter.  Its
+// reads are issued after the atomic has returned (thread 0 waits for the
+// returned count before the second barrier).  Called by all threads; same
+// answer in all.
 constexpr int kSc1 = 1 << 4;                     // buffer cache policy bit: sc1
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, size_t bytes) {
@@ -76,7 +85,7 @@ __device__ __forceinline__ f32x4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 __device__ __forceinline__ bool arrive_last(int32_t* ctr, int total, int* flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // own stores complete
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));          // own stores acknowledged
   __syncthreads();
   if (threadIdx.x == 0) {
     const int prev = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -373,3 +373,32 @@ def test_layer_llama3_8b_shape(dev):
     g = inputs.rng(706, 0)
     slot_par = np.concatenate([[-1], np.zeros(10), 1 + g.integers(0, 10, 10)]).astype(np.int32)
     layer_case(dev, w, 1, 10, 21, np.arange(11, 21), slot_par)
+
+
+def test_split_k_hand_off_is_deterministic(dev):
+    """The split-K few-row projections hand fp32 tiles between workgroups
+    (device-coherent stores, then an arrival count; the last arrival sums the
+    tiles in range order).  If an arrival were counted before its tiles had
+    landed, the summing workgroup would read a partial tile on some calls.
+    Every one of 200 back-to-back calls must be bit-identical to the first,
+    at the draft's down projection (14336 -> 4096, deferred norm) and gate/up
+    (4096 -> 14336) shapes."""
+    g = inputs.rng(720, 0)
+    M = 10
+    x = inputs.normal(g, (M, 14336)).to(dev)
+    W = inputs.normal(g, (4096, 14336), std=float(1 / np.sqrt(14336))).to(dev)
+    gamma = (1 + 0.1 * inputs.normal(g, (4096,), dtype=torch.float32)).to(dev)
+    res = inputs.normal(g, (M, 4096), dtype=torch.float32).to(dev)
+    h = inputs.normal(g, (M, 4096)).to(dev)
+    wg = inputs.normal(g, (14336, 4096), std=float(1 / np.sqrt(4096))).to(dev)
+    wu = inputs.normal(g, (14336, 4096), std=float(1 / np.sqrt(4096))).to(dev)
+    o0, xg0, s0 = [t.clone() for t in _lib.eagle_linear_rmsnorm_deferred(x, W, gamma, residual=res)]
+    y0 = _lib.eagle_linear_swiglu(h, wg, wu).clone()
+    o, xg, s = torch.empty_like(o0), torch.empty_like(xg0), torch.empty_like(s0)
+    y = torch.empty_like(y0)
+    for rep in range(200):
+        _lib.eagle_linear_rmsnorm_deferred(x, W, gamma, residual=res, out=o, xg_out=xg, ssq_out=s)
+        _lib.eagle_linear_swiglu(h, wg, wu, out=y)
+        assert torch.equal(o, o0) and torch.equal(xg, xg0) and torch.equal(s, s0), f"deferred, call {rep}"
+        assert torch.equal(y, y0), f"swiglu, call {rep}"
+    print("200 calls bit-identical", flush=True)

@@ -120,3 +120,20 @@ def test_processed_logits_through_sampling_accept(dev):
         assert int(st.item()) == 0
         assert int(n.item()) == rn and int(b.item()) == rb
         assert path.cpu().numpy()[:rn + 1].tolist() == rp
+
+
+def test_chunk_hand_off_is_deterministic(dev):
+    """The chunked processor hands each chunk's candidate keys to the row's
+    last-arriving workgroup.  200 back-to-back calls at the verify shape
+    (64 x 128256, top-k 40, top-p 0.95) must each be bit-identical to the
+    first call, processed logits and kept counts alike."""
+    g = inputs.rng(930, 0)
+    lg = torch.from_numpy(g.standard_normal((64, 128256)).astype(np.float32) * 3).to(dev)
+    out0, kept0 = [t.clone() for t in _lib.eagle_logits_process(lg, 0.8, 40, 0.95)]
+    out, kept = torch.empty_like(out0), torch.empty_like(kept0)
+    ws = torch.zeros(_lib.lib().eagle_logits_process_workspace(64, 128256, 40), dtype=torch.uint8,
+                     device=dev)
+    for rep in range(200):
+        _lib.eagle_logits_process(lg, 0.8, 40, 0.95, out=out, kept=kept, workspace=ws)
+        assert torch.equal(out, out0) and torch.equal(kept, kept0), f"call {rep}"
+    print("200 calls bit-identical", flush=True)
