@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 4
+#define EAGLE_ABI_VERSION 5
 
 typedef enum {
   EAGLE_OK = 0,
@@ -174,6 +174,31 @@ int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_
                       int32_t k, eagle_dtype dt, const float* in_ssq, int32_t in_parts,
                       float in_eps, int32_t* topk_id, float* topk_logp, float* lse,
                       float* logits, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * eagle_lmhead_topk_noalloc - eagle_lmhead_topk without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, outputs, kernels and results as eagle_lmhead_topk, minus
+ * workspace/ws_bytes.  The partial lists (or the fp32 logits of the f32 path
+ * when logits is NULL) live in a scratch array the library holds on every
+ * GPU it runs on, EAGLE_LMHEAD_SCRATCH_BYTES bytes, kept until the process
+ * ends; its address is looked up once per device on the first call made
+ * with that device current.  The call itself allocates nothing.
+ *   Limit: eagle_lmhead_topk_workspace(T, d, V, k, dt) must not exceed
+ *   EAGLE_LMHEAD_SCRATCH_BYTES (else EAGLE_EWORKSPACE, before any HIP call);
+ *   e.g. T = 128, V = 128256, k = 10 in bf16 needs 11.3 MB.
+ *   stream must belong to the current device (else EAGLE_EINVAL).
+ * Every call on one GPU shares that GPU's scratch, and nothing in it needs
+ * to start zeroed.  Calls that overlap in time on one GPU (two streams, or
+ * two host threads) race on it: serialise them.
+ */
+#define EAGLE_LMHEAD_SCRATCH_BYTES ((size_t)16 << 20)
+int eagle_lmhead_topk_noalloc(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
+                              int32_t k, eagle_dtype dt, const float* in_ssq, int32_t in_parts,
+                              float in_eps, int32_t* topk_id, float* topk_logp, float* lse,
+                              float* logits, hipStream_t stream);
 
 /*
  * eagle_expand_rerank - grow the dynamic draft tree and prune it.

@@ -44,6 +44,8 @@ _PROTOS = {
     "eagle_lmhead_topk_workspace": (_SZ, [_I32, _I32, _I32, _I32, ctypes.c_int]),
     "eagle_lmhead_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I32, _F32, _P,
                                  _P, _P, _P, _P, _SZ, _P]),
+    "eagle_lmhead_topk_noalloc": (_I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.c_int, _P, _I32,
+                                         _F32, _P, _P, _P, _P, _P]),
     "eagle_expand_rerank": (_I32, [_I32, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32,
                                    _P, _I32, _P, _P, _P, _P, _P, _P]),
     "eagle_accept_workspace": (_SZ, [_I32, _I32]),
@@ -284,6 +286,17 @@ def eagle_lmhead_topk(f, W, k, want_logits=False, topk_id=None, topk_logp=None, 
     _check("eagle_lmhead_topk", lib().eagle_lmhead_topk(
         _ptr(f), _ptr(W), T, d, V, k, dt, *_norm_args(in_norm), _ptr(topk_id), _ptr(topk_logp),
         _ptr(lse), _ptr(logits), _ptr(ws), nb, _stream()))
+    return topk_id, topk_logp, lse, logits
+
+
+def eagle_lmhead_topk_noalloc(f, W, k, topk_id, topk_logp, lse, logits=None, in_norm=None):
+    """eagle_lmhead_topk with the library's own scratch: every output is passed
+    in by the caller and nothing is allocated on the way to the kernels."""
+    T, d = f.shape
+    V = W.shape[0]
+    _check("eagle_lmhead_topk_noalloc", lib().eagle_lmhead_topk_noalloc(
+        _ptr(f), _ptr(W), T, d, V, k, _dt(f), *_norm_args(in_norm), _ptr(topk_id), _ptr(topk_logp),
+        _ptr(lse), _ptr(logits), _stream()))
     return topk_id, topk_logp, lse, logits
 
 

@@ -25,6 +25,8 @@
 //     the list prefixes that can still reach the top k and selects among them.
 // fp32 path (small workloads): a plain VALU dot product per logit, then a
 // per-row top-k kernel.
+#include <mutex>
+
 #include "wstream.h"
 
 namespace eagle {
@@ -582,21 +584,23 @@ extern "C" size_t eagle_lmhead_topk_workspace(int32_t T, int32_t d, int32_t V, i
   return eagle::lm_layout(T, V, k, dt).total;
 }
 
-extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
-                                 int32_t k, eagle_dtype dt, const float* in_ssq, int32_t in_parts,
-                                 float in_eps, int32_t* topk_id, float* topk_logp, float* lse,
-                                 float* logits, void* workspace, size_t ws_bytes,
-                                 hipStream_t stream) {
-  using namespace eagle;
-  EAGLE_REQUIRE(f && W && lse && workspace && (k == 0 || (topk_id && topk_logp)), EAGLE_EINVAL);
+namespace eagle {
+
+// The body of both entry points: arguments checked, then the launches, with
+// `ws` holding the partial lists (bf16) or the fp32 logits when the caller
+// passes none.
+static int lm_run(const void* f, const void* W, int32_t T, int32_t d, int32_t V, int32_t k,
+                  eagle_dtype dt, const float* in_ssq, int32_t in_parts, float in_eps,
+                  int32_t* topk_id, float* topk_logp, float* lse, float* logits, char* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  EAGLE_REQUIRE(f && W && lse && ws && (k == 0 || (topk_id && topk_logp)), EAGLE_EINVAL);
   EAGLE_REQUIRE(!in_ssq || (in_parts >= 1 && in_eps >= 0.0f), EAGLE_EINVAL);
   const RowNorm rn{in_ssq, in_ssq ? in_parts : 0, d, in_eps};
   EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && d >= 1 && V >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(k >= 0 && k <= EAGLE_MAX_TOPK && k <= V, EAGLE_EINVAL);
-  EAGLE_REQUIRE(((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(((uintptr_t)ws & 255) == 0, EAGLE_EINVAL);
   const LmLayout l = lm_layout(T, V, k, dt);
   EAGLE_REQUIRE(ws_bytes >= l.total, EAGLE_EWORKSPACE);
-  char* ws = (char*)workspace;
   if (dt == EAGLE_BF16) {
     EAGLE_REQUIRE(d % kWsKG == 0, EAGLE_EUNSUPPORTED);
     EAGLE_REQUIRE(((uintptr_t)f & 15) == 0 && ((uintptr_t)W & 15) == 0, EAGLE_EINVAL);
@@ -625,4 +629,62 @@ extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_
   }
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
+}
+
+// Scratch of eagle_lmhead_topk_noalloc: the library's own copy of what the
+// caller's workspace holds for eagle_lmhead_topk.  Every GPU the library
+// runs on holds one for the life of the process.  Host code never uses the
+// array's name as an address: the per-device address comes from
+// hipGetSymbolAddress with that device current.
+__device__ __attribute__((aligned(256))) char lm_scratch[EAGLE_LMHEAD_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_lm_scratch_mu;
+static char* g_lm_scratch[kMaxDevices] = {};
+
+static int lm_scratch_ptr(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return EAGLE_EHIP;
+  EAGLE_REQUIRE(dev >= 0 && dev < kMaxDevices, EAGLE_EUNSUPPORTED);
+  if (stream) {   // the scratch found is the current device's: the stream must be on it
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return EAGLE_EHIP;
+    EAGLE_REQUIRE((int)sd == dev, EAGLE_EINVAL);
+  }
+  std::lock_guard<std::mutex> lock(g_lm_scratch_mu);
+  if (!g_lm_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(lm_scratch)) != hipSuccess || !ptr) return EAGLE_EHIP;
+    g_lm_scratch[dev] = (char*)ptr;
+  }
+  *out = g_lm_scratch[dev];
+  return EAGLE_OK;
+}
+
+}  // namespace eagle
+
+extern "C" int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
+                                 int32_t k, eagle_dtype dt, const float* in_ssq, int32_t in_parts,
+                                 float in_eps, int32_t* topk_id, float* topk_logp, float* lse,
+                                 float* logits, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  return eagle::lm_run(f, W, T, d, V, k, dt, in_ssq, in_parts, in_eps, topk_id, topk_logp, lse,
+                       logits, (char*)workspace, ws_bytes, stream);
+}
+
+extern "C" int eagle_lmhead_topk_noalloc(const void* f, const void* W, int32_t T, int32_t d,
+                                         int32_t V, int32_t k, eagle_dtype dt,
+                                         const float* in_ssq, int32_t in_parts, float in_eps,
+                                         int32_t* topk_id, float* topk_logp, float* lse,
+                                         float* logits, hipStream_t stream) {
+  using namespace eagle;
+  // size first, so an oversized request fails before any HIP call
+  EAGLE_REQUIRE(T >= 1 && V >= 1 && k >= 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(dt == EAGLE_BF16 || dt == EAGLE_F32, EAGLE_EINVAL);
+  EAGLE_REQUIRE(lm_layout(T, V, k, dt).total <= EAGLE_LMHEAD_SCRATCH_BYTES, EAGLE_EWORKSPACE);
+  char* ws = nullptr;
+  const int rc = lm_scratch_ptr(stream, &ws);
+  if (rc != EAGLE_OK) return rc;
+  return lm_run(f, W, T, d, V, k, dt, in_ssq, in_parts, in_eps, topk_id, topk_logp, lse, logits,
+                ws, EAGLE_LMHEAD_SCRATCH_BYTES, stream);
 }

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.eagle_abi_version() == 4
+    assert lib.eagle_abi_version() == 5
     for code in (0, -1, -2, -3, -4, 7):
         assert lib.eagle_status_string(code)
 
@@ -113,6 +113,19 @@ def test_lmhead_argument_errors(lib):
     assert call(a7=FAKE, a8=0) == EINVAL         # deferred norm without partials
     assert call(a7=FAKE, a8=4, a9=-1.0) == EINVAL
 
+
+
+def test_lmhead_noalloc_rejects_before_any_hip_call(lib):
+    """Sizes beyond the library's scratch, and bad sizes, are refused on the
+    host before the scratch is looked up or anything is enqueued."""
+    f = lib.eagle_lmhead_topk_noalloc
+    args = lambda T, V, k: [FAKE, FAKE, T, 4096, V, k, _lib.EAGLE_BF16, None, 0, 0.0, FAKE, FAKE,
+                            FAKE, None, None]
+    assert lib.eagle_lmhead_topk_workspace(256, 4096, 128256, 64, _lib.EAGLE_BF16) > 16 << 20
+    assert f(*args(256, 128256, 64)) == EWS
+    assert f(*args(0, 128256, 10)) == EINVAL
+    assert f(*args(10, 0, 10)) == EINVAL
+    assert f(*args(10, 1000, -1)) == EINVAL
 
 def test_tree_argument_errors(lib):
     f = lib.eagle_expand_rerank
