@@ -52,15 +52,16 @@ def tree_attention(q, k_cache, v_cache, L: int, k_tree, v_tree, mask, q_mask_row
     for i in range(Tq):
         r = i if q_mask_row is None else int(q_mask_row[i])
         vis = np.nonzero(vis_all[r])[0]
-        for h in range(Hq):
-            g = h // G
-            keys = np.concatenate([kc[g, :L], kt[g, vis]], axis=0)
-            vals = np.concatenate([vc[g, :L], vt[g, vis]], axis=0)
-            if keys.shape[0] == 0:
-                raise ValueError(f"query row {i} sees nothing")
-            s = (keys @ q[i, h]) * scale
-            s = s - s.max()
+        if L + vis.shape[0] == 0:
+            raise ValueError(f"query row {i} sees nothing")
+        for g in range(Hkv):
+            # the G query heads h = g*G .. g*G+G-1 read KV head g: one column each
+            heads = slice(g * G, (g + 1) * G)
+            qg = q[i, heads].T                                        # [hd][G]
+            s = np.concatenate([kc[g, :L] @ qg, kt[g, vis] @ qg], axis=0) * scale   # [L+|vis|][G]
+            s = s - s.max(axis=0)
             p = np.exp(s)
-            p = p / p.sum()
-            out[i, h] = p @ vals
+            p = p / p.sum(axis=0)
+            # sum over the visible set = sum over the prefix + sum over the visible tree nodes
+            out[i, heads] = p[:L].T @ vc[g, :L] + p[L:].T @ vt[g, vis]
     return out
