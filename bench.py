@@ -204,6 +204,236 @@ def long_context_verify(dev, steps):
                                   "latency, not by the HBM roofline"}}
 
 
+MFMA_PEAK_TFLOPS = 2500.0        # dense bf16 (fp32 vector peak 157.3 TFLOP/s for the fp32 config)
+
+
+def roofline_entry(kernel, nbytes, flops, us, mfma_peak=MFMA_PEAK_TFLOPS):
+    """Achieved rate against the roofline that bounds the call: HBM when its
+    bytes take longer at 8 TB/s than its flops at the MFMA peak, else MFMA."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e3)          # µs
+    t_mfma = flops / (mfma_peak * 1e6)             # µs
+    if t_hbm >= t_mfma:
+        a = nbytes / us / 1e3
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "avg_us": round(us, 2),
+                "bytes_per_launch": int(nbytes), "flops_per_launch": int(flops)}
+    a = flops / us / 1e6
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(a, 1), "peak": mfma_peak,
+            "unit": "TFLOP/s", "frac": round(a / mfma_peak, 4), "avg_us": round(us, 2),
+            "bytes_per_launch": int(nbytes), "flops_per_launch": int(flops),
+            "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def event_time_us(fn, iters):
+    """Mean µs per call of calls long enough to time one by one: HIP events
+    around each call on the stream it is launched on."""
+    stream = torch.cuda.current_stream()
+    fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+
+def rotated_graph_time_us(fns, reps=3):
+    """Mean µs per call of short calls over distinct buffers (caches kept
+    cold: the calls of one replay read more than the 256 MB last-level cache
+    holds), captured back to back in one HIP graph."""
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        fns[0]()
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for fn in fns:
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * len(fns))
+
+
+VERIFY_NAMES = {
+    1: "tiny: d=256, 4 Q / 1 KV heads, hd 64, V=1024, fp32, L=128, T=15 depth <= 4, top-4, greedy",
+    2: "qwen2-7b-verify: d=3584, 28 Q / 4 KV heads, hd 128, bf16 L=2048, T=60 depth <= 7, "
+       "LM head V=152064 for all 60 nodes, top-10, greedy",
+    5: "70b-wide-tree: d=8192, 64 Q / 8 KV heads, hd 128, bf16 L=8192, T=128 depth <= 7 (4-way "
+       "near the root), LM head V=128256 with logits, top-10, greedy and sampling acceptance",
+}
+
+
+def verify_leg(dev, cfg, steps):
+    """One verify pass of a workload: tree mask -> tree attention -> LM head
+    -> acceptance (greedy, and sampling where the workload has it), replayed
+    from a HIP graph with every input resident in HBM.  The LM-head weight and
+    the large feature inputs are drawn on the GPU (same distributions as the
+    host generator, other values); the tree, tokens, q and K/V come from the
+    host generator.  Tokens follow the target's top-1 along one deepest path
+    (planted), so acceptance walks to full depth."""
+    w = inputs.WORKLOADS[cfg]
+    fp32 = w.dtype == "f32"
+    dt = torch.float32 if fp32 else torch.bfloat16
+    vi = inputs.verify_inputs(w, with_lmhead=fp32)
+    T, L, V, k = w.T, w.L, w.vocab, w.topk
+    if fp32:
+        f = vi.f.to(dev)
+        W = inputs.lm_head_weight(w).to(dev)
+    else:
+        f = inputs.device_normal((T, w.d), 6000 + cfg, dev)
+        W = (inputs.device_normal((V, w.d), 6100 + cfg, dev, dtype=torch.float32)
+             * float(1.0 / np.sqrt(w.d))).to(torch.bfloat16)
+    par = torch.from_numpy(vi.parents).to(dev)
+    q, kc, vc, kt, vt = (t.to(dev) for t in (vi.q, vi.k_cache, vi.v_cache, vi.k_tree, vi.v_tree))
+    lib = _lib.lib()
+    i32 = dict(dtype=torch.int32, device=dev)
+    mask = torch.empty((T, w.words), dtype=torch.int64, device=dev)
+    depth = torch.empty(T, **i32)
+    attn_out = torch.empty_like(q)
+    ws_attn = torch.zeros(max(lib.eagle_tree_attn_workspace(T, w.hq, w.hkv, w.hd, L, T,
+                                                            _lib._dt(q)), 256),
+                          dtype=torch.uint8, device=dev)
+    ws_lm = torch.zeros(lib.eagle_lmhead_topk_workspace(T, w.d, V, k, _lib._dt(f)),
+                        dtype=torch.uint8, device=dev)
+    ids = torch.empty((T, k), **i32)
+    lp = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    logits = torch.empty((T, V), dtype=torch.float32, device=dev) if w.sampling else None
+    ws_acc = torch.zeros(max(lib.eagle_accept_workspace(T, V), 256), dtype=torch.uint8,
+                         device=dev)
+    u = torch.from_numpy(vi.uniforms).to(dev)
+    outs_g = [torch.empty(T, **i32), torch.empty(1, **i32), torch.empty(1, **i32)]
+    outs_s = [torch.empty(T, **i32), torch.empty(1, **i32), torch.empty(1, **i32)]
+    status = torch.zeros(1, **i32)
+
+    def lmhead():
+        _lib.eagle_lmhead_topk(f, W, k, topk_id=ids, topk_logp=lp, lse=lse, logits=logits,
+                               workspace=ws_lm)
+
+    # plant the target's top-1 along a deepest path (setup, not timed)
+    lmhead()
+    top1 = ids[:, 0].cpu().numpy()
+    g = inputs.rng(w.cfg, inputs.STREAM_TOK, 99)
+    tok_np = inputs.plant_path(vi.tokens, vi.parents, top1, inputs.deepest_leaf(g, vi.parents))
+    tok = torch.from_numpy(tok_np).to(dev)
+
+    def attn():
+        _lib.eagle_tree_attn(q, kc, vc, L, kt, vt, T, mask, out=attn_out, workspace=ws_attn,
+                             dev_status=status)
+
+    def step():
+        _lib.eagle_build_tree_mask(par, mask=mask, depth=depth, dev_status=status)
+        attn()
+        lmhead()
+        _lib.eagle_accept(_lib.EAGLE_GREEDY, tok, par, target_top1=ids[:, 0], path=outs_g[0],
+                          n_accepted=outs_g[1], bonus_token=outs_g[2], dev_status=status)
+        if w.sampling:
+            _lib.eagle_accept(_lib.EAGLE_SAMPLE, tok, par, target_logits=logits,
+                              temperature=1.0, uniforms=u, path=outs_s[0], n_accepted=outs_s[1],
+                              bonus_token=outs_s[2], workspace=ws_acc, dev_status=status)
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dt_step = (time.perf_counter() - t0) / steps
+    assert int(status.item()) == 0, f"config {cfg}: device status {int(status.item())}"
+    depths = depth.cpu().numpy()
+    leg = {"workload": VERIFY_NAMES[cfg], "value": round(T / dt_step, 1), "unit": "nodes/s",
+           "ms_per_step": round(dt_step * 1e3, 4), "steps": steps,
+           "accepted_greedy": int(outs_g[1].item()),
+           "timing": "one step = mask, attention, LM head, acceptance, replayed from a HIP graph"}
+    if w.sampling:
+        leg["accepted_sampling"] = int(outs_s[1].item())
+
+    # attention alone over rotated K/V copies (cold caches), one HIP graph
+    es = 4 if fp32 else 2
+    kv_bytes = 2 * w.hkv * L * w.hd * es
+    n_rot = int(min(256, max(8, -(-(1 << 30) // kv_bytes))))
+    if fp32:
+        n_rot = 8
+    kcs = [kc] + [kc.clone() for _ in range(n_rot - 1)]
+    vcs = [vc] + [vc.clone() for _ in range(n_rot - 1)]
+    fns = [(lambda a=a, b=b: _lib.eagle_tree_attn(q, a, b, L, kt, vt, T, mask, out=attn_out,
+                                                  workspace=ws_attn)) for a, b in zip(kcs, vcs)]
+    attn_us = rotated_graph_time_us(fns)
+    del kcs, vcs, fns
+    nvis = float(np.mean(depths + 1))
+    a_bytes = (2 * w.hkv * L * w.hd * es + 2 * w.hkv * T * w.hd * es + T * w.hq * w.hd * 2 * es
+               + T * w.words * 8)
+    a_flops = 4 * T * w.hq * w.hd * (L + nvis)
+    peak = 157.3 if fp32 else MFMA_PEAK_TFLOPS
+    leg["attention"] = roofline_entry(f"eagle_tree_attn, Tq={T}, {w.hq}/{w.hkv} heads, hd "
+                                      f"{w.hd}, L={L}", a_bytes, a_flops, attn_us, peak)
+    leg["attention"]["timing"] = (f"HIP graph of {n_rot} calls over distinct K/V copies, "
+                                  "replayed 3 times")
+    # LM head alone (its weight alone exceeds the last-level cache at bf16)
+    lm_us = event_time_us(lmhead, 20) if not fp32 else rotated_graph_time_us([lmhead] * 20)
+    l_bytes = V * w.d * es + T * w.d * es + T * (8 * k + 4) + (4 * T * V if w.sampling else 0)
+    l_flops = 2 * T * w.d * V
+    leg["lmhead"] = roofline_entry(f"eagle_lmhead_topk, T={T}, d={w.d}, V={V}, k={k}"
+                                   + (", logits written" if w.sampling else ""),
+                                   l_bytes, l_flops, lm_us, peak)
+    leg["lmhead"]["timing"] = ("HIP events around each of 20 calls" if not fp32
+                               else "HIP graph of 20 calls, replayed 3 times")
+    host = {"vi": vi, "tokens": tok_np, "top1": top1, "W": None if not fp32 else inputs.lm_head_weight(w),
+            "f": vi.f}
+    if not fp32:
+        host["W"] = W.cpu()
+        host["f"] = f.cpu()
+    del W
+    torch.cuda.empty_cache()
+    return leg, host
+
+
+def blas_vendor():
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:                                   # noqa: BLE001
+        return "unknown"
+
+
+def cpu_verify_pass(w, host):
+    """The oracle's verify pass of a workload on the host: mask, attention,
+    LM head (all rows), greedy acceptance; sampling acceptance where the
+    workload has it.  Returns seconds."""
+    import oracle
+    vi = host["vi"]
+    t0 = time.perf_counter()
+    m, _ = oracle.build_tree_mask(vi.parents)
+    oracle.tree_attention(vi.q, vi.k_cache, vi.v_cache, w.L, vi.k_tree, vi.v_tree, m)
+    lg = oracle.lm_head_logits(host["f"], host["W"])
+    ids = oracle.topk_ids(lg, w.topk)
+    oracle.accept_greedy(host["tokens"], vi.parents, ids[:, 0])
+    if w.sampling:
+        oracle.accept_sample(host["tokens"], vi.parents, lg.astype(np.float32), 1.0, vi.uniforms)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(w, ci):
     """The oracle's full cycle on the host cores (one cycle: 6 draft rounds,
     rerank, verify layer, LM head, acceptance)."""
@@ -221,15 +451,20 @@ def cpu_baseline(w, ci):
     cw = CycleWeights(ci["w_fuse"], lw(ci["draft"]), ci["draft_norm"], ci["embed"], ci["w_lm"],
                       lw(ci["target"]), ci["target_norm"], ci["draft_k_cache"],
                       ci["draft_v_cache"], ci["target_k_cache"], ci["target_v_cache"])
-    t0 = time.perf_counter()
-    oracle.draft_and_verify_cycle(cw, ci["root_token"], ci["root_feature"], hq=w.hq, hkv=w.hkv,
-                                  hd=w.hd, L=w.L, rounds=w.rounds, k=w.topk,
-                                  k_select=w.k_select, T=w.T, temperature=w.temperature,
-                                  uniforms=ci["uniforms"], theta=w.rope_theta, eps=w.rms_eps)
-    dt = time.perf_counter() - t0
-    return {"value": w.T / dt, "unit": "nodes/s", "cores": CORES, "kind": "oracle",
-            "sample": "one full cycle of the same workload (6 draft rounds, rerank, verify "
-                      f"layer, LM head with logits, sampling acceptance) in {dt:.1f} s"}
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.draft_and_verify_cycle(cw, ci["root_token"], ci["root_feature"], hq=w.hq,
+                                      hkv=w.hkv, hd=w.hd, L=w.L, rounds=w.rounds, k=w.topk,
+                                      k_select=w.k_select, T=w.T, temperature=w.temperature,
+                                      uniforms=ci["uniforms"], theta=w.rope_theta, eps=w.rms_eps)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {"value": round(w.T / dt, 3), "unit": "nodes/s", "cores": CORES, "kind": "oracle",
+            "blas": blas_vendor(),
+            "sample": "the full cycle of the same workload (6 draft rounds, rerank, verify layer, "
+                      "LM head with logits, sampling acceptance), median of 3 runs: "
+                      + ", ".join(f"{t:.1f}" for t in times) + " s"}
 
 
 def main():
@@ -241,6 +476,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--lm-iters", type=int, default=30)
     ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--no-verify-configs", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy 512 MiB device to device first (counter calibration)")
     args = ap.parse_args()
@@ -375,14 +611,44 @@ def main():
                       "avg_us": round(fuse_us, 2), "bytes_per_launch": fuse_bytes,
                       "timing": "HIP graph of 20 back-to-back calls, replayed 5 times"}
     del hs, w_fc
+    del cyc
+    torch.cuda.empty_cache()
+    hosts = {}
+    if not args.no_verify_configs:
+        for cfg in (2, 5, 1):
+            print(f"[bench] verify pass, config {inputs.WORKLOADS[cfg].name}", file=sys.stderr,
+                  flush=True)
+            line[f"verify_{inputs.WORKLOADS[cfg].name}"], hosts[cfg] = verify_leg(dev, cfg,
+                                                                                 args.steps)
     if not args.no_long_context:
-        del cyc
-        torch.cuda.empty_cache()
         print("[bench] long-context verify (32 layers, L=32768)", file=sys.stderr, flush=True)
         line["long_context_verify"] = long_context_verify(dev, max(1, min(args.steps, 10)))
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one cycle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, ci)
+        per = {}
+        for cfg, host in hosts.items():
+            wc = inputs.WORKLOADS[cfg]
+            print(f"[bench] timing the CPU oracle on one {wc.name} verify pass", file=sys.stderr,
+                  flush=True)
+            t = cpu_verify_pass(wc, host)
+            per[wc.name] = {"value": round(wc.T / t, 2), "unit": "nodes/s",
+                            "sample": f"one verify pass (mask, attention, LM head, acceptance) "
+                                      f"in {t:.2f} s"}
+        if not args.no_long_context:
+            import oracle
+            wl = inputs.LONG_CONTEXT
+            print("[bench] timing the CPU oracle on one long-context layer", file=sys.stderr,
+                  flush=True)
+            vl = inputs.verify_inputs(wl, with_lmhead=False)
+            t0 = time.perf_counter()
+            ml, _ = oracle.build_tree_mask(vl.parents)
+            oracle.tree_attention(vl.q, vl.k_cache, vl.v_cache, wl.L, vl.k_tree, vl.v_tree, ml)
+            t = time.perf_counter() - t0
+            per[wl.name] = {"value": round(wl.T / (wl.layers * t), 3), "unit": "nodes/s",
+                            "sample": f"one of the 32 layers (mask and attention) in {t:.2f} s, "
+                                      "scaled to 32 layers"}
+        line["cpu_baseline"]["per_config"] = per
     print(json.dumps(line), flush=True)
 
 

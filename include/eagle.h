@@ -303,10 +303,12 @@ int eagle_logits_process(const float* logits, int32_t T, int32_t V, float temper
  *
  * Tree: node_token/node_parent int32[T], node 0 the single root, parents
  * before children.
- * GREEDY (target_top1 int32[T], the target's argmax at each node): node c
- *   matches when node_token[c] == target_top1[parent(c)]; the path ends at
- *   the deepest node whose whole root path matches (lowest index among equally
- *   deep ones); bonus = target_top1[end].
+ * GREEDY (target_top1: the target's argmax at each node, node i's at element
+ *   i * top1_stride; top1_stride = 1 for an int32[T] array, or k to read
+ *   column 0 of eagle_lmhead_topk's topk_id[T][k] in place): node c matches
+ *   when node_token[c] == top1(parent(c)); the path ends at the deepest node
+ *   whose whole root path matches (lowest index among equally deep ones);
+ *   bonus = top1(end).  top1_stride < 1 -> EAGLE_EINVAL.
  * SAMPLE (target_logits f32[T][V], temperature > 0, uniforms f32[2T] in
  *   [0,1)): at node u, p = exp((l_u - max l_u) / temperature) in fp64 and
  *   Z_res = sum p minus the mass of tokens already rejected at u; children
@@ -327,7 +329,7 @@ int eagle_logits_process(const float* logits, int32_t T, int32_t V, float temper
 size_t eagle_accept_workspace(int32_t T, int32_t V);
 int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
                  const int32_t* node_parent, const int32_t* target_top1,
-                 const float* target_logits, int32_t V, float temperature,
+                 int32_t top1_stride, const float* target_logits, int32_t V, float temperature,
                  const float* uniforms, int32_t max_path, int32_t* path,
                  int32_t* n_accepted, int32_t* bonus_token,
                  void* workspace, size_t ws_bytes, int32_t* dev_status,
@@ -372,6 +374,35 @@ int eagle_kv_commit(const void* src_k, const void* src_v, int32_t ld_src, int32_
                     int64_t ld_cache, int64_t cache_layer_stride, int32_t layers,
                     int32_t Hkv, int32_t hd, eagle_dtype dt, int32_t* dev_status,
                     hipStream_t stream);
+
+/*
+ * eagle_path_slots - the draft's rows of the accepted path, for the draft's
+ * KV eviction.
+ *
+ * [D] reply on the draft's context: the draft keeps K/V for every candidate
+ * it ran, so after acceptance the rows of the accepted tokens are kept and
+ * the rest dropped.  The draft ran a node (and wrote its K/V at a slot) only
+ * if it expanded it; on the accepted path that is every node but possibly the
+ * last, which may be a leaf.
+ *   path, n_accepted: eagle_accept's outputs (node ids, root first; count
+ *                 n_accepted[0] + 1, cut to max_path).
+ *   node_pool_idx int32[T]: eagle_expand_rerank's pool entry of each node.
+ *   slot_of_pool  int32[pool_cap]: the draft slot of each pool entry, or -1
+ *                 for an entry never expanded.
+ *   slot_rows     int32[max_path] out: slot_of_pool[node_pool_idx[path[j]]]
+ *                 for j < n, then -1; n = the leading path nodes that have a
+ *                 slot in [0, n_slots).
+ *   n_rows_minus_one int32[1] out: n - 1, the count convention of
+ *                 eagle_kv_commit's n_accepted, so the two calls chain.
+ * Device errors: a path node outside [0, T) or a pool index outside
+ * [0, pool_cap) sets EAGLE_DEV_BAD_INDEX and ends the rows there; a root with
+ * no slot (n = 0) sets it too.  Host errors: null pointers, max_path or T
+ * outside [1, EAGLE_MAX_TREE], pool_cap or n_slots < 1 -> EAGLE_EINVAL.
+ */
+int eagle_path_slots(const int32_t* path, const int32_t* n_accepted, int32_t max_path,
+                     const int32_t* node_pool_idx, int32_t T, const int32_t* slot_of_pool,
+                     int32_t pool_cap, int32_t n_slots, int32_t* slot_rows,
+                     int32_t* n_rows_minus_one, int32_t* dev_status, hipStream_t stream);
 
 /*
  * eagle_accept_q - speculative sampling over the tree with the draft's own

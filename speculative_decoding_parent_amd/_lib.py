@@ -49,8 +49,8 @@ _PROTOS = {
     "eagle_expand_rerank": (_I32, [_I32, _P, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _I32,
                                    _P, _I32, _P, _P, _P, _P, _P, _P]),
     "eagle_accept_workspace": (_SZ, [_I32, _I32]),
-    "eagle_accept": (_I32, [_I32, _I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ,
-                            _P, _P]),
+    "eagle_accept": (_I32, [_I32, _I32, _P, _P, _P, _I32, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P,
+                            _SZ, _P, _P]),
     "eagle_linear_workspace": (_SZ, [_I32, _I32, _I32, _I32]),
     "eagle_linear": (_I32, [_P, _I32, _I32, _P, _I32, _P, _P, ctypes.c_int, _P, _SZ, _P]),
     "eagle_linear_swiglu": (_I32, [_P, _I32, _I32, _P, _I32, _F32, _P, _P, _I32, _P, _P, _SZ, _P]),
@@ -74,6 +74,7 @@ _PROTOS = {
     "eagle_logits_process": (_I32, [_P, _I32, _I32, _F32, _I32, _F32, _P, _P, _P, _SZ, _P]),
     "eagle_fuse3": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, ctypes.c_int, _P, _SZ, _P]),
     "eagle_gate_children": (_I32, [_P, _I32, _I32, _F32, _I32, _P, _P, _P, _P]),
+    "eagle_path_slots": (_I32, [_P, _P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P]),
     "eagle_kv_commit": (_I32, [_P, _P, _I32, _I32, _I64, _P, _P, _I32, _P, _P, _I64, _I64, _I64, _I32,
                                _I32, _I32, ctypes.c_int, _P, _P]),
 }
@@ -257,6 +258,22 @@ def eagle_kv_commit(k_src, v_src, rows, k_cache, v_cache, L, n_accepted=None, sr
         _dt(k_src), _ptr(dev_status), _stream()))
 
 
+def eagle_path_slots(path, n_accepted, node_pool_idx, slot_of_pool, n_slots, slot_rows=None,
+                     n_rows_minus_one=None, dev_status=None):
+    """The draft slots of the accepted path's leading expanded nodes; returns
+    (slot_rows int32[max_path], n_rows_minus_one int32[1])."""
+    max_path = path.shape[0]
+    dev = path.device
+    slot_rows = torch.empty(max_path, dtype=torch.int32, device=dev) if slot_rows is None else slot_rows
+    n_rows_minus_one = (torch.empty(1, dtype=torch.int32, device=dev) if n_rows_minus_one is None
+                        else n_rows_minus_one)
+    _check("eagle_path_slots", lib().eagle_path_slots(
+        _ptr(path), _ptr(n_accepted), max_path, _ptr(node_pool_idx), node_pool_idx.shape[0],
+        _ptr(slot_of_pool), slot_of_pool.shape[0], n_slots, _ptr(slot_rows), _ptr(n_rows_minus_one),
+        _ptr(dev_status), _stream()))
+    return slot_rows, n_rows_minus_one
+
+
 def _norm_args(in_norm):
     """(in_ssq, in_parts, in_eps) of an optional deferred RMSNorm given as
     (ssq f32 [P][M], eps), e.g. the last two results of
@@ -339,8 +356,11 @@ def eagle_accept(mode, node_token, node_parent, target_top1=None, target_logits=
     V = target_logits.shape[1] if target_logits is not None else 0
     nb = lib().eagle_accept_workspace(T, V) if mode == EAGLE_SAMPLE else 0
     ws = _workspace(nb, dev, workspace) if mode == EAGLE_SAMPLE else None
+    # target_top1 may be a strided view, e.g. column 0 of the LM head's topk_id [T][k]
+    top1_stride = target_top1.stride(0) if target_top1 is not None else 1
     _check("eagle_accept", lib().eagle_accept(
-        mode, T, _ptr(node_token), _ptr(node_parent), _ptr(target_top1), _ptr(target_logits), V,
+        mode, T, _ptr(node_token), _ptr(node_parent), _ptr(target_top1), top1_stride,
+        _ptr(target_logits), V,
         temperature, _ptr(uniforms), max_path, _ptr(path), _ptr(n_accepted), _ptr(bonus_token),
         _ptr(ws), nb, _ptr(dev_status), _stream()))
     return path, n_accepted, bonus_token

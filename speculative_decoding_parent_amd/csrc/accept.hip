@@ -56,7 +56,7 @@ __device__ __forceinline__ double exp_nonpos(double x) {
 
 __global__ __launch_bounds__(256) void accept_greedy_kernel(
     int T, const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
-    const int32_t* __restrict__ top1, int max_path, int32_t* __restrict__ path,
+    const int32_t* __restrict__ top1, int top1_stride, int max_path, int32_t* __restrict__ path,
     int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus, int32_t* __restrict__ status) {
   __shared__ int32_t par[EAGLE_MAX_TREE];
   __shared__ int32_t tk[EAGLE_MAX_TREE];
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void accept_greedy_kernel(
   for (int i = tid; i < T; i += blockDim.x) {
     par[i] = parent[i];
     tk[i] = token[i];
-    t1[i] = top1[i];
+    t1[i] = top1[(int64_t)i * top1_stride];
   }
   __syncthreads();
   for (int i = tid; i < T; i += blockDim.x) {
@@ -662,17 +662,18 @@ extern "C" size_t eagle_accept_workspace(int32_t T, int32_t V) {
 
 extern "C" int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
                             const int32_t* node_parent, const int32_t* target_top1,
-                            const float* target_logits, int32_t V, float temperature,
+                            int32_t top1_stride, const float* target_logits, int32_t V,
+                            float temperature,
                             const float* uniforms, int32_t max_path, int32_t* path,
                             int32_t* n_accepted, int32_t* bonus_token, void* workspace,
                             size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
   EAGLE_REQUIRE(node_token && node_parent && path && n_accepted && bonus_token, EAGLE_EINVAL);
   EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && max_path >= 1, EAGLE_EINVAL);
   if (mode == EAGLE_GREEDY) {
-    EAGLE_REQUIRE(target_top1, EAGLE_EINVAL);
+    EAGLE_REQUIRE(target_top1 && top1_stride >= 1, EAGLE_EINVAL);
     hipLaunchKernelGGL(eagle::accept_greedy_kernel, dim3(1), dim3(256), 0, stream, T, node_token,
-                       node_parent, target_top1, max_path, path, n_accepted, bonus_token,
-                       dev_status);
+                       node_parent, target_top1, top1_stride, max_path, path, n_accepted,
+                       bonus_token, dev_status);
   } else if (mode == EAGLE_SAMPLE) {
     EAGLE_REQUIRE(target_logits && uniforms && V >= 1, EAGLE_EINVAL);
     EAGLE_REQUIRE(temperature > 0.0f && temperature <= 3.0e38f, EAGLE_EINVAL);

@@ -99,6 +99,49 @@ __global__ __launch_bounds__(kKvThreads) void kv_commit_kernel(KvParams p) {
   }
 }
 
+// The draft's rows of the accepted path: slot_of_pool[node_pool_idx[path[j]]]
+// for the leading path nodes the draft expanded (every accepted node but
+// possibly the last, which may be a leaf the draft never ran).  One thread per
+// path entry, so the three dependent lookups are one round trip each.
+struct PathSlotParams {
+  const int32_t* path;
+  const int32_t* n_acc;
+  const int32_t* node_pool_idx;
+  const int32_t* slot_of_pool;
+  int32_t* rows;
+  int32_t* n_rows_m1;
+  int32_t* status;
+  int max_path, T, pool_cap, n_slots;
+};
+
+__global__ __launch_bounds__(EAGLE_MAX_TREE) void path_slots_kernel(PathSlotParams p) {
+  __shared__ int first_end;
+  const int j = threadIdx.x;
+  const int a = p.n_acc[0];
+  if (j == 0) first_end = p.max_path;
+  __syncthreads();
+  const int n = a < 0 ? 0 : min(a + 1, p.max_path);
+  int slot = -1;
+  if (j < n) {
+    const int node = p.path[j];
+    bool bad = node < 0 || node >= p.T;
+    if (!bad) {
+      const int pi = p.node_pool_idx[node];
+      bad = pi < 0 || pi >= p.pool_cap;
+      if (!bad) slot = p.slot_of_pool[pi];
+    }
+    if (bad) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+    if (bad || slot < 0 || slot >= p.n_slots) atomicMin(&first_end, j);
+  }
+  __syncthreads();
+  const int cnt = min(n, first_end);
+  if (j < p.max_path) p.rows[j] = j < cnt ? slot : -1;
+  if (j == 0) {
+    p.n_rows_m1[0] = cnt - 1;
+    if (cnt == 0) set_status(p.status, EAGLE_DEV_BAD_INDEX);
+  }
+}
+
 }  // namespace eagle
 
 extern "C" int eagle_kv_commit(const void* src_k, const void* src_v, int32_t ld_src,
@@ -145,6 +188,23 @@ extern "C" int eagle_kv_commit(const void* src_k, const void* src_v, int32_t ld_
   p.status = dev_status;
   hipLaunchKernelGGL(kv_commit_kernel, dim3(Hkv, 2, layers), dim3(kKvThreads),
                      (size_t)max_rows * hd * es, stream, p);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_path_slots(const int32_t* path, const int32_t* n_accepted, int32_t max_path,
+                                const int32_t* node_pool_idx, int32_t T,
+                                const int32_t* slot_of_pool, int32_t pool_cap, int32_t n_slots,
+                                int32_t* slot_rows, int32_t* n_rows_minus_one,
+                                int32_t* dev_status, hipStream_t stream) {
+  using namespace eagle;
+  EAGLE_REQUIRE(path && n_accepted && node_pool_idx && slot_of_pool && slot_rows &&
+                    n_rows_minus_one, EAGLE_EINVAL);
+  EAGLE_REQUIRE(max_path >= 1 && max_path <= EAGLE_MAX_TREE, EAGLE_EINVAL);
+  EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && pool_cap >= 1 && n_slots >= 1, EAGLE_EINVAL);
+  PathSlotParams p{path, n_accepted, node_pool_idx, slot_of_pool, slot_rows, n_rows_minus_one,
+                   dev_status, max_path, T, pool_cap, n_slots};
+  hipLaunchKernelGGL(path_slots_kernel, dim3(1), dim3(EAGLE_MAX_TREE), 0, stream, p);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

@@ -5,8 +5,9 @@ frontier row's parent feature with its token embedding, runs one decoder layer
 (attention over the draft's KV prefix and the K/V of every node expanded so
 far, under the slot tree's ancestor mask), scores the rows with the shared LM
 head and appends the top-k children by cumulative log-probability.  The tree is
-then pruned to T nodes, verified by one target layer under the tree mask, and a
-path is accepted by speculative sampling ("EAGLE-2: Feature-Level Speculative
+then pruned to T nodes, verified by one target layer under the tree mask, a
+path is accepted by speculative sampling, and the accepted path's K/V rows are
+committed to both caches ("EAGLE-2: Feature-Level Speculative
 Decoding Guide", Key Architectural Mechanics 1-3; "Support Eagle-3 Speculative
 Decoding in llama.cpp", the dynamic-tree and KV-cache replies).
 
@@ -39,8 +40,14 @@ class DraftVerifyCycle:
         self.target_norm = to(ci["target_norm"])
         self.embed = to(ci["embed"])
         self.w_lm = to(ci["w_lm"])
-        self.dkc, self.dvc = to(ci["draft_k_cache"]), to(ci["draft_v_cache"])
-        self.tkc, self.tvc = to(ci["target_k_cache"]), to(ci["target_v_cache"])
+        # KV caches with room for one cycle's commit: positions 0..L-1 hold the
+        # prefix, and the accepted path's rows are written at L, L+1, ...
+        def cache(t):
+            c = torch.zeros((t.shape[0], L + T, t.shape[2]), dtype=t.dtype, device=dev)
+            c[:, :L] = t[:, :L].to(dev)
+            return c
+        self.dkc, self.dvc = cache(ci["draft_k_cache"]), cache(ci["draft_v_cache"])
+        self.tkc, self.tvc = cache(ci["target_k_cache"]), cache(ci["target_v_cache"])
         self.root_feat = to(ci["root_feature"]).float()
         self.uniforms = torch.as_tensor(ci["uniforms"]).to(dev)
 
@@ -101,6 +108,8 @@ class DraftVerifyCycle:
         self.n_accepted = torch.zeros(1, **i32)
         self.bonus = torch.zeros(1, **i32)
         self.status = torch.zeros(1, **i32)
+        self.draft_rows = torch.zeros(R + 1, **i32)      # the draft's slots of the accepted path
+        self.draft_n = torch.zeros(1, **i32)
         lib = _lib.lib()
         ws_attn = max(lib.eagle_tree_attn_workspace(ks, hq, hkv, hd, L, self.S, _lib.EAGLE_BF16),
                       lib.eagle_tree_attn_workspace(T, hq, hkv, hd, L, T, _lib.EAGLE_BF16))
@@ -199,6 +208,21 @@ class DraftVerifyCycle:
                           target_logits=self.v_logits, temperature=self.temperature,
                           uniforms=self.uniforms, path=self.path, n_accepted=self.n_accepted,
                           bonus_token=self.bonus, workspace=self.ws_acc, dev_status=self.status)
+        self.commit()
+
+    def commit(self):
+        """KV commit after acceptance: the target keeps K/V only for the
+        accepted path (root first) and the draft keeps its rows of the same
+        nodes, both appended at cache position L; every other candidate's rows
+        are dropped ("Support Eagle-3 Speculative Decoding in llama.cpp", the
+        reply on the draft's context).  Counts are read on the device."""
+        _lib.eagle_kv_commit(self.tkt, self.tvt, self.path, self.tkc, self.tvc, self.L,
+                             n_accepted=self.n_accepted, dev_status=self.status)
+        _lib.eagle_path_slots(self.path[:self.R + 1], self.n_accepted, self.node_pool_idx,
+                              self.slot_of_pool, self.S, slot_rows=self.draft_rows,
+                              n_rows_minus_one=self.draft_n, dev_status=self.status)
+        _lib.eagle_kv_commit(self.dkt, self.dvt, self.draft_rows, self.dkc, self.dvc, self.L,
+                             n_accepted=self.draft_n, dev_status=self.status)
 
     def enqueue(self):
         """Enqueue one whole cycle on the current stream."""

@@ -148,16 +148,36 @@ def test_tree_argument_errors(lib):
 
 def test_accept_argument_errors(lib):
     f = lib.eagle_accept
-    assert f(0, 5, FAKE, FAKE, None, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
+    assert f(0, 5, FAKE, FAKE, None, 1, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
              None) == EINVAL                                     # greedy without top1
-    assert f(1, 5, FAKE, FAKE, None, FAKE, 100, 0.0, FAKE, 5, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+    assert f(0, 5, FAKE, FAKE, FAKE, 0, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
+             None) == EINVAL                                     # top1 stride 0
+    assert f(1, 5, FAKE, FAKE, None, 1, FAKE, 100, 0.0, FAKE, 5, FAKE, FAKE, FAKE, FAKE, 1 << 20,
              None, None) == EINVAL                               # temperature 0
-    assert f(1, 5, FAKE, FAKE, None, FAKE, 100, 1.0, FAKE, 5, FAKE, FAKE, FAKE, FAKE, 8, None,
+    assert f(1, 5, FAKE, FAKE, None, 1, FAKE, 100, 1.0, FAKE, 5, FAKE, FAKE, FAKE, FAKE, 8, None,
              None) == EWS
-    assert f(0, 300, FAKE, FAKE, FAKE, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
+    assert f(0, 300, FAKE, FAKE, FAKE, 1, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
              None) == EINVAL                                     # T > 256
-    assert f(3, 5, FAKE, FAKE, FAKE, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
+    assert f(3, 5, FAKE, FAKE, FAKE, 1, None, 0, 1.0, None, 5, FAKE, FAKE, FAKE, None, 0, None,
              None) == EINVAL
+
+
+def test_path_slots_argument_errors(lib):
+    f = lib.eagle_path_slots
+    ok = [FAKE, FAKE, 7, FAKE, 64, FAKE, 511, 51, FAKE, FAKE, None, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a0=None) == EINVAL
+    assert call(a2=0) == EINVAL
+    assert call(a2=257) == EINVAL
+    assert call(a4=0) == EINVAL
+    assert call(a7=0) == EINVAL
+    assert call(a9=None) == EINVAL
 
 
 def test_linear_argument_errors(lib):

@@ -41,6 +41,25 @@ def test_greedy_random_and_planted(dev, T):
         assert path[:rn + 1].tolist() == rp and np.all(path[rn + 1:] == -1)
 
 
+@pytest.mark.parametrize("k", [1, 4, 10])
+def test_greedy_reads_strided_top1(dev, k):
+    """top1 read as column 0 of a [T][k] top-k id array in place (stride k)."""
+    g = inputs.rng(260, k)
+    T, V = 64, 40
+    par = inputs.random_tree(g, T, 7, 4)
+    ids = g.integers(0, V, (T, k)).astype(np.int32)
+    tok = inputs.sibling_distinct_tokens(g, par, V)
+    tok = inputs.plant_path(tok, par, ids[:, 0], inputs.deepest_leaf(g, par))
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ids_d = to(dev, ids)
+    path, n, b = _lib.eagle_accept(_lib.EAGLE_GREEDY, to(dev, tok), to(dev, par),
+                                   target_top1=ids_d[:, 0], dev_status=st)
+    torch.cuda.synchronize()
+    rp, rn, rb = oracle.accept_greedy(tok, par, ids[:, 0])
+    assert int(st.item()) == 0 and int(n.item()) == rn and int(b.item()) == rb
+    assert path.cpu().numpy()[:rn + 1].tolist() == rp
+
+
 def test_greedy_golden_and_truncation(dev):
     import json, os
     gd = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "greedy_accept.json")))

@@ -81,6 +81,46 @@ def compare(cyc, ref, w):
     return f"compared through verify logits (err {err:.3g}); acceptance draw near a boundary"
 
 
+def bits(t):
+    """Raw 16-bit patterns of a bf16 tensor (byte-exact comparisons)."""
+    return t.detach().cpu().view(torch.int16).numpy()
+
+
+def check_commit(cyc, ci, w, ref, how):
+    """Both caches after the cycle, byte for byte, against oracle.kv_commit of
+    the cycle's own tree K/V rows: the target's along the accepted path (the
+    oracle's path where the runs agreed through acceptance), the draft's along
+    the slots of the same path's leading expanded nodes."""
+    L, T = w.L, w.T
+    if how == "compared through acceptance":
+        path = np.asarray(ref["path"], np.int64)
+    else:
+        n = int(cyc.n_accepted.item())
+        path = cyc.path.cpu().numpy()[:n + 1].astype(np.int64)
+
+    def before(key):
+        c = np.zeros((w.hkv, L + T, w.hd), np.int16)
+        c[:, :L] = bits(ci[key][:, :L])
+        return c[None]
+
+    want_k, want_v = oracle.kv_commit(bits(cyc.tkt)[None], bits(cyc.tvt)[None], path, len(path),
+                                      before("target_k_cache"), before("target_v_cache"), L)
+    assert np.array_equal(bits(cyc.tkc), want_k[0]) and np.array_equal(bits(cyc.tvc), want_v[0])
+    pool_idx = cyc.node_pool_idx.cpu().numpy()
+    slot_of_pool = cyc.slot_of_pool.cpu().numpy()
+    rows = []
+    for node in path:
+        slot = int(slot_of_pool[pool_idx[node]])
+        if slot < 0:
+            break
+        rows.append(slot)
+    assert rows and rows[0] == 0 and len(rows) >= len(path) - 1
+    want_k, want_v = oracle.kv_commit(bits(cyc.dkt)[None], bits(cyc.dvt)[None], rows, len(rows),
+                                      before("draft_k_cache"), before("draft_v_cache"), L)
+    assert np.array_equal(bits(cyc.dkc), want_k[0]) and np.array_equal(bits(cyc.dvc), want_v[0])
+    print(f"  commit: target {len(path)} rows, draft {len(rows)} rows", flush=True)
+
+
 @pytest.mark.parametrize("seed", [13, 113, 213])
 def test_small_cycle_end_to_end(dev, seed):
     import dataclasses
@@ -96,6 +136,7 @@ def test_small_cycle_end_to_end(dev, seed):
     print("  " + how, flush=True)
     check_valid_tree(cyc.node_token.cpu().numpy(), cyc.node_parent.cpu().numpy(),
                      cyc.node_depth.cpu().numpy(), w.vocab, w.T)
+    check_commit(cyc, ci, w, ref, how)
 
 
 def test_graph_replay_matches_eager(dev):
@@ -117,11 +158,13 @@ def test_graph_replay_matches_eager(dev):
             assert torch.equal(a, b), f"replay {rep}"
 
 
-def test_llama3_8b_cycle_structure(dev):
-    """The full Llama-3-8B-shaped cycle: 6 rounds of top-10, rerank to 64,
-    one target layer, sampling acceptance.  Checked for validity; numerical
-    parity of its kernels at these shapes is covered kernel by kernel."""
+def test_llama3_8b_cycle_end_to_end(dev):
+    """The full Llama-3-8B-shaped cycle (6 rounds of top-10, rerank to 64, one
+    target layer, sampling acceptance, KV commit) against the oracle's cycle:
+    every decision with a robust oracle margin must agree, in order, and the
+    verify logits of the agreed tree must be within the logit tolerance."""
     w = inputs.LLAMA3_8B_CYCLE
+    print("cycle llama3-8b: drawing inputs", flush=True)
     ci = inputs.cycle_inputs(w)
     cyc = DraftVerifyCycle(w, ci, dev)
     cyc.run()
@@ -134,5 +177,8 @@ def test_llama3_8b_cycle_structure(dev):
     path = cyc.path.cpu().numpy()
     assert path[0] == 0 and all(par[b] == a for a, b in zip(path[:n], path[1:n + 1]))
     assert 0 <= int(cyc.bonus.item()) < w.vocab
-    lg = cyc.v_logits.cpu().numpy()
-    assert np.isfinite(lg).all()
+    print("cycle llama3-8b: oracle cycle", flush=True)
+    ref = run_oracle(w, ci, 1.0)
+    how = compare(cyc, ref, w)
+    print("  " + how, flush=True)
+    check_commit(cyc, ci, w, ref, how)

@@ -375,6 +375,15 @@ def test_layer_llama3_8b_shape(dev):
     layer_case(dev, w, 1, 10, 21, np.arange(11, 21), slot_par)
 
 
+def test_verify_layer_llama3_8b_shape(dev):
+    """The verify pass's layer at full width on all 64 tree rows: the many-row
+    projections (M > 16) composed with the wide-group attention kernel, under
+    a 64-node tree mask, against the oracle's layer."""
+    w = inputs.LLAMA3_8B_CYCLE
+    slot_par = inputs.random_tree(inputs.rng(707, 0), 64, 7, 4).astype(np.int32)
+    layer_case(dev, w, 2, 64, 64, np.arange(64), slot_par)
+
+
 def test_split_k_hand_off_is_deterministic(dev):
     """The split-K few-row projections hand fp32 tiles between workgroups
     (device-coherent stores, then an arrival count; the last arrival sums the
