@@ -136,7 +136,7 @@ def long_context_verify(dev, steps):
     vc[:, :, w.L:] = vt
     out = torch.empty_like(q)
     lib = _lib.lib()
-    ws = torch.empty(lib.eagle_tree_attn_workspace(w.T, w.hq, w.hkv, w.hd, w.L, w.T, 1),
+    ws = torch.zeros(lib.eagle_tree_attn_workspace(w.T, w.hq, w.hkv, w.hd, w.L, w.T, 1),
                      dtype=torch.uint8, device=dev)
     mask = torch.empty((w.T, 1), dtype=torch.int64, device=dev)
     depth = torch.empty(w.T, dtype=torch.int32, device=dev)

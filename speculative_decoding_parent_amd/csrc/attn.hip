@@ -836,10 +836,12 @@ constexpr int kMergeSplits = 1024;
 // bf16 partials.  One block of four waves per RPW consecutive rows (4 rows
 // of 128 dims, 8 of 64).  Lane (row rr, chunk ch) of wave v sums 8 head dims
 // of its row over the splits s = v, v + 4, v + 8, ... in ascending order,
-// one 16-byte load per split; its first 16 loads are issued before anything
-// else, so their latency overlaps wave 0's work on the split weights l_s w_s
-// (split s on lane s mod 64, read once into registers while s < 64).  Wave 0
-// then adds the other waves' sums in wave order and writes the row.
+// one 16-byte load per split; its first LPB loads are issued before anything
+// else, so their latency overlaps the split weights l_s w_s, which wave q
+// forms for rows q, q + 4, ... (lanes over splits) into LDS.  Wave 0 then
+// adds the other waves' sums in wave order and writes the row.  The weights
+// take RPW * nsplit floats of dynamic LDS and the kernel ~108 registers, so
+// four blocks share a CU.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_merge_bf16_kernel(const bf16_t* __restrict__ part_o,
                                                               const float2* __restrict__ part_ml,
@@ -848,8 +850,8 @@ __global__ __launch_bounds__(256) void attn_merge_bf16_kernel(const bf16_t* __re
   constexpr int CPR = HD / 8;    // 16-byte chunks per row
   constexpr int RPW = 64 / CPR;  // rows per block
   constexpr int NWV = 4;         // waves per block
-  constexpr int LPB = 16;        // loads in flight per lane
-  __shared__ float wsh[RPW][kMergeSplits];
+  constexpr int LPB = 8;         // loads in flight per lane
+  extern __shared__ float wsh[];  // [RPW][nsplit]
   __shared__ float dsh[RPW];
   __shared__ f32x4 accs[NWV - 1][2][64];
   const int tid = threadIdx.x;
@@ -873,42 +875,22 @@ __global__ __launch_bounds__(256) void attn_merge_bf16_kernel(const bf16_t* __re
   u32x4 v[LPB];
   load_batch(wave, v);
 
-  if (wave == 0) {
-    float2 ml0[RPW];
-    float M[RPW], den[RPW];
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      ml0[q] = (lane < nsplit && row0 + q < RT) ? part_ml[(size_t)lane * RT + row0 + q]
-                                                : make_float2(kNegBig, 0.f);
-      M[q] = ml0[q].x;
-    }
-    for (int s = lane + 64; s < nsplit; s += 64)
-#pragma unroll
-      for (int q = 0; q < RPW; ++q)
-        if (row0 + q < RT) M[q] = fmaxf(M[q], part_ml[(size_t)s * RT + row0 + q].x);
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      M[q] = wave_max(M[q]);
-      const float w = lane < nsplit ? exp2f((ml0[q].x - M[q]) * c) * ml0[q].y : 0.f;
-      if (lane < nsplit) wsh[q][lane] = w;
-      den[q] = w;
-    }
-    for (int s = lane + 64; s < nsplit; s += 64)
-#pragma unroll
-      for (int q = 0; q < RPW; ++q) {
-        float w = 0.f;
-        if (row0 + q < RT) {
-          const float2 ml = part_ml[(size_t)s * RT + row0 + q];
-          w = exp2f((ml.x - M[q]) * c) * ml.y;
-        }
-        wsh[q][s] = w;
-        den[q] += w;
+  for (int q = wave; q < RPW; q += NWV) {
+    const int r = row0 + q;
+    float M = kNegBig;
+    if (r < RT)
+      for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_ml[(size_t)s * RT + r].x);
+    M = wave_max(M);
+    float den = 0.f;
+    if (r < RT)
+      for (int s = lane; s < nsplit; s += 64) {
+        const float2 ml = part_ml[(size_t)s * RT + r];
+        const float w = exp2f((ml.x - M) * c) * ml.y;
+        wsh[q * nsplit + s] = w;
+        den += w;
       }
-#pragma unroll
-    for (int q = 0; q < RPW; ++q) {
-      const float d = wave_sum(den[q]);
-      if (lane == 0) dsh[q] = d;
-    }
+    den = wave_sum(den);
+    if (lane == 0) dsh[q] = den;
   }
   __syncthreads();
   float acc[8];
@@ -918,7 +900,7 @@ __global__ __launch_bounds__(256) void attn_merge_bf16_kernel(const bf16_t* __re
 #pragma unroll
     for (int u = 0; u < LPB; ++u) {
       const int s = s0 + NWV * u;
-      const float w = s < nsplit ? wsh[rr][s] : 0.f;
+      const float w = s < nsplit ? wsh[rr * nsplit + s] : 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[2 * e] = fmaf(__uint_as_float(v[u][e] << 16), w, acc[2 * e]);
@@ -1007,6 +989,7 @@ constexpr int64_t kCUs = 256;  // MI355X compute units
 
 // The LDS-ring kernel serves 128-dim heads with 256 query rows per workgroup.
 static bool ring_path(int hd, int nw) { return hd == kRingHD && nw == 8; }
+constexpr int64_t kRingSliceOverhead = 3;
 
 static AttnPlan attn_plan(int Tq, int Hq, int Hkv, int hd, int64_t L, eagle_dtype dt) {
   AttnPlan pl{};
@@ -1025,7 +1008,11 @@ static AttnPlan attn_plan(int Tq, int Hq, int Hkv, int hd, int64_t L, eagle_dtyp
     } else if (ring_path(hd, pl.nw)) {
       // One workgroup per CU (the LDS ring): pick the slice length whose
       // grid (prefix slices plus the tree slice) needs the fewest tile-times,
-      // counting whole rounds of kCUs workgroups; ties go to fewer slices.
+      // counting whole rounds of kCUs workgroups and, per workgroup, the fixed
+      // cost of loading its query rows and storing its partials (about
+      // kRingSliceOverhead tile-times; without it one-tile slices win at 1024
+      // rows per KV head and the partials outgrow the K/V); ties go to fewer
+      // slices.
       const int64_t per_split_blocks = (int64_t)Hkv * pl.qgroups;
       const int64_t tps_min = (tiles + kMergeSplits - 2) / (kMergeSplits - 1);
       int64_t best_cost = -1;
@@ -1035,7 +1022,7 @@ static AttnPlan attn_plan(int Tq, int Hq, int Hkv, int hd, int64_t L, eagle_dtyp
         const int64_t n = (tiles + tps - 1) / tps;
         if (n + 1 > kMergeSplits) continue;
         const int64_t rounds = ((n + 1) * per_split_blocks + kCUs - 1) / kCUs;
-        const int64_t cost = rounds * tps;
+        const int64_t cost = rounds * (tps + kRingSliceOverhead);
         if (best_cost < 0 || cost <= best_cost) {
           best_cost = cost;
           pl.tiles_per_split = (int)tps;
@@ -1156,10 +1143,12 @@ extern "C" int eagle_tree_attn(const void* q, const void* k_cache, const void* v
   const int obf = out_dt == EAGLE_BF16 ? 1 : 0;
   if (in_dt == EAGLE_BF16) {
     if (hd == 128)
-      hipLaunchKernelGGL(attn_merge_bf16_kernel<128>, dim3((RT + 3) / 4), dim3(256), 0, stream,
+      hipLaunchKernelGGL(attn_merge_bf16_kernel<128>, dim3((RT + 3) / 4), dim3(256),
+                         (size_t)4 * (pl.n_split + 1) * sizeof(float), stream,
                          (const bf16_t*)p.part_o, p.part_ml, pl.n_split + 1, RT, p.c, out, obf);
     else
-      hipLaunchKernelGGL(attn_merge_bf16_kernel<64>, dim3((RT + 7) / 8), dim3(256), 0, stream,
+      hipLaunchKernelGGL(attn_merge_bf16_kernel<64>, dim3((RT + 7) / 8), dim3(256),
+                         (size_t)8 * (pl.n_split + 1) * sizeof(float), stream,
                          (const bf16_t*)p.part_o, p.part_ml, pl.n_split + 1, RT, p.c, out, obf);
   } else {
     hipLaunchKernelGGL(attn_merge_f32_kernel, dim3(RT), dim3(128), 0, stream,

@@ -113,3 +113,36 @@ def test_full_size_every_row(dev, cfg):
     got, mask = run(dev, vi.q, vi.k_cache, vi.v_cache, w.L, vi.k_tree, vi.v_tree, vi.parents)
     ref = oracle.tree_attention(vi.q, vi.k_cache, vi.v_cache, w.L, vi.k_tree, vi.v_tree, mask)
     check(got, ref)
+
+
+def test_repeated_calls_with_shared_workspace(dev):
+    """50 back-to-back verify-shaped calls (64 nodes x 4 heads per KV head,
+    the wide-group kernel) alternate with draft-round calls (10 rows through a
+    mask-row map, the narrow kernel) on one workspace: every verify result is
+    bit-identical to the first and within the bar of the oracle."""
+    hq, hkv, hd, L = 32, 8, 128, 4096
+    Tv, Tdr = 64, 10
+    par = inputs.random_tree(inputs.rng(640, 0), Tv, 7, 4)
+    q, kc, vc, kt, vt = draw(7, Tv, Tv, L, hq, hkv, hd)
+    qd = inputs.normal(inputs.rng(641, 0), (Tdr, hq, hd))
+    lib = _lib.lib()
+    nb = max(lib.eagle_tree_attn_workspace(Tv, hq, hkv, hd, L, Tv, _lib.EAGLE_BF16),
+             lib.eagle_tree_attn_workspace(Tdr, hq, hkv, hd, L, Tv, _lib.EAGLE_BF16))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    mask, _ = _lib.eagle_build_tree_mask(torch.from_numpy(par.astype(np.int32)).to(dev))
+    qv, qdd, kcd, vcd, ktd, vtd = (t.to(dev) for t in (q, qd, kc, vc, kt, vt))
+    qmap = torch.arange(Tv - Tdr, Tv, dtype=torch.int32, device=dev)
+    first = None
+    for rep in range(50):
+        ov = _lib.eagle_tree_attn(qv, kcd, vcd, L, ktd, vtd, Tv, mask, workspace=ws, dev_status=st)
+        _lib.eagle_tree_attn(qdd, kcd, vcd, L, ktd, vtd, Tv, mask, q_mask_row=qmap, workspace=ws,
+                             dev_status=st)
+        if first is None:
+            first = ov.clone()
+        else:
+            assert torch.equal(ov, first), f"call {rep}"
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    ref = oracle.tree_attention(q, kc, vc, L, kt, vt, mask.cpu().numpy().view(np.uint64))
+    check(first.float().cpu().numpy(), ref)
