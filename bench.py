@@ -586,13 +586,14 @@ def main():
                                                       path=q_out[0], n_accepted=q_out[1],
                                                       bonus_token=q_out[2], workspace=q_ws),
                           n_calls=5, reps=3)
-    line["accept_q"] = {"kernel": f"eagle_accept_q (accept_sample_q_kernel), {w.T} nodes, "
+    line["accept_q"] = {"kernel": f"eagle_accept_q (accept_q_grid_kernel), {w.T} nodes, "
                                   f"V={w.vocab}, draft distribution from draft logits",
                         "avg_us": round(aq_us, 1), "accepted": int(q_out[1].item()),
                         "timing": "HIP graph of 5 back-to-back calls, replayed 3 times",
-                        "note": "row statistics from a many-workgroup prepass; one workgroup "
-                                "walks the tree, passing over the vocabulary only for rejections "
-                                "and the bonus draw"}
+                        "note": "one launch of up to 256 workgroups, each owning a slice of the "
+                                "vocabulary, walks the tree together, meeting at a coordinated "
+                                "grid barrier only for sums over the vocabulary (row statistics "
+                                "of a visited node, a rejection's residual mass, the bonus draw)"}
     del tl, dlq
     # Eagle-3 fusion of the accepted path's three recorded hidden states
     # (8 rows: root + 7 accepted at the tree's depth bound), d = 4096 -> 4096

@@ -73,7 +73,10 @@ enum {
   EAGLE_DEV_BAD_TOKEN = 4,      /* token outside [0, V)                       */
   EAGLE_DEV_BAD_INDEX = 8,      /* frontier / mask-row index out of range     */
   EAGLE_DEV_ORPHAN = 16,        /* rerank kept an entry without its parent    */
-  EAGLE_DEV_PATH_TRUNC = 32     /* accepted path longer than max_path         */
+  EAGLE_DEV_PATH_TRUNC = 32,    /* accepted path longer than max_path         */
+  EAGLE_DEV_TIMEOUT = 64        /* a bounded wait for the other workgroups of
+                                   one launch expired (eagle_accept_q: the GPU
+                                   was shared); outputs are not valid         */
 };
 
 /* Limits of this build. */
@@ -422,15 +425,24 @@ int eagle_path_slots(const int32_t* path, const int32_t* n_accepted, int32_t max
  * smallest token whose running sum of the last residual exceeds
  * uniforms[T + u] times its total.  fp64 from fp32 logits; sums in a fixed
  * order (results can differ from a sequential fp64 evaluation only where a
- * decision's margin is a few ulp).  A many-workgroup prepass takes every
- * row's (max, sum) statistics; one workgroup then walks the tree, passing
- * over the vocabulary only for rejections and the bonus draw.
+ * decision's margin is a few ulp).  One launch of up to 256 workgroups (one
+ * per CU, each owning a slice of the vocabulary) walks the tree together:
+ * every workgroup takes every decision itself, and they meet at a grid
+ * barrier only for the sums over the vocabulary (a visited node's row
+ * statistics, each rejection's residual mass, the bonus draw).  The whole
+ * grid must be resident at once: the call assumes the GPU is not shared with
+ * other work holding CUs; a barrier that never fills sets EAGLE_DEV_TIMEOUT
+ * after about a second instead of hanging (the outputs are then not valid).
  *
  * target_logits, draft_logits f32[T][V]; uniforms f32[2T] in [0, 1);
- * workspace >= eagle_accept_q_workspace(T, V) bytes (8-byte aligned).  Outputs
- * and device errors as eagle_accept.  Host errors: null pointers, T outside
- * [1, EAGLE_MAX_TREE], V or max_path < 1, temperature not in (0, 3e38] ->
- * EAGLE_EINVAL; small workspace -> EAGLE_EWORKSPACE.
+ * workspace >= eagle_accept_q_workspace(T, V) bytes, 256-byte aligned, zero
+ * before its first use (its first 2 KiB hold the barrier flags and a
+ * generation number that every call advances; keep the buffer for later
+ * calls on the same stream, or zero it again before handing it over).
+ * Outputs and device errors as eagle_accept.  Host errors: null pointers, T
+ * outside [1, EAGLE_MAX_TREE], V or max_path < 1, temperature not in
+ * (0, 3e38], a misaligned workspace -> EAGLE_EINVAL; V above 524288 ->
+ * EAGLE_EUNSUPPORTED; small workspace -> EAGLE_EWORKSPACE.
  */
 size_t eagle_accept_q_workspace(int32_t T, int32_t V);
 int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_t* node_parent,

@@ -26,6 +26,7 @@ EAGLE_EXPAND, EAGLE_RERANK = 0, 1
 EAGLE_GREEDY, EAGLE_SAMPLE = 0, 1
 DEV_BAD_PARENT, DEV_BAD_ROOT, DEV_BAD_TOKEN, DEV_BAD_INDEX, DEV_ORPHAN, DEV_PATH_TRUNC = (
     1, 2, 4, 8, 16, 32)
+DEV_TIMEOUT = 64
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

@@ -16,6 +16,8 @@
 // sum of exp((l - chunk max) / temperature)), so the single-workgroup walk
 // only combines ~32 chunk sums per visited node (one wave, in parallel) and
 // rescans one 4096-token chunk for the inverse-CDF draw.
+#include <algorithm>
+
 #include "common.h"
 
 namespace eagle {
@@ -380,132 +382,272 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(
 
 // Speculative sampling with the draft's distribution (recursive rejection
 // sampling over the children of each node, drawn from q without
-// replacement).  A prepass over all rows (accept_row_stats_kernel, many
-// workgroups) gives each row's chunk (max, sum); then one workgroup walks
-// the tree.  At a node the row normalisers Zp, Zq come from the chunk
-// statistics and child i with token x is accepted iff U[c] (q(x) / Zq) <
-// p(x) / Zp, with p = e^((l - max l) / t), q = e^((d - max d) / t) evaluated
-// for x alone.  Only a rejection (or the bonus draw) writes the node's
-// unnormalised rows into the workspace (pres, qres); a rejection then turns
-// pres into max(pres / Zp - qres / Zq, 0) (one pass over the vocabulary,
-// with the reciprocals of Zp and Zq),
-// drops x from qres and Zq, and the next child is tried.  The bonus is drawn
-// from the last pres by inverse CDF.  Sums are taken in a fixed order (each
-// thread's elements in index order, then a fixed butterfly, then the waves in
-// order), so the result does not depend on timing.
-constexpr int kQThreads = 1024;
-constexpr int kQWaves = kQThreads / 64;
-constexpr int kQBatch = 8;
+// replacement), spread over the whole GPU.  G workgroups (one per CU, all
+// resident at once) each own a contiguous chunk of the vocabulary and walk
+// the tree together: every workgroup takes every decision itself from the
+// same data in the same order, so they agree without exchanging decisions,
+// and they meet at a grid barrier only where a decision needs a sum over the
+// vocabulary.  At a visited node u:
+//   * one barrier combines the chunks' (max, sum e^((l - max) / t)) of the
+//     target and draft rows into Zp, Zq; each thread then holds
+//     p1(y) = e^((l_y - M) / t) / Zp and q1(y) for its tokens in fp64;
+//   * child i (ascending index) with token x, not rejected before, is
+//     accepted iff U[c] q_i(x) < p_i(x).  Every workgroup evaluates p_i(x) and
+//     q_i(x) at x alone: p1(x), q1(x) from the logits, then the node's
+//     earlier rejections replayed (p <- max(p - q, 0) / Z, q_i = q1 / D_i with
+//     D_i = 1 - the rejected draft mass);
+//   * a rejection makes every thread form max(p_i(y) - q_i(y), 0) for its
+//     tokens; one barrier gives their sum Z_(i+1); x's draft mass leaves D;
+//   * with no child accepted, the bonus is the smallest token whose running
+//     sum of p exceeds U[T + u] sum(p): one barrier for the chunk sums (each
+//     workgroup then scans its own chunk in token order), one for the
+//     crossing (the lowest token found, or the last token with mass when
+//     rounding leaves none).
+// The workgroups meet at a barrier with a coordinator: each publishes a
+// record (device-coherent stores) and then its arrival flag; workgroup 0
+// waits for every flag, combines the records in a fixed order, publishes the
+// result and a release flag, which the others wait for.  No atomics, so the
+// cost of a barrier does not grow with G.  Flags carry a generation number
+// that workgroup 0 advances at the end of every call (so stale flags never
+// match: flags are compared for equality, and a workgroup cannot publish
+// barrier e + 1's flag before barrier e is released) and the barrier's index
+// within the call.  Every wait is bounded
+// (kQSpinLimit polls): a barrier that never fills sets EAGLE_DEV_TIMEOUT and
+// the walk stops instead of hanging.
+constexpr int kQG = 256;           // workgroups (at most; one per CU)
+constexpr int kQT = 256;           // threads per workgroup
+constexpr int kQE = 8;             // vocabulary entries per thread, at most
+constexpr int kQWv = kQT / 64;
+constexpr uint32_t kQSpinLimit = 1u << 20;   // polls per barrier (about a second)
 
-__device__ __forceinline__ double q_block_sum(double v, double* dred) {
+struct QGridParams {
+  int T, V, G, C, E;               // C: chunk per workgroup, E: entries per thread
+  const int32_t* token;
+  const int32_t* parent;
+  const float* tl;
+  const float* dl;
+  double itemp;
+  const float* U;
+  int max_path;
+  int32_t* path;
+  int32_t* n_acc;
+  int32_t* bonus;
+  int32_t* status;
+  int32_t* sync;                   // [0] generation, [32] release flag, [64 + w] arrival flags
+  double* rec;                     // [2][G][4] published records, alternating per barrier
+  double* res;                     // [2][8 + G] combined results (+ per-chunk prefix sums)
+};
+
+enum { kQStats = 0, kQSum = 1, kQScan = 2 };
+
+// Sum (or max) over the workgroup in a fixed order; every thread gets it.
+__device__ __forceinline__ double q_wg_sum(double v, double* red) {
   v = wave_sum_d(v);
-  const int tid = threadIdx.x;
   __syncthreads();
-  if ((tid & 63) == 0) dred[tid >> 6] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   double s = 0.0;
-  for (int w = 0; w < kQWaves; ++w) s += dred[w];
+#pragma unroll
+  for (int w = 0; w < kQWv; ++w) s += red[w];
   return s;
 }
-
-__device__ __forceinline__ float q_block_max(float v, float* fred) {
-  v = wave_max(v);
-  const int tid = threadIdx.x;
+__device__ __forceinline__ double q_wg_max(double v, double* red) {
+  v = wave_max_d(v);
   __syncthreads();
-  if ((tid & 63) == 0) fred[tid >> 6] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  float m = -INFINITY;
-  for (int w = 0; w < kQWaves; ++w) m = fmaxf(m, fred[w]);
+  double m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kQWv; ++w) m = fmax(m, red[w]);
   return m;
 }
 
-__global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
-    int T, const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
-    const float* __restrict__ tl, const float* __restrict__ dl, int V, double itemp,
-    const float* __restrict__ U, const double* __restrict__ pst, const double* __restrict__ qst,
-    int nchunk, double* pres, double* qres, int max_path,
-    int32_t* __restrict__ path, int32_t* __restrict__ n_acc, int32_t* __restrict__ bonus,
-    int32_t* __restrict__ status) {
+__global__ __launch_bounds__(kQT) void accept_q_grid_kernel(QGridParams p) {
   __shared__ int32_t par[EAGLE_MAX_TREE];
   __shared__ int32_t tk[EAGLE_MAX_TREE];
   __shared__ int32_t kid[EAGLE_MAX_TREE];
   __shared__ int32_t rej[EAGLE_MAX_TREE];
-  __shared__ double dred[kQWaves];
-  __shared__ float fred[kQWaves];
-  __shared__ double csum[kQThreads];
-  __shared__ int sh_nk, sh_hit, sh_acc;
-  __shared__ double sh_qx, sh_ml, sh_md, sh_zp, sh_zq;
+  __shared__ double hz[EAGLE_MAX_TREE];   // 1 / Z after each rejection at this node
+  __shared__ double hd[EAGLE_MAX_TREE];   // 1 / D before each rejection (0: no draft mass)
+  __shared__ double red[kQWv];
+  __shared__ double xch[kQG][4];          // workgroup 0: the G records
+  __shared__ double res[4];               // a barrier's combined result
+  __shared__ double sh_before;
+  __shared__ int sh_ok, sh_nk;
   const int tid = threadIdx.x;
-  for (int i = tid; i < T; i += kQThreads) {
-    int p = parent[i];
-    const int x = token[i];
-    if (i == 0 ? p != -1 : (p < 0 || p >= i)) {
-      set_status(status, (i == 0 || p == -1) ? EAGLE_DEV_BAD_ROOT : EAGLE_DEV_BAD_PARENT);
-      p = i == 0 ? -1 : 0;
+  const int w = blockIdx.x;
+  const int G = p.G, V = p.V, T = p.T, E = p.E;
+  const int c0 = w * p.C;
+  const int c1 = min(c0 + p.C, V);
+  const int e0 = c0 + tid * E;            // this thread's tokens [e0, e0 + E) within [c0, c1)
+  const bool lead = w == 0;
+  int epoch = 0;
+  bool alive = true;
+
+  for (int i = tid; i < T; i += kQT) {
+    int pp = p.parent[i];
+    const int x = p.token[i];
+    if (i == 0 ? pp != -1 : (pp < 0 || pp >= i)) {
+      if (lead) set_status(p.status, (i == 0 || pp == -1) ? EAGLE_DEV_BAD_ROOT : EAGLE_DEV_BAD_PARENT);
+      pp = i == 0 ? -1 : 0;
     }
-    if (x < 0 || x >= V) set_status(status, EAGLE_DEV_BAD_TOKEN);
-    par[i] = p;
+    if (x < 0 || x >= V) {
+      if (lead) set_status(p.status, EAGLE_DEV_BAD_TOKEN);
+    }
+    par[i] = pp;
     tk[i] = min(max(x, 0), V - 1);
   }
   __syncthreads();
-  int u = 0, depth = 0;
-  if (tid == 0) path[0] = 0;
-  for (;;) {
-    const float* lrow = tl + (size_t)u * V;
-    const float* drow = dl + (size_t)u * V;
-    // the row's max and normaliser from the prepass's chunk statistics
-    // (combined in chunk order by wave 0); p(x) and q(x) of single tokens
-    // from the logits; the rows are written out over the vocabulary only
-    // when a rejection or the bonus draw needs them
-    if (tid < 64) {
-      double a = -INFINITY, b = -INFINITY;
-      for (int c = tid; c < nchunk; c += 64) {
-        a = fmax(a, pst[((size_t)u * nchunk + c) * 2]);
-        b = fmax(b, qst[((size_t)u * nchunk + c) * 2]);
-      }
-      a = wave_max_d(a);
-      b = wave_max_d(b);
-      double za = 0.0, zb = 0.0;
-      for (int c = tid; c < nchunk; c += 64) {
-        const double* x = pst + ((size_t)u * nchunk + c) * 2;
-        const double* y = qst + ((size_t)u * nchunk + c) * 2;
-        za += x[1] * exp_nonpos((x[0] - a) * itemp);
-        zb += y[1] * exp_nonpos((y[0] - b) * itemp);
-      }
-      za = wave_sum_d(za);
-      zb = wave_sum_d(zb);
-      if (tid == 0) {
-        sh_ml = a;
-        sh_md = b;
-        sh_zp = za;
-        sh_zq = zb;
-      }
+
+  // Barrier: publish this workgroup's record (a, b, c, d), meet the others,
+  // and receive the combination of all G records in res[]: kQStats -> (M, Zp,
+  // Md, Zq) from chunk (max, sum) pairs; kQSum -> the sum of the a's; kQScan
+  // -> (the sum of the a's, the largest b) and, in sh_before, the sum of the
+  // a's of the chunks before this one.  false: a wait expired.
+  const int gen = __hip_atomic_load(p.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto exchange = [&](int kind, double a, double b, double c, double d) -> bool {
+    const int slot = epoch & 1;
+    const int want = (gen << 10) | (epoch + 1);
+    const __amdgpu_buffer_rsrc_t rrs = dev_rsrc(p.rec + (size_t)slot * G * 4, (size_t)G * 32);
+    const __amdgpu_buffer_rsrc_t ors = dev_rsrc(p.res + (size_t)slot * (8 + G), (size_t)(8 + G) * 8);
+    ++epoch;
+    if (tid == 0) {
+      st_dev4(rrs, (uint32_t)(w * 32), __builtin_bit_cast(f32x4, make_double2(a, b)));
+      st_dev4(rrs, (uint32_t)(w * 32 + 16), __builtin_bit_cast(f32x4, make_double2(c, d)));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));   // the record lands before the flag
+      __hip_atomic_store(p.sync + 64 + w, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
-    const double ml = sh_ml, md = sh_md;
-    double zp = sh_zp, zq = sh_zq;
-    bool rows_out = false;   // pres / qres hold this node's rows
-    // writes pres = p (unnormalised) and qres = q over the vocabulary
-    auto rows = [&]() __attribute__((always_inline)) {
-      for (int v0 = tid; v0 < V; v0 += kQThreads * kQBatch) {
-        float a[kQBatch], b[kQBatch];
-#pragma unroll
-        for (int i = 0; i < kQBatch; ++i) {
-          const int v = v0 + i * kQThreads;
-          a[i] = v < V ? lrow[v] : 0.f;
-          b[i] = v < V ? drow[v] : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < kQBatch; ++i) {
-          const int v = v0 + i * kQThreads;
-          if (v < V) {
-            pres[v] = exp_nonpos(((double)a[i] - ml) * itemp);
-            qres[v] = exp_nonpos(((double)b[i] - md) * itemp);
+    int ok = 1;
+    if (lead) {
+      // workgroup 0: every arrival, then every record, combined in order
+      if (tid < G) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(p.sync + 64 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+               want) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins >= kQSpinLimit) {
+            ok = 0;
+            break;
           }
         }
       }
-      rows_out = true;
-    };
+      if (!ok) set_status(p.status, EAGLE_DEV_TIMEOUT);
+      if (tid == 0) sh_ok = 1;
+      __syncthreads();
+      if (!ok) sh_ok = 0;
+      __syncthreads();
+      if (!sh_ok) return false;
+      double ra = 0.0, rb = 0.0, rc = 0.0, rd = 0.0;
+      if (tid < G) {
+        const double2 x = __builtin_bit_cast(double2, ld_dev4(rrs, (uint32_t)(tid * 32)));
+        const double2 y = __builtin_bit_cast(double2, ld_dev4(rrs, (uint32_t)(tid * 32 + 16)));
+        ra = x.x; rb = x.y; rc = y.x; rd = y.y;
+        xch[tid][0] = ra; xch[tid][1] = rb; xch[tid][2] = rc; xch[tid][3] = rd;
+      }
+      double o0 = 0.0, o1 = 0.0, o2 = 0.0, o3 = 0.0;
+      if (kind == kQStats) {
+        o0 = q_wg_max(tid < G ? ra : -INFINITY, red);
+        o2 = q_wg_max(tid < G ? rc : -INFINITY, red);
+        o1 = q_wg_sum(tid < G && rb > 0.0 ? rb * exp_nonpos((ra - o0) * p.itemp) : 0.0, red);
+        o3 = q_wg_sum(tid < G && rd > 0.0 ? rd * exp_nonpos((rc - o2) * p.itemp) : 0.0, red);
+      } else if (kind == kQSum) {
+        o0 = q_wg_sum(tid < G ? ra : 0.0, red);
+      } else {
+        o1 = q_wg_max(tid < G ? rb : -1.0, red);
+        __syncthreads();                          // xch is complete
+        if (tid == 0) {                           // prefix in chunk order
+          double run = 0.0;
+          for (int v = 0; v < G; ++v) {
+            const double nx = run + xch[v][0];
+            xch[v][1] = run;
+            run = nx;
+          }
+          red[0] = run;
+        }
+        __syncthreads();
+        o0 = red[0];
+        if (tid < G) st_dev2(ors, (uint32_t)((8 + tid) * 8),
+                             __builtin_bit_cast(u32x2, xch[tid][1]));
+        if (tid == 0) sh_before = xch[0][1];
+      }
+      if (tid == 0) {
+        st_dev4(ors, 0, __builtin_bit_cast(f32x4, make_double2(o0, o1)));
+        st_dev4(ors, 16, __builtin_bit_cast(f32x4, make_double2(o2, o3)));
+        res[0] = o0; res[1] = o1; res[2] = o2; res[3] = o3;
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));   // results land before the release
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(p.sync + 32, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      return true;
+    }
+    if (tid == 0) {
+      uint32_t spins = 0;
+      while (__hip_atomic_load(p.sync + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins >= kQSpinLimit) {
+          ok = 0;
+          break;
+        }
+      }
+      if (!ok) set_status(p.status, EAGLE_DEV_TIMEOUT);
+      if (ok) {
+        const double2 x = __builtin_bit_cast(double2, ld_dev4(ors, 0));
+        const double2 y = __builtin_bit_cast(double2, ld_dev4(ors, 16));
+        res[0] = x.x; res[1] = x.y; res[2] = y.x; res[3] = y.y;
+        if (kind == kQScan)
+          sh_before = __builtin_bit_cast(double, ld_dev2(ors, (uint32_t)((8 + w) * 8)));
+      }
+      sh_ok = ok;
+    }
+    __syncthreads();
+    return sh_ok != 0;
+  };
+
+  double pv[kQE], qv[kQE];
+  int u = 0, depth = 0;
+  if (lead && tid == 0) p.path[0] = 0;
+  for (;;) {
+    const float* lrow = p.tl + (size_t)u * V;
+    const float* drow = p.dl + (size_t)u * V;
+    // this chunk's row statistics
+    float lf[kQE], df[kQE];
+    float ml = -INFINITY, md = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kQE; ++e) {
+      const int y = e0 + e;
+      const bool in = e < E && y < c1;
+      lf[e] = in ? lrow[y] : -INFINITY;
+      df[e] = in ? drow[y] : -INFINITY;
+      ml = fmaxf(ml, lf[e]);
+      md = fmaxf(md, df[e]);
+    }
+    const double wml = q_wg_max((double)ml, red);
+    const double wmd = q_wg_max((double)md, red);
+    double sp = 0.0, sq = 0.0;
+#pragma unroll
+    for (int e = 0; e < kQE; ++e) {
+      if (e < E && e0 + e < c1) {
+        sp += exp_nonpos(((double)lf[e] - wml) * p.itemp);
+        sq += exp_nonpos(((double)df[e] - wmd) * p.itemp);
+      }
+    }
+    const double wsp = q_wg_sum(sp, red);
+    const double wsq = q_wg_sum(sq, red);
+    if (!exchange(kQStats, wml, wsp, wmd, wsq)) {
+      alive = false;
+      break;
+    }
+    const double M = res[0], zp = res[1], Md = res[2], zq = res[3];
+    const double izp = 1.0 / zp;
+    const double izq = 1.0 / zq;
+#pragma unroll
+    for (int e = 0; e < kQE; ++e) {
+      const bool in = e < E && e0 + e < c1;
+      pv[e] = in ? exp_nonpos(((double)lf[e] - M) * p.itemp) * izp : 0.0;
+      qv[e] = in ? exp_nonpos(((double)df[e] - Md) * p.itemp) * izq : 0.0;
+    }
     if (tid == 0) {
       int n = 0;
       for (int c = u + 1; c < T; ++c)
@@ -515,141 +657,127 @@ __global__ __launch_bounds__(kQThreads) void accept_sample_q_kernel(
     __syncthreads();
     const int nk = sh_nk;
     int nrej = 0;
+    double D = 1.0;                          // draft mass not yet rejected at u
     int next = -1;
     for (int i = 0; i < nk; ++i) {
       const int c = kid[i];
       const int x = tk[c];
       bool seen = false;
       for (int r = 0; r < nrej; ++r) seen |= rej[r] == x;
-      if (seen) continue;                 // a draw never repeats a token
-      // thread 0 decides and shares the decision and q(x), so every thread
-      // takes the same branch (the rejection pass below has barriers)
-      if (tid == 0) {
-        const double qx = rows_out ? qres[x] : exp_nonpos(((double)drow[x] - md) * itemp);
-        const double px = rows_out ? pres[x] : exp_nonpos(((double)lrow[x] - ml) * itemp);
-        const double qn = zq > 0.0 ? qx / zq : 0.0;   // (no draft mass left: q counts as 0)
-        sh_acc = (double)U[c] * qn < px / zp;
-        sh_qx = qx;
-      }
-      __syncthreads();
-      const double qx = sh_qx;
-      if (sh_acc) {
+      if (seen) continue;                    // a draw never repeats a token
+      // p_i(x), q_i(x) at x alone, replaying this node's rejections
+      const double q1x = exp_nonpos(((double)drow[x] - Md) * p.itemp) * izq;
+      double px = exp_nonpos(((double)lrow[x] - M) * p.itemp) * izp;
+      for (int r = 0; r < nrej; ++r) px = fmax(px - q1x * hd[r], 0.0) * hz[r];
+      const double iD = D > 0.0 ? 1.0 / D : 0.0;
+      const double qx = q1x * iD;
+      if ((double)p.U[c] * qx < px) {
         next = c;
         break;
       }
-      // rejected: p <- max(p / Zp - q / Zq, 0), q <- q without x
-      if (!rows_out) {
-        rows();
-        __syncthreads();
-      }
+      // rejected: p <- max(p - q, 0) / Z, over the vocabulary (the same
+      // operations as the replay above)
       double s = 0.0;
-      const double izp = 1.0 / zp;
-      const double izq = zq > 0.0 ? 1.0 / zq : 0.0;
-      for (int v0 = tid; v0 < V; v0 += kQThreads * kQBatch) {
-        double a[kQBatch], b[kQBatch];
 #pragma unroll
-        for (int i = 0; i < kQBatch; ++i) {
-          const int v = v0 + i * kQThreads;
-          a[i] = v < V ? pres[v] : 0.0;
-          b[i] = v < V ? qres[v] : 0.0;
-        }
-#pragma unroll
-        for (int i = 0; i < kQBatch; ++i) {
-          const int v = v0 + i * kQThreads;
-          if (v < V) {
-            const double r = fmax(a[i] * izp - b[i] * izq, 0.0);
-            pres[v] = r;
-            s += r;
-          }
-        }
+      for (int e = 0; e < kQE; ++e) {
+        const double t = fmax(pv[e] - qv[e] * iD, 0.0);
+        pv[e] = t;
+        s += t;
       }
-      zp = q_block_sum(s, dred);        // (its barriers also order the pres stores)
+#pragma unroll
+      for (int e = 0; e < kQE; ++e)
+        if (e0 + e == x) qv[e] = 0.0;        // x leaves q after this step's update
+      const double ws = q_wg_sum(s, red);
+      if (!exchange(kQSum, ws, 0.0, 0.0, 0.0)) {
+        alive = false;
+        break;
+      }
+      const double iz = 1.0 / res[0];
       if (tid == 0) {
-        qres[x] = 0.0;
+        hd[nrej] = iD;
+        hz[nrej] = iz;
         rej[nrej] = x;
       }
-      zq = zq - qx;
+#pragma unroll
+      for (int e = 0; e < kQE; ++e) pv[e] *= iz;
+      D -= q1x;
       ++nrej;
       __syncthreads();
     }
+    if (!alive) break;
     if (next >= 0) {
       ++depth;
-      if (tid == 0) {
-        if (depth < max_path) path[depth] = next;
-        else set_status(status, EAGLE_DEV_PATH_TRUNC);
+      if (lead && tid == 0) {
+        if (depth < p.max_path) p.path[depth] = next;
+        else set_status(p.status, EAGLE_DEV_PATH_TRUNC);
       }
       u = next;
-      __syncthreads();
       continue;
     }
-    // bonus: smallest token whose running sum of pres exceeds U[T + u] Zp.
-    // Thread t owns the contiguous tokens [t C, (t + 1) C).
-    if (!rows_out) {
-      rows();
-      __syncthreads();
-    }
-    const double target = (double)U[T + u] * zp;
-    const int C = (V + kQThreads - 1) / kQThreads;
-    const int v0 = tid * C;
-    const int v1 = min(V, v0 + C);
+    // bonus: the smallest token whose running sum of p exceeds U[T + u] sum(p)
     double own = 0.0;
-    for (int w0 = v0; w0 < v1; w0 += kQBatch) {
-      double a[kQBatch];
 #pragma unroll
-      for (int i = 0; i < kQBatch; ++i) a[i] = w0 + i < v1 ? pres[w0 + i] : 0.0;
-#pragma unroll
-      for (int i = 0; i < kQBatch; ++i) own += a[i];
-    }
-    csum[tid] = own;
-    if (tid == 0) sh_hit = 0x7fffffff;
+    for (int e = 0; e < kQE; ++e) own += pv[e];
+    // exclusive prefix of the threads' sums, in thread order
+    __shared__ double tsum[kQT];
+    tsum[tid] = own;
     __syncthreads();
     if (tid == 0) {
       double run = 0.0;
-      for (int t = 0; t < kQThreads; ++t) {
-        const double nx = run + csum[t];
-        csum[t] = run;                    // exclusive prefix
+      for (int t = 0; t < kQT; ++t) {
+        const double nx = run + tsum[t];
+        tsum[t] = run;
         run = nx;
       }
+      red[0] = run;
     }
     __syncthreads();
-    {
-      // the crossing: one token in exact arithmetic; rounding at a chunk
-      // border can show it to two threads, and the lower token wins
-      double run = csum[tid];
-      bool found = false;
-      for (int w0 = v0; w0 < v1 && !found; w0 += kQBatch) {
-        double a[kQBatch];
+    const double wtot = red[0];
+    const double tpre = tsum[tid];
+    int last = -1;
 #pragma unroll
-        for (int i = 0; i < kQBatch; ++i) a[i] = w0 + i < v1 ? pres[w0 + i] : 0.0;
+    for (int e = 0; e < kQE; ++e)
+      if (pv[e] > 0.0) last = e0 + e;
+    last = (int)q_wg_max((double)last, red);
+    if (!exchange(kQScan, wtot, (double)last, 0.0, 0.0)) {
+      alive = false;
+      break;
+    }
+    const double total = res[0];
+    const int lastall = (int)res[1];
+    const double before = sh_before;
+    const double target = (double)p.U[T + u] * total;
+    // Chunk boundaries are consistent (each chunk starts where the previous
+    // one's prefix ends), so exactly one chunk holds the crossing when
+    // target < total; it reports the first of its tokens whose running sum
+    // exceeds target (the last token of the chunk with mass if rounding
+    // inside the chunk leaves none).  Otherwise rounding left no crossing at
+    // all: the last token with mass.
+    if (target < total && before <= target && target < before + wtot) {
+      int hit = 0x7fffffff;
+      double run = before + tpre;
 #pragma unroll
-        for (int i = 0; i < kQBatch; ++i) {
-          const int v = w0 + i;
-          const double nx = run + a[i];
-          if (!found && v < v1 && run <= target && nx > target) {
-            atomicMin(&sh_hit, v);
-            found = true;
-          }
-          run = nx;
-        }
+      for (int e = 0; e < kQE; ++e) {
+        const double nx = run + pv[e];
+        if (hit == 0x7fffffff && e < E && e0 + e < c1 && nx > target) hit = e0 + e;
+        run = nx;
       }
+      hit = -(int)q_wg_max(-(double)hit, red);    // lowest in the workgroup
+      if (hit == 0x7fffffff) hit = max(last, 0);
+      if (tid == 0) p.bonus[0] = hit;
+    } else if (!(target < total) && lead && tid == 0) {
+      p.bonus[0] = max(lastall, 0);
     }
-    __syncthreads();
-    if (tid == 0) {
-      int b = sh_hit == 0x7fffffff ? -1 : sh_hit;
-      if (b < 0) {                        // rounding left none: the last token with mass
-        for (int v = V - 1; v >= 0; --v)
-          if (pres[v] > 0.0) {
-            b = v;
-            break;
-          }
-        b = max(b, 0);
-      }
-      bonus[0] = b;
-      n_acc[0] = depth;
-      for (int d = depth + 1; d < max_path; ++d) path[d] = -1;
+    if (lead && tid == 0) {
+      p.n_acc[0] = min(depth, p.max_path - 1);
+      for (int d = depth + 1; d < p.max_path; ++d) p.path[d] = -1;
     }
-    return;
+    break;
   }
+  // a new generation for the next call: its flags never match this call's
+  if (lead && tid == 0)
+    __hip_atomic_store(p.sync, (gen + 1) & 0x1fffff, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  (void)alive;
 }
 
 }  // namespace eagle
@@ -696,9 +824,24 @@ extern "C" int eagle_accept(int32_t mode, int32_t T, const int32_t* node_token,
   return EAGLE_OK;
 }
 
+// Compute units of the current device: the general-q walk needs its whole
+// grid resident at once, one workgroup per CU.
+static int q_device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return eagle::kQG;
+  if (!cached[dev]) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                          hipSuccess && n > 0 ? n : eagle::kQG;
+  }
+  return cached[dev];
+}
+
 extern "C" size_t eagle_accept_q_workspace(int32_t T, int32_t V) {
   if (T < 1 || V < 1) return 0;
-  return (size_t)2 * (size_t)V * sizeof(double) + 2 * eagle_accept_workspace(T, V);
+  return 2048 + (size_t)2 * eagle::kQG * 4 * sizeof(double) +
+         (size_t)2 * (8 + eagle::kQG) * sizeof(double);
 }
 
 extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_t* node_parent,
@@ -711,20 +854,22 @@ extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_
   EAGLE_REQUIRE(path && n_accepted && bonus_token, EAGLE_EINVAL);
   EAGLE_REQUIRE(T >= 1 && T <= EAGLE_MAX_TREE && max_path >= 1 && V >= 1, EAGLE_EINVAL);
   EAGLE_REQUIRE(temperature > 0.0f && temperature <= 3.0e38f, EAGLE_EINVAL);
-  EAGLE_REQUIRE(workspace && ((uintptr_t)workspace & 7) == 0, EAGLE_EINVAL);
+  EAGLE_REQUIRE(workspace && ((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
   EAGLE_REQUIRE(ws_bytes >= eagle_accept_q_workspace(T, V), EAGLE_EWORKSPACE);
-  const int nchunk = (V + eagle::kAcceptChunk - 1) / eagle::kAcceptChunk;
-  const double itemp = 1.0 / (double)temperature;
-  double* pres = (double*)workspace;
-  double* pst = pres + 2 * (size_t)V;
-  double* qst = pst + (size_t)T * nchunk * 2;
-  hipLaunchKernelGGL(eagle::accept_row_stats_kernel, dim3(nchunk, 2 * T), dim3(256), 0, stream,
-                     target_logits, pst, T, draft_logits, qst, V, itemp, nchunk);
-  EAGLE_LAUNCH_CHECK();
-  hipLaunchKernelGGL(eagle::accept_sample_q_kernel, dim3(1), dim3(eagle::kQThreads), 0, stream, T,
-                     node_token, node_parent, target_logits, draft_logits, V, itemp, uniforms,
-                     pst, qst, nchunk, pres, pres + V, max_path, path, n_accepted, bonus_token,
-                     dev_status);
+  const int G = std::min(eagle::kQG, q_device_cus());
+  const int C = (V + G - 1) / G;
+  const int E = (C + eagle::kQT - 1) / eagle::kQT;
+  EAGLE_REQUIRE(E <= eagle::kQE, EAGLE_EUNSUPPORTED);
+  eagle::QGridParams p{};
+  p.T = T; p.V = V; p.G = G; p.C = C; p.E = E;
+  p.token = node_token; p.parent = node_parent; p.tl = target_logits; p.dl = draft_logits;
+  p.itemp = 1.0 / (double)temperature;
+  p.U = uniforms; p.max_path = max_path; p.path = path; p.n_acc = n_accepted;
+  p.bonus = bonus_token; p.status = dev_status;
+  p.sync = (int32_t*)workspace;                                  // 64 + kQG ints
+  p.rec = (double*)((char*)workspace + 2048);                    // [2][G][4]
+  p.res = p.rec + 2 * eagle::kQG * 4;                            // [2][8 + G]
+  hipLaunchKernelGGL(eagle::accept_q_grid_kernel, dim3(G), dim3(eagle::kQT), 0, stream, p);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

@@ -305,8 +305,8 @@ def test_logits_process_argument_errors(lib):
 
 def test_accept_q_argument_errors(lib):
     f = lib.eagle_accept_q
-    nchunk = (128256 + 4095) // 4096
-    assert lib.eagle_accept_q_workspace(64, 128256) == 2 * 128256 * 8 + 2 * 64 * nchunk * 16
+    # barrier flags, two record slots of 256 workgroups x 4 doubles, two result slots
+    assert lib.eagle_accept_q_workspace(64, 128256) == 2048 + 2 * 256 * 4 * 8 + 2 * (8 + 256) * 8
     assert lib.eagle_accept_q_workspace(64, 0) == 0 and lib.eagle_accept_q_workspace(0, 10) == 0
     need = lib.eagle_accept_q_workspace(8, 100)
     ok = [8, FAKE, FAKE, FAKE, FAKE, 100, 1.0, FAKE, 8, FAKE, FAKE, FAKE, FAKE, need, None, None]

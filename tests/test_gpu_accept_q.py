@@ -66,3 +66,30 @@ def test_q_equal_p_accepts_along_the_first_children(dev):
         u = kids[0]
         want.append(u)
     assert path.cpu().numpy()[:len(want)].tolist() == want and int(n.item()) == len(want) - 1
+
+
+def test_grid_walk_repeated_calls_on_one_workspace(dev):
+    """The walk meets at grid barriers whose flags live in the workspace: 20
+    calls in a row on one workspace (each advancing the flags' generation)
+    give the same walk each time and no wait expires."""
+    T, V = 64, 128256
+    g = inputs.rng(980, 0)
+    par = inputs.random_tree(g, T, 7, 4)
+    tl = (g.standard_normal((T, V), dtype=np.float32) * 2.0).astype(np.float32)
+    dl = (0.5 * tl + g.standard_normal((T, V), dtype=np.float32)).astype(np.float32)
+    tok = inputs.sibling_distinct_tokens(g, par, V)
+    tok = inputs.plant_path(tok, par, tl.argmax(1).astype(np.int32), inputs.deepest_leaf(g, par))
+    U = inputs.uniforms(g, 2 * T)
+    rp, rn, rb, margin = oracle.accept_sample_q(tok, par, tl, dl, 1.0, U, return_margin=True)
+    assert margin >= 1e-12
+    ws = torch.zeros(_lib.lib().eagle_accept_q_workspace(T, V), dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    args = (to(dev, tok), to(dev, par), to(dev, tl, torch.float32), to(dev, dl, torch.float32), 1.0,
+            to(dev, U, torch.float32))
+    for rep in range(20):
+        path, n, b = _lib.eagle_accept_q(*args, workspace=ws, dev_status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, f"call {rep}: status {int(st.item())}"
+        assert int(n.item()) == rn and int(b.item()) == rb, f"call {rep}"
+        assert path.cpu().numpy()[:rn + 1].tolist() == rp
+    assert int(ws[:4].view(torch.int32).item()) == 20      # one generation per call
