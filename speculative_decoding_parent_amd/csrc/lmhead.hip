@@ -39,13 +39,15 @@ constexpr int kLmBlockK = 16;
 static_assert(2 * 16 * kWsLds * 2 >= 4 * 16 * (kLmBlockK + 1) * 8, "lists exceed staging LDS");
 static_assert(sizeof(selkey_t) == 8, "key size");
 
-// W tiles of 16 rows per wave: 8 (128 rows) while the feature rows fit one MFMA
-// tile, which keeps the most weight bytes in flight per wave; fewer as more
-// feature rows need accumulator registers (no spills up to T = 256).  At
-// T <= 64 four tiles give 501 workgroups for V = 128256, one wave of
-// workgroups at two per CU.
+// W tiles of 16 rows per wave: 8 (128 rows, one 4-wave workgroup per CU) while
+// the feature rows fit two MFMA tiles, which keeps the most weight bytes in
+// flight per wave; fewer as more feature rows need accumulator registers (no
+// spills up to T = 256).  At 32 < T <= 64 four tiles give 501 workgroups for
+// V = 128256, one wave of workgroups at two per CU (eight tiles would spill).
+// Measured at V = 128256, d = 4096: T = 32 takes 197 us with eight tiles and
+// 243 us with four.
 __host__ __device__ constexpr int lm_mt(int T) {
-  return T <= 16 ? 8 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
+  return T <= 32 ? 8 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
 }
 
 // The feature-row tiles a launch is compiled for (1, 2, 4, 8 or 16 of 16 rows).

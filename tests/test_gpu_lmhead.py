@@ -48,6 +48,7 @@ def check(ids, logp, lse, lg, f, W, k, exact=False):
 @pytest.mark.parametrize("T,d,V,k", [(60, 3584, 5000, 10), (64, 4096, 4096, 10), (1, 128, 300, 10),
                                      (10, 4096, 2000, 10), (128, 1024, 3000, 10),
                                      (17, 512, 777, 64), (3, 256, 20, 20), (200, 256, 1100, 8),
+                                     (32, 4096, 6000, 10), (24, 1024, 2500, 16), (31, 384, 1031, 40),
                                      (10, 512, 20000, 16), (64, 256, 9000, 17),
                                      (16, 256, 70000, 1),
                                      # 256 lists of 16 (one-pass merge) and 257 (two-pass merge)
