@@ -429,16 +429,18 @@ int eagle_path_slots(const int32_t* path, const int32_t* n_accepted, int32_t max
  * per CU, each owning a slice of the vocabulary) walks the tree together:
  * every workgroup takes every decision itself, and they meet at a grid
  * barrier only for the sums over the vocabulary (a visited node's row
- * statistics, each rejection's residual mass, the bonus draw).  The whole
+ * statistics, each rejection's residual mass, the bonus draw); a barrier is
+ * an all-gather of tagged records in the workspace, which every workgroup
+ * combines itself in the same fixed order.  The whole
  * grid must be resident at once: the call assumes the GPU is not shared with
  * other work holding CUs; a barrier that never fills sets EAGLE_DEV_TIMEOUT
  * after about a second instead of hanging (the outputs are then not valid).
  *
  * target_logits, draft_logits f32[T][V]; uniforms f32[2T] in [0, 1);
  * workspace >= eagle_accept_q_workspace(T, V) bytes, 256-byte aligned, zero
- * before its first use (its first 2 KiB hold the barrier flags and a
- * generation number that every call advances; keep the buffer for later
- * calls on the same stream, or zero it again before handing it over).
+ * before its first use (it holds a generation number that every call
+ * advances and the tagged barrier records; keep the buffer for later calls
+ * on the same stream, or zero it again before handing it over).
  * Outputs and device errors as eagle_accept.  Host errors: null pointers, T
  * outside [1, EAGLE_MAX_TREE], V or max_path < 1, temperature not in
  * (0, 3e38], a misaligned workspace -> EAGLE_EINVAL; V above 524288 ->

@@ -34,7 +34,8 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   constexpr double kLn2Hi = 6.93147180369123816490e-01;
   constexpr double kLn2Lo = 1.90821492927058770002e-10;
   constexpr double kLog2e = 1.4426950408889634;
-  if (!(x > -745.2)) return 0.0;
+  const bool under = !(x > -745.2);     // (no branch: callers evaluate many at once)
+  x = under ? 0.0 : x;
   const double k = rint(x * kLog2e);
   double r = fma(-k, kLn2Hi, x);
   r = fma(-k, kLn2Lo, r);
@@ -51,7 +52,8 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   p = fma(p, r, 0.5);
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
-  return ldexp(p, (int)k);
+  const double v = ldexp(p, (int)k);
+  return under ? 0.0 : v;
 }
 
 // ---------------------------------------------------------------- greedy
@@ -403,15 +405,19 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(
 //     workgroup then scans its own chunk in token order), one for the
 //     crossing (the lowest token found, or the last token with mass when
 //     rounding leaves none).
-// The workgroups meet at a barrier with a coordinator: each publishes a
-// record (device-coherent stores) and then its arrival flag; workgroup 0
-// waits for every flag, combines the records in a fixed order, publishes the
-// result and a release flag, which the others wait for.  No atomics, so the
-// cost of a barrier does not grow with G.  Flags carry a generation number
-// that workgroup 0 advances at the end of every call (so stale flags never
-// match: flags are compared for equality, and a workgroup cannot publish
-// barrier e + 1's flag before barrier e is released) and the barrier's index
-// within the call.  Every wait is bounded
+// A barrier is an all-gather of tagged records: each workgroup stores its
+// record (four doubles) as eight 64-bit words with device-coherent stores,
+// the low half of each word carrying half of a value and the high half the
+// barrier's tag; thread v of every workgroup polls record v until all eight
+// of its tags match, and every workgroup then combines the G records itself
+// in the same fixed order.  Aligned 64-bit accesses are single-copy atomic,
+// so a word whose tag matches carries this barrier's value; one memory round
+// trip after the last record lands, every workgroup has them all.  Records
+// alternate between two slots (a workgroup writes barrier e + 2's record only
+// after everyone has written barrier e + 1's, that is, after everyone has read
+// barrier e's).  Tags hold a generation number that workgroup 0 advances at
+// the end of every call (so records of earlier calls never match) and the
+// barrier's index within the call.  Every wait is bounded
 // (kQSpinLimit polls): a barrier that never fills sets EAGLE_DEV_TIMEOUT and
 // the walk stops instead of hanging.
 constexpr int kQG = 256;           // workgroups (at most; one per CU)
@@ -433,57 +439,97 @@ struct QGridParams {
   int32_t* n_acc;
   int32_t* bonus;
   int32_t* status;
-  int32_t* sync;                   // [0] generation, [32] release flag, [64 + w] arrival flags
-  double* rec;                     // [2][G][4] published records, alternating per barrier
-  double* res;                     // [2][8 + G] combined results (+ per-chunk prefix sums)
+  int32_t* sync;                   // [0] generation
+  uint64_t* rec;                   // [2][G][8] tagged records, alternating per barrier
 };
 
 enum { kQStats = 0, kQSum = 1, kQScan = 2 };
 
-// Sum (or max) over the workgroup in a fixed order; every thread gets it.
-__device__ __forceinline__ double q_wg_sum(double v, double* red) {
-  v = wave_sum_d(v);
+// Sums and maxima over the workgroup in a fixed order (every thread gets
+// them); two values share one pair of barriers.
+__device__ __forceinline__ double2 q_wg_sum2(double a, double b, double2* red) {
+  a = wave_sum_d(a);
+  b = wave_sum_d(b);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_double2(a, b);
   __syncthreads();
-  double s = 0.0;
+  double2 s = make_double2(0.0, 0.0);
 #pragma unroll
-  for (int w = 0; w < kQWv; ++w) s += red[w];
+  for (int w = 0; w < kQWv; ++w) {
+    s.x += red[w].x;
+    s.y += red[w].y;
+  }
   return s;
 }
-__device__ __forceinline__ double q_wg_max(double v, double* red) {
-  v = wave_max_d(v);
+__device__ __forceinline__ double2 q_wg_max2(double a, double b, double2* red) {
+  a = wave_max_d(a);
+  b = wave_max_d(b);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_double2(a, b);
   __syncthreads();
-  double m = -INFINITY;
+  double2 m = make_double2(-INFINITY, -INFINITY);
 #pragma unroll
-  for (int w = 0; w < kQWv; ++w) m = fmax(m, red[w]);
+  for (int w = 0; w < kQWv; ++w) {
+    m.x = fmax(m.x, red[w].x);
+    m.y = fmax(m.y, red[w].y);
+  }
   return m;
+}
+// Exclusive prefix sums of v in thread order, and in *total the sum of all.
+// The additions follow a fixed pattern, so equal inputs give equal results
+// in every workgroup.
+__device__ __forceinline__ double q_wg_excl_scan(double v, double2* red, double* total) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  double x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  double ex = __shfl_up(x, 1, 64);
+  if (lane == 0) ex = 0.0;
+  __syncthreads();
+  if (lane == 63) red[wv] = make_double2(x, 0.0);
+  __syncthreads();
+  double off = 0.0, tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kQWv; ++w) {
+    if (w < wv) off += red[w].x;
+    tot += red[w].x;
+  }
+  *total = tot;
+  return off + ex;
 }
 
 __global__ __launch_bounds__(kQT) void accept_q_grid_kernel(QGridParams p) {
+  constexpr int kWords = EAGLE_MAX_TREE / 64;
   __shared__ int32_t par[EAGLE_MAX_TREE];
   __shared__ int32_t tk[EAGLE_MAX_TREE];
-  __shared__ int32_t kid[EAGLE_MAX_TREE];
+  __shared__ uint64_t cmask[EAGLE_MAX_TREE][kWords];   // the children of each node, as bits
+  __shared__ int32_t fc[EAGLE_MAX_TREE];  // the first child of each node (T: none)
+  __shared__ double cp1[EAGLE_MAX_TREE];  // a child's p1 and q1 at its token (row of its
+  __shared__ double cq1[EAGLE_MAX_TREE];  //   parent), and its uniform
+  __shared__ float chu[EAGLE_MAX_TREE];
   __shared__ int32_t rej[EAGLE_MAX_TREE];
   __shared__ double hz[EAGLE_MAX_TREE];   // 1 / Z after each rejection at this node
   __shared__ double hd[EAGLE_MAX_TREE];   // 1 / D before each rejection (0: no draft mass)
-  __shared__ double red[kQWv];
-  __shared__ double xch[kQG][4];          // workgroup 0: the G records
-  __shared__ double res[4];               // a barrier's combined result
-  __shared__ double sh_before;
-  __shared__ int sh_ok, sh_nk;
+  __shared__ double2 red[kQWv];
+  __shared__ double xb[kQG + 1];          // chunk boundaries of the bonus draw
+  __shared__ double xw[kQG];              // and the chunks' masses
+  __shared__ double tb[kQT + 1];          // thread boundaries within this chunk
+  __shared__ float sh_ub;
+  __shared__ int sh_fail;
   const int tid = threadIdx.x;
   const int w = blockIdx.x;
   const int G = p.G, V = p.V, T = p.T, E = p.E;
   const int c0 = w * p.C;
   const int c1 = min(c0 + p.C, V);
   const int e0 = c0 + tid * E;            // this thread's tokens [e0, e0 + E) within [c0, c1)
-  const bool lead = w == 0;
+  const bool lead = w == 0;               // writes the outputs
   int epoch = 0;
-  bool alive = true;
 
+  if (tid == 0) sh_fail = 0;
   for (int i = tid; i < T; i += kQT) {
     int pp = p.parent[i];
     const int x = p.token[i];
@@ -497,212 +543,229 @@ __global__ __launch_bounds__(kQT) void accept_q_grid_kernel(QGridParams p) {
     par[i] = pp;
     tk[i] = min(max(x, 0), V - 1);
   }
+  for (int i = tid; i < EAGLE_MAX_TREE * kWords; i += kQT) (&cmask[0][0])[i] = 0ull;
+  for (int i = tid; i < EAGLE_MAX_TREE; i += kQT) fc[i] = T;
+  __syncthreads();
+  for (int c = 1 + tid; c < T; c += kQT) {
+    atomicOr((unsigned long long*)&cmask[par[c]][c >> 6], 1ull << (c & 63));
+    atomicMin(&fc[par[c]], c);
+  }
   __syncthreads();
 
-  // Barrier: publish this workgroup's record (a, b, c, d), meet the others,
-  // and receive the combination of all G records in res[]: kQStats -> (M, Zp,
-  // Md, Zq) from chunk (max, sum) pairs; kQSum -> the sum of the a's; kQScan
-  // -> (the sum of the a's, the largest b) and, in sh_before, the sum of the
-  // a's of the chunks before this one.  false: a wait expired.
+  // Barrier: publish this workgroup's record (a, b, c, d), wait for every
+  // workgroup's record of the same barrier, and combine all G of them in a
+  // fixed order (every workgroup computes the same result) into r:
+  // kQStats -> (M, Zp, Md, Zq) from chunk (max, sum) pairs; kQSum -> the sum
+  // of the a's; kQScan -> (the sum of the a's, the largest b), with the
+  // chunk boundaries (running sums of the a's in chunk order) in xb[0..G]
+  // and the a's in xw.
+  // false: a wait expired.
   const int gen = __hip_atomic_load(p.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  auto exchange = [&](int kind, double a, double b, double c, double d) -> bool {
+  auto exchange = [&](int kind, double a, double b, double c, double d, double (&r)[4]) -> bool {
     const int slot = epoch & 1;
-    const int want = (gen << 10) | (epoch + 1);
-    const __amdgpu_buffer_rsrc_t rrs = dev_rsrc(p.rec + (size_t)slot * G * 4, (size_t)G * 32);
-    const __amdgpu_buffer_rsrc_t ors = dev_rsrc(p.res + (size_t)slot * (8 + G), (size_t)(8 + G) * 8);
+    const uint32_t want = (uint32_t)((gen << 10) | (epoch + 1));
+    const __amdgpu_buffer_rsrc_t rrs = dev_rsrc(p.rec + (size_t)slot * G * 8, (size_t)G * 64);
     ++epoch;
-    if (tid == 0) {
-      st_dev4(rrs, (uint32_t)(w * 32), __builtin_bit_cast(f32x4, make_double2(a, b)));
-      st_dev4(rrs, (uint32_t)(w * 32 + 16), __builtin_bit_cast(f32x4, make_double2(c, d)));
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));   // the record lands before the flag
-      __hip_atomic_store(p.sync + 64 + w, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < 4) {
+      // word 2 k + h of the record: half h of value k below, the tag above
+      const double v = tid == 0 ? a : tid == 1 ? b : tid == 2 ? c : d;
+      const uint64_t bits = __builtin_bit_cast(uint64_t, v);
+      st_dev4(rrs, (uint32_t)(w * 64 + tid * 16),
+              __builtin_bit_cast(f32x4, u32x4{(uint32_t)bits, want, (uint32_t)(bits >> 32), want}));
     }
-    int ok = 1;
-    if (lead) {
-      // workgroup 0: every arrival, then every record, combined in order
-      if (tid < G) {
-        uint32_t spins = 0;
-        while (__hip_atomic_load(p.sync + 64 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
-               want) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins >= kQSpinLimit) {
-            ok = 0;
-            break;
-          }
-        }
-      }
-      if (!ok) set_status(p.status, EAGLE_DEV_TIMEOUT);
-      if (tid == 0) sh_ok = 1;
-      __syncthreads();
-      if (!ok) sh_ok = 0;
-      __syncthreads();
-      if (!sh_ok) return false;
-      double ra = 0.0, rb = 0.0, rc = 0.0, rd = 0.0;
-      if (tid < G) {
-        const double2 x = __builtin_bit_cast(double2, ld_dev4(rrs, (uint32_t)(tid * 32)));
-        const double2 y = __builtin_bit_cast(double2, ld_dev4(rrs, (uint32_t)(tid * 32 + 16)));
-        ra = x.x; rb = x.y; rc = y.x; rd = y.y;
-        xch[tid][0] = ra; xch[tid][1] = rb; xch[tid][2] = rc; xch[tid][3] = rd;
-      }
-      double o0 = 0.0, o1 = 0.0, o2 = 0.0, o3 = 0.0;
-      if (kind == kQStats) {
-        o0 = q_wg_max(tid < G ? ra : -INFINITY, red);
-        o2 = q_wg_max(tid < G ? rc : -INFINITY, red);
-        o1 = q_wg_sum(tid < G && rb > 0.0 ? rb * exp_nonpos((ra - o0) * p.itemp) : 0.0, red);
-        o3 = q_wg_sum(tid < G && rd > 0.0 ? rd * exp_nonpos((rc - o2) * p.itemp) : 0.0, red);
-      } else if (kind == kQSum) {
-        o0 = q_wg_sum(tid < G ? ra : 0.0, red);
-      } else {
-        o1 = q_wg_max(tid < G ? rb : -1.0, red);
-        __syncthreads();                          // xch is complete
-        if (tid == 0) {                           // prefix in chunk order
-          double run = 0.0;
-          for (int v = 0; v < G; ++v) {
-            const double nx = run + xch[v][0];
-            xch[v][1] = run;
-            run = nx;
-          }
-          red[0] = run;
-        }
-        __syncthreads();
-        o0 = red[0];
-        if (tid < G) st_dev2(ors, (uint32_t)((8 + tid) * 8),
-                             __builtin_bit_cast(u32x2, xch[tid][1]));
-        if (tid == 0) sh_before = xch[0][1];
-      }
-      if (tid == 0) {
-        st_dev4(ors, 0, __builtin_bit_cast(f32x4, make_double2(o0, o1)));
-        st_dev4(ors, 16, __builtin_bit_cast(f32x4, make_double2(o2, o3)));
-        res[0] = o0; res[1] = o1; res[2] = o2; res[3] = o3;
-      }
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));   // results land before the release
-      __syncthreads();
-      if (tid == 0)
-        __hip_atomic_store(p.sync + 32, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      return true;
-    }
-    if (tid == 0) {
+    // thread v polls record v until all eight of its tags are this barrier's
+    double rv[4] = {0.0, 0.0, 0.0, 0.0};
+    if (tid < G) {
       uint32_t spins = 0;
-      while (__hip_atomic_load(p.sync + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+      for (;;) {
+        u32x4 x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          x[k] = __builtin_bit_cast(u32x4, ld_dev4(rrs, (uint32_t)(tid * 64 + k * 16)));
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) all = all && x[k][1] == want && x[k][3] == want;
+        if (all) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            rv[k] = __builtin_bit_cast(double, ((uint64_t)x[k][2] << 32) | x[k][0]);
+          break;
+        }
         __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");   // the next poll reloads the record
         if (++spins >= kQSpinLimit) {
-          ok = 0;
+          set_status(p.status, EAGLE_DEV_TIMEOUT);
+          sh_fail = 1;
           break;
         }
       }
-      if (!ok) set_status(p.status, EAGLE_DEV_TIMEOUT);
-      if (ok) {
-        const double2 x = __builtin_bit_cast(double2, ld_dev4(ors, 0));
-        const double2 y = __builtin_bit_cast(double2, ld_dev4(ors, 16));
-        res[0] = x.x; res[1] = x.y; res[2] = y.x; res[3] = y.y;
-        if (kind == kQScan)
-          sh_before = __builtin_bit_cast(double, ld_dev2(ors, (uint32_t)((8 + w) * 8)));
-      }
-      sh_ok = ok;
     }
     __syncthreads();
-    return sh_ok != 0;
+    if (sh_fail) return false;
+    const bool in = tid < G;
+    if (kind == kQStats) {
+      const double2 mx = q_wg_max2(in ? rv[0] : -INFINITY, in ? rv[2] : -INFINITY, red);
+      const double2 sm = q_wg_sum2(in && rv[1] > 0.0 ? rv[1] * exp_nonpos((rv[0] - mx.x) * p.itemp) : 0.0,
+                                   in && rv[3] > 0.0 ? rv[3] * exp_nonpos((rv[2] - mx.y) * p.itemp) : 0.0,
+                                   red);
+      r[0] = mx.x; r[1] = sm.x; r[2] = mx.y; r[3] = sm.y;
+    } else if (kind == kQSum) {
+      r[0] = q_wg_sum2(in ? rv[0] : 0.0, 0.0, red).x;
+    } else {
+      r[1] = q_wg_max2(in ? rv[1] : -1.0, 0.0, red).x;
+      double tot;
+      const double ex = q_wg_excl_scan(in ? rv[0] : 0.0, red, &tot);
+      if (in) {
+        xb[tid] = ex;
+        xw[tid] = rv[0];
+      }
+      if (tid == 0) xb[G] = tot;
+      r[0] = tot;
+      __syncthreads();
+    }
+    return true;
+  };
+
+  // this chunk of node v's target and draft rows (-inf outside the chunk)
+  auto load_rows = [&](int v, float (&lr)[kQE], float (&dr)[kQE]) __attribute__((always_inline)) {
+    const float* lrow = p.tl + (size_t)v * V;
+    const float* drow = p.dl + (size_t)v * V;
+#pragma unroll
+    for (int e = 0; e < kQE; ++e) {
+      lr[e] = -INFINITY;
+      dr[e] = -INFINITY;
+      if (e < E) {                        // (uniform)
+        const int y = e0 + e;
+        const int yc = min(y, V - 1);
+        const float a = lrow[yc], b = drow[yc];
+        lr[e] = y < c1 ? a : -INFINITY;
+        dr[e] = y < c1 ? b : -INFINITY;
+      }
+    }
   };
 
   double pv[kQE], qv[kQE];
+  double r4[4];
+  float lf[kQE], df[kQE];                 // rows of the visited node
+  float pl[kQE], pd[kQE];                 // rows of its first child, fetched ahead
   int u = 0, depth = 0;
   if (lead && tid == 0) p.path[0] = 0;
+  load_rows(0, lf, df);
   for (;;) {
     const float* lrow = p.tl + (size_t)u * V;
     const float* drow = p.dl + (size_t)u * V;
+    const int first = fc[u];
+    if (first < T) load_rows(first, pl, pd);
+    // the children's logits at their tokens and their uniforms (to LDS
+    // before the next barrier)
+    const bool ischild = tid < T && tid > u && par[tid] == u;
+    float cl = 0.f, cd = 0.f, cu = 0.f, ub = 0.f;
+    if (ischild) {
+      const int x = tk[tid];
+      cl = lrow[x];
+      cd = drow[x];
+      cu = p.U[tid];
+    }
+    if (tid == 0) ub = p.U[T + u];
     // this chunk's row statistics
-    float lf[kQE], df[kQE];
     float ml = -INFINITY, md = -INFINITY;
 #pragma unroll
     for (int e = 0; e < kQE; ++e) {
-      const int y = e0 + e;
-      const bool in = e < E && y < c1;
-      lf[e] = in ? lrow[y] : -INFINITY;
-      df[e] = in ? drow[y] : -INFINITY;
       ml = fmaxf(ml, lf[e]);
       md = fmaxf(md, df[e]);
     }
-    const double wml = q_wg_max((double)ml, red);
-    const double wmd = q_wg_max((double)md, red);
+    const double2 wm = q_wg_max2((double)ml, (double)md, red);
+    // e^((l - m) / t) against the chunk maxima m, kept: p1 and q1 of the
+    // chunk are these times one factor per row once the global maxima are known
     double sp = 0.0, sq = 0.0;
 #pragma unroll
     for (int e = 0; e < kQE; ++e) {
-      if (e < E && e0 + e < c1) {
-        sp += exp_nonpos(((double)lf[e] - wml) * p.itemp);
-        sq += exp_nonpos(((double)df[e] - wmd) * p.itemp);
+      pv[e] = 0.0;
+      qv[e] = 0.0;
+      if (e < E) {                        // (uniform; -inf outside the chunk gives 0)
+        pv[e] = exp_nonpos(((double)lf[e] - wm.x) * p.itemp);
+        qv[e] = exp_nonpos(((double)df[e] - wm.y) * p.itemp);
+        sp += pv[e];
+        sq += qv[e];
       }
     }
-    const double wsp = q_wg_sum(sp, red);
-    const double wsq = q_wg_sum(sq, red);
-    if (!exchange(kQStats, wml, wsp, wmd, wsq)) {
-      alive = false;
-      break;
-    }
-    const double M = res[0], zp = res[1], Md = res[2], zq = res[3];
+    const double2 ws = q_wg_sum2(sp, sq, red);
+    if (ischild) chu[tid] = cu;
+    if (tid == 0) sh_ub = ub;
+    if (!exchange(kQStats, wm.x, ws.x, wm.y, ws.y, r4)) break;
+    const double M = r4[0], zp = r4[1], Md = r4[2], zq = r4[3];
     const double izp = 1.0 / zp;
     const double izq = 1.0 / zq;
-#pragma unroll
-    for (int e = 0; e < kQE; ++e) {
-      const bool in = e < E && e0 + e < c1;
-      pv[e] = in ? exp_nonpos(((double)lf[e] - M) * p.itemp) * izp : 0.0;
-      qv[e] = in ? exp_nonpos(((double)df[e] - Md) * p.itemp) * izq : 0.0;
-    }
-    if (tid == 0) {
-      int n = 0;
-      for (int c = u + 1; c < T; ++c)
-        if (par[c] == u) kid[n++] = c;
-      sh_nk = n;
+    // p1 and q1 of every child at its own token, in parallel
+    if (ischild) {
+      cq1[tid] = exp_nonpos(((double)cd - Md) * p.itemp) * izq;
+      cp1[tid] = exp_nonpos(((double)cl - M) * p.itemp) * izp;
     }
     __syncthreads();
-    const int nk = sh_nk;
+    // children in ascending index; p_i(x), q_i(x) at x alone, replaying this
+    // node's rejections; a rejection forms the residual over the vocabulary
+    // (p1, q1 of this chunk scaled from the kept terms at the first one)
     int nrej = 0;
     double D = 1.0;                          // draft mass not yet rejected at u
     int next = -1;
-    for (int i = 0; i < nk; ++i) {
-      const int c = kid[i];
-      const int x = tk[c];
-      bool seen = false;
-      for (int r = 0; r < nrej; ++r) seen |= rej[r] == x;
-      if (seen) continue;                    // a draw never repeats a token
-      // p_i(x), q_i(x) at x alone, replaying this node's rejections
-      const double q1x = exp_nonpos(((double)drow[x] - Md) * p.itemp) * izq;
-      double px = exp_nonpos(((double)lrow[x] - M) * p.itemp) * izp;
-      for (int r = 0; r < nrej; ++r) px = fmax(px - q1x * hd[r], 0.0) * hz[r];
-      const double iD = D > 0.0 ? 1.0 / D : 0.0;
-      const double qx = q1x * iD;
-      if ((double)p.U[c] * qx < px) {
-        next = c;
-        break;
-      }
-      // rejected: p <- max(p - q, 0) / Z, over the vocabulary (the same
-      // operations as the replay above)
-      double s = 0.0;
+    bool have = false, alive = true;
+    for (int wd = 0; wd < kWords && next < 0 && alive; ++wd) {
+      uint64_t bits = cmask[u][wd];
+      while (bits != 0ull) {
+        const int c = wd * 64 + __builtin_ctzll(bits);
+        bits &= bits - 1ull;
+        const int x = tk[c];
+        bool seen = false;
+        for (int r = 0; r < nrej; ++r) seen |= rej[r] == x;
+        if (seen) continue;                  // a draw never repeats a token
+        const double q1x = cq1[c];
+        double px = cp1[c];
+        for (int r = 0; r < nrej; ++r) px = fmax(px - q1x * hd[r], 0.0) * hz[r];
+        const double iD = D > 0.0 ? 1.0 / D : 0.0;
+        const double qx = q1x * iD;
+        if ((double)chu[c] * qx < px) {
+          next = c;
+          break;
+        }
+        if (!have) {
+          const double fp = exp_nonpos((wm.x - M) * p.itemp) * izp;
+          const double fq = exp_nonpos((wm.y - Md) * p.itemp) * izq;
 #pragma unroll
-      for (int e = 0; e < kQE; ++e) {
-        const double t = fmax(pv[e] - qv[e] * iD, 0.0);
-        pv[e] = t;
-        s += t;
-      }
+          for (int e = 0; e < kQE; ++e) {
+            pv[e] *= fp;
+            qv[e] *= fq;
+          }
+          have = true;
+        }
+        // rejected: p <- max(p - q, 0) / Z over the vocabulary (the same
+        // operations as the replay above)
+        double s = 0.0;
 #pragma unroll
-      for (int e = 0; e < kQE; ++e)
-        if (e0 + e == x) qv[e] = 0.0;        // x leaves q after this step's update
-      const double ws = q_wg_sum(s, red);
-      if (!exchange(kQSum, ws, 0.0, 0.0, 0.0)) {
-        alive = false;
-        break;
-      }
-      const double iz = 1.0 / res[0];
-      if (tid == 0) {
-        hd[nrej] = iD;
-        hz[nrej] = iz;
-        rej[nrej] = x;
-      }
+        for (int e = 0; e < kQE; ++e) {
+          const double t = fmax(pv[e] - qv[e] * iD, 0.0);
+          pv[e] = t;
+          s += t;
+        }
 #pragma unroll
-      for (int e = 0; e < kQE; ++e) pv[e] *= iz;
-      D -= q1x;
-      ++nrej;
-      __syncthreads();
+        for (int e = 0; e < kQE; ++e)
+          if (e0 + e == x) qv[e] = 0.0;      // x leaves q after this step's update
+        const double wsum = q_wg_sum2(s, 0.0, red).x;
+        if (!exchange(kQSum, wsum, 0.0, 0.0, 0.0, r4)) {
+          alive = false;
+          break;
+        }
+        const double iz = 1.0 / r4[0];
+        if (tid == 0) {
+          hd[nrej] = iD;
+          hz[nrej] = iz;
+          rej[nrej] = x;
+        }
+#pragma unroll
+        for (int e = 0; e < kQE; ++e) pv[e] *= iz;
+        D -= q1x;
+        ++nrej;
+        __syncthreads();
+      }
     }
     if (!alive) break;
     if (next >= 0) {
@@ -711,61 +774,78 @@ __global__ __launch_bounds__(kQT) void accept_q_grid_kernel(QGridParams p) {
         if (depth < p.max_path) p.path[depth] = next;
         else set_status(p.status, EAGLE_DEV_PATH_TRUNC);
       }
+      if (next == first) {
+#pragma unroll
+        for (int e = 0; e < kQE; ++e) {
+          lf[e] = pl[e];
+          df[e] = pd[e];
+        }
+      } else {
+        load_rows(next, lf, df);
+      }
       u = next;
+      __syncthreads();                       // cp1 / cq1 / chu are reused
       continue;
     }
     // bonus: the smallest token whose running sum of p exceeds U[T + u] sum(p)
+    if (!have) {
+      const double fp = exp_nonpos((wm.x - M) * p.itemp) * izp;
+#pragma unroll
+      for (int e = 0; e < kQE; ++e) pv[e] *= fp;
+    }
     double own = 0.0;
+    int last = -1, lastm = -1;
 #pragma unroll
-    for (int e = 0; e < kQE; ++e) own += pv[e];
-    // exclusive prefix of the threads' sums, in thread order
-    __shared__ double tsum[kQT];
-    tsum[tid] = own;
-    __syncthreads();
-    if (tid == 0) {
-      double run = 0.0;
-      for (int t = 0; t < kQT; ++t) {
-        const double nx = run + tsum[t];
-        tsum[t] = run;
-        run = nx;
+    for (int e = 0; e < kQE; ++e) {
+      own += pv[e];
+      if (pv[e] > 0.0) {
+        last = e0 + e;
+        lastm = e;
       }
-      red[0] = run;
     }
-    __syncthreads();
-    const double wtot = red[0];
-    const double tpre = tsum[tid];
-    int last = -1;
+    double wtot;
+    const double tpre = q_wg_excl_scan(own, red, &wtot);
+    const double lastc = q_wg_max2((double)last, 0.0, red).x;
+    if (!exchange(kQScan, wtot, lastc, 0.0, 0.0, r4)) break;
+    const double total = r4[0];
+    const int lastall = (int)r4[1];
+    const double target = (double)sh_ub * total;
+    // The running sums split [0, total) into consecutive intervals: chunk v
+    // holds [xb[v], xb[v + 1]), thread t of it [tb[t], tb[t + 1]), and the
+    // entries of a thread follow in token order.  The crossing belongs to
+    // the first chunk (and in it the first thread) with mass whose interval
+    // ends above target: every workgroup finds the same chunk, and only that
+    // one searches.  With target >= total (rounding) it is the last token
+    // with mass.
+    if (target < total) {
+      const bool cl = tid < G && xw[tid] > 0.0 && xb[tid + 1] > target;
+      const int owner = kQT - (int)q_wg_max2(cl ? (double)(kQT - tid) : 0.0, 0.0, red).x;
+      if (owner == w) {
+        tb[tid] = tid == 0 ? xb[w] : fmin(xb[w] + tpre, xb[w + 1]);
+        if (tid == 0) tb[kQT] = xb[w + 1];
+        __syncthreads();
+        const bool tc = own > 0.0 && tb[tid + 1] > target;
+        const int first = kQT - (int)q_wg_max2(tc ? (double)(kQT - tid) : 0.0, 0.0, red).x;
+        if (tid == first) {
+          const double end = tb[tid + 1];
+          double run = tb[tid];
+          int hit = -1;
 #pragma unroll
-    for (int e = 0; e < kQE; ++e)
-      if (pv[e] > 0.0) last = e0 + e;
-    last = (int)q_wg_max((double)last, red);
-    if (!exchange(kQScan, wtot, (double)last, 0.0, 0.0)) {
-      alive = false;
-      break;
-    }
-    const double total = res[0];
-    const int lastall = (int)res[1];
-    const double before = sh_before;
-    const double target = (double)p.U[T + u] * total;
-    // Chunk boundaries are consistent (each chunk starts where the previous
-    // one's prefix ends), so exactly one chunk holds the crossing when
-    // target < total; it reports the first of its tokens whose running sum
-    // exceeds target (the last token of the chunk with mass if rounding
-    // inside the chunk leaves none).  Otherwise rounding left no crossing at
-    // all: the last token with mass.
-    if (target < total && before <= target && target < before + wtot) {
-      int hit = 0x7fffffff;
-      double run = before + tpre;
-#pragma unroll
-      for (int e = 0; e < kQE; ++e) {
-        const double nx = run + pv[e];
-        if (hit == 0x7fffffff && e < E && e0 + e < c1 && nx > target) hit = e0 + e;
-        run = nx;
+          for (int e = 0; e < kQE; ++e) {
+            if (hit < 0 && pv[e] > 0.0) {
+              const double nx = e == lastm ? end : fmin(run + pv[e], end);
+              if (nx > target) hit = e0 + e;
+              run = nx;
+            }
+          }
+          p.bonus[0] = hit >= 0 ? hit : e0 + lastm;
+        } else if (first >= kQT && tid == 0) {
+          p.bonus[0] = max(lastall, 0);       // (no thread with mass claimed it)
+        }
+      } else if (owner >= kQT && lead && tid == 0) {
+        p.bonus[0] = max(lastall, 0);         // (no chunk with mass claimed it)
       }
-      hit = -(int)q_wg_max(-(double)hit, red);    // lowest in the workgroup
-      if (hit == 0x7fffffff) hit = max(last, 0);
-      if (tid == 0) p.bonus[0] = hit;
-    } else if (!(target < total) && lead && tid == 0) {
+    } else if (lead && tid == 0) {
       p.bonus[0] = max(lastall, 0);
     }
     if (lead && tid == 0) {
@@ -774,10 +854,9 @@ __global__ __launch_bounds__(kQT) void accept_q_grid_kernel(QGridParams p) {
     }
     break;
   }
-  // a new generation for the next call: its flags never match this call's
+  // a new generation for the next call: its records never match this call's
   if (lead && tid == 0)
     __hip_atomic_store(p.sync, (gen + 1) & 0x1fffff, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  (void)alive;
 }
 
 }  // namespace eagle
@@ -840,8 +919,7 @@ static int q_device_cus() {
 
 extern "C" size_t eagle_accept_q_workspace(int32_t T, int32_t V) {
   if (T < 1 || V < 1) return 0;
-  return 2048 + (size_t)2 * eagle::kQG * 4 * sizeof(double) +
-         (size_t)2 * (8 + eagle::kQG) * sizeof(double);
+  return 256 + (size_t)2 * eagle::kQG * 8 * sizeof(uint64_t);
 }
 
 extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_t* node_parent,
@@ -856,7 +934,10 @@ extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_
   EAGLE_REQUIRE(temperature > 0.0f && temperature <= 3.0e38f, EAGLE_EINVAL);
   EAGLE_REQUIRE(workspace && ((uintptr_t)workspace & 255) == 0, EAGLE_EINVAL);
   EAGLE_REQUIRE(ws_bytes >= eagle_accept_q_workspace(T, V), EAGLE_EWORKSPACE);
-  const int G = std::min(eagle::kQG, q_device_cus());
+  // 128 workgroups while they can hold the vocabulary (fewer records to
+  // gather at every barrier), all CUs beyond that
+  const int G = std::min(V <= eagle::kQG / 2 * eagle::kQT * eagle::kQE ? eagle::kQG / 2 : eagle::kQG,
+                         q_device_cus());
   const int C = (V + G - 1) / G;
   const int E = (C + eagle::kQT - 1) / eagle::kQT;
   EAGLE_REQUIRE(E <= eagle::kQE, EAGLE_EUNSUPPORTED);
@@ -866,9 +947,8 @@ extern "C" int eagle_accept_q(int32_t T, const int32_t* node_token, const int32_
   p.itemp = 1.0 / (double)temperature;
   p.U = uniforms; p.max_path = max_path; p.path = path; p.n_acc = n_accepted;
   p.bonus = bonus_token; p.status = dev_status;
-  p.sync = (int32_t*)workspace;                                  // 64 + kQG ints
-  p.rec = (double*)((char*)workspace + 2048);                    // [2][G][4]
-  p.res = p.rec + 2 * eagle::kQG * 4;                            // [2][8 + G]
+  p.sync = (int32_t*)workspace;                                  // generation
+  p.rec = (uint64_t*)((char*)workspace + 256);                   // [2][G][8]
   hipLaunchKernelGGL(eagle::accept_q_grid_kernel, dim3(G), dim3(eagle::kQT), 0, stream, p);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;

@@ -305,8 +305,8 @@ def test_logits_process_argument_errors(lib):
 
 def test_accept_q_argument_errors(lib):
     f = lib.eagle_accept_q
-    # barrier flags, two record slots of 256 workgroups x 4 doubles, two result slots
-    assert lib.eagle_accept_q_workspace(64, 128256) == 2048 + 2 * 256 * 4 * 8 + 2 * (8 + 256) * 8
+    # generation word, two record slots of 256 workgroups x 8 tagged 64-bit words
+    assert lib.eagle_accept_q_workspace(64, 128256) == 256 + 2 * 256 * 8 * 8
     assert lib.eagle_accept_q_workspace(64, 0) == 0 and lib.eagle_accept_q_workspace(0, 10) == 0
     need = lib.eagle_accept_q_workspace(8, 100)
     ok = [8, FAKE, FAKE, FAKE, FAKE, 100, 1.0, FAKE, 8, FAKE, FAKE, FAKE, FAKE, need, None, None]
