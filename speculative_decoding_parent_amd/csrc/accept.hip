@@ -626,20 +626,21 @@ __global__ __launch_bounds__(kQT) void accept_q_grid_kernel(QGridParams p) {
     return true;
   };
 
-  // this chunk of node v's target and draft rows (-inf outside the chunk)
+  // this chunk of node v's target and draft rows; entries outside the chunk
+  // (in[e] false) load a valid address and are read as -inf by the users, so
+  // the loads stay in flight until then
+  bool in[kQE];
+#pragma unroll
+  for (int e = 0; e < kQE; ++e) in[e] = e < E && e0 + e < c1;
   auto load_rows = [&](int v, float (&lr)[kQE], float (&dr)[kQE]) __attribute__((always_inline)) {
     const float* lrow = p.tl + (size_t)v * V;
     const float* drow = p.dl + (size_t)v * V;
 #pragma unroll
     for (int e = 0; e < kQE; ++e) {
-      lr[e] = -INFINITY;
-      dr[e] = -INFINITY;
       if (e < E) {                        // (uniform)
-        const int y = e0 + e;
-        const int yc = min(y, V - 1);
-        const float a = lrow[yc], b = drow[yc];
-        lr[e] = y < c1 ? a : -INFINITY;
-        dr[e] = y < c1 ? b : -INFINITY;
+        const int yc = min(e0 + e, V - 1);
+        lr[e] = lrow[yc];
+        dr[e] = drow[yc];
       }
     }
   };
@@ -671,8 +672,12 @@ __global__ __launch_bounds__(kQT) void accept_q_grid_kernel(QGridParams p) {
     float ml = -INFINITY, md = -INFINITY;
 #pragma unroll
     for (int e = 0; e < kQE; ++e) {
-      ml = fmaxf(ml, lf[e]);
-      md = fmaxf(md, df[e]);
+      if (e < E) {                        // (uniform)
+        lf[e] = in[e] ? lf[e] : -INFINITY;
+        df[e] = in[e] ? df[e] : -INFINITY;
+        ml = fmaxf(ml, lf[e]);
+        md = fmaxf(md, df[e]);
+      }
     }
     const double2 wm = q_wg_max2((double)ml, (double)md, red);
     // e^((l - m) / t) against the chunk maxima m, kept: p1 and q1 of the
