@@ -11,8 +11,13 @@
 // HBM once.  Design:
 //   * MFMA v_mfma_f32_16x16x32_bf16 with W rows as the M dimension (16 rows per
 //     tile, 8 or 4 tiles = 128 or 64 rows per wave, 4 waves per workgroup) and the
-//     feature rows as N (16 per tile, NT tiles).  W goes straight from HBM into
-//     MFMA A operands (the shared weight-streaming core, wstream.h).
+//     feature rows as N (16 per tile, NT tiles), from the shared weight-streaming
+//     core (wstream.h).  With 8 tiles per wave W is read in runs of 256 bytes
+//     per row with non-temporal loads and passed through a wave-private LDS tile
+//     into the operand layout (6.0 against 5.5 TB/s at T = 10 for W read
+//     straight into operands, 16 rows x 64 bytes per load instruction); with 4
+//     tiles the LDS it would need leaves one workgroup per CU, so W goes
+//     straight into A operands.
 //   * f is shared by all workgroups (<= 512 KB at T = 64): each 128-wide k
 //     slice is staged once per workgroup in LDS (double-buffered, rows padded
 //     by 16 bytes so the 16 lanes of a b128 read hit distinct banks).
@@ -98,7 +103,25 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
     for (int q = q0; q < p.in.parts; q += rows16 ? 16 : 1) in_ss += p.in.ssq[(size_t)q * p.T + rm];
 
   f32x4 acc[kLmMT][NT];
-  wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
+  if constexpr (kLmMT == 8) {
+    // row-run loads through a wave-private LDS tile while W fits one buffer
+    // range (31-bit byte offsets)
+    __shared__ __attribute__((aligned(16))) char wlds[kLmWaves][kLmMT * 4096];
+    if ((size_t)p.V * p.d * sizeof(bf16_t) <= 0x7fffffffull) {
+      int trow[kLmMT], wsel[kLmMT];
+#pragma unroll
+      for (int mt = 0; mt < kLmMT; ++mt) {
+        trow[mt] = v0 + mt * 16;
+        wsel[mt] = 0;
+      }
+      wstream_mfma_rr<NT, kLmMT>(p.W, nullptr, p.V, trow, wsel, p.f, p.d, p.T, p.d, fs,
+                                 wlds[wave], acc);
+    } else {
+      wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
+    }
+  } else {
+    wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
+  }
 
   if (p.in.ssq) {
     if (rows16) {

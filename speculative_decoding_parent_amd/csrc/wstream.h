@@ -125,4 +125,120 @@ __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], co
   }
 }
 
+
+// Row-run variant: each 16-byte load instruction of a wave covers 4 weight
+// rows x 256 contiguous bytes (lane l: row 4 i + l / 16 of the tile, bytes
+// 16 (l % 16) of the k step), issued with the non-temporal policy; the wave
+// then passes the step through a private LDS tile (rows of 256 bytes, 16-byte
+// chunks XOR-swizzled by row so that both the writes and the operand reads
+// touch 64 distinct banks per 16 lanes) to reach the MFMA operand layout.
+// tile_row0[mt]: first weight row of tile mt (rows past the buffer read zero);
+// wsel[mt]: 0 -> matrix w0, 1 -> w1; nrows: rows per matrix.  wl: MT x 4 KB of
+// LDS private to the wave.
+constexpr int kNtPolicy = 1 << 1;    // buffer cache policy bit: nt
+
+template <int NT, int MT>
+__device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* w1, int nrows,
+                                                const int (&tile_row0)[MT], const int (&wsel)[MT],
+                                                const bf16_t* X, int ldx, int M, int K,
+                                                bf16_t* fs, char* wl, f32x4 (&acc)[MT][NT]) {
+  constexpr int TP = 16 * NT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  bf16_t* fs0 = fs;
+  bf16_t* fs1 = fs + TP * kWsLds;
+  const size_t mbytes = (size_t)nrows * K * sizeof(bf16_t);
+  const __amdgpu_buffer_rsrc_t rs0 = buf_rsrc(w0, mbytes);
+  const __amdgpu_buffer_rsrc_t rs1 = buf_rsrc(w1 ? w1 : w0, mbytes);
+  // byte offset of this lane's run in instruction 0 of each tile; instruction
+  // i adds 4 i rows, step kk adds 256 kk bytes
+  uint32_t voff[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    voff[mt] = (uint32_t)((size_t)(tile_row0[mt] + g) * K * sizeof(bf16_t)) + r16 * 16;
+  const uint32_t istride = 4u * K * sizeof(bf16_t);
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_x = [&](int kk, u32x4 (&fr)[NT]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      const int row = c >> 4;
+      const int col = (c & 15) * 8;
+      fr[j] = row < M ? *(const u32x4*)(X + (size_t)row * ldx + kk * kWsKG + col)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_x = [&](bf16_t* buf, const u32x4 (&fr)[NT]) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int c = tid + 256 * j;
+      *(u32x4*)(&buf[(c >> 4) * kWsLds + (c & 15) * 8]) = fr[j];
+    }
+  };
+  auto load_w = [&](int kk, u32x4 (&wr)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wr[mt][i] = __builtin_amdgcn_raw_buffer_load_b128(wsel[mt] ? rs1 : rs0, voff[mt],
+                                                          (uint32_t)(i * istride + kk * 256),
+                                                          kNtPolicy);
+  };
+  // instruction i's lane l holds row 4 i + g, chunk r16
+  auto put_w = [&](const u32x4 (&wr)[MT][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + g;
+        *(u32x4*)(wl + mt * 4096 + row * 256 + ((r16 ^ row) << 4)) = wr[mt][i];
+      }
+  };
+  auto compute = [&](const bf16_t* fb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8 b[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        b[nt] = *(const bf16x8*)(fb + (nt * 16 + r16) * kWsLds + i * 32 + g * 8);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a = *(const bf16x8*)(wl + mt * 4096 + r16 * 256 + (((4 * i + g) ^ r16) << 4));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nk = K / kWsKG;
+  u32x4 wr[MT][4];
+  u32x4 fr[NT];
+  load_x(0, fr);
+  load_w(0, wr);
+  store_x(fs0, fr);
+  put_w(wr);
+  __syncthreads();
+  for (int kk = 0; kk < nk; ++kk) {
+    const bool more = kk + 1 < nk;
+    if (more) {
+      load_x(kk + 1, fr);
+      load_w(kk + 1, wr);
+    }
+    compute((kk & 1) ? fs1 : fs0);
+    if (more) {
+      store_x((kk & 1) ? fs0 : fs1, fr);
+      put_w(wr);     // (after this wave's operand reads of step kk: LDS keeps a wave's order)
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace eagle
