@@ -505,9 +505,10 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 // Projections of M <= 16 activation rows (the draft rounds) run as ONE kernel
 // each, epilogue included.  A workgroup owns 64 weight rows (4 MFMA tiles of
 // 16) and a range of 128-wide k steps; its four waves take interleaved steps of
-// that range, each streaming W straight from HBM into MFMA A operands and the
-// activation rows straight from L2 into B operands (no LDS staging and no
-// barrier in the loop), and the four wave tiles are added in LDS.  A column
+// that range, each streaming W from HBM in 256-byte row runs (non-temporal)
+// through a wave-private LDS tile into MFMA A operands, and the activation
+// rows straight from L2 into B operands (no barrier in the loop); the four
+// wave tiles are added in LDS.  A column
 // block's k range is split over S workgroups so that ~256 are in flight; each
 // writes its fp32 tile to the workspace and the last one to arrive (a
 // per-column-block counter) sums the S tiles in range order, so the result
@@ -567,7 +568,9 @@ __device__ __forceinline__ int sk_wrow(const SkParams& p, int xb, int mt) {
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
-  __shared__ f32x4 red[4][kSkMT][64];
+  // a wave's k step of W (row runs, see below); after the loop each wave's
+  // first 4 KB hold its tiles for the sum over the waves
+  __shared__ __attribute__((aligned(16))) char wlds[4][kSkMT * 4096];
   __shared__ float ssl[4][kSkMaxRows];
   __shared__ float rsc[kSkMaxRows];
   __shared__ double sinv[MODE == SK_ROPE ? kRopeMaxHalf : 1];
@@ -588,13 +591,24 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
   if (p.in.ssq && rm < M)
     for (int q = q0; q < p.in.parts; q += 16) in_ss += p.in.ssq[(size_t)q * M + rm];
 
-  const bf16_t* wr[kSkMT];
+  // W is read in runs of 256 bytes per row with non-temporal loads (load
+  // instruction i of tile mt: lane l takes row 4 i + l / 16 of the tile, bytes
+  // 16 (l % 16) of the k step) and passed through the wave's LDS tile into the
+  // MFMA operand layout.  Buffer ranges start at the workgroup's first row of
+  // each matrix (rows past N read zero).
+  const int wrow0 = sk_wrow<MODE>(p, xb, 0);
+  const int wspan = MODE == SK_ROPE ? p.rope.hd : 64;
+  const int wrows = max(0, min(wspan, N - wrow0));
+  const size_t wbytes = (size_t)wrows * K * sizeof(bf16_t);
+  const __amdgpu_buffer_rsrc_t wrs0 = buf_rsrc(p.w0 + (size_t)wrow0 * K, wbytes);
+  const __amdgpu_buffer_rsrc_t wrs1 =
+      buf_rsrc((MODE == SK_SWIGLU ? p.w1 : p.w0) + (size_t)wrow0 * K, wbytes);
+  uint32_t wvo[kSkMT];
 #pragma unroll
-  for (int mt = 0; mt < kSkMT; ++mt) {
-    const bf16_t* w = (MODE == SK_SWIGLU && mt >= 2) ? p.w1 : p.w0;
-    const int row = min(sk_wrow<MODE>(p, xb, mt) + r16, N - 1);   // N rows per matrix
-    wr[mt] = w + (size_t)row * K + g * 8;
-  }
+  for (int mt = 0; mt < kSkMT; ++mt)
+    wvo[mt] = (uint32_t)((sk_wrow<MODE>(p, xb, mt) - wrow0 + g) * K * sizeof(bf16_t)) + r16 * 16;
+  const uint32_t wistride = 4u * K * sizeof(bf16_t);
+  char* wl = wlds[wave];
   const bool xok = r16 < M;
   const int xrow = min(r16, M - 1);
   const bf16_t* xr = p.x + (size_t)xrow * K + g * 8;
@@ -619,16 +633,29 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
 #pragma unroll
     for (int mt = 0; mt < kSkMT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[mt][i] = *(const u32x4*)(wr[mt] + kk * kWsKG + i * 32);
+      for (int i = 0; i < 4; ++i)
+        w[mt][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            (MODE == SK_SWIGLU && mt >= 2) ? wrs1 : wrs0, wvo[mt],
+            (uint32_t)(i * wistride + kk * kWsKG * sizeof(bf16_t)), kNtPolicy);
   };
   auto compute = [&](const u32x4 (&w)[kSkMT][4], const u32x4 (&xv)[4]) {
+    // to the operand layout: row r of a tile at r * 256, 16-byte chunk c at
+    // (c ^ r) * 16 (64 distinct banks per 16 lanes, writes and reads alike)
+#pragma unroll
+    for (int mt = 0; mt < kSkMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * i + g;
+        *(u32x4*)(wl + mt * 4096 + row * 256 + ((r16 ^ row) << 4)) = w[mt][i];
+      }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bf16x8 b = ws_as_bf16x8(xv[i]);
 #pragma unroll
-      for (int mt = 0; mt < kSkMT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ws_as_bf16x8(w[mt][i]), b, acc[mt], 0,
-                                                          0, 0);
+      for (int mt = 0; mt < kSkMT; ++mt) {
+        const bf16x8 a = *(const bf16x8*)(wl + mt * 4096 + r16 * 256 + (((4 * i + g) ^ r16) << 4));
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mt], 0, 0, 0);
+      }
     }
   };
   int kk = kb + wave;
@@ -646,8 +673,13 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
   in_ss += dpp_move<kDppRowMirror>(in_ss);
   if (q0 == 0 && rm < M)
     rsc[rm] = p.in.ssq ? 1.0f / sqrtf(in_ss / (float)p.in.n + p.in.eps) : 1.0f;
+  // each wave's tiles go to the start of its own LDS tile (no other wave reads
+  // that tile), then every wave reads all four
+  auto redp = [&](int w, int mt) -> f32x4* {
+    return (f32x4*)(wlds[w]) + mt * 64;
+  };
 #pragma unroll
-  for (int mt = 0; mt < kSkMT; ++mt) red[wave][mt][lane] = acc[mt];
+  for (int mt = 0; mt < kSkMT; ++mt) redp(wave, mt)[lane] = acc[mt];
   __syncthreads();
 
   // tiles finished by this wave: one (plain, ressq) or a (first, second) pair
@@ -655,14 +687,14 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
   const bool owner = kPair ? wave < 2 : true;
   const int ta = wave, tb = wave + 2;
   const int m = r16;
-  f32x4 ya = red[0][ta & 3][lane] + red[1][ta & 3][lane];
-  ya = ya + red[2][ta & 3][lane];
-  ya = ya + red[3][ta & 3][lane];
+  f32x4 ya = redp(0, ta & 3)[lane] + redp(1, ta & 3)[lane];
+  ya = ya + redp(2, ta & 3)[lane];
+  ya = ya + redp(3, ta & 3)[lane];
   f32x4 yb2 = f32x4{0.f, 0.f, 0.f, 0.f};
   if (kPair) {
-    yb2 = red[0][tb & 3][lane] + red[1][tb & 3][lane];
-    yb2 = yb2 + red[2][tb & 3][lane];
-    yb2 = yb2 + red[3][tb & 3][lane];
+    yb2 = redp(0, tb & 3)[lane] + redp(1, tb & 3)[lane];
+    yb2 = yb2 + redp(2, tb & 3)[lane];
+    yb2 = yb2 + redp(3, tb & 3)[lane];
   }
   if (p.S > 1) {
     const __amdgpu_buffer_rsrc_t rpart =
