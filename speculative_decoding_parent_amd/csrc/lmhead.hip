@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
         trow[mt] = v0 + mt * 16;
         wsel[mt] = 0;
       }
-      wstream_mfma_rr<NT, kLmMT>(p.W, nullptr, p.V, trow, wsel, p.f, p.d, p.T, p.d, fs,
+      wstream_mfma_rr<NT, kLmMT>(p.W, nullptr, p.V, p.d, trow, wsel, p.f, p.d, p.T, p.d, fs,
                                  wlds[wave], acc);
     } else {
       wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);

@@ -133,15 +133,17 @@ __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], co
 // chunks XOR-swizzled by row so that both the writes and the operand reads
 // touch 64 distinct banks per 16 lanes) to reach the MFMA operand layout.
 // tile_row0[mt]: first weight row of tile mt (rows past the buffer read zero);
-// wsel[mt]: 0 -> matrix w0, 1 -> w1; nrows: rows per matrix.  wl: MT x 4 KB of
-// LDS private to the wave.
+// wsel[mt]: 0 -> matrix w0, 1 -> w1; nrows rows of ldw elements per matrix,
+// w0 / w1 / X pointing at the first k of the range (K wide, K % 128 == 0);
+// nrows * ldw * 2 < 2^31.  wl: MT x 4 KB of LDS private to the wave.
 constexpr int kNtPolicy = 1 << 1;    // buffer cache policy bit: nt
 
 template <int NT, int MT>
 __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* w1, int nrows,
-                                                const int (&tile_row0)[MT], const int (&wsel)[MT],
-                                                const bf16_t* X, int ldx, int M, int K,
-                                                bf16_t* fs, char* wl, f32x4 (&acc)[MT][NT]) {
+                                                int ldw, const int (&tile_row0)[MT],
+                                                const int (&wsel)[MT], const bf16_t* X, int ldx,
+                                                int M, int K, bf16_t* fs, char* wl,
+                                                f32x4 (&acc)[MT][NT]) {
   constexpr int TP = 16 * NT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -149,7 +151,7 @@ __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* 
   const int r16 = lane & 15;
   bf16_t* fs0 = fs;
   bf16_t* fs1 = fs + TP * kWsLds;
-  const size_t mbytes = (size_t)nrows * K * sizeof(bf16_t);
+  const size_t mbytes = (size_t)nrows * ldw * sizeof(bf16_t);
   const __amdgpu_buffer_rsrc_t rs0 = buf_rsrc(w0, mbytes);
   const __amdgpu_buffer_rsrc_t rs1 = buf_rsrc(w1 ? w1 : w0, mbytes);
   // byte offset of this lane's run in instruction 0 of each tile; instruction
@@ -157,8 +159,8 @@ __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* 
   uint32_t voff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    voff[mt] = (uint32_t)((size_t)(tile_row0[mt] + g) * K * sizeof(bf16_t)) + r16 * 16;
-  const uint32_t istride = 4u * K * sizeof(bf16_t);
+    voff[mt] = (uint32_t)((size_t)(tile_row0[mt] + g) * ldw * sizeof(bf16_t)) + r16 * 16;
+  const uint32_t istride = 4u * ldw * sizeof(bf16_t);
 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
