@@ -590,10 +590,12 @@ def main():
                                   f"V={w.vocab}, draft distribution from draft logits",
                         "avg_us": round(aq_us, 1), "accepted": int(q_out[1].item()),
                         "timing": "HIP graph of 5 back-to-back calls, replayed 3 times",
-                        "note": "one launch of up to 256 workgroups, each owning a slice of the "
-                                "vocabulary, walks the tree together, meeting at a coordinated "
-                                "grid barrier only for sums over the vocabulary (row statistics "
-                                "of a visited node, a rejection's residual mass, the bonus draw)"}
+                        "note": "one launch of 128 workgroups (256 beyond 262144 tokens), each "
+                                "owning a slice of the vocabulary, walks the tree together and "
+                                "meets only for sums over the vocabulary (row statistics of a "
+                                "visited node, a rejection's residual mass, the bonus draw), each "
+                                "meeting an all-gather of tagged records that every workgroup "
+                                "combines in the same order"}
     del tl, dlq
     # Eagle-3 fusion of the accepted path's three recorded hidden states
     # (8 rows: root + 7 accepted at the tree's depth bound), d = 4096 -> 4096
