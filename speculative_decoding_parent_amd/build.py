@@ -29,9 +29,15 @@ SOURCES = ["mask.hip", "tree.hip", "accept.hip", "lmhead.hip", "attn.hip", "laye
            "status.hip"]
 
 
+# Per-source options.  lmhead.hip: MFMA results in VGPR form, with AGPRs as
+# spill space (the 8-tile LM head at 32 < T <= 64 holds 128 accumulators next
+# to a k step of W; the default form spills 136 registers to memory).
+SOURCE_FLAGS = {"lmhead.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -44,15 +44,17 @@ constexpr int kLmBlockK = 16;
 static_assert(2 * 16 * kWsLds * 2 >= 4 * 16 * (kLmBlockK + 1) * 8, "lists exceed staging LDS");
 static_assert(sizeof(selkey_t) == 8, "key size");
 
-// W tiles of 16 rows per wave: 8 (128 rows, one 4-wave workgroup per CU) while
-// the feature rows fit two MFMA tiles, which keeps the most weight bytes in
-// flight per wave; fewer as more feature rows need accumulator registers (no
-// spills up to T = 256).  At 32 < T <= 64 four tiles give 501 workgroups for
-// V = 128256, one wave of workgroups at two per CU (eight tiles would spill).
-// Measured at V = 128256, d = 4096: T = 32 takes 197 us with eight tiles and
-// 243 us with four.
+// W tiles of 16 rows per wave: 8 (128 rows, one 4-wave workgroup per CU) up to
+// T = 64, which keeps the most weight bytes in flight per wave; fewer as more
+// feature rows need accumulator registers.  Eight tiles at 32 < T <= 64 fit
+// because W then passes through registers one k step at a time (row runs,
+// wstream_mfma_rr) and the accumulators may live in AGPRs (this file is built
+// with the MFMA results in VGPR form, spilling to AGPRs: none to memory).
+// Measured at V = 128256, d = 4096: T = 32 takes 197 us with eight tiles
+// straight into operands and 243 us with four; T = 64 with logits 268 us with
+// four tiles and 213 us with eight in row runs.
 __host__ __device__ constexpr int lm_mt(int T) {
-  return T <= 32 ? 8 : (T <= 64 ? 4 : (T <= 128 ? 2 : 1));
+  return T <= 64 ? 8 : (T <= 128 ? 2 : 1);
 }
 
 // The feature-row tiles a launch is compiled for (1, 2, 4, 8 or 16 of 16 rows).
@@ -77,7 +79,11 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
     LmParams p) {
   constexpr int kLmRowsWave = 16 * kLmMT;
   constexpr int kLmRowsBlock = kLmRowsWave * kLmWaves;
-  __shared__ __attribute__((aligned(16))) bf16_t fs[ws_lds_elems<NT>()];
+  // (8 W tiles with 4 or more feature tiles: one activation buffer, so that
+  // the W tiles of the row-run path fit)
+  constexpr bool kXSingle = kLmMT == 8 && NT >= 4;
+  __shared__ __attribute__((aligned(16))) bf16_t fs[kXSingle ? ws_lds_elems<NT>() / 2
+                                                             : ws_lds_elems<NT>()];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -103,22 +109,18 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
     for (int q = q0; q < p.in.parts; q += rows16 ? 16 : 1) in_ss += p.in.ssq[(size_t)q * p.T + rm];
 
   f32x4 acc[kLmMT][NT];
+  // W tiles of the row-run path; after the main loop, the epilogue's lists
+  __shared__ __attribute__((aligned(16))) char wlds[kLmMT == 8 ? kLmWaves : 1][kLmMT * 4096];
   if constexpr (kLmMT == 8) {
-    // row-run loads through a wave-private LDS tile while W fits one buffer
-    // range (31-bit byte offsets)
-    __shared__ __attribute__((aligned(16))) char wlds[kLmWaves][kLmMT * 4096];
-    if ((size_t)p.V * p.d * sizeof(bf16_t) <= 0x7fffffffull) {
-      int trow[kLmMT], wsel[kLmMT];
+    // row-run loads through a wave-private LDS tile
+    int trow[kLmMT], wsel[kLmMT];
 #pragma unroll
-      for (int mt = 0; mt < kLmMT; ++mt) {
-        trow[mt] = v0 + mt * 16;
-        wsel[mt] = 0;
-      }
-      wstream_mfma_rr<NT, kLmMT>(p.W, nullptr, p.V, p.d, trow, wsel, p.f, p.d, p.T, p.d, fs,
-                                 wlds[wave], acc);
-    } else {
-      wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
+    for (int mt = 0; mt < kLmMT; ++mt) {
+      trow[mt] = v0 + mt * 16;
+      wsel[mt] = 0;
     }
+    wstream_mfma_rr<NT, kLmMT, kXSingle>(p.W, nullptr, p.V, p.d, trow, wsel, p.f, p.d, p.T, p.d,
+                                         fs, wlds[wave], acc);
   } else {
     wstream_mfma<NT, kLmMT>(wrow, p.f, p.d, p.T, p.d, fs, acc);
   }
@@ -208,7 +210,9 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
   // workgroup; otherwise every wave writes its own.
   const bool block_lists = p.k <= kLmBlockK;
   constexpr int TP = 16 * NT;
-  selkey_t* lk = (selkey_t*)fs;                 // [4][TP][k]
+  static_assert(kLmMT != 8 || kLmWaves * kLmMT * 4096 >= 4 * TP * (kLmBlockK + 1) * 8,
+                "lists exceed the W tiles' LDS");
+  selkey_t* lk = kLmMT == 8 ? (selkey_t*)&wlds[0][0] : (selkey_t*)fs;   // [4][TP][k]
   float2* ls = (float2*)(lk + 4 * TP * p.k);    // [4][TP]
   const int nb = block_lists ? gridDim.x : gridDim.x * kLmWaves;
   const int list = block_lists ? blockIdx.x : wglob;

@@ -132,13 +132,16 @@ __device__ __forceinline__ void wstream_mfma(const bf16_t* const (&wrow)[MT], co
 // then passes the step through a private LDS tile (rows of 256 bytes, 16-byte
 // chunks XOR-swizzled by row so that both the writes and the operand reads
 // touch 64 distinct banks per 16 lanes) to reach the MFMA operand layout.
-// tile_row0[mt]: first weight row of tile mt (rows past the buffer read zero);
+// tile_row0[mt]: first weight row of tile mt (rows past nrows read zero: each
+// tile has its own buffer range, so offsets stay small at any matrix size);
 // wsel[mt]: 0 -> matrix w0, 1 -> w1; nrows rows of ldw elements per matrix,
-// w0 / w1 / X pointing at the first k of the range (K wide, K % 128 == 0);
-// nrows * ldw * 2 < 2^31.  wl: MT x 4 KB of LDS private to the wave.
+// w0 / w1 / X pointing at the first k of the range (K wide, K % 128 == 0).
+// wl: MT x 4 KB of LDS private to the wave.
 constexpr int kNtPolicy = 1 << 1;    // buffer cache policy bit: nt
 
-template <int NT, int MT>
+// XSINGLE: one activation buffer instead of two (half the LDS; one more
+// barrier per k step).
+template <int NT, int MT, bool XSINGLE = false>
 __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* w1, int nrows,
                                                 int ldw, const int (&tile_row0)[MT],
                                                 const int (&wsel)[MT], const bf16_t* X, int ldx,
@@ -151,15 +154,16 @@ __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* 
   const int r16 = lane & 15;
   bf16_t* fs0 = fs;
   bf16_t* fs1 = fs + TP * kWsLds;
-  const size_t mbytes = (size_t)nrows * ldw * sizeof(bf16_t);
-  const __amdgpu_buffer_rsrc_t rs0 = buf_rsrc(w0, mbytes);
-  const __amdgpu_buffer_rsrc_t rs1 = buf_rsrc(w1 ? w1 : w0, mbytes);
-  // byte offset of this lane's run in instruction 0 of each tile; instruction
-  // i adds 4 i rows, step kk adds 256 kk bytes
-  uint32_t voff[MT];
+  __amdgpu_buffer_rsrc_t trs[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    voff[mt] = (uint32_t)((size_t)(tile_row0[mt] + g) * ldw * sizeof(bf16_t)) + r16 * 16;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int rows = max(0, min(16, nrows - tile_row0[mt]));
+    trs[mt] = buf_rsrc((wsel[mt] ? w1 : w0) + (size_t)tile_row0[mt] * ldw,
+                       (size_t)rows * ldw * sizeof(bf16_t));
+  }
+  // byte offset of this lane's run in instruction 0 of a tile; instruction i
+  // adds 4 i rows, step kk adds 256 kk bytes
+  const uint32_t voff = (uint32_t)(g * ldw * sizeof(bf16_t)) + r16 * 16;
   const uint32_t istride = 4u * ldw * sizeof(bf16_t);
 
 #pragma unroll
@@ -189,7 +193,7 @@ __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        wr[mt][i] = __builtin_amdgcn_raw_buffer_load_b128(wsel[mt] ? rs1 : rs0, voff[mt],
+        wr[mt][i] = __builtin_amdgcn_raw_buffer_load_b128(trs[mt], voff,
                                                           (uint32_t)(i * istride + kk * 256),
                                                           kNtPolicy);
   };
@@ -234,10 +238,19 @@ __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* 
       load_x(kk + 1, fr);
       load_w(kk + 1, wr);
     }
-    compute((kk & 1) ? fs1 : fs0);
-    if (more) {
-      store_x((kk & 1) ? fs0 : fs1, fr);
-      put_w(wr);     // (after this wave's operand reads of step kk: LDS keeps a wave's order)
+    if (XSINGLE) {
+      compute(fs0);
+      __syncthreads();   // every wave is done with step kk's activations
+      if (more) {
+        store_x(fs0, fr);
+        put_w(wr);
+      }
+    } else {
+      compute((kk & 1) ? fs1 : fs0);
+      if (more) {
+        store_x((kk & 1) ? fs0 : fs1, fr);
+        put_w(wr);     // (after this wave's operand reads of step kk: LDS keeps a wave's order)
+      }
     }
     __syncthreads();
   }
