@@ -32,7 +32,7 @@ def test_version_and_strings(lib):
 
 def test_workspace_queries(lib):
     # LM head: per-workgroup statistics and top-k key lists (k <= 16), per-wave above
-    nb = (128256 + 255) // 256                # T = 64: 256 vocabulary rows per workgroup
+    nb = (128256 + 511) // 512                # T = 64: 512 vocabulary rows per workgroup
     want = 0
     for n in (nb * 64 * 8, nb * 64 * 10 * 8):
         want += (n + 255) // 256 * 256
