@@ -81,6 +81,10 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
   constexpr int kLmRowsBlock = kLmRowsWave * kLmWaves;
   // (8 W tiles with 4 or more feature tiles: one activation buffer, so that
   // the W tiles of the row-run path fit)
+  // Row-run weight streaming (through a wave-private LDS tile) for eight
+  // tiles per wave, and for four at T <= 16 (the tile count that lm_mt_for
+  // picks for vocabularies past one round of 512-row workgroups).
+  constexpr bool kRowRuns = kLmMT == 8 || (kLmMT == 4 && NT == 1);
   constexpr bool kXSingle = kLmMT == 8 && NT >= 4;
   __shared__ __attribute__((aligned(16))) bf16_t fs[kXSingle ? ws_lds_elems<NT>() / 2
                                                              : ws_lds_elems<NT>()];
@@ -110,8 +114,8 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
 
   f32x4 acc[kLmMT][NT];
   // W tiles of the row-run path; after the main loop, the epilogue's lists
-  __shared__ __attribute__((aligned(16))) char wlds[kLmMT == 8 ? kLmWaves : 1][kLmMT * 4096];
-  if constexpr (kLmMT == 8) {
+  __shared__ __attribute__((aligned(16))) char wlds[kRowRuns ? kLmWaves : 1][kLmMT * 4096];
+  if constexpr (kRowRuns) {
     // row-run loads through a wave-private LDS tile
     int trow[kLmMT], wsel[kLmMT];
 #pragma unroll
@@ -205,14 +209,15 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
   }
   // Per wave and feature row: (max, sum exp(l - max)) and the top-k as
   // selection keys, by k rounds of "largest key below the previous pick".
-  // With k <= kLmBlockK the four waves' sorted lists go to LDS (the X staging
-  // buffer, free after the main loop) and are merged into one list per
-  // workgroup; otherwise every wave writes its own.
+  // With k <= kLmBlockK the four waves' sorted lists go to LDS (the W tiles on
+  // the row-run path, else the X staging buffer: both free after the main
+  // loop) and are merged into one list per workgroup; otherwise every wave
+  // writes its own.
   const bool block_lists = p.k <= kLmBlockK;
   constexpr int TP = 16 * NT;
-  static_assert(kLmMT != 8 || kLmWaves * kLmMT * 4096 >= 4 * TP * (kLmBlockK + 1) * 8,
+  static_assert(!kRowRuns || kLmWaves * kLmMT * 4096 >= 4 * TP * (kLmBlockK + 1) * 8,
                 "lists exceed the W tiles' LDS");
-  selkey_t* lk = kLmMT == 8 ? (selkey_t*)&wlds[0][0] : (selkey_t*)fs;   // [4][TP][k]
+  selkey_t* lk = kRowRuns ? (selkey_t*)&wlds[0][0] : (selkey_t*)fs;   // [4][TP][k]
   float2* ls = (float2*)(lk + 4 * TP * p.k);    // [4][TP]
   const int nb = block_lists ? gridDim.x : gridDim.x * kLmWaves;
   const int list = block_lists ? blockIdx.x : wglob;
@@ -581,10 +586,23 @@ struct LmLayout {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kLmCUs = 256;   // MI355X compute units
+
+// W tiles per wave for a launch: lm_mt, except that eight tiles (512 rows per
+// workgroup, one workgroup per CU) are traded for four (two per CU) when the
+// vocabulary needs more than one round of kLmCUs workgroups: at V = 152064
+// eight tiles leave 41 workgroups for a second round (T = 10: 246 us with
+// four tiles in the operand layout, 214 us with four on row runs).  The launch and the
+// workspace layout both take the tile count from here.
+static int lm_mt_for(int T, int V) {
+  const int mt = lm_mt(16 * lm_nt(T));
+  return mt == 8 && (V + 511) / 512 > kLmCUs ? 4 : mt;
+}
+
 static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   LmLayout l{};
   if (dt == EAGLE_BF16) {
-    const int rows_block = 16 * lm_mt(16 * lm_nt(T)) * kLmWaves;
+    const int rows_block = 16 * lm_mt_for(T, V) * kLmWaves;
     l.nb = ((V + rows_block - 1) / rows_block) * (k <= kLmBlockK ? 1 : kLmWaves);
     l.stat_off = 0;
     l.key_off = align256((size_t)l.nb * T * sizeof(float2));
@@ -596,9 +614,8 @@ static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   return l;
 }
 
-template <int NT>
+template <int NT, int MT>
 static void launch_lm(const LmParams& p, hipStream_t s) {
-  constexpr int MT = lm_mt(16 * NT);
   const int rows_block = 16 * MT * kLmWaves;
   hipLaunchKernelGGL((lmhead_bf16_kernel<NT, MT>), dim3((p.V + rows_block - 1) / rows_block),
                      dim3(256), 0, s, p);
@@ -636,12 +653,13 @@ static int lm_run(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
     EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
                (float2*)(ws + l.stat_off), (selkey_t*)(ws + l.key_off), rn};
+    const bool eight = lm_mt_for(T, V) == 8;
     switch (lm_nt(T)) {
-      case 1: launch_lm<1>(p, stream); break;
-      case 2: launch_lm<2>(p, stream); break;
-      case 4: launch_lm<4>(p, stream); break;
-      case 8: launch_lm<8>(p, stream); break;
-      default: launch_lm<16>(p, stream); break;
+      case 1: eight ? launch_lm<1, 8>(p, stream) : launch_lm<1, 4>(p, stream); break;
+      case 2: eight ? launch_lm<2, 8>(p, stream) : launch_lm<2, 4>(p, stream); break;
+      case 4: eight ? launch_lm<4, 8>(p, stream) : launch_lm<4, 4>(p, stream); break;
+      case 8: launch_lm<8, lm_mt(128)>(p, stream); break;
+      default: launch_lm<16, lm_mt(256)>(p, stream); break;
     }
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmhead_merge_kernel, dim3(T), dim3(256), 0, stream, p.part_stat,

@@ -107,13 +107,14 @@ def test_confidence_ratio(dev):
     np.testing.assert_allclose(c, np.exp(l12[:, 0] - l12[:, 1]), rtol=1e-5)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_full_size_every_row(dev, cfg):
-    """The workloads' full LM heads (Qwen2-7B T = 60, V = 152064; Llama-3-8B
+@pytest.mark.parametrize("cfg,T", [(2, None), (2, 10), (3, 64), (5, None)])
+def test_full_size_every_row(dev, cfg, T):
+    """The workloads' full LM heads (Qwen2-7B T = 60, V = 152064, and one
+    draft level's T = 10 on it, the four-tile row-run launch; Llama-3-8B
     verify T = 64, V = 128256; 70B wide tree T = 128, d = 8192): every logit,
     lse and top-k row against the oracle."""
     w = inputs.WORKLOADS[cfg]
-    T = w.T if cfg != 3 else 64
+    T = T or w.T
     f = inputs.normal(inputs.rng(w.cfg, inputs.STREAM_F), (T, w.d))
     W = inputs.lm_head_weight(w)
     ids, logp, lse, lg = run(dev, f, W, w.topk)
