@@ -245,8 +245,10 @@ __device__ __forceinline__ void tile_softmax_shifted(int t, int npos, bool is_tr
   }
 }
 
+// (one 16-row tile per wave: registers for two workgroups per CU, so that a
+// grid of a few hundred slices runs in one round)
 template <int HD, int NTW, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void tree_attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW, NTW == 1 ? 2 : 1) void tree_attn_bf16_kernel(AttnParams p) {
   constexpr int NTH = 64 * NW;
   constexpr int KB = HD / 32;
   constexpr int MTV = HD / 16;

@@ -54,6 +54,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, siz
                                            (int)(bytes < 0x7fffffffull ? bytes : 0x7fffffffull),
                                            kRsrcWord3);
 }
+// The same for a range that is the same in every lane of the wave: the count
+// is made a scalar, so the descriptor lives in SGPRs (a count the compiler
+// computes with vector instructions would otherwise make it wrap every load
+// in a loop over the distinct descriptors of the wave).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc_uniform(const void* base,
+                                                                   size_t bytes) {
+  const int n = (int)(bytes < 0x7fffffffull ? bytes : 0x7fffffffull);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           __builtin_amdgcn_readfirstlane(n), kRsrcWord3);
+}
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt
 // not waited on.  On gfx9 vmcnt counts vector-memory stores as well as loads.
@@ -362,6 +372,34 @@ struct RowNorm {
   int n;
   float eps;
 };
+
+// Sum of x[q stride] over q = q0, q0 + step, ... < parts, added in that order.
+// The first kPartBatch terms are loaded by strided_load (issued together, so
+// that they can stay in flight across other work) and added, with the rest,
+// by strided_finish, which loads the rest kPartBatch at a time: a plain loop
+// would wait for each load before issuing the next.
+constexpr int kPartBatch = 8;
+__device__ __forceinline__ void strided_load(const float* x, int parts, size_t stride, int q0,
+                                             int step, float (&v)[kPartBatch]) {
+#pragma unroll
+  for (int u = 0; u < kPartBatch; ++u) {
+    const int q = q0 + u * step;
+    v[u] = q < parts ? x[(size_t)q * stride] : 0.f;
+  }
+}
+__device__ __forceinline__ float strided_finish(const float* x, int parts, size_t stride, int q0,
+                                                int step, const float (&v)[kPartBatch]) {
+  float s = 0.f;   // (sums of squares: adding +0 for absent terms changes nothing)
+#pragma unroll
+  for (int u = 0; u < kPartBatch; ++u) s += v[u];
+  for (int b = q0 + kPartBatch * step; b < parts; b += kPartBatch * step) {
+    float w[kPartBatch];
+    strided_load(x, parts, stride, b, step, w);
+#pragma unroll
+    for (int u = 0; u < kPartBatch; ++u) s += w[u];
+  }
+  return s;
+}
 
 __device__ __forceinline__ float row_norm_scale(const RowNorm& rn, int M, int m) {
   float tot = 0.f;

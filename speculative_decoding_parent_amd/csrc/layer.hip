@@ -587,9 +587,9 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
   // input row scales: lanes (row rm, q0) add the partials q0, q0 + 16, ... of
   // row rm; the loads overlap the main loop, the sums are finished after it
   const int rm = threadIdx.x >> 4, q0 = threadIdx.x & 15;
-  float in_ss = 0.f;
-  if (p.in.ssq && rm < M)
-    for (int q = q0; q < p.in.parts; q += 16) in_ss += p.in.ssq[(size_t)q * M + rm];
+  const bool has_in = p.in.ssq && rm < M;
+  float in_part[kPartBatch];
+  if (has_in) strided_load(p.in.ssq + rm, p.in.parts, (size_t)M, q0, 16, in_part);
 
   // W is read in runs of 256 bytes per row with non-temporal loads (load
   // instruction i of tile mt: lane l takes row 4 i + l / 16 of the tile, bytes
@@ -667,6 +667,7 @@ __global__ __launch_bounds__(256, 2) void linear_rows_kernel(SkParams p) {
     if (kk + 8 < ke) load(kk + 8, wa, xa);
     compute(wb, xbv);
   }
+  float in_ss = has_in ? strided_finish(p.in.ssq + rm, p.in.parts, (size_t)M, q0, 16, in_part) : 0.f;
   in_ss += dpp_move<kDppQuadXor1>(in_ss);      // the 16 lanes of a row: a DPP row
   in_ss += dpp_move<kDppQuadXor2>(in_ss);
   in_ss += dpp_move<kDppHalfMirror>(in_ss);

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
                                                              : ws_lds_elems<NT>()];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index as a scalar, so that the row-run path's per-tile buffer
+  // descriptors are uniform (held in SGPRs, no per-load waterfall loop)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int r16 = lane & 15;
   const int v0 = blockIdx.x * kLmRowsBlock + wave * kLmRowsWave;
@@ -101,16 +103,22 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
     const int v = min(v0 + mt * 16 + r16, p.V - 1);
     wrow[mt] = p.W + (size_t)v * p.d + g * 8;
   }
-  // deferred RMSNorm of the feature rows: partial sums are loaded before the
-  // main loop and finished after it.  T <= 16: lanes (row tid / 16, q0 =
-  // tid % 16) take partials q0, q0 + 16, ...; otherwise thread t takes row t.
+  // deferred RMSNorm of the feature rows: the first partial sums are loaded
+  // before the main loop and the sums finished after it.  2^tsh consecutive
+  // lanes share a row (16 at T <= 16, 8 at T <= 32, ..., 1 at T > 128): lane
+  // q0 of row rm takes partials q0, q0 + 2^tsh, ...
   __shared__ float rsc[EAGLE_MAX_TREE];
-  const bool rows16 = p.T <= 16;
-  const int rm = rows16 ? tid >> 4 : tid;
-  const int q0 = rows16 ? (tid & 15) : 0;
+  const int tsh = p.T <= 16 ? 4 : p.T <= 32 ? 3 : p.T <= 64 ? 2 : p.T <= 128 ? 1 : 0;
+  const int rm = tid >> tsh;
+  const int q0 = tid & ((1 << tsh) - 1);
+  const bool has_in = p.in.ssq && rm < p.T;
+  float in_part[kPartBatch];
+  if (has_in) strided_load(p.in.ssq + rm, p.in.parts, (size_t)p.T, q0, 1 << tsh, in_part);
+  // (4 x 4 tiles: no registers to spare for the partials across the loop)
+  constexpr bool kInAcross = !(NT == 4 && kLmMT == 4);
   float in_ss = 0.f;
-  if (p.in.ssq && rm < p.T)
-    for (int q = q0; q < p.in.parts; q += rows16 ? 16 : 1) in_ss += p.in.ssq[(size_t)q * p.T + rm];
+  if (!kInAcross && has_in)
+    in_ss = strided_finish(p.in.ssq + rm, p.in.parts, (size_t)p.T, q0, 1 << tsh, in_part);
 
   f32x4 acc[kLmMT][NT];
   // W tiles of the row-run path; after the main loop, the epilogue's lists
@@ -130,12 +138,13 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
   }
 
   if (p.in.ssq) {
-    if (rows16) {
-      in_ss += dpp_move<kDppQuadXor1>(in_ss);
-      in_ss += dpp_move<kDppQuadXor2>(in_ss);
-      in_ss += dpp_move<kDppHalfMirror>(in_ss);
-      in_ss += dpp_move<kDppRowMirror>(in_ss);
-    }
+    if (kInAcross && has_in)
+      in_ss = strided_finish(p.in.ssq + rm, p.in.parts, (size_t)p.T, q0, 1 << tsh, in_part);
+    // sum over the row's lanes (pairs, quads, 8, 16: a butterfly inside each group)
+    if (tsh > 0) in_ss += dpp_move<kDppQuadXor1>(in_ss);
+    if (tsh > 1) in_ss += dpp_move<kDppQuadXor2>(in_ss);
+    if (tsh > 2) in_ss += dpp_move<kDppHalfMirror>(in_ss);
+    if (tsh > 3) in_ss += dpp_move<kDppRowMirror>(in_ss);
     if (rm < p.T && q0 == 0) rsc[rm] = 1.0f / sqrtf(in_ss / (float)p.in.n + p.in.eps);
     __syncthreads();
 #pragma unroll

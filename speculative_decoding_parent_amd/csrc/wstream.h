@@ -158,8 +158,8 @@ __device__ __forceinline__ void wstream_mfma_rr(const bf16_t* w0, const bf16_t* 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int rows = max(0, min(16, nrows - tile_row0[mt]));
-    trs[mt] = buf_rsrc((wsel[mt] ? w1 : w0) + (size_t)tile_row0[mt] * ldw,
-                       (size_t)rows * ldw * sizeof(bf16_t));
+    trs[mt] = buf_rsrc_uniform((wsel[mt] ? w1 : w0) + (size_t)tile_row0[mt] * ldw,
+                               (size_t)rows * ldw * sizeof(bf16_t));
   }
   // byte offset of this lane's run in instruction 0 of a tile; instruction i
   // adds 4 i rows, step kk adds 256 kk bytes
