@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 5
+#define EAGLE_ABI_VERSION 6
 
 typedef enum {
   EAGLE_OK = 0,
@@ -171,6 +171,13 @@ int eagle_tree_attn(const void* q,
  *   lse      f32[T] out: log sum_v exp(logit[t][v]).
  *   logits   f32[T][V] out, or NULL: the fp32 logits.
  *   workspace >= eagle_lmhead_topk_workspace(...) bytes, 256-byte aligned.
+ *            bf16: the first 2 KiB hold one 64-bit key bound per feature
+ *            row, raised by the partial lists as they finish so that later
+ *            lists skip keys below it.  They must be zero before the first
+ *            call that uses the buffer (allocate it zeroed); every call leaves
+ *            them zero, so the buffer can be reused by later calls on the same
+ *            stream, also under graph capture.  The results do not depend on
+ *            the order in which the lists finish.
  */
 size_t eagle_lmhead_topk_workspace(int32_t T, int32_t d, int32_t V, int32_t k, eagle_dtype dt);
 int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
@@ -193,9 +200,10 @@ int eagle_lmhead_topk(const void* f, const void* W, int32_t T, int32_t d, int32_
  *   EAGLE_LMHEAD_SCRATCH_BYTES (else EAGLE_EWORKSPACE, before any HIP call);
  *   e.g. T = 128, V = 128256, k = 10 in bf16 needs 11.3 MB.
  *   stream must belong to the current device (else EAGLE_EINVAL).
- * Every call on one GPU shares that GPU's scratch, and nothing in it needs
- * to start zeroed.  Calls that overlap in time on one GPU (two streams, or
- * two host threads) race on it: serialise them.
+ * Every call on one GPU shares that GPU's scratch.  It starts zeroed (static
+ * device memory), and every call leaves its key bounds (see the workspace of
+ * eagle_lmhead_topk) zero again.  Calls that overlap in time on one GPU (two
+ * streams, or two host threads) race on it: serialise them.
  */
 #define EAGLE_LMHEAD_SCRATCH_BYTES ((size_t)16 << 20)
 int eagle_lmhead_topk_noalloc(const void* f, const void* W, int32_t T, int32_t d, int32_t V,

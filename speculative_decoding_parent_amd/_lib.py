@@ -139,8 +139,9 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
-    # zero-filled: the projection entry points keep self-resetting counters at
-    # the start of their workspace, which must be zero before first use
+    # zero-filled: the projection entry points keep self-resetting counters,
+    # and the LM head its per-row key bounds, at the start of their workspace,
+    # which must be zero before first use
     if ws is not None and ws.numel() * ws.element_size() >= nbytes:
         return ws
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)

@@ -402,8 +402,9 @@ __device__ __forceinline__ float strided_finish(const float* x, int parts, size_
 }
 
 __device__ __forceinline__ float row_norm_scale(const RowNorm& rn, int M, int m) {
-  float tot = 0.f;
-  for (int q = 0; q < rn.parts; ++q) tot += rn.ssq[(size_t)q * M + m];
+  float v[kPartBatch];
+  strided_load(rn.ssq + m, rn.parts, (size_t)M, 0, 1, v);
+  const float tot = strided_finish(rn.ssq + m, rn.parts, (size_t)M, 0, 1, v);
   return 1.0f / sqrtf(tot / (float)rn.n + rn.eps);
 }
 

@@ -173,12 +173,20 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(LinParams p, int swi
     }
   }
   if (p.in.ssq) {
+    if (vec) {   // the four outputs share a row
+      const float rs = row_norm_scale(p.in, p.M, (int)(e0 / p.N));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (e0 + j >= MN) break;
-      const float rs = row_norm_scale(p.in, p.M, (int)((e0 + j) / p.N));
-      a[j] *= rs;
-      b[j] *= rs;
+      for (int j = 0; j < 4; ++j) {
+        a[j] *= rs;
+        b[j] *= rs;
+      }
+    } else {
+      for (int j = 0; j < 4; ++j) {
+        if (e0 + j >= MN) break;
+        const float rs = row_norm_scale(p.in, p.M, (int)((e0 + j) / p.N));
+        a[j] *= rs;
+        b[j] *= rs;
+      }
     }
   }
   float y[4];

@@ -72,6 +72,8 @@ struct LmParams {
   float2* part_stat;   // [T][nb] (max, sum exp(l - max))
   selkey_t* part_key;  // [T][nb][k] sorted selection keys
   RowNorm in;          // deferred RMSNorm of the feature rows (in.ssq null: none)
+  selkey_t* thr;       // [T] per row, a key that is at most its k-th largest
+                       // (0 between calls; see the epilogue)
 };
 
 template <int NT, int kLmMT>
@@ -230,6 +232,23 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
   float2* ls = (float2*)(lk + 4 * TP * p.k);    // [4][TP]
   const int nb = block_lists ? gridDim.x : gridDim.x * kLmWaves;
   const int list = block_lists ? blockIdx.x : wglob;
+  // A key below row t's k-th largest over the whole vocabulary is never
+  // needed.  p.thr[t] is a lower bound of that k-th largest: the largest k-th
+  // entry of any list finished so far in this call (every list is a set of
+  // keys of row t, so its k-th entry has k keys at or above it).  A list
+  // therefore keeps only keys >= the bound it reads, and its selection rounds
+  // stop once every row of the wave has run out of them: the lists finished
+  // last, which end the call, usually need a round or two instead of k.  The
+  // merged top-k does not depend on the bounds read (every key of the row's
+  // top-k is >= every bound), so the results stay identical from call to call.
+  selkey_t thr[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int t = nt * 16 + r16;
+    thr[nt] = t < T && p.k > 0 ? __hip_atomic_load(p.thr + t, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : ~0ull;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int t = nt * 16 + r16;
@@ -264,10 +283,19 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
           best = ((key < last) & (key > best)) ? key : best;
         }
       best = rows_max_key(best);
-      if (g == 0) {
-        if (block_lists) lk[(wave * TP + t) * p.k + r] = best;
-        else if (t < T) p.part_key[((size_t)t * nb + list) * p.k + r] = best;
+      best = best >= thr[nt] ? best : 0ull;
+      const bool more = __any(best != 0ull);
+      // this round's entry, and none for the rounds skipped below
+      for (int e = r; e < (more ? r + 1 : p.k); ++e) {
+        const selkey_t x = e == r ? best : 0ull;
+        if (g == 0) {
+          if (block_lists) lk[(wave * TP + t) * p.k + e] = x;
+          else if (t < T) p.part_key[((size_t)t * nb + list) * p.k + e] = x;
+        }
       }
+      if (!block_lists && r == p.k - 1 && g == 0 && t < T && best != 0ull)
+        __hip_atomic_fetch_max(p.thr + t, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!more) break;
       last = best;
     }
   }
@@ -292,7 +320,12 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
       ptr += adv ? 1 : 0;
       const selkey_t nxt = my[min(ptr, p.k - 1)];
       h = adv ? (ptr < p.k ? nxt : 0ull) : h;
-      if (g == 0 && t < T) p.part_key[((size_t)t * nb + list) * p.k + r] = b;
+      const bool more = __any(b != 0ull);
+      for (int e = r; e < (more ? r + 1 : p.k); ++e)
+        if (g == 0 && t < T) p.part_key[((size_t)t * nb + list) * p.k + e] = e == r ? b : 0ull;
+      if (r == p.k - 1 && g == 0 && t < T && b != 0ull)   // the list's k-th entry
+        __hip_atomic_fetch_max(p.thr + t, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!more) break;
     }
   }
 }
@@ -355,7 +388,7 @@ __device__ __forceinline__ void fold_stat_wave(float& m, float& s) {
 __global__ __launch_bounds__(256) void lmhead_merge_kernel(
     const float2* __restrict__ part_stat, const selkey_t* __restrict__ part_key, int nb, int T,
     int k, int32_t* __restrict__ topk_id, float* __restrict__ topk_logp,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, selkey_t* __restrict__ thr) {
   __shared__ float2 red[4];
   __shared__ selkey_t ck[4 * EAGLE_MAX_TOPK];
   __shared__ int slist[EAGLE_MAX_TOPK];
@@ -368,6 +401,8 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(
   const float2* st = part_stat + (size_t)t * nb;
   const selkey_t* pk = part_key + (size_t)t * nb * k;
   if (tid == 0) nsl = 0;
+  // the main kernel is done with row t's bound: zero for the next call
+  if (tid == 0) __hip_atomic_store(thr + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Short lists (nb <= 256, nb k <= 4096 keys): all keys go to LDS in one
   // pass and wave 0 merges every list directly, lane l following lists l,
@@ -589,9 +624,12 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(
 // ---------------------------------------------------------------- host side
 
 struct LmLayout {
-  size_t stat_off, key_off, logits_off, total;
+  size_t thr_off, stat_off, key_off, logits_off, total;
   int nb;   // partial lists per feature row
 };
+
+// bf16 path: the per-row key bounds sit first, at a fixed place for every T
+constexpr size_t kLmThrBytes = EAGLE_MAX_TREE * sizeof(selkey_t);
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -613,8 +651,9 @@ static LmLayout lm_layout(int T, int V, int k, eagle_dtype dt) {
   if (dt == EAGLE_BF16) {
     const int rows_block = 16 * lm_mt_for(T, V) * kLmWaves;
     l.nb = ((V + rows_block - 1) / rows_block) * (k <= kLmBlockK ? 1 : kLmWaves);
-    l.stat_off = 0;
-    l.key_off = align256((size_t)l.nb * T * sizeof(float2));
+    l.thr_off = 0;
+    l.stat_off = kLmThrBytes;
+    l.key_off = l.stat_off + align256((size_t)l.nb * T * sizeof(float2));
     l.total = l.key_off + align256((size_t)l.nb * T * k * sizeof(selkey_t));
   } else {
     l.logits_off = 0;
@@ -661,7 +700,8 @@ static int lm_run(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
     EAGLE_REQUIRE(((uintptr_t)f & 15) == 0 && ((uintptr_t)W & 15) == 0, EAGLE_EINVAL);
     EAGLE_REQUIRE(!logits || ((uintptr_t)logits & 15) == 0, EAGLE_EINVAL);
     LmParams p{(const bf16_t*)f, (const bf16_t*)W, T, d, V, k, logits,
-               (float2*)(ws + l.stat_off), (selkey_t*)(ws + l.key_off), rn};
+               (float2*)(ws + l.stat_off), (selkey_t*)(ws + l.key_off), rn,
+               (selkey_t*)(ws + l.thr_off)};
     const bool eight = lm_mt_for(T, V) == 8;
     switch (lm_nt(T)) {
       case 1: eight ? launch_lm<1, 8>(p, stream) : launch_lm<1, 4>(p, stream); break;
@@ -672,7 +712,7 @@ static int lm_run(const void* f, const void* W, int32_t T, int32_t d, int32_t V,
     }
     EAGLE_LAUNCH_CHECK();
     hipLaunchKernelGGL(lmhead_merge_kernel, dim3(T), dim3(256), 0, stream, p.part_stat,
-                       p.part_key, l.nb, T, k, topk_id, topk_logp, lse);
+                       p.part_key, l.nb, T, k, topk_id, topk_logp, lse, p.thr);
   } else if (dt == EAGLE_F32) {
     float* lg = logits ? logits : (float*)(ws + l.logits_off);
     hipLaunchKernelGGL(lmhead_f32_logits_kernel, dim3((V + 255) / 256, T), dim3(256), 0, stream,

@@ -116,7 +116,7 @@ class DraftVerifyCycle:
         ws_lm = max(lib.eagle_lmhead_topk_workspace(ks, d, V, k, _lib.EAGLE_BF16),
                     lib.eagle_lmhead_topk_workspace(T, d, V, k, _lib.EAGLE_BF16))
         self.ws_attn = torch.empty(ws_attn, dtype=torch.uint8, device=dev)
-        self.ws_lm = torch.empty(ws_lm, dtype=torch.uint8, device=dev)
+        self.ws_lm = torch.zeros(ws_lm, dtype=torch.uint8, device=dev)     # row bounds start at 0
         self.ws_acc = torch.empty(lib.eagle_accept_workspace(T, V), dtype=torch.uint8, device=dev)
         ws_lin = 256
         for M in (1, ks, T):

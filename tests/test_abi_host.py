@@ -25,20 +25,21 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.eagle_abi_version() == 5
+    assert lib.eagle_abi_version() == 6
     for code in (0, -1, -2, -3, -4, 7):
         assert lib.eagle_status_string(code)
 
 
 def test_workspace_queries(lib):
-    # LM head: per-workgroup statistics and top-k key lists (k <= 16), per-wave above
+    # LM head: per-row key bounds (256 rows x 8 bytes), then per-workgroup
+    # statistics and top-k key lists (k <= 16), per-wave above
     nb = (128256 + 511) // 512                # T = 64: 512 vocabulary rows per workgroup
-    want = 0
+    want = 256 * 8
     for n in (nb * 64 * 8, nb * 64 * 10 * 8):
         want += (n + 255) // 256 * 256
     assert lib.eagle_lmhead_topk_workspace(64, 4096, 128256, 10, _lib.EAGLE_BF16) == want
     nb = (128256 + 511) // 512 * 4            # T = 10, k = 20: per-wave lists
-    want = 0
+    want = 256 * 8
     for n in (nb * 10 * 8, nb * 10 * 20 * 8):
         want += (n + 255) // 256 * 256
     assert lib.eagle_lmhead_topk_workspace(10, 4096, 128256, 20, _lib.EAGLE_BF16) == want

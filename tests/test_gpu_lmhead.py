@@ -125,3 +125,31 @@ def test_full_size_every_row(dev, cfg, T):
     assert np.array_equal(ids, oracle.topk_ids(lg, w.topk))
     _, _, rlse = oracle.softmax_stats(ref)
     assert np.abs(lse - rlse).max() <= 1e-3
+
+
+@pytest.mark.parametrize("k", [10, 20])
+def test_key_bounds_reset_between_calls(dev, k):
+    """The partial lists skip keys below a per-row bound that lists finished
+    earlier in the same call raise; every call must leave the bounds at zero.
+    One workspace serves a call whose top keys are large, then one whose top
+    keys all lie below them (negated features), then the first again: each
+    matches the oracle and the repeat is bit-identical to the first call
+    (k = 10: workgroup lists, k = 20: per-wave lists)."""
+    g = inputs.rng(405, k)
+    T, d, V = 10, 256, 70000
+    f = inputs.normal(g, (T, d))
+    W = inputs.normal(g, (V, d), std=float(1 / np.sqrt(d)))
+    fd, Wd = f.to(dev), W.to(dev)
+    nb = _lib.lib().eagle_lmhead_topk_workspace(T, d, V, k, _lib.EAGLE_BF16)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    outs = []
+    for x in (fd, -fd, fd):
+        print(f"lmhead bounds T={T} d={d} V={V} k={k}", flush=True)
+        ids, logp, lse, lg = _lib.eagle_lmhead_topk(x, Wd, k, want_logits=True, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((ids.cpu().numpy(), logp.cpu().numpy(), lse.cpu().numpy(), lg.cpu().numpy()))
+    check(*outs[0], f, W, k)
+    check(*outs[1], -f, W, k)
+    for a, b in zip(outs[0], outs[2]):
+        assert np.array_equal(a, b)
+    assert not ws[:256 * 8].any().item(), "key bounds left nonzero"
