@@ -67,7 +67,10 @@ __host__ __device__ constexpr int lin_cols_block(int mt, int swiglu) {
   return swiglu ? 4 * 8 * mt : 4 * 16 * mt;
 }
 
-template <int NT, int SWIGLU, int MT>
+// RR: W read in 256-byte row runs through a wave-private LDS tile (the
+// streaming core's row-run variant) instead of 16-row operand-layout loads;
+// chosen by the host for long k ranges, where it streams faster.
+template <int NT, int SWIGLU, int MT, bool RR>
 __global__ __launch_bounds__(256, (NT * MT <= 8 ? 2 : 1)) void linear_bf16_kernel(LinParams p) {
   static_assert(!SWIGLU || MT % 2 == 0, "SwiGLU pairs gate and up tiles");
   constexpr int HALF = SWIGLU ? MT / 2 : MT;      // output tiles per wave
@@ -87,10 +90,23 @@ __global__ __launch_bounds__(256, (NT * MT <= 8 ? 2 : 1)) void linear_bf16_kerne
   // k slice of this workgroup
   const int kc = p.K / p.ksplit;
   const int k0 = blockIdx.y * kc;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) wrow[mt] += k0;
   f32x4 acc[MT][NT];
-  wstream_mfma<NT, MT>(wrow, p.x + k0, p.K, p.M, kc, fs, acc);
+  __shared__ __attribute__((aligned(16))) char wlds[RR ? 4 : 1][RR ? MT * 4096 : 16];
+  if constexpr (RR) {
+    int trow[MT], wsel[MT];
+    const int n0s = __builtin_amdgcn_readfirstlane(n0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      trow[mt] = n0s + (mt % HALF) * 16;
+      wsel[mt] = (SWIGLU && mt >= HALF) ? 1 : 0;
+    }
+    wstream_mfma_rr<NT, MT, false>(p.w0 + k0, SWIGLU ? p.w1 + k0 : nullptr, p.N, p.K, trow, wsel,
+                                   p.x + k0, p.K, p.M, kc, fs, wlds[wave], acc);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) wrow[mt] += k0;
+    wstream_mfma<NT, MT>(wrow, p.x + k0, p.K, p.M, kc, fs, acc);
+  }
 
   if (p.to_part) {
     // fp32 partials; a SwiGLU wave's up tiles go to plane 1
@@ -856,6 +872,12 @@ static void launch_rows(SkParams p, const SkPlan& pl, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(linear_rows_kernel<MODE>, dim3(pl.nblk, pl.S), dim3(256), 0, s, p);
 }
 
+// Row runs for up to 64 activation rows when a workgroup's k range has at
+// least kLinRrSteps steps (M = 64: the SwiGLU's 16 and 32 and the down
+// projection's 7 steps run 7-11% faster that way; the 4-step o and qkv
+// slices 1-15% slower).
+constexpr int kLinRrSteps = 6;
+
 // k slices for a projection: enough workgroups to fill the chip (about two per
 // CU) while the fp32 partials stay below a quarter of the weight bytes; the
 // count divides K / 128.
@@ -863,6 +885,10 @@ static int lin_ksplit(int M, int K, int N, int swiglu) {
   const int cols = lin_cols_block(lin_mt((M + 15) / 16, swiglu), swiglu);
   const int nblk = (N + cols - 1) / cols;
   const int nk = K / kWsKG;
+  // SwiGLU with up to 64 rows and column blocks for most of the CUs: one
+  // k slice, so no partials and no reduce launch (M = 64, N = 14336: 224
+  // workgroups on row runs, 62 against 65 us with two slices and the reduce)
+  if (swiglu && M <= 64 && 4 * nblk >= 3 * 256 && nk >= kLinRrSteps) return 1;
   const int want = (512 + nblk - 1) / nblk;
   int best = 1;
   for (int s = 1; s <= nk; ++s) {
@@ -906,12 +932,19 @@ static_assert(lin_mt(3, 0) == lin_mt(4, 0) && lin_mt(5, 0) == lin_mt(8, 0) &&
                   lin_mt(5, 1) == lin_mt(8, 1) && lin_mt(9, 1) == lin_mt(16, 1),
               "row-tile buckets must not change the W tiling");
 
+static bool lin_rr(const LinParams& p) {
+  return p.M <= 64 && p.K / p.ksplit / kWsKG >= kLinRrSteps;
+}
+
 template <int NT, int SWIGLU>
 static void launch_lin(const LinParams& p, hipStream_t s) {
   constexpr int MT = lin_mt(NT, SWIGLU);
   const int cols = lin_cols_block(MT, SWIGLU);
-  hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU, MT>),
-                     dim3((p.N + cols - 1) / cols, p.ksplit), dim3(256), 0, s, p);
+  const dim3 grid((p.N + cols - 1) / cols, p.ksplit);
+  if (NT <= 4 && lin_rr(p))
+    hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU, MT, NT <= 4>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((linear_bf16_kernel<NT, SWIGLU, MT, false>), grid, dim3(256), 0, s, p);
 }
 
 // GEMM only, writing fp32 partials (ksplit >= 1) for a row-wise epilogue.
