@@ -557,7 +557,8 @@ int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const void* W, int
  * norm deferred to the consumer (one launch for M <= 16, two otherwise):
  * out[m] = x[m] W^T + residual[m] (f32), xg_out[m] = out[m] * gamma (bf16,
  * [M][N]) and ssq_out [P][M] f32, P = eagle_linear_norm_parts(M, K, N):
- * sums of out[m][n]^2 over disjoint column sets.  Used for the layer's
+ * sums of out[m][n]^2 over disjoint column sets (64 columns each for
+ * M <= 16, 1024 otherwise).  Used for the layer's
  * residual adds, each of which is followed by a norm that feeds a product.
  * N % 4 == 0, N <= 8192; workspace >= eagle_linear_rows_workspace(M, K, N).
  */

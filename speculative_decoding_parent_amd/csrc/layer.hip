@@ -243,13 +243,10 @@ __device__ __forceinline__ f32x4 sum_slices4(const LinParams& p, size_t off) {
   return a;
 }
 
-// out = sum + residual (fp32), then norm_out = RMSNorm(out) * gamma (bf16), or
-// with DEFER: norm_out = out * gamma (bf16) and ssq_out[m] = sum out[m]^2 (the
-// row scale is left to the consumer).
-template <bool DEFER>
+// out = sum + residual (fp32), then norm_out = RMSNorm(out) * gamma (bf16):
+// one workgroup per row m.
 __global__ __launch_bounds__(kRowThreads) void linear_reduce_norm_kernel(
-    LinParams p, const float* __restrict__ gamma, float eps, bf16_t* __restrict__ norm_out,
-    float* __restrict__ ssq_out) {
+    LinParams p, const float* __restrict__ gamma, float eps, bf16_t* __restrict__ norm_out) {
   __shared__ float red[kRowThreads / 64];
   const int m = blockIdx.x;
   const int N = p.N;
@@ -273,8 +270,7 @@ __global__ __launch_bounds__(kRowThreads) void linear_reduce_norm_kernel(
   float tot = 0.f;
 #pragma unroll
   for (int w = 0; w < kRowThreads / 64; ++w) tot += red[w];
-  if (DEFER && threadIdx.x == 0) ssq_out[m] = tot;
-  const float r = DEFER ? 1.0f : 1.0f / sqrtf(tot / (float)N + eps);
+  const float r = 1.0f / sqrtf(tot / (float)N + eps);
 #pragma unroll
   for (int q = 0; q < kRowVec; ++q) {
     const int n = (threadIdx.x + kRowThreads * q) * 4;
@@ -284,6 +280,39 @@ __global__ __launch_bounds__(kRowThreads) void linear_reduce_norm_kernel(
         u32x2{pack_bf16x2(v[q][0] * r * gm[0], v[q][1] * r * gm[1]),
               pack_bf16x2(v[q][2] * r * gm[2], v[q][3] * r * gm[3])};
   }
+}
+
+// The deferred form over column chunks: workgroup (m, c) sums the k-slice
+// partials of row m's columns [c kRedCols, (c + 1) kRedCols) (slice order),
+// adds the residual, writes out (fp32) and xg = out * gamma (bf16), and the
+// chunk's sum of squares to ssq_out[c][m]: one part per chunk, so a whole
+// row needs no single workgroup.
+constexpr int kRedCols = 1024;
+__global__ __launch_bounds__(256) void linear_reduce_dnorm_kernel(LinParams p,
+                                                                  const float* __restrict__ gamma,
+                                                                  bf16_t* __restrict__ xg_out,
+                                                                  float* __restrict__ ssq_out) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  const int c = blockIdx.y;
+  const int N = p.N;
+  const int n = c * kRedCols + threadIdx.x * 4;
+  float ss = 0.f;
+  if (n < N) {
+    const size_t off = (size_t)m * N + n;
+    f32x4 v = sum_slices4(p, off);
+    if (p.residual) v += *(const f32x4*)(p.residual + off);
+    *(f32x4*)((float*)p.out + off) = v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ss = fmaf(v[j], v[j], ss);
+    const f32x4 gm = *(const f32x4*)(gamma + n);
+    *(u32x2*)(xg_out + off) = u32x2{pack_bf16x2(v[0] * gm[0], v[1] * gm[1]),
+                                    pack_bf16x2(v[2] * gm[2], v[3] * gm[3])};
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) ssq_out[(size_t)c * p.M + m] = ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 // cos and sin of the rotary angle pos * inv: the angle is formed and reduced
@@ -309,22 +338,24 @@ struct RopeArgs {
   int32_t* status;
 };
 
-// Rotate one row held in LDS (q heads, k heads, v heads of hd) and place it:
-// q -> q_out[m], rotated k and plain v -> tree slot row_slot[m].
-__device__ void rope_place_row(const float* row, int m, const RopeArgs& r, const double* inv) {
+// Rotate heads [h0, h1) of one row held in LDS (row[] starts at head h0; q
+// heads, then k heads, then v heads of hd) and place them: q -> q_out[m],
+// rotated k and plain v -> tree slot row_slot[m].
+__device__ void rope_place_row(const float* row, int m, const RopeArgs& r, const double* inv,
+                               int h0, int h1) {
   const int half = r.hd / 2;
-  const int H = r.Hq + 2 * r.Hkv;
   int slot = r.row_slot ? r.row_slot[m] : m;
   if (slot < 0 || slot >= r.slot_cap) {
     if (threadIdx.x == 0) set_status(r.status, EAGLE_DEV_BAD_INDEX);
     slot = -1;
   }
   const double pos = (double)(r.pos_base + r.depth[m]);
-  for (int e = threadIdx.x; e < H * half; e += blockDim.x) {
-    const int hh = e / half;
-    const int i = e - hh * half;
-    const float x1 = row[hh * r.hd + i];
-    const float x2 = row[hh * r.hd + i + half];
+  for (int e = threadIdx.x; e < (h1 - h0) * half; e += blockDim.x) {
+    const int hl = e / half;
+    const int hh = h0 + hl;
+    const int i = e - hl * half;
+    const float x1 = row[hl * r.hd + i];
+    const float x2 = row[hl * r.hd + i + half];
     if (hh < r.Hq + r.Hkv) {
       float cs, sn;
       rope_cs(pos, inv[i], cs, sn);
@@ -349,19 +380,25 @@ __device__ void rope_place_row(const float* row, int m, const RopeArgs& r, const
 
 constexpr int kRopeMaxHalf = 128;
 
-// qkv projection epilogue: sum the row's partials into LDS, then RoPE + place.
-__global__ __launch_bounds__(kRowThreads) void linear_reduce_rope_kernel(LinParams p, RopeArgs r) {
+// qkv projection epilogue: workgroup (m, group) sums the partials of row m's
+// heads [kRopeHeads group, ...) into LDS, then RoPE + place.
+constexpr int kRopeHeads = 8;
+__global__ __launch_bounds__(256) void linear_reduce_rope_kernel(LinParams p, RopeArgs r) {
   extern __shared__ float row[];
   __shared__ double inv[kRopeMaxHalf];
   const int m = blockIdx.x;
+  const int H = r.Hq + 2 * r.Hkv;
+  const int h0 = blockIdx.y * kRopeHeads;
+  const int h1 = min(H, h0 + kRopeHeads);
   const int half = r.hd / 2;
   for (int i = threadIdx.x; i < half; i += blockDim.x)
     inv[i] = pow(r.theta, -2.0 * (double)i / (double)r.hd);
   const float rs = p.in.ssq ? row_norm_scale(p.in, p.M, m) : 1.0f;
-  for (int n = threadIdx.x * 4; n < p.N; n += kRowThreads * 4)
-    *(f32x4*)(row + n) = sum_slices4(p, (size_t)m * p.N + n) * rs;
+  const int c0 = h0 * r.hd, nc = (h1 - h0) * r.hd;
+  for (int n = threadIdx.x * 4; n < nc; n += 256 * 4)
+    *(f32x4*)(row + n) = sum_slices4(p, (size_t)m * p.N + c0 + n) * rs;
   __syncthreads();
-  rope_place_row(row, m, r, inv);
+  rope_place_row(row, m, r, inv, h0, h1);
 }
 
 // out[m] = x[m] / sqrt(mean(x[m]^2) + eps) * gamma, fp32 in, bf16 out.  One
@@ -420,7 +457,7 @@ __global__ __launch_bounds__(256) void rope_qkv_kernel(const float* __restrict__
   for (int i = threadIdx.x; i < half; i += blockDim.x)
     inv[i] = pow(r.theta, -2.0 * (double)i / (double)r.hd);
   __syncthreads();
-  rope_place_row(qkv + (size_t)m * (r.Hq + 2 * r.Hkv) * r.hd, m, r, inv);
+  rope_place_row(qkv + (size_t)m * (r.Hq + 2 * r.Hkv) * r.hd, m, r, inv, 0, r.Hq + 2 * r.Hkv);
 }
 
 // One draft round's preparation, one workgroup per row j (frontier entry f):
@@ -1122,8 +1159,8 @@ extern "C" int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const v
                      eagle::lin_ksplit(M, K, N, 0), eagle::lin_partials(workspace)};
   p.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
   eagle::launch_lin_partials(p, stream);
-  hipLaunchKernelGGL(eagle::linear_reduce_norm_kernel<false>, dim3(M), dim3(eagle::kRowThreads),
-                     0, stream, p, gamma, eps, (bf16_t*)norm_out, nullptr);
+  hipLaunchKernelGGL(eagle::linear_reduce_norm_kernel, dim3(M), dim3(eagle::kRowThreads),
+                     0, stream, p, gamma, eps, (bf16_t*)norm_out);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }
@@ -1131,7 +1168,7 @@ extern "C" int eagle_linear_rmsnorm(const void* x, int32_t M, int32_t K, const v
 extern "C" int32_t eagle_linear_norm_parts(int32_t M, int32_t K, int32_t N) {
   (void)K;
   if (M < 1 || N < 1) return 0;
-  return M <= eagle::kSkMaxRows ? (N + 63) / 64 : 1;
+  return M <= eagle::kSkMaxRows ? (N + 63) / 64 : (N + eagle::kRedCols - 1) / eagle::kRedCols;
 }
 
 extern "C" int eagle_linear_rmsnorm_deferred(const void* x, int32_t M, int32_t K, const void* W,
@@ -1162,8 +1199,9 @@ extern "C" int eagle_linear_rmsnorm_deferred(const void* x, int32_t M, int32_t K
                      eagle::lin_ksplit(M, K, N, 0), eagle::lin_partials(workspace)};
   p.ksplit = p.ksplit < 1 ? 1 : p.ksplit;
   eagle::launch_lin_partials(p, stream);
-  hipLaunchKernelGGL(eagle::linear_reduce_norm_kernel<true>, dim3(M), dim3(eagle::kRowThreads), 0,
-                     stream, p, gamma, 0.0f, (bf16_t*)xg_out, ssq_out);
+  hipLaunchKernelGGL(eagle::linear_reduce_dnorm_kernel,
+                     dim3(M, (N + eagle::kRedCols - 1) / eagle::kRedCols), dim3(256), 0, stream, p,
+                     gamma, (bf16_t*)xg_out, ssq_out);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }
@@ -1206,8 +1244,10 @@ extern "C" int eagle_linear_rope_qkv(const void* x, int32_t M, int32_t K, const 
                      0, eagle::lin_ksplit(M, K, N, 0), eagle::lin_partials(workspace)};
   p.in = rn;
   eagle::launch_lin_partials(p, stream);
-  hipLaunchKernelGGL(eagle::linear_reduce_rope_kernel, dim3(M), dim3(eagle::kRowThreads),
-                     N * sizeof(float), stream, p, r);
+  const int H = Hq + 2 * Hkv;
+  hipLaunchKernelGGL(eagle::linear_reduce_rope_kernel,
+                     dim3(M, (H + eagle::kRopeHeads - 1) / eagle::kRopeHeads), dim3(256),
+                     (size_t)eagle::kRopeHeads * hd * sizeof(float), stream, p, r);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;
 }

@@ -200,7 +200,8 @@ def test_linear_argument_errors(lib):
     # partial counts: one per 64 columns for few rows, one otherwise
     assert lib.eagle_linear_norm_parts(10, 4096, 4096) == 64
     assert lib.eagle_linear_norm_parts(16, 4096, 100) == 2
-    assert lib.eagle_linear_norm_parts(64, 4096, 4096) == 1
+    assert lib.eagle_linear_norm_parts(64, 4096, 4096) == 4
+    assert lib.eagle_linear_norm_parts(64, 4096, 1000) == 1
     # consumers reject a deferred norm without partials
     sw = lib.eagle_linear_swiglu
     assert sw(FAKE, 10, 256, FAKE, 0, 1e-5, FAKE, FAKE, 512, FAKE, FAKE, 1 << 30, None) == EINVAL
