@@ -637,6 +637,18 @@ int eagle_draft_prepare(const int32_t* frontier, int32_t kf, const int32_t* pool
 int eagle_embed(int32_t M, const int32_t* token, const void* embed, int32_t V, int32_t d,
                 float* out, int32_t* dev_status, hipStream_t stream);
 
+/*
+ * eagle_embed_deferred - eagle_embed with the RMSNorm that follows it
+ * deferred to the next product (see "Deferred RMSNorm" above): out[m] =
+ * embed[token[m]] as f32 ([M][d]), xg_out[m] = bf16(out[m] * gamma) ([M][d])
+ * and ssq_out[m] = sum_n out[m][n]^2 ([1][M] f32: one part).  d % 8 == 0;
+ * embed, gamma, out and xg_out 16-byte aligned.  A token outside [0, V) sets
+ * EAGLE_DEV_BAD_TOKEN and reads row 0.
+ */
+int eagle_embed_deferred(int32_t M, const int32_t* token, const void* embed, int32_t V,
+                         int32_t d, const float* gamma, float* out, void* xg_out, float* ssq_out,
+                         int32_t* dev_status, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,7 @@ _PROTOS = {
     "eagle_draft_prepare": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P,
                                    _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P]),
     "eagle_embed": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "eagle_embed_deferred": (_I32, [_I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "eagle_accept_q_workspace": (_SZ, [_I32, _I32]),
     "eagle_accept_q": (_I32, [_I32, _P, _P, _P, _P, _I32, _F32, _P, _I32, _P, _P, _P, _P, _SZ, _P,
                               _P]),
@@ -504,3 +505,19 @@ def eagle_embed(token, embed, out=None, dev_status=None):
     _check("eagle_embed", lib().eagle_embed(M, _ptr(token), _ptr(embed), V, d, _ptr(out),
                                             _ptr(dev_status), _stream()))
     return out
+
+
+def eagle_embed_deferred(token, embed, gamma, out=None, xg_out=None, ssq_out=None,
+                         dev_status=None):
+    """out = f32 embed rows, xg = bf16(out * gamma), ssq [1][M] = row sums of
+    out^2 (the RMSNorm that follows, deferred)."""
+    M = token.shape[0]
+    V, d = embed.shape
+    dev = embed.device
+    out = torch.empty((M, d), dtype=torch.float32, device=dev) if out is None else out
+    xg_out = torch.empty((M, d), dtype=torch.bfloat16, device=dev) if xg_out is None else xg_out
+    ssq_out = torch.empty((1, M), dtype=torch.float32, device=dev) if ssq_out is None else ssq_out
+    _check("eagle_embed_deferred", lib().eagle_embed_deferred(
+        M, _ptr(token), _ptr(embed), V, d, _ptr(gamma), _ptr(out), _ptr(xg_out), _ptr(ssq_out),
+        _ptr(dev_status), _stream()))
+    return out, xg_out, ssq_out

@@ -561,6 +561,48 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
   }
 }
 
+// out[m] = float(embed[token[m]]) with the norm that follows deferred:
+// xg[m] = bf16(out[m] * gamma) and ssq[m] = sum_n out[m][n]^2 (one part).
+__global__ __launch_bounds__(256) void embed_deferred_kernel(
+    const int32_t* __restrict__ token, const bf16_t* __restrict__ embed, int V, int d,
+    const float* __restrict__ gamma, float* __restrict__ out, bf16_t* __restrict__ xg,
+    float* __restrict__ ssq, int32_t* __restrict__ status) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  int tok = token[m];
+  if (tok < 0 || tok >= V) {
+    if (threadIdx.x == 0) set_status(status, EAGLE_DEV_BAD_TOKEN);
+    tok = 0;
+  }
+  const bf16_t* e = embed + (size_t)tok * d;
+  float* o = out + (size_t)m * d;
+  bf16_t* x = xg + (size_t)m * d;
+  float ss = 0.f;
+  for (int n = threadIdx.x * 8; n < d; n += 256 * 8) {   // d % 8 == 0
+    const u32x4 b = *(const u32x4*)(e + n);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_bits_to_f32(b[j] & 0xffffu);
+      v[2 * j + 1] = bf16_bits_to_f32(b[j] >> 16);
+    }
+    *(f32x4*)(o + n) = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)(o + n + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    const f32x4 g0 = *(const f32x4*)(gamma + n);
+    const f32x4 g1 = *(const f32x4*)(gamma + n + 4);
+    *(u32x4*)(x + n) = u32x4{pack_bf16x2(v[0] * g0[0], v[1] * g0[1]),
+                             pack_bf16x2(v[2] * g0[2], v[3] * g0[3]),
+                             pack_bf16x2(v[4] * g1[0], v[5] * g1[1]),
+                             pack_bf16x2(v[6] * g1[2], v[7] * g1[3])};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(v[j], v[j], ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) ssq[m] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
 // ---------------------------------------------------------------- few rows
 //
 // Projections of M <= 16 activation rows (the draft rounds) run as ONE kernel
@@ -1272,6 +1314,22 @@ extern "C" int eagle_draft_prepare(const int32_t* frontier, int32_t kf, const in
                      pool_token, pool_parent, pool_depth, pool_n, slot_of_pool, slot_base,
                      slot_cap, slot_parent, slot_mask, words, row_token, row_depth, row_slot,
                      row_src, feat, root_feat, (const bf16_t*)embed, V, d, (bf16_t*)x_in,
+                     dev_status);
+  EAGLE_LAUNCH_CHECK();
+  return EAGLE_OK;
+}
+
+extern "C" int eagle_embed_deferred(int32_t M, const int32_t* token, const void* embed,
+                                    int32_t V, int32_t d, const float* gamma, float* out,
+                                    void* xg_out, float* ssq_out, int32_t* dev_status,
+                                    hipStream_t stream) {
+  EAGLE_REQUIRE(token && embed && gamma && out && xg_out && ssq_out && M >= 1 && V >= 1 && d >= 1,
+                EAGLE_EINVAL);
+  EAGLE_REQUIRE(d % 8 == 0, EAGLE_EUNSUPPORTED);
+  EAGLE_REQUIRE(aligned16(embed) && aligned16(gamma) && aligned16(out) && aligned16(xg_out),
+                EAGLE_EINVAL);
+  hipLaunchKernelGGL(eagle::embed_deferred_kernel, dim3(M), dim3(256), 0, stream, token,
+                     (const bf16_t*)embed, V, d, gamma, out, (bf16_t*)xg_out, ssq_out,
                      dev_status);
   EAGLE_LAUNCH_CHECK();
   return EAGLE_OK;

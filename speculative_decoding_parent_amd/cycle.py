@@ -100,6 +100,7 @@ class DraftVerifyCycle:
         self.vmask = torch.zeros((T, (T + 63) // 64), dtype=torch.int64, device=dev)
         self.vdepth = torch.zeros(T, **i32)
         self.vx = torch.zeros((T, d), **f32)
+        self.vssq = torch.zeros((1, T), **f32)     # the embedded rows' sums of squares
         self.vout = torch.zeros((T, d), **f32)
         self.tkt = torch.zeros((hkv, T, hd), **bf)
         self.tvt = torch.zeros((hkv, T, hd), **bf)
@@ -196,9 +197,10 @@ class DraftVerifyCycle:
                                  dev_status=self.status)
         _lib.eagle_build_tree_mask(self.node_parent, mask=self.vmask, depth=self.vdepth,
                                    dev_status=self.status)
-        _lib.eagle_embed(self.node_token, self.embed, out=self.vx, dev_status=self.status)
-        _lib.eagle_rmsnorm(self.vx, self.target["norm1"], w.rms_eps, out=self.n1[:T])
-        sz = self._layer(self.target, T, self.n1[:T], None, self.vx, self.node_depth, None,
+        _lib.eagle_embed_deferred(self.node_token, self.embed, self.target["norm1"], out=self.vx,
+                                  xg_out=self.n1[:T], ssq_out=self.vssq, dev_status=self.status)
+        sz = self._layer(self.target, T, self.n1[:T], (self.vssq, w.rms_eps), self.vx,
+                         self.node_depth, None,
                          self.tkc, self.tvc, self.tkt, self.tvt, T, self.vmask, self.vout, None,
                          self.target_norm)
         # sampling acceptance reads the logits; no top-k is needed (k = 0)

@@ -318,6 +318,33 @@ def test_draft_prepare_and_embed(dev):
     assert torch.equal(e, emb[[7, 8, 499]].float())
 
 
+@pytest.mark.parametrize("M,d", [(64, 4096), (3, 256), (1, 8)])
+def test_embed_deferred(dev, M, d):
+    """Embedding rows with the next RMSNorm deferred: out exact, xg the bf16
+    rounding of out * gamma, ssq the row sums of squares; a bad token reads
+    row 0 and sets the status."""
+    g = inputs.rng(716, M, d)
+    V = 500
+    emb = inputs.normal(g, (V, d))
+    gamma = inputs.normal(g, (d,), dtype=torch.float32)
+    tok = torch.from_numpy(g.integers(0, V, M).astype(np.int32))
+    if M > 1:
+        tok[1] = V + 3
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    print(f"embed deferred M={M} d={d}", flush=True)
+    out, xg, ssq = _lib.eagle_embed_deferred(tok.to(dev), emb.to(dev), gamma.to(dev),
+                                             dev_status=status)
+    torch.cuda.synchronize()
+    rows = tok.clone().long()
+    rows[(rows < 0) | (rows >= V)] = 0
+    x = emb[rows].double()
+    assert torch.equal(out.cpu(), emb[rows].float())
+    want_xg = (emb[rows].float() * gamma).to(torch.bfloat16)
+    assert torch.equal(xg.cpu(), want_xg)
+    np.testing.assert_allclose(ssq.cpu().numpy()[0], (x * x).sum(1).numpy(), rtol=1e-5)
+    assert int(status.item()) == (_lib.DEV_BAD_TOKEN if M > 1 else 0)
+
+
 def layer_case(dev, w, seed, n, Tk, slots, slot_par):
     """One decoder layer on n rows at the given slots vs the oracle."""
     ci = inputs.cycle_inputs(w)
