@@ -416,6 +416,26 @@ int eagle_path_slots(const int32_t* path, const int32_t* n_accepted, int32_t max
                      int32_t* n_rows_minus_one, int32_t* dev_status, hipStream_t stream);
 
 /*
+ * eagle_kv_commit_pair - both commits of a cycle in one launch, for one layer
+ * each: eagle_kv_commit of the target's tree rows (rows = path, n_accepted)
+ * and eagle_kv_commit of the draft's rows of the same nodes, with those rows
+ * found as eagle_path_slots finds them (path[0 .. max_path), node_pool_idx
+ * [T], slot_of_pool [pool_cap], the draft's n_slots = d_src_rows).  Both
+ * caches take the rows at position L and share Hkv, hd and dt; sources and
+ * caches are [Hkv][ld][hd] (ld = *_ld_src, *_ld_cache rows).  max_path <=
+ * max_rows <= 256.  Status codes as for the two calls it replaces.
+ */
+int eagle_kv_commit_pair(const void* t_src_k, const void* t_src_v, int32_t t_ld_src,
+                         int32_t t_src_rows, void* t_cache_k, void* t_cache_v,
+                         int64_t t_ld_cache, const void* d_src_k, const void* d_src_v,
+                         int32_t d_ld_src, int32_t d_src_rows, void* d_cache_k, void* d_cache_v,
+                         int64_t d_ld_cache, int64_t L, const int32_t* path,
+                         const int32_t* n_accepted, int32_t max_rows,
+                         const int32_t* node_pool_idx, int32_t T, const int32_t* slot_of_pool,
+                         int32_t pool_cap, int32_t max_path, int32_t Hkv, int32_t hd,
+                         eagle_dtype dt, int32_t* dev_status, hipStream_t stream);
+
+/*
  * eagle_accept_q - speculative sampling over the tree with the draft's own
  * distribution instead of a point mass.
  *

@@ -77,6 +77,9 @@ _PROTOS = {
     "eagle_fuse3": (_I32, [_P, _P, _P, _I32, _I32, _P, _I32, _P, ctypes.c_int, _P, _SZ, _P]),
     "eagle_gate_children": (_I32, [_P, _I32, _I32, _F32, _I32, _P, _P, _P, _P]),
     "eagle_path_slots": (_I32, [_P, _P, _I32, _P, _I32, _P, _I32, _I32, _P, _P, _P, _P]),
+    "eagle_kv_commit_pair": (_I32, [_P, _P, _I32, _I32, _P, _P, _I64, _P, _P, _I32, _I32, _P, _P,
+                                    _I64, _I64, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32,
+                                    _I32, ctypes.c_int, _P, _P]),
     "eagle_kv_commit": (_I32, [_P, _P, _I32, _I32, _I64, _P, _P, _I32, _P, _P, _I64, _I64, _I64, _I32,
                                _I32, _I32, ctypes.c_int, _P, _P]),
 }
@@ -275,6 +278,23 @@ def eagle_path_slots(path, n_accepted, node_pool_idx, slot_of_pool, n_slots, slo
         _ptr(slot_of_pool), slot_of_pool.shape[0], n_slots, _ptr(slot_rows), _ptr(n_rows_minus_one),
         _ptr(dev_status), _stream()))
     return slot_rows, n_rows_minus_one
+
+
+def eagle_kv_commit_pair(t_k, t_v, t_kc, t_vc, d_k, d_v, d_kc, d_vc, L, path, n_accepted,
+                         node_pool_idx, slot_of_pool, max_path, dev_status=None):
+    """eagle_kv_commit of the target's rows path[0 .. n) and of the draft's
+    rows of the same nodes (eagle_path_slots' rule over path[:max_path]) in
+    one launch; every tensor is [Hkv][rows][hd] with contiguous rows."""
+    Hkv, _, hd = t_k.shape
+    for t in (t_k, t_v, t_kc, t_vc, d_k, d_v, d_kc, d_vc):
+        if t.dim() != 3 or t.shape[0] != Hkv or t.shape[2] != hd or not t.is_contiguous():
+            raise ValueError("sources and caches need contiguous [Hkv][rows][hd] tensors")
+    _check("eagle_kv_commit_pair", lib().eagle_kv_commit_pair(
+        _ptr(t_k), _ptr(t_v), t_k.shape[1], t_k.shape[1], _ptr(t_kc), _ptr(t_vc), t_kc.shape[1],
+        _ptr(d_k), _ptr(d_v), d_k.shape[1], d_k.shape[1], _ptr(d_kc), _ptr(d_vc), d_kc.shape[1],
+        L, _ptr(path), _ptr(n_accepted), path.shape[0], _ptr(node_pool_idx), node_pool_idx.shape[0],
+        _ptr(slot_of_pool), slot_of_pool.shape[0], max_path, Hkv, hd, _dt(t_k), _ptr(dev_status),
+        _stream()))
 
 
 def _norm_args(in_norm):

@@ -218,13 +218,10 @@ class DraftVerifyCycle:
         nodes, both appended at cache position L; every other candidate's rows
         are dropped ("Support Eagle-3 Speculative Decoding in llama.cpp", the
         reply on the draft's context).  Counts are read on the device."""
-        _lib.eagle_kv_commit(self.tkt, self.tvt, self.path, self.tkc, self.tvc, self.L,
-                             n_accepted=self.n_accepted, dev_status=self.status)
-        _lib.eagle_path_slots(self.path[:self.R + 1], self.n_accepted, self.node_pool_idx,
-                              self.slot_of_pool, self.S, slot_rows=self.draft_rows,
-                              n_rows_minus_one=self.draft_n, dev_status=self.status)
-        _lib.eagle_kv_commit(self.dkt, self.dvt, self.draft_rows, self.dkc, self.dvc, self.L,
-                             n_accepted=self.draft_n, dev_status=self.status)
+        _lib.eagle_kv_commit_pair(self.tkt, self.tvt, self.tkc, self.tvc, self.dkt, self.dvt,
+                                  self.dkc, self.dvc, self.L, self.path,
+                                  self.n_accepted, self.node_pool_idx, self.slot_of_pool,
+                                  self.R + 1, dev_status=self.status)
 
     def enqueue(self):
         """Enqueue one whole cycle on the current stream."""

@@ -126,3 +126,47 @@ def test_counts_and_status(dev):
     rk, rv = oracle.kv_commit(bits(sk), bits(sv), [0, 4], 2, bits(ck), bits(cv), L)
     rk[:, :, L + 3], rv[:, :, L + 3] = bits(sk)[:, :, 9], bits(sv)[:, :, 9]
     assert np.array_equal(bits(gk), rk) and np.array_equal(bits(gv), rv)
+
+
+@pytest.mark.parametrize("case", ["leaf_last", "all_expanded", "bad_node"])
+def test_pair_matches_separate_calls(dev, case):
+    """eagle_kv_commit_pair against eagle_kv_commit (target rows = path),
+    eagle_path_slots and eagle_kv_commit (draft rows): caches byte for byte,
+    the same status."""
+    g = inputs.rng(720, len(case))
+    hkv, hd, T, S, L, R = 8, 128, 64, 51, 100, 6
+    tk, tv = (inputs.normal(g, (hkv, T, hd)) for _ in range(2))
+    dk, dv = (inputs.normal(g, (hkv, S, hd)) for _ in range(2))
+    tkc, tvc = (inputs.normal(g, (hkv, L + T, hd)) for _ in range(2))
+    dkc, dvc = (inputs.normal(g, (hkv, L + T, hd)) for _ in range(2))
+    pool_cap = 600
+    node_pool_idx = torch.from_numpy(g.permutation(pool_cap)[:T].astype(np.int32))
+    slot_of_pool = torch.full((pool_cap,), -1, dtype=torch.int32)
+    nodes = [0, 5, 9, 17, 30, 41, 55]                     # a root path of 7 nodes
+    for j, nd in enumerate(nodes):
+        slot_of_pool[node_pool_idx[nd]] = 3 * j + 1
+    if case == "leaf_last":
+        slot_of_pool[node_pool_idx[nodes[-1]]] = -1      # the last node was never expanded
+    path = torch.full((T,), -1, dtype=torch.int32)
+    path[:len(nodes)] = torch.tensor(nodes, dtype=torch.int32)
+    if case == "bad_node":
+        path[3] = T + 2
+    n_acc = torch.tensor([len(nodes) - 1], dtype=torch.int32)
+    d = lambda t: t.clone().to(dev)
+    st_a = torch.zeros(1, dtype=torch.int32, device=dev)
+    a = [d(t) for t in (tkc, tvc, dkc, dvc)]
+    print(f"kv commit pair {case}", flush=True)
+    _lib.eagle_kv_commit(d(tk), d(tv), d(path), a[0], a[1], L, n_accepted=d(n_acc), dev_status=st_a)
+    rows, n_m1 = _lib.eagle_path_slots(d(path[:R + 1]), d(n_acc), d(node_pool_idx),
+                                       d(slot_of_pool), S, dev_status=st_a)
+    _lib.eagle_kv_commit(d(dk), d(dv), rows, a[2], a[3], L, n_accepted=n_m1, dev_status=st_a)
+    st_b = torch.zeros(1, dtype=torch.int32, device=dev)
+    b = [d(t) for t in (tkc, tvc, dkc, dvc)]
+    _lib.eagle_kv_commit_pair(d(tk), d(tv), b[0], b[1], d(dk), d(dv), b[2], b[3], L, d(path),
+                              d(n_acc), d(node_pool_idx), d(slot_of_pool), R + 1, dev_status=st_b)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert np.array_equal(bits(x), bits(y))
+    assert int(st_a.item()) == int(st_b.item())
+    if case != "bad_node":
+        assert int(st_b.item()) == 0
