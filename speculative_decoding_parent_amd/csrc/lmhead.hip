@@ -259,12 +259,15 @@ __global__ __launch_bounds__(256, (kLmMT >= 8 || NT >= 16 ? 1 : 2)) void lmhead_
       for (int j = 0; j < 4; ++j)
         if (v0 + mt * 16 + 4 * g + j < V) m = fmaxf(m, acc[mt][nt][j]);
     m = rows_max(m);
+    // exp(l - m) as the hardware base-2 exponential of (l - m) log2(e)
+    // (about 1e-6 relative: far below the bf16 rounding of the logits)
     float s = 0.f;
 #pragma unroll
     for (int mt = 0; mt < kLmMT; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (v0 + mt * 16 + 4 * g + j < V) s += expf(acc[mt][nt][j] - m);
+        if (v0 + mt * 16 + 4 * g + j < V)
+          s += __builtin_amdgcn_exp2f((acc[mt][nt][j] - m) * 1.4426950408889634f);
     s = rows_sum(s);
     if (g == 0) {
       if (block_lists) ls[wave * TP + t] = make_float2(m, s);
