@@ -933,6 +933,13 @@ static SkPlan sk_plan(int mode, int M, int K, int N, int heads, int hd) {
   const int nk = K / kWsKG;
   int S = 1;
   while (S < kSkMaxS && pl.nblk * S < 256 && 2 * S <= nk / 4) S *= 2;
+  // k ranges of at most 8 steps (two per wave, all in flight at once) when
+  // one round of workgroups would otherwise hold more, for K <= 8192: the
+  // draft's fuse product (K = 8192, 64 column blocks) then runs 512
+  // workgroups, two per CU, in 17 instead of 20 us; longer K keeps fewer,
+  // longer ranges (down: 25 against 24 us)
+  if (pl.nblk * S <= 256 && nk <= 64)
+    while (S < kSkMaxS && nk / S > 8) S *= 2;
   pl.S = S;
   pl.part_off = kSkCounterBytes;
   pl.total = pl.S > 1
