@@ -52,7 +52,11 @@ def check(ids, logp, lse, lg, f, W, k, exact=False):
                                      (10, 512, 20000, 16), (64, 256, 9000, 17),
                                      (16, 256, 70000, 1),
                                      # 256 lists of 16 (one-pass merge) and 257 (two-pass merge)
-                                     (4, 128, 131072, 16), (4, 128, 131073, 16)])
+                                     (4, 128, 131072, 16), (4, 128, 131073, 16),
+                                     # ragged last workgroups: scalar (V odd) and 16-byte
+                                     # logits stores
+                                     (10, 256, 99999, 10), (64, 256, 100000, 10),
+                                     (33, 128, 128256, 12)])
 def test_bf16_random(dev, T, d, V, k):
     g = inputs.rng(400, T, V)
     f = inputs.normal(g, (T, d))
@@ -81,7 +85,8 @@ def test_exact_inputs_with_planted_ties(dev, dt):
     assert np.array_equal(lg.astype(np.float64), oracle.lm_head_logits(f, W))
 
 
-@pytest.mark.parametrize("T,d,V", [(64, 512, 5000), (10, 256, 3001), (1, 128, 300)])
+@pytest.mark.parametrize("T,d,V", [(64, 512, 5000), (10, 256, 3001), (1, 128, 300),
+                                   (64, 128, 99999)])
 def test_lse_and_logits_only(dev, T, d, V):
     """k = 0: no top-k, lse and logits as with k > 0."""
     g = inputs.rng(404, T, V)
