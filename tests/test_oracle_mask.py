@@ -6,7 +6,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle.mask import build_tree_mask, mask_bits, mask_popcount
+from oracle.mask import build_tree_mask, mask_bits, mask_popcount, validate_parents
 from speculative_decoding_parent_amd import inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -101,6 +101,19 @@ def test_forest_allowed_and_validation():
         build_tree_mask(np.array([0, -1]))
     with pytest.raises(ValueError):
         build_tree_mask(np.array([-1, 0, 5]))
+
+
+def test_validate_parents_exhaustive_small():
+    """validate_parents accepts exactly the arrays whose every entry is -1 or
+    an earlier index: every array of length 3 over {-2, ..., 2} (125 of them),
+    by brute force."""
+    for par in itertools.product(range(-2, 3), repeat=3):
+        ok = all(p == -1 or 0 <= p < i for i, p in enumerate(par))
+        if ok:
+            validate_parents(np.array(par))
+        else:
+            with pytest.raises(ValueError):
+                validate_parents(np.array(par))
 
 
 def test_planted_mistake_is_caught():
